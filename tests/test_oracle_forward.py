@@ -1,0 +1,126 @@
+"""Pins for the oracle's forward pass (blog post "What it is selling": W13 ->
+SwiGLU -> W2 -> score-weighted combine).
+
+Each check would catch a different plausible mistake: the dense-MLP identity
+against torch's float64 matmul (a transposed weight, gate/up swapped, a wrong
+activation), identical experts (wrong expert indexing), linearity in the
+scores and the +0 result for zero scores (score applied twice or not at
+all), token and expert relabelling (wrong gather), and a hand-derived tiny
+example stored under tests/golden/.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_routed_dispatch_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def torch_dense_mlp(x, w1, w3, w2):
+    """Library reference: dense SwiGLU MLP in float64 with torch CPU ops."""
+    x = torch.from_numpy(x).double()
+    g = x @ torch.from_numpy(w1).double().T
+    u = x @ torch.from_numpy(w3).double().T
+    return (torch.nn.functional.silu(g) * u) @ torch.from_numpy(w2).double().T
+
+
+def f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_dense_mlp_identity(orc):
+    # E = 1, k = 1, s = 1: the layer is the dense SwiGLU MLP.
+    inp = inputs.generate(T=37, d=96, I=40, E=1, k=1, seed=3)
+    scores = np.ones((inp.T, 1), np.float32)
+    y = orc.forward_tokens(inp.x, inp.ids, scores, inp.w13, inp.w2)
+    w13 = f32(inp.w13[0])
+    ref = torch_dense_mlp(f32(inp.x), w13[:40], w13[40:], f32(inp.w2[0])).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_identical_experts_reduce_to_dense(orc):
+    inp = inputs.generate(T=20, d=64, I=32, E=6, k=3, seed=4)
+    w13 = np.repeat(inp.w13[:1], 6, axis=0)
+    w2 = np.repeat(inp.w2[:1], 6, axis=0)
+    y = orc.forward_tokens(inp.x, inp.ids, inp.scores, w13, w2)       # sum_j s = 1 per token
+    w13f = f32(inp.w13[0])
+    ref = torch_dense_mlp(f32(inp.x), w13f[:32], w13f[32:], f32(inp.w2[0])).numpy()
+    ref *= inp.scores.astype(np.float64).sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_expert_mix_matches_per_expert_dense(orc):
+    # y_t = sum_j s_tj * dense_{e_tj}(x_t), each dense MLP from torch.
+    inp = inputs.generate(T=24, d=64, I=32, E=5, k=2, seed=5)
+    y = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    xf = f32(inp.x)
+    ref = np.zeros_like(y)
+    for e in range(inp.E):
+        w13f = f32(inp.w13[e])
+        de = torch_dense_mlp(xf, w13f[:32], w13f[32:], f32(inp.w2[e])).numpy()
+        mask = (inp.ids == e)
+        ref += (inp.scores.astype(np.float64) * mask).sum(axis=1, keepdims=True) * de
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_linear_in_scores_and_zero_scores(orc):
+    inp = inputs.generate(T=16, d=64, I=32, E=4, k=2, seed=6)
+    y1 = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    y2 = orc.forward_tokens(inp.x, inp.ids, inp.scores * np.float32(2.0), inp.w13, inp.w2)
+    np.testing.assert_array_equal(y2, 2.0 * y1)                       # exact: power of two
+    y0 = orc.forward_tokens(inp.x, inp.ids, np.zeros_like(inp.scores), inp.w13, inp.w2)
+    assert np.all(y0 == 0.0) and not np.any(np.signbit(y0))
+
+
+def test_token_permutation_and_expert_relabel(orc):
+    inp = inputs.generate(T=18, d=64, I=32, E=6, k=3, seed=7)
+    y = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    perm = np.random.default_rng(0).permutation(inp.T)
+    yp = orc.forward_tokens(inp.x[perm], inp.ids[perm], inp.scores[perm], inp.w13, inp.w2)
+    np.testing.assert_array_equal(yp, y[perm])
+    lab = np.random.default_rng(1).permutation(inp.E)                 # expert e is stored at lab[e]
+    w13 = np.empty_like(inp.w13); w13[lab] = inp.w13
+    w2 = np.empty_like(inp.w2); w2[lab] = inp.w2
+    yl = orc.forward_tokens(inp.x, lab[inp.ids].astype(np.int32), inp.scores, w13, w2)
+    np.testing.assert_array_equal(yl, y)
+
+
+def test_token_subset_equals_full(orc):
+    inp = inputs.generate(T=30, d=64, I=32, E=4, k=2, seed=8)
+    y = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    toks = np.array([29, 0, 7, 7, 13], np.int32)
+    ys = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
+    np.testing.assert_array_equal(ys, y[toks])
+
+
+def test_silu_closed_forms(orc):
+    # With d = I = 1 and W3 = W2 = 1: y = s * silu(w1 * x) * x; silu(0) = 0 and
+    # silu(z) -> z for large z, silu(z) -> 0 for very negative z.
+    def run(w1, x):
+        xb = inputs.to_bf16_bits(np.array([[x]], np.float32))
+        w13 = inputs.to_bf16_bits(np.array([[[w1], [1.0]]], np.float32))
+        w2 = inputs.to_bf16_bits(np.array([[[1.0]]], np.float32))
+        return orc.forward_tokens(xb, np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32),
+                                  w13, w2)[0, 0]
+    assert run(0.0, 3.0) == 0.0
+    assert abs(run(64.0, 1.0) - 64.0) < 1e-20
+    assert abs(run(-64.0, 1.0)) < 1e-25
+
+
+def test_golden_hand_example(orc):
+    with open(os.path.join(GOLDEN, "forward_tiny.json")) as f:
+        g = json.load(f)
+    x = inputs.to_bf16_bits(np.array(g["x"], np.float32))
+    w13 = inputs.to_bf16_bits(np.array(g["w13"], np.float32))
+    w2 = inputs.to_bf16_bits(np.array(g["w2"], np.float32))
+    ids = np.array(g["ids"], np.int32)
+    scores = np.array(g["scores"], np.float32)
+    assert np.array_equal(f32(x), np.array(g["x"], np.float32))      # fixture values are BF16-exact
+    y = orc.forward_tokens(x, ids, scores, w13, w2)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=1e-15, atol=1e-15)
+    assert math.isclose(g["silu_1"], 1.0 / (1.0 + math.exp(-1.0)), rel_tol=1e-15)
