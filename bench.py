@@ -1,0 +1,243 @@
+"""Benchmark of the routed expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one call of the layer's hot path on one batch of seeded synthetic
+input already resident in HBM: for the forward workloads dispatch, W13 grouped
+GEMM with the SwiGLU epilogue, W2 grouped GEMM and the score-weighted combine;
+for "train" also the whole backward (router gradient, DGRAD, WGRAD, dX
+combine).  Timing uses HIP events on the stream the library launches on;
+per-kernel durations come from the library's own event pairs around each
+stage during the same timed region.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd TFLOP/s & tokens/s (1 MI355X), % MFMA peak; decode % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
+
+WORKLOADS = {
+    # name: (config in inputs.CONFIGS, training)
+    "prefill": ("prefill", False),
+    "tiny": ("tiny", False),
+    "train": ("train", True),
+    "decode1": ("decode1", False),
+    "decode32": ("decode32", False),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, srcs, units_per_launch: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash(srcs):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def oracle_threads():
+    import oracle
+    try:
+        return int(oracle.num_threads())
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, training: bool, target_s: float):
+    """The oracle as it stands, on a bounded token sample of the same batch."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    T, d, I, k = inp.T, inp.d, inp.I, inp.k
+    flop_per_token = 6.0 * k * I * d * (3.0 if training else 1.0)
+    n = min(T, 4)
+    rng = np.random.default_rng(123)
+    spent = 0.0
+    while True:
+        toks = np.sort(rng.choice(T, size=n, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
+        if training:
+            oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, toks=toks)
+        dt = time.perf_counter() - t0
+        spent += dt
+        if dt >= target_s * 0.5 or n >= T or spent > 3 * target_s:
+            break
+        n = min(T, max(n + 1, int(n * min(8.0, target_s / max(dt, 1e-3)))))
+    tflops = flop_per_token * n / dt / 1e12
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "cores": oracle_threads(),
+        "kind": "oracle",
+        "sample": "%d of %d tokens of the same batch, %s in the fp64 C oracle (token-major, "
+                  "OpenMP over tokens), %.1f s; flop counted as %d*k*I*d per token"
+                  % (n, T, "forward + backward" if training else "forward", dt,
+                     18 if training else 6),
+        "tokens_per_s": n / dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU; --gpus %d is not supported "
+              "(no collectives, no sharding)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mixture_experts_routed_dispatch_amd import inputs, moe
+    from tests.gpu_util import device_inputs
+
+    cfg_name, training = WORKLOADS[args.workload]
+    inp = inputs.generate_config(cfg_name, seed=0, with_dy=training)
+    T, d, I, E, k = inp.T, inp.d, inp.I, inp.E, inp.k
+    R = T * k
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, training=training)
+    stream = torch.cuda.current_stream()
+    sp = int(stream.cuda_stream)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
+    if training:
+        dx = torch.empty_like(y)
+        dw13 = torch.empty((E, 2 * I, d), dtype=torch.bfloat16, device="cuda")
+        dw2 = torch.empty((E, d, I), dtype=torch.bfloat16, device="cuda")
+        ds = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    w = moe.weights(t["w13"].data_ptr(), t["w2"].data_ptr())
+
+    def step():
+        moe.moe_forward(layer.plan, t["x"].data_ptr(), t["ids"].data_ptr(),
+                        t["scores"].data_ptr(), w, y.data_ptr(), sp)
+        if training:
+            moe.moe_backward(layer.plan, t["dy"].data_ptr(), t["x"].data_ptr(), w, dx.data_ptr(),
+                             dw13.data_ptr(), dw2.data_ptr(), ds.data_ptr(), sp)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    if flags:
+        raise SystemExit("device routing flags set: %d" % flags)
+
+    moe.moe_profile(layer.plan, True)
+    moe.moe_profile_read(layer.plan)           # drop anything recorded before
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    moe.moe_profile(layer.plan, False)
+    stages = moe.moe_profile_read(layer.plan)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+
+    fwd_flop = 6.0 * R * I * d
+    flop = fwd_flop * (3.0 if training else 1.0)
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    stage_us = {kname: 1e3 * ms / max(n, 1) for kname, (ms, n) in stages.items()}
+
+    # dominant kernel: the longest stage
+    dom = max(stage_us, key=stage_us.get)
+    gemm_flop = {"w13": 4.0 * R * I * d, "w2": 2.0 * R * I * d,
+                 "dgrad_w2": 2.0 * R * I * d, "wgrad_w2": 2.0 * R * I * d,
+                 "dgrad_w13": 4.0 * R * I * d, "wgrad_w13": 4.0 * R * I * d}
+    if dom in gemm_flop:
+        achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
+                "traffic": traffic_for("grouped_gemm_" + dom,
+                                       ["mixture_experts_routed_dispatch_amd/csrc/gemm_bf16.hip"], 1)}
+    else:
+        # HBM-bound stage: bytes it must move at least once
+        nbytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
+                  "dispatch": 8.0 * R + 4.0 * (E + 1) + 12.0 * R}.get(dom, float("nan"))
+        achieved = nbytes / (stage_us[dom] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                "algorithmic_per_launch": nbytes, "avg_launch_us": stage_us[dom], "traffic": None}
+    gemm_us = sum(stage_us.get(s, 0.0) for s in gemm_flop)
+    gemm_tflops = sum(gemm_flop[s] for s in gemm_flop if s in stage_us) / (gemm_us * 1e-6) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded numpy draws, x ~ N(0,1), W ~ N(0,1/fan_in) in BF16, "
+                + ("Zipf(1.2) top-k routing with 8 forced-empty experts, dY ~ N(0,1)"
+                   if cfg_name == "train" else "uniform distinct top-k routing")
+                + ", softmax-of-normal scores",
+        "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d BF16 %s" % (
+            cfg_name, T, d, I, E, k, "forward+backward" if training else "forward"),
+            "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
+            "flop_per_step": flop},
+        "tokens_per_s": T / (ms_step * 1e-3),
+        "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
+        "gemm_tflops": gemm_tflops,
+        "gemm_mfma_frac": gemm_tflops / PEAK_BF16_TFLOPS,
+        "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
+        "wall_ms_per_step": 1e3 * wall / args.steps,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, training, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    layer.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

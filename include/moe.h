@@ -1,0 +1,203 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts expert layer.
+ *
+ * The layer ("Dist-MoE" blog post, section "What it is selling": caller routing
+ * gives x, top-k expert ids and scores; then route on GPU -> W13 -> SwiGLU ->
+ * W2 -> combine; forward is FPROP, backward splits into DGRAD and WGRAD)
+ * computes, for every token t,
+ *
+ *     y[t] = sum_{j<k} scores[t][j] * W2_e ( silu(W1_e x[t]) * W3_e x[t] ),
+ *            e = ids[t][j],  silu(z) = z / (1 + exp(-z)),
+ *
+ * on one GPU.  There is no expert parallelism and no collective.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, row-major, contiguous device buffers owned by the
+ *     caller.  BF16 is the IEEE-754 binary32 upper half (uint16 bit pattern).
+ *   - x, y, dy, dx: BF16 [T, d].  ids: int32 [T, k], distinct values in [0, E)
+ *     per row (nvfp4moe README, "MoE layer").  scores, dscores: float32 [T, k].
+ *   - w13: [E, 2I, d], rows [0, I) are the gate projection W1, rows [I, 2I)
+ *     the up projection W3; w2: [E, d, I].  Each expert matrix is used as
+ *     out = A * B^T with B stored [N, K] (nvfp4moe README, "Dense GEMM" and
+ *     "Grouped GEMM").
+ *   - `stream` is a hipStream_t (NULL means the null stream).  Every call that
+ *     takes a stream only enqueues work on it: it never allocates device
+ *     memory, never synchronises and never reads device data on the host, so
+ *     it can be captured in a HIP graph (nvfp4moe README, "MoE layer": a
+ *     warmed plan does not allocate and can be graph-captured).
+ *   - A plan is host-side state plus a caller-allocated workspace.  It is not
+ *     reentrant: use one plan per concurrently running stream (nvfp4moe README,
+ *     "MoE layer"; blog post, "Caveats", item 6).
+ *   - Errors found on the host are returned before anything is enqueued.
+ *     Routing errors found on the device (an id outside [0, E) or repeated in
+ *     a row) set a sticky flag read by moe_get_status; outputs of that call are
+ *     then unspecified.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_plan_s* moe_plan_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,  /* NULL pointer, bad size, bad enum */
+    MOE_ERR_UNSUPPORTED = -2,  /* shape or mode outside the supported limits */
+    MOE_ERR_WORKSPACE = -3,    /* no workspace bound, or the bound one is too small */
+    MOE_ERR_STATE = -4,        /* e.g. backward without a preceding training forward */
+    MOE_ERR_HIP = -5,          /* a HIP runtime call or kernel launch failed */
+    MOE_ERR_ROUTING = -6       /* device-detected invalid routing (moe_get_status) */
+} moe_status_t;
+
+typedef enum {
+    MOE_BF16 = 0,              /* BF16 operands, FP32 accumulate (blog post: "BF16 Standard") */
+    MOE_MXFP8_E4M3 = 1         /* OCP MXFP8: E4M3 elements, E8M0 scale per 32 along K */
+} moe_precision_t;
+
+/* path selection (moe_config_t.path) */
+#define MOE_PATH_AUTO 0        /* decode kernels when T*k <= 256 and inference, else prefill */
+#define MOE_PATH_PREFILL 1     /* grouped-GEMM path */
+#define MOE_PATH_DECODE 2      /* weight-streaming path; requires T*k <= 256, inference, BF16 */
+
+/* device status bits (moe_get_status) */
+#define MOE_DEV_ID_OUT_OF_RANGE 1
+#define MOE_DEV_ID_DUPLICATE 2
+
+typedef struct {
+    int32_t T;          /* physical token count, fixed per plan (blog post, "Caveats", item 2) */
+    int32_t d;          /* hidden size; multiple of 64 */
+    int32_t I;          /* expert intermediate size; multiple of 64 */
+    int32_t E;          /* experts, 1..256 (nvfp4moe README, "Limits") */
+    int32_t k;          /* experts per token, 1..min(E, 32) */
+    int32_t precision;  /* moe_precision_t */
+    int32_t training;   /* 1: forward saves what moe_backward needs (BF16 only) */
+    int32_t path;       /* MOE_PATH_* */
+} moe_config_t;
+
+typedef struct {
+    const void* w13;          /* BF16 [E, 2I, d], or E4M3 codes (uint8) [E, 2I, d] */
+    const void* w2;           /* BF16 [E, d, I],  or E4M3 codes (uint8) [E, d, I]  */
+    const uint8_t* w13_scale; /* MXFP8 only: E8M0 [E, 2I, d/32]; NULL for BF16 */
+    const uint8_t* w2_scale;  /* MXFP8 only: E8M0 [E, d, I/32];  NULL for BF16 */
+} moe_weights_t;
+
+/* Validate cfg against the limits (K = d and I multiples of 64, at most 256
+ * experts, at most 131072 routed rows T*k; nvfp4moe README, "Limits"), choose
+ * the kernels and lay out the workspace.  Host only: touches no device.
+ * Returns MOE_ERR_UNSUPPORTED for MXFP8 with training = 1 and for shapes
+ * outside the limits, MOE_ERR_INVALID_ARG for NULL or non-positive sizes.
+ * On success *out owns host memory released by moe_plan_destroy. */
+moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out);
+
+/* Bytes of device workspace the plan needs (the analogue of planning memory
+ * before creating a context; blog post, "Caveats", item 7).  0 on NULL. */
+size_t moe_workspace_bytes(moe_plan_t plan);
+
+/* Give the plan a device buffer of at least moe_workspace_bytes bytes,
+ * 256-byte aligned; the caller keeps ownership and must keep it alive while
+ * the plan is used.  Clears the device status word (synchronously, with a
+ * plain memset: call it outside graph capture).  Rebinding forgets the saved
+ * forward state. */
+moe_status_t moe_bind_workspace(moe_plan_t plan, void* dptr, size_t bytes);
+
+/* Release the host plan (not the caller's workspace).  NULL is accepted. */
+moe_status_t moe_plan_destroy(moe_plan_t plan);
+
+/* Deterministic dispatch (nvfp4moe README, "Grouped GEMM" and "Training"):
+ *   m_indptr int32 [E+1]: exclusive scan of per-expert row counts (empty
+ *            experts valid, m_indptr[E] = T*k);
+ *   gather   int32 [T*k]: token of each expert-major routed row; rows of one
+ *            expert are in ascending token order;
+ *   slots    int32 [T, k]: routed row that holds (t, j);
+ *   probs    float [T*k]: scores[t][j] moved to its routed row.
+ * Bit-exact and run-to-run identical.  Uses the plan's workspace. */
+moe_status_t moe_dispatch(moe_plan_t plan, const int32_t* ids, const float* scores,
+                          int32_t* m_indptr, int32_t* gather, int32_t* slots, float* probs,
+                          void* stream);
+
+/* OCP MXFP8 conversion of `rows` BF16 rows of length K (a multiple of 32):
+ * per block of 32 consecutive elements the E8M0 byte is
+ * clamp(floor(log2(max|v|)) - 8 + 127, 0, 254) (0 for an all-zero block) and
+ * each element is E4M3(v / 2^(byte - 127)), nearest-even, clamped to +-448.
+ * codes uint8 [rows, K]; scales uint8 [rows, K/32].  Needs no plan. */
+moe_status_t moe_quantize_mxfp8(const void* v_bf16, int64_t rows, int32_t K,
+                                uint8_t* codes, uint8_t* scales, void* stream);
+
+/* Prepare BF16 weights for the MXFP8 pipeline (blog post, "What it is
+ * selling": MXFP8 accepts prepared weights): quantize w13 [E,2I,d] and
+ * w2 [E,d,I] along their K (last) dimension with moe_quantize_mxfp8's rule.
+ * Outputs are caller-owned: w13_q [E,2I,d], w13_s [E,2I,d/32], w2_q [E,d,I],
+ * w2_s [E,d,I/32].  Meant to run outside any timed region. */
+moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const void* w2_bf16,
+                                 uint8_t* w13_q, uint8_t* w13_s, uint8_t* w2_q, uint8_t* w2_s,
+                                 void* stream);
+
+/* Forward (FPROP): dispatch, [MXFP8: quantize x], grouped W13 GEMM with the
+ * SwiGLU epilogue, [MXFP8: re-quantize the SwiGLU output], grouped W2 GEMM,
+ * score-weighted combine in FP32 with j ascending from +0.0 and one rounding
+ * to BF16 (nvfp4moe README, "MoE layer": the timed path).  y is BF16 [T, d].
+ * With cfg.training = 1 the workspace keeps the dispatch, the W13 outputs and
+ * the W2 outputs for moe_backward; a later forward overwrites them. */
+moe_status_t moe_forward(moe_plan_t plan, const void* x, const int32_t* ids, const float* scores,
+                         const moe_weights_t* w, void* y, void* stream);
+
+/* Backward (DGRAD + WGRAD + router gradient; blog post, "What it is selling";
+ * nvfp4moe README, "Training") of the most recent training forward on this
+ * plan, which must have used the same x, ids, scores and weights (unchanged):
+ *   dx      BF16 [T, d]   = dL/dx
+ *   dw13    BF16 [E,2I,d] = dL/dW13, overwritten (+0.0 for experts with no row)
+ *   dw2     BF16 [E,d,I]  = dL/dW2, overwritten
+ *   dscores f32  [T, k]   = dL/dscores[t][j] = <dy[t], expert output of (t, j)>
+ * Returns MOE_ERR_STATE if no training forward ran since the workspace was
+ * bound.  BF16 plans only. */
+moe_status_t moe_backward(moe_plan_t plan, const void* dy, const void* x, const moe_weights_t* w,
+                          void* dx, void* dw13, void* dw2, float* dscores, void* stream);
+
+/* Synchronise `stream`, copy the sticky device status word (MOE_DEV_* bits)
+ * into *device_flags, and clear it when `clear` is non-zero.  Returns
+ * MOE_ERR_ROUTING when a bit is set, MOE_OK otherwise. */
+moe_status_t moe_get_status(moe_plan_t plan, int32_t* device_flags, int32_t clear, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* Kernel stages of moe_forward / moe_backward, in launch order. */
+#define MOE_STAGE_DISPATCH 0
+#define MOE_STAGE_QUANT_X 1
+#define MOE_STAGE_W13 2
+#define MOE_STAGE_W2 3
+#define MOE_STAGE_COMBINE 4
+#define MOE_STAGE_SCORE_GRAD 5
+#define MOE_STAGE_DGRAD_W2 6
+#define MOE_STAGE_WGRAD_W2 7
+#define MOE_STAGE_DGRAD_W13 8
+#define MOE_STAGE_WGRAD_W13 9
+#define MOE_STAGE_DX_COMBINE 10
+#define MOE_STAGE_DECODE_W13 11
+#define MOE_STAGE_DECODE_W2 12
+#define MOE_STAGE_COUNT 13
+
+/* Per-stage timing with HIP events, for measurement only.  While enabled,
+ * moe_forward and moe_backward record a pair of HIP events around each kernel
+ * stage on the caller's stream (events are created by the library on first
+ * use and kept by the plan; at most 4096 pairs are held, later stages of a
+ * full buffer are not recorded).  Do not enable it under graph capture.
+ * moe_profile(plan, 0) disables recording and keeps what was recorded. */
+moe_status_t moe_profile(moe_plan_t plan, int32_t enable);
+
+/* Wait for the recorded events, then write for each stage s < max_stages the
+ * summed duration in milliseconds (total_ms[s]) and the number of recorded
+ * launches (count[s]); forget the recorded events. */
+moe_status_t moe_profile_read(moe_plan_t plan, float* total_ms, int32_t* count, int32_t max_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,120 @@
+// combine.hip -- score-weighted deterministic combine and its gradients on gfx950.
+//
+// nvfp4moe README, "MoE layer": the timed path ends with probability weighting
+// and a deterministic combine; "Training": router gradients.  Both are
+// HBM-streaming gathers: each thread owns 8 consecutive features (one 16-byte
+// load per routed row) and sums the k rows of its token in FP32 with j
+// ascending from +0.0, so the result does not depend on the launch shape.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ src,
+                                                           const int32_t* __restrict__ slots,
+                                                           const float* __restrict__ w, int T, int k,
+                                                           int d, uint16_t* __restrict__ y) {
+    const int t = blockIdx.y;
+    const int n = (blockIdx.x * kThreads + threadIdx.x) * 8;
+    if (n >= d) return;
+    float acc[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) acc[z] = 0.0f;
+    const int32_t* sl = slots + (size_t)t * k;
+    const float* wt = w ? w + (size_t)t * k : nullptr;
+    int j = 0;
+    for (; j + 4 <= k; j += 4) {       // four rows in flight per step; summation order unchanged
+        uint4 v[4];
+        float s[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v[u] = *reinterpret_cast<const uint4*>(src + (size_t)sl[j + u] * d + n);
+            s[u] = wt ? wt[j + u] : 1.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t ww[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                acc[2 * z] = __builtin_fmaf(s[u], bf16lo(ww[z]), acc[2 * z]);
+                acc[2 * z + 1] = __builtin_fmaf(s[u], bf16hi(ww[z]), acc[2 * z + 1]);
+            }
+        }
+    }
+    for (; j < k; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)sl[j] * d + n);
+        const float s = wt ? wt[j] : 1.0f;
+        const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int z = 0; z < 4; ++z) {
+            acc[2 * z] = __builtin_fmaf(s, bf16lo(ww[z]), acc[2 * z]);
+            acc[2 * z + 1] = __builtin_fmaf(s, bf16hi(ww[z]), acc[2 * z + 1]);
+        }
+    }
+    uint4 o;
+    o.x = pack_bf16(acc[0], acc[1]);
+    o.y = pack_bf16(acc[2], acc[3]);
+    o.z = pack_bf16(acc[4], acc[5]);
+    o.w = pack_bf16(acc[6], acc[7]);
+    *reinterpret_cast<uint4*>(y + (size_t)t * d + n) = o;
+}
+
+// ds[t][j] = <dy[t], o[slots[t][j]]>: one workgroup per token, fixed reduction tree.
+constexpr int kMaxK = 32;
+
+__global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __restrict__ dy,
+                                                              const uint16_t* __restrict__ o,
+                                                              const int32_t* __restrict__ slots,
+                                                              int T, int k, int d,
+                                                              float* __restrict__ ds) {
+    __shared__ float part[kThreads / MOE_WAVE][kMaxK];
+    const int t = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int32_t* sl = slots + (size_t)t * k;
+    for (int j = 0; j < k; ++j) {
+        float acc = 0.0f;
+        const size_t r = (size_t)sl[j];
+        for (int n = threadIdx.x * 8; n < d; n += kThreads * 8) {
+            const uint4 a = *reinterpret_cast<const uint4*>(dy + (size_t)t * d + n);
+            const uint4 b = *reinterpret_cast<const uint4*>(o + r * d + n);
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                acc = __builtin_fmaf(bf16lo(aw[z]), bf16lo(bw[z]), acc);
+                acc = __builtin_fmaf(bf16hi(aw[z]), bf16hi(bw[z]), acc);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, MOE_WAVE);
+        if (lane == 0) part[wave][j] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < k) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kThreads / MOE_WAVE; ++w) s += part[w][threadIdx.x];
+        ds[(size_t)t * k + threadIdx.x] = s;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,
+                          int d, uint16_t* y, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const dim3 grid((d / 8 + kThreads - 1) / kThreads, T);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, src, slots, w, T, k, d, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_t* slots, int T,
+                             int k, int d, float* ds, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(score_grad_kernel, dim3(T), dim3(kThreads), 0, s, dy, o, slots, T, k, d, ds);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to libmoe).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Entries (t, j) handled by one dispatch workgroup.
+constexpr int kDispatchChunk = 2048;
+
+inline int dispatch_chunks(int64_t R) { return (int)((R + kDispatchChunk - 1) / kDispatchChunk); }
+
+// dispatch: hist is int32 [nchunks, E] scratch; status is the sticky flag word.
+hipError_t launch_dispatch(const int32_t* ids, const float* scores, int T, int k, int E,
+                           int32_t* hist, int32_t* m_indptr, int32_t* gather, int32_t* slots,
+                           float* probs, int32_t* status, hipStream_t s);
+
+enum GemmMode { FWD_W13 = 0, FWD_W2 = 1, DGRAD_W2 = 2, DGRAD_W13 = 3, WGRAD_W2 = 4, WGRAD_W13 = 5 };
+
+struct GemmArgs {
+    int T, d, I, E, k;
+    const int32_t* m_indptr;
+    const int32_t* gather;
+    const float* probs;
+    const uint16_t* x;    // [T, d]
+    const uint16_t* w13;  // [E, 2I, d]
+    const uint16_t* w2;   // [E, d, I]
+    const uint16_t* a;    // [R, I]   SwiGLU output
+    const uint16_t* h;    // [R, 2I]  saved gate/up pre-activations
+    const uint16_t* dy;   // [T, d]
+    const uint16_t* dh;   // [R, 2I]  gradient w.r.t. (gate, up)
+    uint16_t* out;        // mode output
+    uint16_t* out_h;      // FWD_W13 with save: h
+};
+
+hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
+
+// y[t] = sum_j w[t][j] * src[slots[t][j]] (w = NULL means weight 1), FP32, j ascending.
+hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,
+                          int d, uint16_t* y, hipStream_t s);
+// ds[t][j] = <dy[t], o[slots[t][j]]> in FP32.
+hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_t* slots, int T,
+                             int k, int d, float* ds, hipStream_t s);
+
+hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,351 @@
+// moe_api.cpp -- host side of libmoe: plan, validation, workspace layout and launch
+// sequencing behind the C ABI declared in include/moe.h.
+//
+// Nothing here reads device data or synchronises, except moe_bind_workspace
+// (clears the status word) and moe_get_status (reads it); every other entry
+// point only enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int64_t kMaxRoutedRows = 131072;   // nvfp4moe README, "Limits"
+constexpr int kMaxExperts = 256;             // nvfp4moe README, "Limits"
+constexpr int kMaxTopK = 32;
+constexpr size_t kMaxProfileRecords = 4096;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+}  // namespace
+
+struct moe_plan_s {
+    moe_config_t cfg;
+    int64_t R;
+    int nchunks;
+    bool decode;
+    // workspace offsets (bytes)
+    size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
+    size_t off_a, off_o, off_h, off_dh, off_dxp, off_xq, off_xs, off_aq, off_as;
+    size_t ws_bytes;
+    char* ws;
+    size_t ws_size;
+    int num_cu;
+    bool have_saved_forward;
+    // measurement-only event pairs around kernel stages (moe_profile)
+    struct ProfRec { int stage; hipEvent_t a, b; };
+    bool prof_on = false;
+    std::vector<hipEvent_t> ev_free;
+    std::vector<ProfRec> recs;
+
+    template <class T> T* at(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+
+    hipEvent_t take_event() {
+        hipEvent_t e = nullptr;
+        if (!ev_free.empty()) { e = ev_free.back(); ev_free.pop_back(); return e; }
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    // returns a record index, or -1 when not recording
+    int stage_begin(int stage, hipStream_t s) {
+        if (!prof_on || recs.size() >= kMaxProfileRecords) return -1;
+        ProfRec r{stage, take_event(), take_event()};
+        if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
+            if (r.a) ev_free.push_back(r.a);
+            if (r.b) ev_free.push_back(r.b);
+            return -1;
+        }
+        recs.push_back(r);
+        return (int)recs.size() - 1;
+    }
+    void stage_end(int idx, hipStream_t s) {
+        if (idx >= 0) (void)hipEventRecord(recs[(size_t)idx].b, s);
+    }
+    ~moe_plan_s() {
+        for (auto& r : recs) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+        for (auto e : ev_free) (void)hipEventDestroy(e);
+    }
+};
+
+namespace {
+// launch `fn` as one profiled stage
+template <class F>
+hipError_t staged(moe_plan_s* p, int stage, hipStream_t s, F&& fn) {
+    const int idx = p->stage_begin(stage, s);
+    const hipError_t e = fn();
+    p->stage_end(idx, s);
+    return e;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
+    if (!cfg || !out) return MOE_ERR_INVALID_ARG;
+    *out = nullptr;
+    const moe_config_t c = *cfg;
+    if (c.T < 0 || c.d <= 0 || c.I <= 0 || c.E <= 0 || c.k <= 0) return MOE_ERR_INVALID_ARG;
+    if (c.precision != MOE_BF16 && c.precision != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (c.training != 0 && c.training != 1) return MOE_ERR_INVALID_ARG;
+    if (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_PREFILL && c.path != MOE_PATH_DECODE)
+        return MOE_ERR_INVALID_ARG;
+    if (c.d % 64 != 0 || c.I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (c.E > kMaxExperts || c.k > c.E || c.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)c.T * c.k;
+    if (R > kMaxRoutedRows) return MOE_ERR_UNSUPPORTED;
+    if (c.precision == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward added below
+    if (c.path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+
+    moe_plan_s* p = new (std::nothrow) moe_plan_s();
+    if (!p) return MOE_ERR_INVALID_ARG;
+    p->cfg = c;
+    p->R = R;
+    p->nchunks = dispatch_chunks(R);
+    p->decode = false;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
+    p->off_status = take(sizeof(int32_t));
+    p->off_hist = take(sizeof(int32_t) * (size_t)(p->nchunks > 0 ? p->nchunks : 1) * c.E);
+    p->off_m_indptr = take(sizeof(int32_t) * (size_t)(c.E + 1));
+    p->off_gather = take(sizeof(int32_t) * (size_t)R);
+    p->off_slots = take(sizeof(int32_t) * (size_t)R);
+    p->off_probs = take(sizeof(float) * (size_t)R);
+    p->off_a = take(2 * (size_t)R * c.I);
+    p->off_o = take(2 * (size_t)R * c.d);
+    p->off_h = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
+    p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
+    p->off_dxp = c.training ? take(2 * (size_t)R * c.d) : 0;
+    p->off_xq = p->off_xs = p->off_aq = p->off_as = 0;
+    p->ws_bytes = off;
+    p->ws = nullptr;
+    p->ws_size = 0;
+    p->num_cu = 0;
+    p->have_saved_forward = false;
+    *out = p;
+    return MOE_OK;
+}
+
+size_t moe_workspace_bytes(moe_plan_t p) { return p ? p->ws_bytes : 0; }
+
+moe_status_t moe_bind_workspace(moe_plan_t p, void* dptr, size_t bytes) {
+    if (!p || !dptr) return MOE_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(dptr) % 256 != 0) return MOE_ERR_INVALID_ARG;
+    if (bytes < p->ws_bytes) return MOE_ERR_WORKSPACE;
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (hipMemset(static_cast<char*>(dptr) + p->off_status, 0, sizeof(int32_t)) != hipSuccess)
+        return MOE_ERR_HIP;
+    p->ws = static_cast<char*>(dptr);
+    p->ws_size = bytes;
+    p->num_cu = ncu > 0 ? ncu : 256;
+    p->have_saved_forward = false;
+    return MOE_OK;
+}
+
+moe_status_t moe_plan_destroy(moe_plan_t p) {
+    delete p;
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch(moe_plan_t p, const int32_t* ids, const float* scores, int32_t* m_indptr,
+                          int32_t* gather, int32_t* slots, float* probs, void* stream) {
+    if (!p || !m_indptr) return MOE_ERR_INVALID_ARG;
+    if (p->R > 0 && (!ids || !scores || !gather || !slots || !probs)) return MOE_ERR_INVALID_ARG;
+    if (!p->ws) return MOE_ERR_WORKSPACE;
+    const moe_config_t& c = p->cfg;
+    hipError_t e = launch_dispatch(ids, scores, c.T, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr,
+                                   gather, slots, probs, p->at<int32_t>(p->off_status),
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_quantize_mxfp8(const void* v, int64_t rows, int32_t K, uint8_t* codes,
+                                uint8_t* scales, void* stream) {
+    if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
+    if (rows > 0 && (!v || !codes || !scales)) return MOE_ERR_INVALID_ARG;
+    hipError_t e = launch_quantize_mxfp8(static_cast<const uint16_t*>(v), rows, K, codes, scales,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status_t moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, uint8_t* w13_q,
+                                 uint8_t* w13_s, uint8_t* w2_q, uint8_t* w2_s, void* stream) {
+    if (!p || !w13 || !w2 || !w13_q || !w13_s || !w2_q || !w2_s) return MOE_ERR_INVALID_ARG;
+    const moe_config_t& c = p->cfg;
+    moe_status_t st = moe_quantize_mxfp8(w13, (int64_t)c.E * 2 * c.I, c.d, w13_q, w13_s, stream);
+    if (st != MOE_OK) return st;
+    return moe_quantize_mxfp8(w2, (int64_t)c.E * c.d, c.I, w2_q, w2_s, stream);
+}
+
+moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const float* scores,
+                         const moe_weights_t* w, void* y, void* stream) {
+    if (!p || !w) return MOE_ERR_INVALID_ARG;
+    const moe_config_t& c = p->cfg;
+    if (c.T > 0 && (!x || !ids || !scores || !y || !w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+    if (!p->ws) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    p->have_saved_forward = false;
+    if (c.T == 0) {
+        p->have_saved_forward = c.training != 0;
+        return MOE_OK;
+    }
+    int32_t* m_indptr = p->at<int32_t>(p->off_m_indptr);
+    int32_t* gather = p->at<int32_t>(p->off_gather);
+    int32_t* slots = p->at<int32_t>(p->off_slots);
+    float* probs = p->at<float>(p->off_probs);
+    hipError_t e = staged(p, MOE_STAGE_DISPATCH, s, [&] {
+        return launch_dispatch(ids, scores, c.T, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr,
+                               gather, slots, probs, p->at<int32_t>(p->off_status), s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+
+    GemmArgs g{};
+    g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.m_indptr = m_indptr; g.gather = gather; g.probs = probs;
+    g.x = static_cast<const uint16_t*>(x);
+    g.w13 = static_cast<const uint16_t*>(w->w13);
+    g.w2 = static_cast<const uint16_t*>(w->w2);
+    g.out = p->at<uint16_t>(p->off_a);
+    g.out_h = c.training ? p->at<uint16_t>(p->off_h) : nullptr;
+    e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm(FWD_W13, g, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    g.a = p->at<uint16_t>(p->off_a);
+    g.out = p->at<uint16_t>(p->off_o);
+    g.out_h = nullptr;
+    e = staged(p, MOE_STAGE_W2, s, [&] { return launch_gemm(FWD_W2, g, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = staged(p, MOE_STAGE_COMBINE, s, [&] {
+        return launch_combine(p->at<uint16_t>(p->off_o), slots, scores, c.T, c.k, c.d,
+                              static_cast<uint16_t*>(y), s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    p->have_saved_forward = c.training != 0;
+    return MOE_OK;
+}
+
+moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe_weights_t* w,
+                          void* dx, void* dw13, void* dw2, float* dscores, void* stream) {
+    if (!p || !w) return MOE_ERR_INVALID_ARG;
+    const moe_config_t& c = p->cfg;
+    if (!c.training || c.precision != MOE_BF16) return MOE_ERR_STATE;
+    if (!dw13 || !dw2 || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
+    if (c.T > 0 && (!dy || !x || !dx || !dscores)) return MOE_ERR_INVALID_ARG;
+    if (!p->ws) return MOE_ERR_WORKSPACE;
+    if (!p->have_saved_forward) return MOE_ERR_STATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    const int32_t* slots = p->at<int32_t>(p->off_slots);
+    if (c.T > 0) {
+        e = staged(p, MOE_STAGE_SCORE_GRAD, s, [&] {
+            return launch_score_grad(static_cast<const uint16_t*>(dy), p->at<uint16_t>(p->off_o),
+                                     slots, c.T, c.k, c.d, dscores, s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    GemmArgs g{};
+    g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.m_indptr = p->at<int32_t>(p->off_m_indptr);
+    g.gather = p->at<int32_t>(p->off_gather);
+    g.probs = p->at<float>(p->off_probs);
+    g.x = static_cast<const uint16_t*>(x);
+    g.w13 = static_cast<const uint16_t*>(w->w13);
+    g.w2 = static_cast<const uint16_t*>(w->w2);
+    g.a = p->at<uint16_t>(p->off_a);
+    g.h = p->at<uint16_t>(p->off_h);
+    g.dy = static_cast<const uint16_t*>(dy);
+    g.dh = p->at<uint16_t>(p->off_dh);
+    if (c.T == 0) {
+        // no routed rows: every expert gradient is +0 (the weight-gradient kernels write them)
+        g.m_indptr = p->at<int32_t>(p->off_m_indptr);
+        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E, p->at<int32_t>(p->off_hist),
+                                 p->at<int32_t>(p->off_m_indptr), nullptr, nullptr, nullptr,
+                                 p->at<int32_t>(p->off_status), s)) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        g.out = p->at<uint16_t>(p->off_dh);
+        e = staged(p, MOE_STAGE_DGRAD_W2, s, [&] { return launch_gemm(DGRAD_W2, g, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    g.out = static_cast<uint16_t*>(dw2);
+    e = staged(p, MOE_STAGE_WGRAD_W2, s, [&] { return launch_gemm(WGRAD_W2, g, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (c.T > 0) {
+        g.out = p->at<uint16_t>(p->off_dxp);
+        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm(DGRAD_W13, g, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    g.out = static_cast<uint16_t*>(dw13);
+    e = staged(p, MOE_STAGE_WGRAD_W13, s, [&] { return launch_gemm(WGRAD_W13, g, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    if (c.T > 0) {
+        e = staged(p, MOE_STAGE_DX_COMBINE, s, [&] {
+            return launch_combine(p->at<uint16_t>(p->off_dxp), slots, nullptr, c.T, c.k, c.d,
+                                  static_cast<uint16_t*>(dx), s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+moe_status_t moe_get_status(moe_plan_t p, int32_t* device_flags, int32_t clear, void* stream) {
+    if (!p || !device_flags) return MOE_ERR_INVALID_ARG;
+    if (!p->ws) return MOE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    int32_t* dflag = p->at<int32_t>(p->off_status);
+    if (hipMemcpyAsync(&v, dflag, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    if (clear && v) {
+        if (hipMemsetAsync(dflag, 0, sizeof(int32_t), s) != hipSuccess) return MOE_ERR_HIP;
+        if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+    }
+    *device_flags = v;
+    return v ? MOE_ERR_ROUTING : MOE_OK;
+}
+
+moe_status_t moe_profile(moe_plan_t p, int32_t enable) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    p->prof_on = enable != 0;
+    return MOE_OK;
+}
+
+moe_status_t moe_profile_read(moe_plan_t p, float* total_ms, int32_t* count, int32_t max_stages) {
+    if (!p || max_stages < 0 || (max_stages > 0 && (!total_ms || !count))) return MOE_ERR_INVALID_ARG;
+    for (int i = 0; i < max_stages; ++i) { total_ms[i] = 0.f; count[i] = 0; }
+    moe_status_t st = MOE_OK;
+    for (auto& r : p->recs) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+            st = MOE_ERR_HIP;
+        else if (r.stage < max_stages) { total_ms[r.stage] += ms; count[r.stage] += 1; }
+        p->ev_free.push_back(r.a);
+        p->ev_free.push_back(r.b);
+    }
+    p->recs.clear();
+    return st;
+}
+
+const char* moe_status_string(moe_status_t st) {
+    switch (st) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or mode";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_STATE: return "invalid call order (no saved training forward)";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_ROUTING: return "invalid routing detected on the device";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -47,6 +47,8 @@ def _L():
         lib = ctypes.CDLL(_LIB_PATH)
         i32, f64p = ctypes.c_int, ctypes.POINTER(ctypes.c_double)
         vp = ctypes.c_void_p
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_check_routing.argtypes = [i32, i32, i32, vp]
         lib.orc_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
         lib.orc_forward_tokens.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, vp, vp]
@@ -91,6 +93,10 @@ def _check(rc: int):
         raise MemoryError("oracle allocation failed")
     if rc != ORC_OK:
         raise RuntimeError("oracle error %d" % rc)
+
+
+def num_threads() -> int:
+    return int(_L().orc_num_threads())
 
 
 def check_routing(ids: np.ndarray, E: int) -> int:

@@ -37,6 +37,7 @@
  *   - dS[t][j] = <dY[t], o_(t,j)> with o the unscaled expert output.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -45,6 +46,9 @@
 #define ORC_ERR_RANGE 1
 #define ORC_ERR_DUPLICATE 2
 #define ORC_ERR_ALLOC 3
+
+/* threads the OpenMP loops below use */
+int orc_num_threads(void) { return omp_get_max_threads(); }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }

@@ -1,0 +1,138 @@
+"""The C-ABI library (include/moe.h): it loads without a GPU, exports every
+declared entry point, and rejects bad calls on the host before touching the
+device (the plan's limits follow the nvfp4moe README, "Limits"; the refusal
+of unsupported modes at creation follows the blog post, "What it is
+selling")."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_routed_dispatch_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "moe.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from mixture_experts_routed_dispatch_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert set(syms) == set(moe.EXPORTS)
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def test_status_strings(L):
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert len(moe.status_string(st)) >= 2 and moe.status_string(st) != "unknown status"
+    assert moe.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("cfg,expect", [
+    (dict(T=64, d=256, I=128, E=8, k=2), moe.MOE_OK),
+    (dict(T=0, d=256, I=128, E=8, k=2), moe.MOE_OK),                 # empty batch is valid
+    (dict(T=-1, d=256, I=128, E=8, k=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=0, I=128, E=8, k=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=256, I=128, E=8, k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=250, I=128, E=8, k=2), moe.MOE_ERR_UNSUPPORTED),    # K not a multiple of 64
+    (dict(T=8, d=256, I=100, E=8, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d=256, I=128, E=257, k=2), moe.MOE_ERR_UNSUPPORTED),  # > 256 experts
+    (dict(T=8, d=256, I=128, E=4, k=5), moe.MOE_ERR_UNSUPPORTED),    # k > E
+    (dict(T=16385, d=256, I=128, E=64, k=8), moe.MOE_ERR_UNSUPPORTED),  # > 131072 rows
+    (dict(T=16384, d=256, I=128, E=64, k=8), moe.MOE_OK),            # exactly at the limit
+    (dict(T=8, d=256, I=128, E=8, k=2, precision=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=256, I=128, E=8, k=2, training=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=256, I=128, E=8, k=2, path=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=8, d=256, I=128, E=8, k=2, precision=1, training=1), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_plan_validation(L, cfg, expect):
+    c = moe.MoeConfig(cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"], cfg.get("precision", 0),
+                      cfg.get("training", 0), cfg.get("path", 0))
+    h = ctypes.c_void_p()
+    st = L.moe_plan(ctypes.byref(c), ctypes.byref(h))
+    assert st == expect
+    if st == moe.MOE_OK:
+        assert h.value
+        assert L.moe_workspace_bytes(h) > 0
+        L.moe_plan_destroy(h)
+    else:
+        assert not h.value
+
+
+def test_null_arguments_and_unbound_workspace(L):
+    assert L.moe_plan(None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_bytes(None) == 0
+    assert L.moe_plan_destroy(None) == moe.MOE_OK
+    plan = moe.moe_plan(64, 256, 128, 8, 2, training=1)
+    w = moe.weights(0x1000, 0x2000)
+    # no workspace bound yet: rejected before any launch
+    assert L.moe_forward(plan, 0x1000, 0x1000, 0x1000, ctypes.byref(w), 0x1000, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_dispatch(plan, 0x10, 0x10, 0x10, 0x10, 0x10, 0x10, None) == moe.MOE_ERR_WORKSPACE
+    # NULL tensors
+    assert L.moe_forward(plan, None, 0x1000, 0x1000, ctypes.byref(w), 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(plan, 0x1000, 0x1000, 0x1000, None, 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    wn = moe.weights(0, 0x2000)
+    assert L.moe_forward(plan, 0x1000, 0x1000, 0x1000, ctypes.byref(wn), 0x1000, None) == moe.MOE_ERR_INVALID_ARG
+    # bind rejects misaligned or short buffers without touching the device
+    assert L.moe_bind_workspace(plan, 0x1001, 1 << 30) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_bind_workspace(plan, 0x1000, 16) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_bind_workspace(plan, None, 1 << 30) == moe.MOE_ERR_INVALID_ARG
+    # backward: workspace checked after arguments
+    assert L.moe_backward(plan, 0x10, 0x10, ctypes.byref(w), 0x10, 0x10, 0x10, 0x10, None) == moe.MOE_ERR_WORKSPACE
+    f = ctypes.c_int32()
+    assert L.moe_get_status(plan, ctypes.byref(f), 0, None) == moe.MOE_ERR_WORKSPACE
+    moe.moe_plan_destroy(plan)
+
+
+def test_backward_on_inference_plan_is_a_state_error(L):
+    plan = moe.moe_plan(64, 256, 128, 8, 2, training=0)
+    w = moe.weights(0x1000, 0x2000)
+    assert L.moe_backward(plan, 0x10, 0x10, ctypes.byref(w), 0x10, 0x10, 0x10, 0x10, None) == moe.MOE_ERR_STATE
+    moe.moe_plan_destroy(plan)
+
+
+def test_quantize_argument_checks(L):
+    assert L.moe_quantize_mxfp8(0x10, 4, 48, 0x10, 0x10, None) == moe.MOE_ERR_INVALID_ARG  # K % 32
+    assert L.moe_quantize_mxfp8(None, 4, 64, 0x10, 0x10, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_mxfp8(0x10, -1, 64, 0x10, 0x10, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_training_state(L):
+    a = moe.moe_plan(8192, 2048, 768, 16, 8, training=0)
+    b = moe.moe_plan(8192, 2048, 768, 16, 8, training=1)
+    R = 8192 * 8
+    assert moe.moe_workspace_bytes(a) >= R * (768 + 2048) * 2
+    assert moe.moe_workspace_bytes(b) >= moe.moe_workspace_bytes(a) + R * (4 * 768 + 2048) * 2
+    moe.moe_plan_destroy(a)
+    moe.moe_plan_destroy(b)
+
+
+def test_oracle_and_library_share_nothing():
+    """The oracle package and the HIP library do not import or include each other."""
+    pkg = os.path.join(ROOT, "mixture_experts_routed_dispatch_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".cpp", ".h")):
+                with open(os.path.join(dirpath, fn)) as f:
+                    src = f.read()
+                assert "import oracle" not in src and "from oracle" not in src, fn
+                assert "moe_oracle" not in src and "liborc" not in src, fn
+    with open(os.path.join(ROOT, "oracle", "moe_oracle.c")) as f:
+        src = f.read()
+    assert "#include \"" not in src
+    with open(os.path.join(ROOT, "oracle", "__init__.py")) as f:
+        src = f.read()
+    assert "mixture_experts_routed_dispatch_amd" not in src

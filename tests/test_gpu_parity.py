@@ -1,0 +1,322 @@
+"""HIP path against the CPU oracle, through the C ABI (include/moe.h).
+
+* Dispatch (nvfp4moe README "Grouped GEMM", "Training"): bit-exact m_indptr,
+  gather, slots and probs on every workload's routing and on adversarial ones;
+  the device status word flags invalid routing.
+* Forward (blog post "What it is selling"; nvfp4moe README "MoE layer"):
+  norm-wise relative error <= 2e-2 (BF16) against the fp64 oracle, on small
+  layers that span several tiles with ragged tails, and at the full workload
+  sizes on sampled tokens, with the launch configuration the benchmark times.
+* Backward (DGRAD, WGRAD, router gradient): the same bound on dx, dscores,
+  dW13 and dW2; experts with no row get exactly +0.0.
+* Run-to-run bitwise determinism and HIP-graph replay equal to eager calls.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_routed_dispatch_amd import inputs
+from tests.gpu_util import bf16_dev, dev, device_inputs, maxrel, np_of, rel, say
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from mixture_experts_routed_dispatch_amd import moe
+    moe.lib()
+    oracle.build(force=False)
+    return torch
+
+
+def make_layer(inp, training=False, path=0):
+    from mixture_experts_routed_dispatch_amd import moe
+    return moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, training=training, path=path)
+
+
+# ------------------------------------------------------------------ dispatch
+
+def _routing_cases():
+    cases = []
+    for name in ("tiny", "prefill", "train", "decode1", "decode32", "mxfp8"):
+        c = inputs.CONFIGS[name]
+        cases.append((name, c["T"], c["E"], c["k"], c["routing"]))
+    cases += [("k1", 3000, 16, 1, "uniform"), ("E256k32", 4096, 256, 32, "uniform"),
+              ("ragged_chunk", 2049, 7, 3, "uniform"), ("same_experts", 5000, 64, 4, "same"),
+              ("descending", 700, 40, 6, "descending"), ("zipf_small", 333, 128, 8, "zipf"),
+              ("one_token", 1, 8, 8, "uniform"), ("max_rows", 16384, 256, 8, "uniform")]
+    return cases
+
+
+def _routing(kind, T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "uniform":
+        return inputs.uniform_routing(rng, T, E, k)
+    if kind == "zipf":
+        return inputs.zipf_routing(rng, T, E, k)
+    if kind == "same":
+        return np.tile(rng.permutation(E)[:k].astype(np.int32), (T, 1))
+    if kind == "descending":
+        return np.tile(np.arange(E - 1, E - 1 - k, -1, dtype=np.int32), (T, 1))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("name,T,E,k,kind", _routing_cases())
+def test_dispatch_bit_exact(torch_cuda, name, T, E, k, kind):
+    torch = torch_cuda
+    say("dispatch case", name, T, E, k, kind)
+    ids = _routing(kind, T, E, k, seed=T + E)
+    scores = np.random.default_rng(1).random((T, k)).astype(np.float32)
+    from mixture_experts_routed_dispatch_amd import moe
+    layer = moe.Layer(T, 64, 64, E, k)
+    m_indptr, gather, slots, probs = layer.dispatch(torch.from_numpy(ids).to(dev()),
+                                                    torch.from_numpy(scores).to(dev()))
+    st, flags = layer.status()
+    assert st == moe.MOE_OK and flags == 0
+    ref = oracle.dispatch(ids, scores, E)
+    assert np.array_equal(m_indptr.cpu().numpy(), ref[0])
+    assert np.array_equal(gather.cpu().numpy(), ref[1])
+    assert np.array_equal(slots.cpu().numpy(), ref[2])
+    assert np.array_equal(probs.cpu().numpy().view(np.uint32), ref[3].view(np.uint32))
+    # run-to-run identical
+    again = layer.dispatch(torch.from_numpy(ids).to(dev()), torch.from_numpy(scores).to(dev()))
+    for a, b in zip((m_indptr, gather, slots, probs), again):
+        assert torch.equal(a, b)
+    layer.close()
+
+
+def test_dispatch_flags_invalid_routing(torch_cuda):
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, E, k = 100, 8, 2
+    ids = _routing("uniform", T, E, k, 3)
+    scores = np.ones((T, k), np.float32)
+    layer = moe.Layer(T, 64, 64, E, k)
+    bad = ids.copy()
+    bad[7, 1] = E            # out of range
+    layer.dispatch(torch.from_numpy(bad).to(dev()), torch.from_numpy(scores).to(dev()))
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags & moe.MOE_DEV_ID_OUT_OF_RANGE
+    bad = ids.copy()
+    bad[9, 1] = bad[9, 0]    # repeated in a row
+    layer.dispatch(torch.from_numpy(bad).to(dev()), torch.from_numpy(scores).to(dev()))
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags == moe.MOE_DEV_ID_DUPLICATE
+    layer.dispatch(torch.from_numpy(ids).to(dev()), torch.from_numpy(scores).to(dev()))
+    st, flags = layer.status()
+    assert st == moe.MOE_OK and flags == 0   # the flag was cleared and stays clear
+    layer.close()
+
+
+# ------------------------------------------------------------------ forward
+
+SMALL_SHAPES = [
+    # T, d, I, E, k, routing
+    (64, 256, 128, 8, 2, "uniform"),       # the tiny workload
+    (600, 512, 384, 6, 3, "uniform"),      # ~300 rows/expert: 2 row tiles, ragged tail; 3 W13 tiles
+    (257, 320, 192, 5, 2, "uniform"),      # d, I not multiples of the tile: masked tails
+    (300, 256, 128, 128, 8, "zipf"),       # skew, 8+ empty experts, many 1-row experts
+    (130, 128, 64, 1, 1, "uniform"),       # dense layer (E = 1, k = 1)
+    (1, 256, 128, 16, 4, "uniform"),       # one token
+]
+
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", SMALL_SHAPES)
+def test_forward_small(torch_cuda, T, d, I, E, k, routing):
+    torch = torch_cuda
+    say("forward small", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=11)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=1)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    e = rel(np_of(y), ref)
+    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
+    assert e <= TOL_BF16
+    layer.close()
+
+
+def test_forward_zero_scores_give_zero(torch_cuda):
+    torch = torch_cuda
+    inp = inputs.generate(96, 256, 128, 8, 2, seed=2)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=1)
+    y = layer.forward(t["x"], t["ids"], torch.zeros_like(t["scores"]), t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    yb = y.view(torch.int16).cpu().numpy()
+    assert np.all(yb == 0)          # +0.0 exactly: sums start at +0 and 0 * o = +-0
+    layer.close()
+
+
+@pytest.mark.parametrize("name", ["prefill", "train", "decode1", "decode32"])
+def test_forward_full_size_sampled(torch_cuda, name):
+    torch = torch_cuda
+    say("forward full size", name)
+    inp = inputs.generate_config(name, seed=0, with_dy=False)
+    t = device_inputs(inp)
+    layer = make_layer(inp)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    y2 = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    assert flags == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # bitwise deterministic
+    rng = np.random.default_rng(5)
+    n = min(inp.T, 48)
+    toks = np.sort(rng.choice(inp.T, size=n, replace=False)).astype(np.int32)
+    toks[0] = 0
+    toks[-1] = inp.T - 1
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
+    got = np_of(y)[toks]
+    e = rel(got, ref)
+    say("  rel %.3e maxrel %.3e" % (e, maxrel(got, ref)))
+    assert e <= TOL_BF16
+    layer.close()
+
+
+def test_graph_replay_matches_eager(torch_cuda):
+    torch = torch_cuda
+    inp = inputs.generate(512, 512, 256, 8, 4, seed=4)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=1)
+    y_eager = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    y_out = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)   # warm
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)
+    for rep in range(4):
+        y_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_out.view(torch.int16), y_eager.view(torch.int16)), rep
+        # eager work between replays
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+    layer.close()
+
+
+# ------------------------------------------------------------------ backward
+
+BWD_SHAPES = [
+    (64, 256, 128, 8, 2, "uniform"),
+    (400, 512, 384, 6, 3, "uniform"),
+    (257, 320, 192, 5, 2, "uniform"),
+    (300, 256, 128, 128, 8, "zipf"),
+    (130, 128, 64, 1, 1, "uniform"),
+]
+
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", BWD_SHAPES)
+def test_backward_small(torch_cuda, T, d, I, E, k, routing):
+    torch = torch_cuda
+    say("backward small", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=13, with_dy=True)
+    t = device_inputs(inp)
+    layer = make_layer(inp, training=True)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    y_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    dw13_ref = dw13_ref.reshape(E, 2 * I, d)
+    errs = dict(y=rel(np_of(y), y_ref), dx=rel(np_of(dx), dx_ref), ds=rel(np_of(ds), ds_ref),
+                dw2=rel(np_of(dw2), dw2_ref), dw13=rel(np_of(dw13), dw13_ref))
+    say("  " + " ".join("%s %.3e" % kv for kv in errs.items()))
+    for kname, v in errs.items():
+        assert v <= TOL_BF16, kname
+    counts = np.bincount(inp.ids.ravel(), minlength=E)
+    for e in np.nonzero(counts == 0)[0]:
+        assert np.all(dw2[e].view(torch.int16).cpu().numpy() == 0)
+        assert np.all(dw13[e].view(torch.int16).cpu().numpy() == 0)
+    layer.close()
+
+
+def test_backward_full_size_sampled(torch_cuda):
+    torch = torch_cuda
+    say("backward full size: train workload")
+    inp = inputs.generate_config("train", seed=0, with_dy=True)
+    t = device_inputs(inp)
+    layer = make_layer(inp, training=True)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    dx2, dw13b, dw2b, ds2 = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    for a, b in ((dx, dx2), (dw13, dw13b), (dw2, dw2b), (ds, ds2)):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(inp.T, size=32, replace=False)).astype(np.int32)
+    dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy,
+                                            toks=toks)
+    e_dx, e_ds = rel(np_of(dx)[toks], dx_ref), rel(np_of(ds)[toks], ds_ref)
+    cols = np.sort(rng.choice(inp.I, size=6, replace=False)).astype(np.int32)
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy,
+                                          icols=cols)
+    dw2_np = np_of(dw2)[:, :, cols]
+    dw13_np = np.stack([np_of(dw13[:, cols, :]), np_of(dw13[:, inp.I + cols, :])], axis=1)
+    e_w2, e_w13 = rel(dw2_np, dw2_ref), rel(dw13_np, dw13_ref)
+    say("  dx %.3e ds %.3e dw2 %.3e dw13 %.3e" % (e_dx, e_ds, e_w2, e_w13))
+    assert max(e_dx, e_ds, e_w2, e_w13) <= TOL_BF16
+    counts = np.bincount(inp.ids.ravel(), minlength=inp.E)
+    empty = np.nonzero(counts == 0)[0]
+    assert len(empty) >= 8
+    for e in empty:
+        assert not torch.any(dw2[e].view(torch.int16) != 0)
+        assert not torch.any(dw13[e].view(torch.int16) != 0)
+    layer.close()
+
+
+# ------------------------------------------------------------------ MXFP8 conversion
+
+def test_quantize_bit_exact(torch_cuda):
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    rng = np.random.default_rng(0)
+    rows, K = 300, 256
+    v = (rng.standard_normal((rows, K)) * np.exp(rng.normal(0, 4, (rows, 1)))).astype(np.float32)
+    v[0] = 0.0
+    v[1, :32] = -0.0
+    v[2] = 448.0 * np.sign(rng.standard_normal(K))
+    v[3] = 1e-40                                         # float32 subnormal: bf16 subnormal after rounding
+    v[4] = 3.0e38
+    bits = inputs.to_bf16_bits(v)
+    bits[5] = rng.integers(0, 65536, K).astype(np.uint16)   # arbitrary bit patterns ...
+    finite = np.isfinite((bits[5].astype(np.uint32) << 16).view(np.float32))
+    bits[5][~finite] = 0                                     # ... except Inf / NaN
+    src = bf16_dev(bits)
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=dev())
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev())
+    moe.moe_quantize_mxfp8(src.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(bits)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
+def test_prepare_weights_bit_exact(torch_cuda):
+    torch = torch_cuda
+    inp = inputs.generate(16, 256, 128, 4, 2, seed=3)
+    t = device_inputs(inp)
+    layer = make_layer(inp)
+    w13_q, w13_s, w2_q, w2_s = layer.prepare_weights(t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    r13 = oracle.mx_quantize(inp.w13)
+    r2 = oracle.mx_quantize(inp.w2)
+    assert np.array_equal(w13_q.cpu().numpy(), r13[0]) and np.array_equal(w13_s.cpu().numpy(), r13[1])
+    assert np.array_equal(w2_q.cpu().numpy(), r2[0]) and np.array_equal(w2_s.cpu().numpy(), r2[1])
+    layer.close()
