@@ -47,30 +47,88 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="before warm-up, run one plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc csv files and exit")
     return ap.parse_args()
 
 
-def source_hash(paths):
+KERNEL_OF_STAGE = {
+    # stage name (library event pairs) -> substring of the kernel symbol rocprofv3 reports
+    "dispatch": "dispatch_place", "w13": "grouped_gemm<0>", "w2": "grouped_gemm<1>",
+    "combine": "combine_kernel", "score_grad": "score_grad_kernel",
+    "dgrad_w2": "grouped_gemm<2>", "dgrad_w13": "grouped_gemm<3>",
+    "wgrad_w2": "grouped_gemm<4>", "wgrad_w13": "grouped_gemm<5>",
+}
+TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash():
+    """Hash of every kernel and host source of the library: traffic figures taken on
+    other sources are stale."""
+    import glob
     h = hashlib.sha256()
-    for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in sorted(glob.glob(os.path.join(ROOT, "mixture_experts_routed_dispatch_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str, srcs, units_per_launch: float):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_for(stage: str, workload: str):
+    """HBM bytes (read + written) per launch of the stage's kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current sources and workload."""
     try:
-        with open(path) as f:
+        with open(TRAFFIC_PATH) as f:
             tab = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = tab.get(kernel)
-    if not ent or ent.get("source_hash") != source_hash(srcs):
+    if tab.get("source_hash") != source_hash() or tab.get("workload") != workload:
         return None
-    return ent.get("bytes_per_launch")
+    ent = tab.get("kernels", {}).get(KERNEL_OF_STAGE.get(stage, "?"))
+    return None if ent is None else ent["read_bytes"] + ent["write_bytes"]
+
+
+def _pmc_values(path: str, counter: str):
+    """{kernel symbol: [counter value of each dispatch]} from a rocprofv3 --pmc csv."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return vals
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of
+    `bench.py --copy-probe N` into bytes per launch for each kernel.  Each counter is
+    scaled by the factor that makes the plain copy of N bytes read and write N bytes."""
+    fetch = _pmc_values(fetch_csv, "FETCH_SIZE")
+    write = _pmc_values(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copy" in k.lower() and "moe" not in k and k in write]
+    if not copy:
+        raise SystemExit("no copy kernel in %s" % fetch_csv)
+    # the probe is the largest copy dispatch of the run
+    ck = max(copy, key=lambda k: max(fetch[k]))
+    f_fetch = copy_bytes / (max(fetch[ck]) * 1024.0)
+    f_write = copy_bytes / (max(write[ck]) * 1024.0)
+    fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
+    write = {k: sum(v) / len(v) for k, v in write.items()}
+    kernels = {}
+    for stage, sub in KERNEL_OF_STAGE.items():
+        names = [k for k in fetch if sub in k]
+        if names and names[0] in write:
+            kernels[sub] = {"read_bytes": fetch[names[0]] * 1024.0 * f_fetch,
+                            "write_bytes": write[names[0]] * 1024.0 * f_write,
+                            "fetch_kib_raw": fetch[names[0]], "write_kib_raw": write[names[0]]}
+    tab = {"workload": workload, "source_hash": source_hash(), "copy_kernel": ck,
+           "copy_bytes": copy_bytes, "fetch_factor": f_fetch, "write_factor": f_write,
+           "kernels": kernels}
+    with open(TRAFFIC_PATH, "w") as f:
+        json.dump(tab, f, indent=1)
+    return tab
 
 
 def oracle_threads():
@@ -118,6 +176,11 @@ def cpu_baseline(inp, training: bool, target_s: float):
 
 def main():
     args = parse()
+    if args.traffic:
+        tab = write_traffic(args.traffic[0], args.traffic[1], args.workload,
+                            args.copy_probe or (1 << 30))
+        print(json.dumps(tab, indent=1))
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU; --gpus %d is not supported "
               "(no collectives, no sharding)" % args.gpus, file=sys.stderr)
@@ -151,6 +214,13 @@ def main():
             moe.moe_backward(layer.plan, t["dy"].data_ptr(), t["x"].data_ptr(), w, dx.data_ptr(),
                              dw13.data_ptr(), dw2.data_ptr(), ds.data_ptr(), sp)
 
+    if args.copy_probe:
+        src_buf = torch.ones(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst_buf = torch.empty_like(src_buf)
+        torch.cuda.synchronize()
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -190,8 +260,7 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                 "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
-                "traffic": traffic_for("grouped_gemm_" + dom,
-                                       ["mixture_experts_routed_dispatch_amd/csrc/gemm_bf16.hip"], 1)}
+                "traffic": traffic_for(dom, args.workload)}
     else:
         # HBM-bound stage: bytes it must move at least once
         nbytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
@@ -199,7 +268,8 @@ def main():
         achieved = nbytes / (stage_us[dom] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                "algorithmic_per_launch": nbytes, "avg_launch_us": stage_us[dom], "traffic": None}
+                "algorithmic_per_launch": nbytes, "avg_launch_us": stage_us[dom],
+                "traffic": traffic_for(dom, args.workload)}
     gemm_us = sum(stage_us.get(s, 0.0) for s in gemm_flop)
     gemm_tflops = sum(gemm_flop[s] for s in gemm_flop if s in stage_us) / (gemm_us * 1e-6) / 1e12
 
