@@ -196,6 +196,7 @@ def main():
     T, d, I, E, k = inp.T, inp.d, inp.I, inp.E, inp.k
     R = T * k
     t = device_inputs(inp)
+    decode = cfg_name.startswith("decode")
     layer = moe.Layer(T, d, I, E, k, training=training)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
@@ -205,10 +206,32 @@ def main():
         dw13 = torch.empty((E, 2 * I, d), dtype=torch.bfloat16, device="cuda")
         dw2 = torch.empty((E, d, I), dtype=torch.bfloat16, device="cuda")
         ds = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    w = moe.weights(t["w13"].data_ptr(), t["w2"].data_ptr())
+
+    # Per-step inputs.  Decode moves each active expert's weights once per call, so
+    # consecutive calls must not find them in the 256 MB MALL: batch-one decode cycles
+    # through 16 routings that split the experts into disjoint groups, and the 32-token
+    # batch rotates over 4 copies of the whole weight set (1.2 GB each).
+    ids_list = [t["ids"]]
+    w_list = [(t["w13"], t["w2"])]
+    if cfg_name == "decode1":
+        rout = inputs.disjoint_routings(E, k, E // k, seed=1)
+        ids_list = [torch.from_numpy(rout[i:i + 1]).to("cuda") for i in range(len(rout))]
+    elif cfg_name == "decode32":
+        for _ in range(3):
+            w_list.append((t["w13"].clone(), t["w2"].clone()))
+    n_active = []
+    for ids_dev in ids_list:
+        n_active.append(len(np.unique(ids_dev.cpu().numpy())))
+    n_active_mean = float(np.mean(n_active))
+    wlist = [moe.weights(a.data_ptr(), b.data_ptr()) for a, b in w_list]
+    state = {"i": 0}
 
     def step():
-        moe.moe_forward(layer.plan, t["x"].data_ptr(), t["ids"].data_ptr(),
+        i = state["i"]
+        state["i"] = i + 1
+        ids_dev = ids_list[i % len(ids_list)]
+        w = wlist[i % len(wlist)]
+        moe.moe_forward(layer.plan, t["x"].data_ptr(), ids_dev.data_ptr(),
                         t["scores"].data_ptr(), w, y.data_ptr(), sp)
         if training:
             moe.moe_backward(layer.plan, t["dy"].data_ptr(), t["x"].data_ptr(), w, dx.data_ptr(),
@@ -228,22 +251,35 @@ def main():
     if flags:
         raise SystemExit("device routing flags set: %d" % flags)
 
-    moe.moe_profile(layer.plan, True)
-    moe.moe_profile_read(layer.plan)           # drop anything recorded before
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    moe.moe_profile(layer.plan, False)
-    stages = moe.moe_profile_read(layer.plan)
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    def timed(profile: bool):
+        """Run args.steps steps back to back; returns (ms per step, wall s, stage table)."""
+        if profile:
+            moe.moe_profile(layer.plan, True)
+            moe.moe_profile_read(layer.plan)       # drop anything recorded before
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        # Hold the stream with a short spin so that the host has enqueued every timed step
+        # before the first one starts: the steps then run back to back, whatever the host's
+        # launch overhead (which matters for the few-microsecond decode calls).
+        torch.cuda._sleep(int(2e6 + 2e5 * args.steps))
+        wall0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - wall0
+        tab = None
+        if profile:
+            moe.moe_profile(layer.plan, False)
+            tab = moe.moe_profile_read(layer.plan)
+        return ev0.elapsed_time(ev1) / args.steps, wall_s, tab
+
+    # whole-step time without per-kernel events, then per-kernel times (library event
+    # pairs around each kernel on the launch stream) in a second pass of the same length
+    ms_step, wall, _ = timed(False)
+    ms_step_profiled, _, stages = timed(True)
 
     fwd_flop = 6.0 * R * I * d
     flop = fwd_flop * (3.0 if training else 1.0)
@@ -255,6 +291,12 @@ def main():
     gemm_flop = {"w13": 4.0 * R * I * d, "w2": 2.0 * R * I * d,
                  "dgrad_w2": 2.0 * R * I * d, "wgrad_w2": 2.0 * R * I * d,
                  "dgrad_w13": 4.0 * R * I * d, "wgrad_w13": 4.0 * R * I * d}
+    # bytes each stage must move at least once
+    min_bytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
+                 "dispatch": 8.0 * R + 4.0 * (E + 1) + 12.0 * R,
+                 "decode_w13": n_active_mean * 2 * I * d * 2.0 + 2.0 * T * d + 2.0 * R * I + 4.0 * R,
+                 "decode_w2": n_active_mean * d * I * 2.0 + 2.0 * R * I + 2.0 * R * d + 2.0 * T * d
+                 + 8.0 * R}
     if dom in gemm_flop:
         achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
@@ -262,21 +304,21 @@ def main():
                 "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
                 "traffic": traffic_for(dom, args.workload)}
     else:
-        # HBM-bound stage: bytes it must move at least once
-        nbytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
-                  "dispatch": 8.0 * R + 4.0 * (E + 1) + 12.0 * R}.get(dom, float("nan"))
+        nbytes = min_bytes.get(dom, float("nan"))
         achieved = nbytes / (stage_us[dom] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "algorithmic_per_launch": nbytes, "avg_launch_us": stage_us[dom],
                 "traffic": traffic_for(dom, args.workload)}
     gemm_us = sum(stage_us.get(s, 0.0) for s in gemm_flop)
-    gemm_tflops = sum(gemm_flop[s] for s in gemm_flop if s in stage_us) / (gemm_us * 1e-6) / 1e12
+    gemm_tflops = (sum(gemm_flop[s] for s in gemm_flop if s in stage_us) / (gemm_us * 1e-6) / 1e12
+                   if gemm_us > 0 else None)
+    layer_bytes = n_active_mean * 3 * I * d * 2.0 + 4.0 * T * d + 8.0 * R
 
     out = {
         "metric": METRIC,
-        "value": tflops,
-        "unit": "TFLOP/s",
+        "value": layer_bytes / (ms_step * 1e-3) / 1e9 if decode else tflops,
+        "unit": "GB/s" if decode else "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -288,19 +330,28 @@ def main():
         "data": "synthetic: seeded numpy draws, x ~ N(0,1), W ~ N(0,1/fan_in) in BF16, "
                 + ("Zipf(1.2) top-k routing with 8 forced-empty experts, dY ~ N(0,1)"
                    if cfg_name == "train" else "uniform distinct top-k routing")
-                + ", softmax-of-normal scores",
+                + ", softmax-of-normal scores"
+                + ("; 16 routings over disjoint expert groups, cycled" if cfg_name == "decode1" else "")
+                + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
         "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d BF16 %s" % (
             cfg_name, T, d, I, E, k, "forward+backward" if training else "forward"),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},
         "tokens_per_s": T / (ms_step * 1e-3),
+        "tflops": tflops,
         "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
         "gemm_tflops": gemm_tflops,
-        "gemm_mfma_frac": gemm_tflops / PEAK_BF16_TFLOPS,
+        "gemm_mfma_frac": gemm_tflops / PEAK_BF16_TFLOPS if gemm_tflops else None,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
         "wall_ms_per_step": 1e3 * wall / args.steps,
+        "ms_per_step_with_kernel_events": ms_step_profiled,
         "roofline": roof,
     }
+    if decode:
+        out["decode"] = {"active_experts_per_call": n_active_mean,
+                         "weight_bytes_per_call": n_active_mean * 3 * I * d * 2.0,
+                         "layer_hbm_gbs": layer_bytes / (ms_step * 1e-3) / 1e9,
+                         "layer_hbm_frac": layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, training, args.cpu_seconds)
     else:

@@ -23,15 +23,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
     float acc[8];
 #pragma unroll
     for (int z = 0; z < 8; ++z) acc[z] = 0.0f;
-    const int32_t* sl = slots + (size_t)t * k;
+    const int32_t* sl = slots ? slots + (size_t)t * k : nullptr;
     const float* wt = w ? w + (size_t)t * k : nullptr;
+    auto row = [&](int j) { return sl ? (size_t)sl[j] : (size_t)t * k + j; };
     int j = 0;
     for (; j + 4 <= k; j += 4) {       // four rows in flight per step; summation order unchanged
         uint4 v[4];
         float s[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            v[u] = *reinterpret_cast<const uint4*>(src + (size_t)sl[j + u] * d + n);
+            v[u] = *reinterpret_cast<const uint4*>(src + row(j + u) * d + n);
             s[u] = wt ? wt[j + u] : 1.0f;
         }
 #pragma unroll
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
         }
     }
     for (; j < k; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)sl[j] * d + n);
+        const uint4 v = *reinterpret_cast<const uint4*>(src + row(j) * d + n);
         const float s = wt ? wt[j] : 1.0f;
         const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

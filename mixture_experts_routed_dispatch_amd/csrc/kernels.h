@@ -6,6 +6,10 @@
 
 namespace moe {
 
+// Device status bits (the MOE_DEV_* values of moe.h).
+constexpr int kDevIdOutOfRange = 1;
+constexpr int kDevIdDuplicate = 2;
+
 // Entries (t, j) handled by one dispatch workgroup.
 constexpr int kDispatchChunk = 2048;
 
@@ -36,12 +40,32 @@ struct GemmArgs {
 
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
 
-// y[t] = sum_j w[t][j] * src[slots[t][j]] (w = NULL means weight 1), FP32, j ascending.
+// y[t] = sum_j w[t][j] * src[slots[t][j]] (w = NULL means weight 1; slots = NULL means
+// row t*k + j), FP32, j ascending.
 hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,
                           int d, uint16_t* y, hipStream_t s);
 // ds[t][j] = <dy[t], o[slots[t][j]]> in FP32.
 hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_t* slots, int T,
                              int k, int d, float* ds, hipStream_t s);
+
+// Small-batch (decode) path: T*k <= kMaxDecodeRows routed entries, E <= 256.
+constexpr int kMaxDecodeRows = 256;
+
+struct DecodeArgs {
+    int T, d, I, E, k;
+    const int32_t* ids;    // [T, k]
+    const float* scores;   // [T, k]
+    const uint16_t* x;     // [T, d]
+    const uint16_t* w13;   // [E, 2I, d]
+    const uint16_t* w2;    // [E, d, I]
+    uint16_t* a;           // [T*k, I]  SwiGLU output of entry t*k + j
+    uint16_t* o;           // [T*k, d]  expert output of entry t*k + j
+    uint16_t* y;           // [T, d]
+    int32_t* status;       // sticky routing flags
+};
+
+hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s);
+hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s);
 
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);

@@ -102,14 +102,18 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     const int64_t R = (int64_t)c.T * c.k;
     if (R > kMaxRoutedRows) return MOE_ERR_UNSUPPORTED;
     if (c.precision == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward added below
-    if (c.path == MOE_PATH_DECODE) return MOE_ERR_UNSUPPORTED;
+    // small-batch inference runs the weight-streaming kernels (nvfp4moe README,
+    // "MoE layer": batch-one and small-batch decode get their own launch grid)
+    const bool decode_ok = c.training == 0 && c.precision == MOE_BF16 && R > 0 &&
+                           R <= kMaxDecodeRows;
+    if (c.path == MOE_PATH_DECODE && !decode_ok) return MOE_ERR_UNSUPPORTED;
 
     moe_plan_s* p = new (std::nothrow) moe_plan_s();
     if (!p) return MOE_ERR_INVALID_ARG;
     p->cfg = c;
     p->R = R;
     p->nchunks = dispatch_chunks(R);
-    p->decode = false;
+    p->decode = c.path == MOE_PATH_DECODE || (c.path == MOE_PATH_AUTO && decode_ok);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
     p->off_status = take(sizeof(int32_t));
@@ -198,6 +202,26 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     if (c.T == 0) {
         p->have_saved_forward = c.training != 0;
         return MOE_OK;
+    }
+    if (p->decode) {
+        DecodeArgs dg{};
+        dg.T = c.T; dg.d = c.d; dg.I = c.I; dg.E = c.E; dg.k = c.k;
+        dg.ids = ids; dg.scores = scores;
+        dg.x = static_cast<const uint16_t*>(x);
+        dg.w13 = static_cast<const uint16_t*>(w->w13);
+        dg.w2 = static_cast<const uint16_t*>(w->w2);
+        dg.a = p->at<uint16_t>(p->off_a);
+        dg.o = p->at<uint16_t>(p->off_o);
+        dg.y = static_cast<uint16_t*>(y);
+        dg.status = p->at<int32_t>(p->off_status);
+        hipError_t e = staged(p, MOE_STAGE_DECODE_W13, s, [&] { return launch_decode_w13(dg, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_DECODE_W2, s, [&] { return launch_decode_w2(dg, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_COMBINE, s, [&] {
+            return launch_combine(dg.o, nullptr, scores, c.T, c.k, c.d, dg.y, s);
+        });
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
     }
     int32_t* m_indptr = p->at<int32_t>(p->off_m_indptr);
     int32_t* gather = p->at<int32_t>(p->off_gather);

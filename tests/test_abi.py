@@ -57,6 +57,10 @@ def test_status_strings(L):
     (dict(T=8, d=256, I=128, E=8, k=2, training=2), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, path=9), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, precision=1, training=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=32, d=2048, I=768, E=128, k=8, path=2), moe.MOE_OK),      # decode: T*k <= 256
+    (dict(T=33, d=2048, I=768, E=128, k=8, path=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1, d=256, I=128, E=8, k=2, path=2, training=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=0, d=256, I=128, E=8, k=2, path=2), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_plan_validation(L, cfg, expect):
     c = moe.MoeConfig(cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"], cfg.get("precision", 0),

@@ -153,13 +153,14 @@ def test_forward_zero_scores_give_zero(torch_cuda):
     layer.close()
 
 
-@pytest.mark.parametrize("name", ["prefill", "train", "decode1", "decode32"])
-def test_forward_full_size_sampled(torch_cuda, name):
+@pytest.mark.parametrize("name,path", [("prefill", 0), ("train", 0), ("decode1", 0), ("decode32", 0),
+                                       ("decode1", 1), ("decode32", 1)])
+def test_forward_full_size_sampled(torch_cuda, name, path):
     torch = torch_cuda
-    say("forward full size", name)
+    say("forward full size", name, "path", path)
     inp = inputs.generate_config(name, seed=0, with_dy=False)
     t = device_inputs(inp)
-    layer = make_layer(inp)
+    layer = make_layer(inp, path=path)
     y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
     y2 = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
     torch.cuda.synchronize()
@@ -205,6 +206,109 @@ def test_graph_replay_matches_eager(torch_cuda):
         # eager work between replays
         layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
         torch.cuda.synchronize()
+    layer.close()
+
+
+# ------------------------------------------------------------------ decode path
+
+DECODE_SHAPES = [
+    # T, d, I, E, k, routing
+    (1, 256, 128, 8, 2, "uniform"),
+    (7, 512, 384, 16, 4, "uniform"),
+    (3, 256, 128, 8, 8, "uniform"),        # every token picks every expert: 3 rows each
+    (20, 256, 192, 4, 4, "uniform"),       # 20 rows per expert: two 16-row groups
+    (64, 128, 64, 1, 1, "uniform"),        # dense layer through the decode kernels, 64 rows
+    (8, 320, 192, 64, 32, "uniform"),      # k = 32
+    (30, 256, 128, 128, 8, "zipf"),        # skewed, some experts with many rows, most empty
+    (256, 128, 64, 200, 1, "uniform"),     # T*k at the decode limit
+]
+
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", DECODE_SHAPES)
+def test_decode_small(torch_cuda, T, d, I, E, k, routing):
+    torch = torch_cuda
+    say("decode small", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=17)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=2)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    y2 = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    assert flags == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # counters reset between calls
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    e = rel(np_of(y), ref)
+    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
+    assert e <= TOL_BF16
+    layer.close()
+
+
+def test_decode_zero_scores_and_rerouting(torch_cuda):
+    torch = torch_cuda
+    inp = inputs.generate(16, 256, 128, 32, 4, seed=21)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=2)
+    y0 = layer.forward(t["x"], t["ids"], torch.zeros_like(t["scores"]), t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert np.all(y0.view(torch.int16).cpu().numpy() == 0)
+    # a different routing in between must not disturb the next call
+    other = inputs.uniform_routing(np.random.default_rng(99), inp.T, inp.E, inp.k)
+    layer.forward(t["x"], torch.from_numpy(other).to(dev()), t["scores"], t["w13"], t["w2"])
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    assert rel(np_of(y), ref) <= TOL_BF16
+    layer.close()
+
+
+def test_decode_graph_replay_matches_eager(torch_cuda):
+    torch = torch_cuda
+    inp = inputs.generate(4, 512, 256, 16, 4, seed=23)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=2)
+    y_eager = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    y_out = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)
+    for rep in range(4):
+        y_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_out.view(torch.int16), y_eager.view(torch.int16)), rep
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+    layer.close()
+
+
+def test_decode_flags_invalid_routing(torch_cuda):
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    inp = inputs.generate(4, 256, 128, 8, 2, seed=5)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=2)
+    bad = inp.ids.copy()
+    bad[1, 1] = bad[1, 0]
+    layer.forward(t["x"], torch.from_numpy(bad).to(dev()), t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags == moe.MOE_DEV_ID_DUPLICATE
+    bad = inp.ids.copy()
+    bad[2, 0] = -3
+    layer.forward(t["x"], torch.from_numpy(bad).to(dev()), t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags & moe.MOE_DEV_ID_OUT_OF_RANGE
+    layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status()
+    assert st == moe.MOE_OK and flags == 0
     layer.close()
 
 
