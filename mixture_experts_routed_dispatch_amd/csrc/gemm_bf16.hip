@@ -19,25 +19,36 @@
 //   WGRAD_W2   a^T     (MN-major)           (probs * dy[gather])^T    R_e    dW2_e [d, I]
 //   WGRAD_W13  x[gather]^T (MN-major)       dh^T                      R_e    dW13_e [2I, d]
 //
-// Tiles are 256 (p) x 256 (q) with a K step of 64, four waves of 128 x 128
-// (4 x 4 MFMA blocks of 32 x 32, 256 FP32 accumulators per lane).  Operand
-// tiles are staged through registers into a double-buffered LDS area
-// (rows padded to 144 bytes so the 32 rows a fragment read touches fall on
-// distinct banks).  K-major operands are copied as 16-byte chunks;
-// MN-major operands are loaded as 8 x 8 blocks and transposed in registers
-// before the LDS write.  The grid is persistent: each workgroup walks a tile
-// list built from m_indptr on the device, so the host never reads routing
-// counts; consecutive tile ids are given to workgroups of the same XCD so
-// that the operand slices they share stay in that XCD's L2.
+// Workgroup tile 256 (p) x 256 (q), four waves of 128 x 128 (4 x 4 MFMA blocks
+// of 32 x 32, 256 FP32 accumulators per lane).  K advances in stages of 32
+// through a ring of four LDS buffers (32 KiB each: both operands, rows of 64
+// bytes whose 16-byte chunks are XOR-swizzled so fragment reads and chunk writes
+// are bank-conflict free).  A workgroup walks its tiles as one continuous stream
+// of stages; during stage s it
+//   * computes stage s from buffer s % 4 (two k steps of 16 MFMAs; the fragments
+//     of the second step are read in the shadow of the first step's MFMAs, and
+//     those of stage s + 1's first step in the shadow of the second step's),
+//   * writes the global data of stage s + 2 (held in registers) into buffer
+//     (s + 2) % 4 and issues the global loads of stage s + 3 into those
+//     registers,
+// and ends with one barrier.  Buffer s + 1 was completed before the previous
+// barrier, so the barrier is never waited on for fresh data and the stream does
+// not stall at tile boundaries.  K-major operands are copied as 16-byte chunks;
+// MN-major ones (the transposed products of backward) as 8 x 8 blocks transposed
+// in registers.  The tile list is built on the device from m_indptr, so the host
+// never reads routing counts; consecutive tile ids go to workgroups of one XCD
+// so that the operand slices they share stay in that XCD's L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int TP = 256, TQ = 256, TK = 64;
-constexpr int LDS_STRIDE = TK + 8;   // elements; 144-byte rows
+constexpr int TP = 256, TQ = 256, TK = 32;
+constexpr int NBUF = 4;
 constexpr int NTHR = 256;
+constexpr int OPB = TP * TK * 2;          // one operand of one stage: 16 KiB
+constexpr int BUFB = 2 * OPB;             // one stage buffer (P then Q): 32 KiB
 
 struct __attribute__((aligned(16))) Chunk { uint32_t w[4]; };
 
@@ -46,10 +57,12 @@ __device__ __forceinline__ Chunk ld16(const uint16_t* p) {
     Chunk c; c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
     return c;
 }
-__device__ __forceinline__ void st16(uint16_t* p, const Chunk& c) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
-}
 __device__ __forceinline__ Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0; return c; }
+
+// Byte offset of logical 16-byte chunk c (k = 8c .. 8c+7 of the stage) of row r in
+// an operand tile: 64-byte rows, chunk slot c ^ ((r >> 1) & 3).  Eight consecutive
+// rows at one chunk then cover all eight 16-byte bank groups.
+__device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
 
 // out[m] holds element m of each in[k] (k = 0..7): the 8 x 8 BF16 transpose.
 __device__ __forceinline__ void transpose8x8(const Chunk in[8], Chunk out[8]) {
@@ -89,20 +102,21 @@ template <int MODE> __device__ __forceinline__ int k_size(const GemmArgs& g, int
 }
 
 struct TileCtx {
-    int e, mb, rows, pt, qt;
+    int e, mb, rows, pt, qt, nk;
 };
 
 template <int MODE>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t sP[2][TP * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TQ * LDS_STRIDE];
+    __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ int cum[257];
     __shared__ int wtot[NTHR / MOE_WAVE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wp = wave & 1, wq = wave >> 1;
     const int E = g.E;
     const int nPt = num_p_tiles<MODE>(g);
+    constexpr bool kPk = Traits<MODE>::kP_kmajor, kQk = Traits<MODE>::kQ_kmajor;
 
     // ---- tile list: tiles of expert e are cum[e] .. cum[e+1]-1
     {
@@ -131,10 +145,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     const int total = cum[E];
     const int G = gridDim.x;
     const int vid = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    if (vid >= total) return;
 
-    for (int tile = vid; tile < total; tile += G) {
-        // expert owning this tile: largest e with cum[e] <= tile
-        int lo = 0, hi = E - 1;
+    auto coords = [&](int tile) {
+        int lo = 0, hi = E - 1;                   // largest e with cum[e] <= tile
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (cum[mid] <= tile) lo = mid; else hi = mid - 1;
@@ -146,221 +160,284 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         c.rows = g.m_indptr[lo + 1] - c.mb;
         c.qt = local / nPt;
         c.pt = local - c.qt * nPt;
+        const int nk = (k_size<MODE>(g, c.rows) + TK - 1) / TK;
+        c.nk = nk > 0 ? nk : 1;                   // an empty expert still runs one all-zero stage
+        return c;
+    };
 
-        const int Ksz = k_size<MODE>(g, c.rows);
-        const int nk = (Ksz + TK - 1) / TK;
-
-        // ---- per-tile operand addressing
-        // K-major operands: thread owns chunk column kc and rows (tid>>3) + 32 i.
-        const int kc = tid & 7;
-        const uint16_t* rowP[8];
-        const uint16_t* rowQ[8];
-        if constexpr (Traits<MODE>::kP_kmajor) {
+    // ------------------------------------------------------------ K-major operands: direct copies
+    // A K-major operand tile of one stage is 16 blocks of 1 KiB (16 rows x 64 bytes).
+    // Wave w copies blocks 4w .. 4w+3 of each K-major operand with
+    // global_load_lds_dwordx4: lane L fetches 16 bytes from global memory and the
+    // hardware writes them to LDS at (block start + 16 L), i.e. row 16 blk + L/4,
+    // chunk slot L%4, which holds logical chunk (L%4) ^ ((row >> 1) & 3).  The copies
+    // bypass registers; they are issued three stages ahead and waited for with
+    // explicit vmcnt counts (issued as inline assembly, so the compiler neither
+    // tracks nor waits for them: loads complete in issue order, and the wait before a
+    // barrier leaves exactly the younger copies outstanding).
+    constexpr int kDmaOps = (kPk ? 4 : 0) + (kQk ? 4 : 0);     // copies per wave per stage
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+    const int drow_in_blk = lane >> 2;
+    // byte offsets of this lane's rows: P blocks (j = 0..3), then Q blocks
+    uint32_t dvoff[8];
+    const char* pbase_e = nullptr;        // P base of the load cursor's expert
+    auto dma_offsets = [&](const TileCtx& c, const int src[4]) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int pr = (tid >> 3) + 32 * i;
-                if constexpr (MODE == FWD_W13) {
-                    const int half = pr >> 7, wi = pr & 127;
-                    int ii = c.pt * 128 + half * 64 + (wi & 63);
-                    if (ii >= g.I) ii = g.I - 1;
-                    const int wrow = (wi >= 64) ? g.I + ii : ii;
-                    rowP[i] = g.w13 + ((size_t)c.e * 2 * g.I + wrow) * g.d + kc * 8;
-                } else {  // FWD_W2
-                    int p = c.pt * TP + pr;
-                    if (p >= g.d) p = g.d - 1;
-                    rowP[i] = g.w2 + ((size_t)c.e * g.d + p) * g.I + kc * 8;
-                }
+        for (int j = 0; j < 4; ++j) {
+            const int r = (4 * wave + j) * 16 + drow_in_blk;       // row of the stage tile
+            const int cl = (lane & 3) ^ ((r >> 1) & 3);           // logical chunk it holds
+            if constexpr (MODE == FWD_W13) {
+                // rows [0,64) gate i0.., [64,128) up i0.., [128,192) gate i0+64.., [192,256) up i0+64..
+                int ii = c.pt * 128 + (r >> 7) * 64 + (r & 63);
+                if (ii >= g.I) ii = g.I - 1;
+                const int wrow = ((r >> 6) & 1) ? g.I + ii : ii;
+                dvoff[j] = (uint32_t)(wrow * g.d + 8 * cl) * 2u;
+            } else if constexpr (MODE == FWD_W2) {
+                int pr = c.pt * TP + r;
+                if (pr >= g.d) pr = g.d - 1;
+                dvoff[j] = (uint32_t)(pr * g.I + 8 * cl) * 2u;
+            }
+            if constexpr (kQk) {
+                const int qs = src[j];
+                if constexpr (MODE == FWD_W13 || MODE == DGRAD_W2) dvoff[4 + j] = (uint32_t)(qs * g.d + 8 * cl) * 2u;
+                else if constexpr (MODE == FWD_W2) dvoff[4 + j] = (uint32_t)(qs * g.I + 8 * cl) * 2u;
+                else dvoff[4 + j] = (uint32_t)(qs * 2 * g.I + 8 * cl) * 2u;   // DGRAD_W13
             }
         }
-        if constexpr (Traits<MODE>::kQ_kmajor) {
+        if constexpr (MODE == FWD_W13) pbase_e = reinterpret_cast<const char*>(g.w13 + (size_t)c.e * 2 * g.I * g.d);
+        if constexpr (MODE == FWD_W2) pbase_e = reinterpret_cast<const char*>(g.w2 + (size_t)c.e * g.d * g.I);
+    };
+    const char* qbase = nullptr;
+    if constexpr (MODE == FWD_W13) qbase = reinterpret_cast<const char*>(g.x);
+    if constexpr (MODE == DGRAD_W2) qbase = reinterpret_cast<const char*>(g.dy);
+    if constexpr (MODE == FWD_W2) qbase = reinterpret_cast<const char*>(g.a);
+    if constexpr (MODE == DGRAD_W13) qbase = reinterpret_cast<const char*>(g.dh);
+    // source rows (token or routed row) of this lane's 4 Q block rows in tile c
+    auto q_src = [&](const TileCtx& c, int src[4]) {
+        if constexpr (kQk) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int rr = c.qt * TQ + (tid >> 3) + 32 * i;
-                if (rr >= c.rows) rr = 0;            // ragged tail: any row of the expert
-                const int r = c.mb + rr;
-                if constexpr (MODE == FWD_W13) rowQ[i] = g.x + (size_t)g.gather[r] * g.d + kc * 8;
-                else if constexpr (MODE == FWD_W2) rowQ[i] = g.a + (size_t)r * g.I + kc * 8;
-                else if constexpr (MODE == DGRAD_W2) rowQ[i] = g.dy + (size_t)g.gather[r] * g.d + kc * 8;
-                else rowQ[i] = g.dh + (size_t)r * 2 * g.I + kc * 8;  // DGRAD_W13
+            for (int j = 0; j < 4; ++j) {
+                int rr = c.qt * TQ + (4 * wave + j) * 16 + drow_in_blk;
+                if (rr >= c.rows) rr = c.rows > 0 ? c.rows - 1 : 0;   // ragged tail: a row of the expert
+                if constexpr (MODE == FWD_W13 || MODE == DGRAD_W2) src[j] = g.gather[c.mb + rr];
+                else src[j] = c.mb + rr;
             }
         }
-        // MN-major operands: thread owns an 8 x 8 block: mn block mnb, k block kb.
-        const int mnb = tid & 31, kb = tid >> 5;
+    };
+    auto dma1 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(base) : "memory");
+    };
+    // copies of stage kt of the load cursor's tile into ring buffer buf
+    auto dma_stage = [&](int kt, int buf) {
+        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
+        const int kbytes = kt * TK * 2;
+        if constexpr (kPk) {
+            const char* b = pbase_e + kbytes;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dma1(dst + j * 1024, dvoff[j], b);
+        }
+        if constexpr (kQk) {
+            const char* b = qbase + kbytes;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dma1(dst + OPB + j * 1024, dvoff[4 + j], b);
+        }
+    };
+    // wait until at most n of this wave's copies are outstanding
+    auto wait_dma = [&]() {
+        if constexpr (kDmaOps == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if constexpr (kDmaOps == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    };
 
-        Chunk regP[8], regQ[8];
-
-        auto load_stage = [&](int kt) {
+    // ------------------------------------------------------------ MN-major operands: via registers
+    // One 8 (k) x 8 (mn) block per thread: threads 0..127 own a P block; with an
+    // MN-major Q too (weight gradients), threads 128..255 own a Q block.  Loaded one
+    // stage before it is written, transposed in registers on the way to LDS.
+    constexpr bool kStaged = !kPk;
+    Chunk st[8];
+    auto load_stage = [&](const TileCtx& c, int kt) {
+        if constexpr (kStaged) {
             const int k0 = kt * TK;
-            if constexpr (Traits<MODE>::kP_kmajor) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) regP[i] = ld16(rowP[i] + k0);
-            } else {
-                const int p = c.pt * TP + mnb * 8;
+            const int bt = tid & 127;
+            const int mnb = bt & 31, kb = bt >> 5;
+            if (tid < 128) {
+                const int pcol = c.pt * TP + mnb * 8;
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const int k = k0 + kb * 8 + kk;
+                    Chunk v = zero_chunk();
                     if constexpr (MODE == DGRAD_W2) {
-                        regP[kk] = (p < g.I) ? ld16(g.w2 + ((size_t)c.e * g.d + k) * g.I + p) : zero_chunk();
+                        if (pcol < g.I) v = ld16(g.w2 + ((size_t)c.e * g.d + k) * g.I + pcol);
                     } else if constexpr (MODE == DGRAD_W13) {
-                        regP[kk] = (p < g.d) ? ld16(g.w13 + ((size_t)c.e * 2 * g.I + k) * g.d + p) : zero_chunk();
+                        if (pcol < g.d) v = ld16(g.w13 + ((size_t)c.e * 2 * g.I + k) * g.d + pcol);
                     } else if constexpr (MODE == WGRAD_W2) {
-                        regP[kk] = (k < c.rows && p < g.I) ? ld16(g.a + (size_t)(c.mb + k) * g.I + p) : zero_chunk();
+                        if (k < c.rows && pcol < g.I) v = ld16(g.a + (size_t)(c.mb + k) * g.I + pcol);
                     } else {  // WGRAD_W13
-                        regP[kk] = (k < c.rows && p < g.d)
-                                       ? ld16(g.x + (size_t)g.gather[c.mb + k] * g.d + p) : zero_chunk();
+                        if (k < c.rows && pcol < g.d) v = ld16(g.x + (size_t)g.gather[c.mb + k] * g.d + pcol);
                     }
+                    st[kk] = v;
                 }
-            }
-            if constexpr (Traits<MODE>::kQ_kmajor) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) regQ[i] = ld16(rowQ[i] + k0);
-            } else {
-                const int q = c.qt * TQ + mnb * 8;
+            } else if constexpr (!kQk) {
+                const int qcol = c.qt * TQ + mnb * 8;
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const int k = k0 + kb * 8 + kk;
+                    Chunk v = zero_chunk();
                     if constexpr (MODE == WGRAD_W2) {
-                        if (k < c.rows && q < g.d) {
+                        if (k < c.rows && qcol < g.d) {
                             const int r = c.mb + k;
-                            const Chunk v = ld16(g.dy + (size_t)g.gather[r] * g.d + q);
-                            const float s = g.probs[r];
-                            Chunk o;
+                            const Chunk dv = ld16(g.dy + (size_t)g.gather[r] * g.d + qcol);
+                            const float sc = g.probs[r];
 #pragma unroll
-                            for (int w = 0; w < 4; ++w) o.w[w] = pack_bf16(bf16lo(v.w[w]) * s, bf16hi(v.w[w]) * s);
-                            regQ[kk] = o;
-                        } else {
-                            regQ[kk] = zero_chunk();
+                            for (int w = 0; w < 4; ++w)
+                                v.w[w] = pack_bf16(bf16lo(dv.w[w]) * sc, bf16hi(dv.w[w]) * sc);
                         }
                     } else {  // WGRAD_W13
-                        regQ[kk] = (k < c.rows && q < 2 * g.I)
-                                       ? ld16(g.dh + (size_t)(c.mb + k) * 2 * g.I + q) : zero_chunk();
+                        if (k < c.rows && qcol < 2 * g.I) v = ld16(g.dh + (size_t)(c.mb + k) * 2 * g.I + qcol);
                     }
+                    st[kk] = v;
                 }
             }
-        };
-
-        auto store_stage = [&](int buf) {
-            if constexpr (Traits<MODE>::kP_kmajor) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) st16(&sP[buf][((tid >> 3) + 32 * i) * LDS_STRIDE + kc * 8], regP[i]);
-            } else {
+        }
+    };
+    auto store_stage = [&](int buf) {
+        if constexpr (kStaged) {
+            const int bt = tid & 127;
+            const int mnb = bt & 31, kb = bt >> 5;
+            if (tid < 128 || !kQk) {
+                char* dst = lds + buf * BUFB + (tid < 128 ? 0 : OPB);
                 Chunk t[8];
-                transpose8x8(regP, t);
+                transpose8x8(st, t);
 #pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int mm = (m + mnb) & 7;
-                    st16(&sP[buf][(mnb * 8 + mm) * LDS_STRIDE + kb * 8], t[mm]);
-                }
+                for (int m = 0; m < 8; ++m)
+                    *reinterpret_cast<uint4*>(dst + lofs(mnb * 8 + m, kb)) =
+                        make_uint4(t[m].w[0], t[m].w[1], t[m].w[2], t[m].w[3]);
             }
-            if constexpr (Traits<MODE>::kQ_kmajor) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) st16(&sQ[buf][((tid >> 3) + 32 * i) * LDS_STRIDE + kc * 8], regQ[i]);
-            } else {
-                Chunk t[8];
-                transpose8x8(regQ, t);
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    const int mm = (m + mnb) & 7;
-                    st16(&sQ[buf][(mnb * 8 + mm) * LDS_STRIDE + kb * 8], t[mm]);
-                }
-            }
-        };
+        }
+    };
 
-        f32x16_t acc[4][4];
+    // ------------------------------------------------------------ fragments
+    // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
+    // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
+    int fragP[4], fragQ[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        fragP[b] = lofs(wp * 128 + b * 32 + (lane & 31), lane >> 5);
+        fragQ[b] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), lane >> 5);
+    }
+    auto read_frags = [&](int buf, int ks, bf16x8_t pf[4], bf16x8_t qf[4]) {
+        const char* base = lds + buf * BUFB;
+        const int x = ks ? 32 : 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragP[b] ^ x));
+            qf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragQ[b] ^ x));
+        }
+    };
+
+    f32x16_t acc[4][4];
+    auto mfma_step = [&](const bf16x8_t pf[4], const bf16x8_t qf[4]) {
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[b], acc[a][b], 0, 0, 0);
+    };
 
-        if (nk > 0) {
-            load_stage(0);
-            store_stage(0);
-        }
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) load_stage(kt + 1);
+    // ------------------------------------------------------------ epilogue
+    // lane holds D[q][p .. p+3] for q = q0 + 32 b + (lane & 31), p = p0 + 32 a + 8 grp + p_sub
+    const int q_in = lane & 31;
+    const int p_sub = 4 * (lane >> 5);
+    // Plain BF16 outputs go through LDS (this wave's 8 KiB of the stage buffer just
+    // consumed) so that each store instruction writes whole 256-byte row segments:
+    // per block b, 32 rows x 128 columns are written as 8-byte pieces (16-byte chunk
+    // slot c ^ (row & 15)), read back as 16-byte chunks and stored row-contiguously.
+    auto store_rows_bf16 = [&](char* stg, int b, uint16_t* out, size_t ld, int q_first, int q_limit,
+                               int p_first, int p_limit) {
 #pragma unroll
-            for (int ks = 0; ks < TK / 16; ++ks) {
-                bf16x8_t pf[4], qf[4];
-                const int kofs = ks * 16 + (lane >> 5) * 8;
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    pf[b] = *reinterpret_cast<const bf16x8_t*>(&sP[buf][(wp * 128 + b * 32 + (lane & 31)) * LDS_STRIDE + kofs]);
-                    qf[b] = *reinterpret_cast<const bf16x8_t*>(&sQ[buf][(wq * 128 + b * 32 + (lane & 31)) * LDS_STRIDE + kofs]);
-                }
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[b], acc[a][b], 0, 0, 0);
+            for (int grp = 0; grp < 4; ++grp) {
+                const int c16 = 4 * a + grp;
+                uint2 v;
+                v.x = pack_bf16(acc[a][b][4 * grp + 0], acc[a][b][4 * grp + 1]);
+                v.y = pack_bf16(acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]);
+                *reinterpret_cast<uint2*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4) + (p_sub << 1)) = v;
             }
-            if (kt + 1 < nk) store_stage(buf ^ 1);
-            __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the wave's own LDS writes are done
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int row = 4 * it + (lane >> 4);
+            const int c16 = lane & 15;
+            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
+            const int q = q_first + row;
+            const int p = p_first + 8 * c16;
+            if (q < q_limit && p < p_limit) *reinterpret_cast<uint4*>(out + (size_t)q * ld + p) = v;
         }
-
-        // ---- epilogue: lane holds D[q][p .. p+3] for p = pbase + 8 grp
-        const int q_in = lane & 31;
-        const int p_sub = 4 * (lane >> 5);
+        __builtin_amdgcn_s_waitcnt(0xc07f);      // reads done before the slot is rewritten
+    };
+    auto epilogue = [&](const TileCtx& c, int buf) {
+        char* stg = lds + buf * BUFB + wave * 8192;
         if constexpr (MODE == FWD_W13) {
+            // a[r][i] for i = pt*128 + wp*64 + (0..63): 64 columns, 128-byte row segments
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                if (rr >= c.rows) continue;
-                const size_t r = (size_t)c.mb + rr;
 #pragma unroll
-                for (int a = 0; a < 2; ++a) {
+                for (int a = 0; a < 2; ++a)
 #pragma unroll
                     for (int grp = 0; grp < 4; ++grp) {
-                        const int i = c.pt * 128 + wp * 64 + a * 32 + 8 * grp + p_sub;
-                        if (i >= g.I) continue;
-                        float gv[4], uv[4];
+                        const int c8 = 4 * a + grp;
+                        float gv[4], uv[4], av[4];
 #pragma unroll
-                        for (int z = 0; z < 4; ++z) { gv[z] = acc[a][b][4 * grp + z]; uv[z] = acc[a + 2][b][4 * grp + z]; }
-                        uint2 av;
-                        av.x = pack_bf16(silu_f(gv[0]) * uv[0], silu_f(gv[1]) * uv[1]);
-                        av.y = pack_bf16(silu_f(gv[2]) * uv[2], silu_f(gv[3]) * uv[3]);
-                        *reinterpret_cast<uint2*>(g.out + r * g.I + i) = av;
+                        for (int z = 0; z < 4; ++z) {
+                            gv[z] = acc[a][b][4 * grp + z];
+                            uv[z] = acc[a + 2][b][4 * grp + z];
+                            av[z] = silu_f(gv[z]) * uv[z];
+                        }
+                        uint2 v;
+                        v.x = pack_bf16(av[0], av[1]);
+                        v.y = pack_bf16(av[2], av[3]);
+                        *reinterpret_cast<uint2*>(stg + q_in * 128 + ((c8 ^ (q_in & 7)) << 4) + (p_sub << 1)) = v;
                         if (g.out_h) {
-                            uint2 hg, hu;
-                            hg.x = pack_bf16(gv[0], gv[1]); hg.y = pack_bf16(gv[2], gv[3]);
-                            hu.x = pack_bf16(uv[0], uv[1]); hu.y = pack_bf16(uv[2], uv[3]);
-                            *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + i) = hg;
-                            *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + g.I + i) = hu;
+                            const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
+                            const int i = c.pt * 128 + wp * 64 + a * 32 + 8 * grp + p_sub;
+                            if (rr < c.rows && i < g.I) {
+                                const size_t r = (size_t)c.mb + rr;
+                                uint2 hg, hu;
+                                hg.x = pack_bf16(gv[0], gv[1]); hg.y = pack_bf16(gv[2], gv[3]);
+                                hu.x = pack_bf16(uv[0], uv[1]); hu.y = pack_bf16(uv[2], uv[3]);
+                                *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + i) = hg;
+                                *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + g.I + i) = hu;
+                            }
                         }
                     }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int row = 8 * it + (lane >> 3);
+                    const int c8 = lane & 7;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c8 ^ (row & 7)) << 4));
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
+                    const int i = c.pt * 128 + wp * 64 + 8 * c8;
+                    if (rr < c.rows && i < g.I)
+                        *reinterpret_cast<uint4*>(g.out + ((size_t)c.mb + rr) * g.I + i) = v;
                 }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
             }
         } else if constexpr (MODE == FWD_W2 || MODE == DGRAD_W13) {
             // o [R, d] or dxp [R, d]
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                if (rr >= c.rows) continue;
-                const size_t r = (size_t)c.mb + rr;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-#pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        const int p = c.pt * TP + wp * 128 + a * 32 + 8 * grp + p_sub;
-                        if (p >= g.d) continue;
-                        uint2 v;
-                        v.x = pack_bf16(acc[a][b][4 * grp + 0], acc[a][b][4 * grp + 1]);
-                        v.y = pack_bf16(acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]);
-                        *reinterpret_cast<uint2*>(g.out + r * g.d + p) = v;
-                    }
-                }
-            }
+            for (int b = 0; b < 4; ++b)
+                store_rows_bf16(stg, b, g.out + (size_t)c.mb * g.d, g.d, c.qt * TQ + wq * 128 + b * 32,
+                                c.rows, c.pt * TP + wp * 128, g.d);
         } else if constexpr (MODE == DGRAD_W2) {
-            // dA = probs[r] * acc; dg = dA u s(g)(1 + g(1 - s(g))), du = dA silu(g)
+            // dA = probs[r] * acc; dg = dA u s(g)(1 + g(1 - s(g))), du = dA g s(g)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
                 if (rr >= c.rows) continue;
                 const size_t r = (size_t)c.mb + rr;
-                const float s = g.probs[r];
+                const float sc = g.probs[r];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
 #pragma unroll
@@ -374,7 +451,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                         float dg[4], du[4];
 #pragma unroll
                         for (int z = 0; z < 4; ++z) {
-                            const float dA = s * acc[a][b][4 * grp + z];
+                            const float dA = sc * acc[a][b][4 * grp + z];
                             const float sg = sigmoid_f(gv[z]);
                             dg[z] = dA * uv[z] * sg * (1.0f + gv[z] * (1.0f - sg));
                             du[z] = dA * gv[z] * sg;
@@ -391,25 +468,89 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             // weight gradients: out[e][q][p], q < Qsz rows, p < Psz columns
             const int Psz = (MODE == WGRAD_W2) ? g.I : g.d;
             const int Qsz = (MODE == WGRAD_W2) ? g.d : 2 * g.I;
-            uint16_t* base = g.out + (size_t)c.e * Qsz * Psz;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int q = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                if (q >= Qsz) continue;
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-#pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        const int p = c.pt * TP + wp * 128 + a * 32 + 8 * grp + p_sub;
-                        if (p >= Psz) continue;
-                        uint2 v;
-                        v.x = pack_bf16(acc[a][b][4 * grp + 0], acc[a][b][4 * grp + 1]);
-                        v.y = pack_bf16(acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]);
-                        *reinterpret_cast<uint2*>(base + (size_t)q * Psz + p) = v;
-                    }
-                }
-            }
+            for (int b = 0; b < 4; ++b)
+                store_rows_bf16(stg, b, g.out + (size_t)c.e * Qsz * Psz, Psz, c.qt * TQ + wq * 128 + b * 32,
+                                Qsz, c.pt * TP + wp * 128, Psz);
         }
+    };
+
+    // ------------------------------------------------------------ stage stream
+    // Stage s of the stream lives in ring buffer s % 4.  During stage s the copies
+    // of stage s + 3 are issued (K-major) and the registers of stage s + 2 are
+    // written (MN-major); the barrier ending stage s publishes stage s + 2 (its
+    // copies, issued during stage s - 1, are waited for) and ring buffer s + 1 was
+    // published one barrier earlier, so the first fragments of stage s + 1 are read
+    // before it.  The load cursor runs three stages ahead of the compute cursor;
+    // once the stream is exhausted it repeats its last stage into buffers no later
+    // stage reads.
+    int l_tile = vid, l_kt = 0;
+    TileCtx lc = coords(l_tile);
+    int n_src[4] = {0, 0, 0, 0};
+    {
+        int src[4] = {0, 0, 0, 0};
+        q_src(lc, src);
+        dma_offsets(lc, src);
+    }
+    if (l_tile + G < total) q_src(coords(l_tile + G), n_src);
+    auto advance_load = [&]() {
+        if (++l_kt < lc.nk) return;
+        if (l_tile + G >= total) { l_kt = lc.nk - 1; return; }
+        l_kt = 0;
+        l_tile += G;
+        lc = coords(l_tile);
+        dma_offsets(lc, n_src);
+        if (l_tile + G < total) q_src(coords(l_tile + G), n_src);   // lands during this tile
+    };
+
+    // prologue: stages 0, 1, 2
+    if constexpr (kDmaOps > 0) {
+        dma_stage(l_kt, 0);
+    }
+    if constexpr (kStaged) { load_stage(lc, l_kt); store_stage(0); }
+    advance_load();
+    if constexpr (kDmaOps > 0) dma_stage(l_kt, 1);
+    if constexpr (kStaged) { load_stage(lc, l_kt); store_stage(1); }
+    advance_load();
+    if constexpr (kDmaOps > 0) dma_stage(l_kt, 2);
+    if constexpr (kStaged) load_stage(lc, l_kt);
+    advance_load();
+    wait_dma();                        // stages 0 and 1 copied (stage 2 may be in flight)
+    __syncthreads();
+
+    bf16x8_t fa[4], fb[4], fc[4], fd[4];
+    read_frags(0, 0, fa, fc);
+
+    int c_tile = vid;
+    TileCtx cc = coords(c_tile);
+    int gs = 0;
+    while (true) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+        for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
+            // k step 0: MFMAs on (fa, fc); meanwhile read step 1's fragments, issue the
+            // copies of stage gs + 3, write the registers of stage gs + 2
+            read_frags(gs & 3, 1, fb, fd);
+            if constexpr (kDmaOps > 0) dma_stage(l_kt, (gs + 3) & 3);
+            if constexpr (kStaged) store_stage((gs + 2) & 3);
+            mfma_step(fa, fc);
+            if constexpr (kStaged) load_stage(lc, l_kt);
+            // k step 1: MFMAs on (fb, fd); meanwhile read stage gs + 1's first fragments
+            read_frags((gs + 1) & 3, 0, fa, fc);
+            mfma_step(fb, fd);
+            advance_load();
+            wait_dma();                // this wave's copies of stage gs + 2 have landed
+            __syncthreads();
+        }
+        epilogue(cc, (gs - 1) & 3);
+        c_tile += G;
+        if (c_tile >= total) break;
+        __syncthreads();               // the staging slots are copied into again from the next stage
+        cc = coords(c_tile);
     }
 }
 
