@@ -60,9 +60,13 @@ __device__ __forceinline__ Chunk ld16(const uint16_t* p) {
 __device__ __forceinline__ Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0; return c; }
 
 // Byte offset of logical 16-byte chunk c (k = 8c .. 8c+7 of the stage) of row r in
-// an operand tile: 64-byte rows, chunk slot c ^ ((r >> 1) & 3).  Eight consecutive
-// rows at one chunk then cover all eight 16-byte bank groups.
-__device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
+// an operand tile: 64-byte rows, chunk slot c ^ swz(r).  swz maps bits (2, 3) of r
+// one-to-one for fixed bits (0, 1), and bits (1, 2) one-to-one for fixed bits
+// (0, 3), so the same chunk of 16 consecutive rows covers all sixteen 16-byte slots
+// of a 256-byte bank line, and of 8 consecutive rows all eight slots of a 128-byte
+// line: fragment reads are free of bank conflicts with 64 or 32 banks.
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+__device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
 
 // out[m] holds element m of each in[k] (k = 0..7): the 8 x 8 BF16 transpose.
 __device__ __forceinline__ void transpose8x8(const Chunk in[8], Chunk out[8]) {
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = (4 * wave + j) * 16 + drow_in_blk;       // row of the stage tile
-            const int cl = (lane & 3) ^ ((r >> 1) & 3);           // logical chunk it holds
+            const int cl = (lane & 3) ^ swz(r);                   // logical chunk it holds
             if constexpr (MODE == FWD_W13) {
                 // rows [0,64) gate i0.., [64,128) up i0.., [128,192) gate i0+64.., [192,256) up i0+64..
                 int ii = c.pt * 128 + (r >> 7) * 64 + (r & 63);
@@ -241,6 +245,17 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             const char* b = qbase + kbytes;
 #pragma unroll
             for (int j = 0; j < 4; ++j) dma1(dst + OPB + j * 1024, dvoff[4 + j], b);
+        }
+    };
+    // copy j of stage kt (j < 4: P block j, else Q block j - 4; only K-major operands)
+    auto dma_one = [&](int kt, int buf, int j) {
+        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
+        const int kbytes = kt * TK * 2;
+        if constexpr (kPk && kQk) {
+            if (j < 4) dma1(dst + j * 1024, dvoff[j], pbase_e + kbytes);
+            else dma1(dst + OPB + (j - 4) * 1024, dvoff[j], qbase + kbytes);
+        } else if constexpr (kQk) {
+            if (j < 4) dma1(dst + OPB + j * 1024, dvoff[4 + j], qbase + kbytes);
         }
     };
     // wait until at most n of this wave's copies are outstanding
@@ -336,12 +351,32 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
 
     f32x16_t acc[4][4];
-    auto mfma_step = [&](const bf16x8_t pf[4], const bf16x8_t qf[4]) {
+    // One k step: 16 MFMAs on (pf, qf) in four groups of four (row block a).  Into
+    // each group go the LDS reads of P and Q fragment a of the next k step (from ring
+    // buffer rbuf, k step rks, into npf / nqf) and, after it, copy `dma_first + a` of
+    // the stage being prefetched, so that reads and copies are spread over the MFMAs
+    // instead of queueing up together.  The scheduling fences keep that order (the
+    // copies are inline assembly, which the MFMAs could otherwise drift across).
+    auto mfma_step = [&](const bf16x8_t pf[4], const bf16x8_t qf[4], int rbuf, int rks,
+                         bf16x8_t npf[4], bf16x8_t nqf[4], int dma_kt, int dma_buf, int dma_first) {
+        const char* rbase = lds + rbuf * BUFB;
+        const int x = rks ? 32 : 0;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[b], acc[a][b], 0, 0, 0);
+        for (int a = 0; a < 4; ++a) {
+            acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[0], acc[a][0], 0, 0, 0);
+            npf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[a] ^ x));
+            acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[1], acc[a][1], 0, 0, 0);
+            nqf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[a] ^ x));
+            acc[a][2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[2], acc[a][2], 0, 0, 0);
+            acc[a][3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[3], acc[a][3], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if constexpr (kDmaOps > 0) dma_one(dma_kt, dma_buf, dma_first + a);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // ------------------------------------------------------------ epilogue
@@ -534,14 +569,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
             // k step 0: MFMAs on (fa, fc); meanwhile read step 1's fragments, issue the
             // copies of stage gs + 3, write the registers of stage gs + 2
-            read_frags(gs & 3, 1, fb, fd);
-            if constexpr (kDmaOps > 0) dma_stage(l_kt, (gs + 3) & 3);
+            // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd),
+            // issuing the copies of stage gs + 3 and writing the registers of stage gs + 2
             if constexpr (kStaged) store_stage((gs + 2) & 3);
-            mfma_step(fa, fc);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(fa, fc, gs & 3, 1, fb, fd, l_kt, (gs + 3) & 3, 0);
             if constexpr (kStaged) load_stage(lc, l_kt);
-            // k step 1: MFMAs on (fb, fd); meanwhile read stage gs + 1's first fragments
-            read_frags((gs + 1) & 3, 0, fa, fc);
-            mfma_step(fb, fd);
+            // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, l_kt, (gs + 3) & 3, 4);
             advance_load();
             wait_dma();                // this wave's copies of stage gs + 2 have landed
             __syncthreads();
