@@ -35,6 +35,7 @@ WORKLOADS = {
     "train": ("train", True),
     "decode1": ("decode1", False),
     "decode32": ("decode32", False),
+    "mxfp8": ("mxfp8", False),
 }
 
 
@@ -197,7 +198,9 @@ def main():
     R = T * k
     t = device_inputs(inp)
     decode = cfg_name.startswith("decode")
-    layer = moe.Layer(T, d, I, E, k, training=training)
+    mx = cfg_name == "mxfp8"
+    layer = moe.Layer(T, d, I, E, k, training=training,
+                      precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
@@ -213,6 +216,12 @@ def main():
     # batch rotates over 4 copies of the whole weight set (1.2 GB each).
     ids_list = [t["ids"]]
     w_list = [(t["w13"], t["w2"])]
+    w_scales = [(None, None)]
+    if mx:
+        # weights prepared to MXFP8 once, outside the timed region
+        w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+        w_list, w_scales = [(w13q, w2q)], [(w13s, w2s)]
+        del t["w13"], t["w2"]
     if cfg_name == "decode1":
         rout = inputs.disjoint_routings(E, k, E // k, seed=1)
         ids_list = [torch.from_numpy(rout[i:i + 1]).to("cuda") for i in range(len(rout))]
@@ -223,7 +232,11 @@ def main():
     for ids_dev in ids_list:
         n_active.append(len(np.unique(ids_dev.cpu().numpy())))
     n_active_mean = float(np.mean(n_active))
-    wlist = [moe.weights(a.data_ptr(), b.data_ptr()) for a, b in w_list]
+    if len(w_scales) < len(w_list):
+        w_scales = w_scales + [(None, None)] * (len(w_list) - len(w_scales))
+    wlist = [moe.weights(a.data_ptr(), b.data_ptr(), sa.data_ptr() if sa is not None else 0,
+                         sb.data_ptr() if sb is not None else 0)
+             for (a, b), (sa, sb) in zip(w_list, w_scales)]
     state = {"i": 0}
 
     def step():
@@ -294,13 +307,15 @@ def main():
     # bytes each stage must move at least once
     min_bytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
                  "dispatch": 8.0 * R + 4.0 * (E + 1) + 12.0 * R,
+                 "quant_x": T * d * (2.0 + 1.0 + 1.0 / 32),
                  "decode_w13": n_active_mean * 2 * I * d * 2.0 + 2.0 * T * d + 2.0 * R * I + 4.0 * R,
                  "decode_w2": n_active_mean * d * I * 2.0 + 2.0 * R * I + 2.0 * R * d + 2.0 * T * d
                  + 8.0 * R}
+    mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     if dom in gemm_flop:
         achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": achieved / mfma_peak,
                 "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
                 "traffic": traffic_for(dom, args.workload)}
     else:
@@ -326,22 +341,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8-e4m3" if mx else "bf16",
         "data": "synthetic: seeded numpy draws, x ~ N(0,1), W ~ N(0,1/fan_in) in BF16, "
                 + ("Zipf(1.2) top-k routing with 8 forced-empty experts, dY ~ N(0,1)"
                    if cfg_name == "train" else "uniform distinct top-k routing")
                 + ", softmax-of-normal scores"
                 + ("; 16 routings over disjoint expert groups, cycled" if cfg_name == "decode1" else "")
                 + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
-        "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d BF16 %s" % (
-            cfg_name, T, d, I, E, k, "forward+backward" if training else "forward"),
+        "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s" % (
+            cfg_name, T, d, I, E, k, "MXFP8-E4M3" if mx else "BF16",
+            "forward+backward" if training else "forward"),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},
         "tokens_per_s": T / (ms_step * 1e-3),
         "tflops": tflops,
-        "mfma_frac_layer": tflops / PEAK_BF16_TFLOPS,
+        "mfma_frac_layer": tflops / mfma_peak,
         "gemm_tflops": gemm_tflops,
-        "gemm_mfma_frac": gemm_tflops / PEAK_BF16_TFLOPS if gemm_tflops else None,
+        "gemm_mfma_frac": gemm_tflops / mfma_peak if gemm_tflops else None,
         "stage_us": {s: round(v, 2) for s, v in stage_us.items()},
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "ms_per_step_with_kernel_events": ms_step_profiled,

@@ -90,9 +90,12 @@ typedef struct {
 /* Validate cfg against the limits (K = d and I multiples of 64, at most 256
  * experts, at most 131072 routed rows T*k; nvfp4moe README, "Limits"), choose
  * the kernels and lay out the workspace.  Host only: touches no device.
- * Returns MOE_ERR_UNSUPPORTED for MXFP8 with training = 1 and for shapes
- * outside the limits, MOE_ERR_INVALID_ARG for NULL or non-positive sizes.
- * On success *out owns host memory released by moe_plan_destroy. */
+ * MXFP8 plans are forward only and need d % 256 == 0 and I % 128 == 0.
+ * Shapes whose activations (T*d*2 bytes), routed intermediates (T*k*2I*2) or
+ * per-expert W13 (2I*d*2) reach 2^31 bytes are refused (the kernels address them
+ * with 32-bit offsets).  Returns MOE_ERR_UNSUPPORTED for MXFP8 with training = 1
+ * and for shapes outside the limits, MOE_ERR_INVALID_ARG for NULL or non-positive
+ * sizes.  On success *out owns host memory released by moe_plan_destroy. */
 moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out);
 
 /* Bytes of device workspace the plan needs (the analogue of planning memory
@@ -142,6 +145,10 @@ moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const vo
  * SwiGLU epilogue, [MXFP8: re-quantize the SwiGLU output], grouped W2 GEMM,
  * score-weighted combine in FP32 with j ascending from +0.0 and one rounding
  * to BF16 (nvfp4moe README, "MoE layer": the timed path).  y is BF16 [T, d].
+ * BF16 plans take BF16 weights; MXFP8 plans take the prepared codes in w13 / w2
+ * and their E8M0 scales in w13_scale / w2_scale (moe_prepare_weights layout;
+ * NULL scales are MOE_ERR_INVALID_ARG).  Plans with T*k <= 256 (BF16, inference)
+ * run the weight-streaming decode kernels unless cfg.path forces the prefill path.
  * With cfg.training = 1 the workspace keeps the dispatch, the W13 outputs and
  * the W2 outputs for moe_backward; a later forward overwrites them. */
 moe_status_t moe_forward(moe_plan_t plan, const void* x, const int32_t* ids, const float* scores,

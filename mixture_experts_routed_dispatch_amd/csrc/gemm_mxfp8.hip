@@ -1,0 +1,420 @@
+// gemm_mxfp8.hip -- grouped MXFP8 GEMMs of the routed expert layer's forward on gfx950.
+//
+// The blog post ("What it is selling") lists an MXFP8 E4M3 mode: activations are
+// quantized after routing and the weights are prepared beforehand.  Both expert
+// products then run on OCP MXFP8 operands (E4M3 codes with one E8M0 scale per 32
+// consecutive K elements) with FP32 accumulation, using the block-scaled MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4:
+//
+//   mode     P (p, k)                  Q (q, k)                K    output
+//   MX_W13   W13_e rows, gate/up pairs xq[gather[r]], xs       d    a = silu(g)*u re-quantized to
+//                                                                   MXFP8 along I: aq [R, I], as [R, I/32]
+//   MX_W2    W2_e rows                 aq[r], as               I    o [R, d] BF16
+//
+// The structure is the BF16 kernel's (workgroup tile 256 x 256, four waves of
+// 128 x 128, a ring of four 32 KiB LDS buffers, direct global-to-LDS copies issued
+// three stages ahead, one continuous stream of stages per workgroup); a stage is
+// 64 K elements = 64 bytes per row = two MX blocks, consumed by one MFMA per
+// (row block, column block).  Lane l of an MFMA supplies row l & 31: codes
+// 16 (l >> 5) .. + 15 of each of the stage's two MX blocks, and the scale byte of MX
+// block (l >> 5) of that row (the instruction applies lane half h's scale to block h
+// of the row, whichever lane half holds its codes).
+//
+// Scales travel as direct copies too: the 4 bytes (blocks 2 kt .. 2 kt + 3) of a
+// row cover a pair of stages; per stage pair, each wave copies the words of 64 P
+// rows and 64 Q rows into one of three 2 KiB scale slots, together with the data
+// copies of the pair's first stage.  A lane then reads the words of its four row
+// blocks once per pair and shifts them by 8 (lane >> 5) bits, so that byte 0 holds
+// its scale for the first stage of the pair and byte 2 for the second (the MFMA's
+// op_sel picks the byte).
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int TP = 256, TQ = 256, TKB = 64;   // TKB: K elements (bytes) per stage
+constexpr int NBUF = 4;
+constexpr int NTHR = 256;
+constexpr int OPB = TP * TKB;                 // one operand of one stage: 16 KiB
+constexpr int BUFB = 2 * OPB;                 // one stage buffer (P then Q): 32 KiB
+constexpr int SCB = 2048;                     // one scale slot: P words then Q words
+constexpr int NSC = 3;
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// 64-byte rows, chunk slot c ^ swz(r): conflict-free reads of one chunk of 16 (or 8)
+// consecutive rows (see the BF16 kernel).
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
+__device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
+
+struct TileCtx {
+    int e, mb, rows, pt, qt, nk;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
+    __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
+    __shared__ __attribute__((aligned(1024))) char lsc[NSC * SCB];
+    __shared__ int cum[257];
+    __shared__ int wtot[NTHR / MOE_WAVE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wp = wave & 1, wq = wave >> 1;
+    const int E = g.E;
+    const int K = MODE == MX_W13 ? g.d : g.I;          // K of the product (bytes per row)
+    const int KB = K / 32;                             // scale bytes per row
+    const int nPt = MODE == MX_W13 ? g.I / 128 : g.d / TP;
+
+    // ---- tile list: tiles of expert e are cum[e] .. cum[e+1]-1
+    {
+        int cnt = 0;
+        if (tid < E) {
+            const int rows = g.m_indptr[tid + 1] - g.m_indptr[tid];
+            cnt = ((rows + TQ - 1) / TQ) * nPt;
+        }
+        int incl = cnt;
+        for (int off = 1; off < MOE_WAVE; off <<= 1) {
+            const int v = __shfl_up(incl, off, MOE_WAVE);
+            if (lane >= off) incl += v;
+        }
+        if (lane == MOE_WAVE - 1) wtot[wave] = incl;
+        __syncthreads();
+        int pre = 0;
+        for (int w = 0; w < wave; ++w) pre += wtot[w];
+        if (tid < E) cum[tid + 1] = pre + incl;
+        if (tid == 0) cum[0] = 0;
+        __syncthreads();
+    }
+    const int total = cum[E];
+    const int G = gridDim.x;
+    const int vid = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    if (vid >= total) return;
+
+    auto coords = [&](int tile) {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (cum[mid] <= tile) lo = mid; else hi = mid - 1;
+        }
+        TileCtx c;
+        c.e = lo;
+        const int local = tile - cum[lo];
+        c.mb = g.m_indptr[lo];
+        c.rows = g.m_indptr[lo + 1] - c.mb;
+        c.qt = local / nPt;
+        c.pt = local - c.qt * nPt;
+        c.nk = K / TKB;                               // even: K is a multiple of 128
+        return c;
+    };
+
+    // row of the P operand (weight row of expert e) behind P tile row r
+    auto p_row = [&](const TileCtx& c, int r) {
+        if constexpr (MODE == MX_W13) {
+            // rows [0,64) gate i0.., [64,128) up i0.., [128,192) gate i0+64.., [192,256) up i0+64..
+            int ii = c.pt * 128 + (r >> 7) * 64 + (r & 63);
+            if (ii >= g.I) ii = g.I - 1;
+            return ((r >> 6) & 1) ? g.I + ii : ii;
+        } else {
+            const int pr = c.pt * TP + r;
+            return pr < g.d ? pr : g.d - 1;
+        }
+    };
+    // row of the Q operand (token of xq, or routed row of aq) behind Q tile row r
+    auto q_row = [&](const TileCtx& c, int r) {
+        int rr = c.qt * TQ + r;
+        if (rr >= c.rows) rr = c.rows - 1;            // ragged tail: a row of the expert
+        if constexpr (MODE == MX_W13) return (int)g.gather[c.mb + rr];
+        else return c.mb + rr;
+    };
+    const uint8_t* pdata = MODE == MX_W13 ? g.w13q : g.w2q;
+    const uint8_t* pscale = MODE == MX_W13 ? g.w13s : g.w2s;
+    const uint8_t* qdata = MODE == MX_W13 ? g.xq : g.aq;
+    const uint8_t* qscale = MODE == MX_W13 ? g.xs : g.as;
+    const size_t prows_e = MODE == MX_W13 ? (size_t)2 * g.I : (size_t)g.d;   // P rows per expert
+
+    // ------------------------------------------------------------ direct copies
+    // Data: wave w copies the 1 KiB blocks 4w .. 4w+3 of each operand of a stage;
+    // lane L fetches 16 bytes that land at (block start + 16 L) = row 16 blk + L/4,
+    // chunk slot L%4, i.e. logical chunk (L%4) ^ swz(row).
+    // Scales: wave w copies the 4-byte words (blocks 2 kt .. 2 kt+3) of P and Q tile
+    // rows 64 w + L to (slot + 256 w + 4 L) and (slot + 1024 + 256 w + 4 L).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
+    const uint32_t lsc0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lsc;
+    uint32_t dvoff[8];
+    uint32_t svoffP = 0, svoffQ = 0;
+    const char* pbase_e = nullptr;
+    const char* psbase_e = nullptr;
+    auto copy_offsets = [&](const TileCtx& c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = (4 * wave + j) * 16 + (lane >> 2);
+            const int cl = (lane & 3) ^ swz(r);
+            dvoff[j] = (uint32_t)(p_row(c, r) * K + 16 * cl);
+            dvoff[4 + j] = (uint32_t)(q_row(c, r) * K + 16 * cl);
+        }
+        const int rs = 64 * wave + lane;
+        svoffP = (uint32_t)(p_row(c, rs) * KB);
+        svoffQ = (uint32_t)(q_row(c, rs) * KB);
+        pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
+        psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * KB);
+    };
+    auto dma16 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(base) : "memory");
+    };
+    auto dma4 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(base) : "memory");
+    };
+    // data copy j (0..3 P, 4..7 Q) of stage kt into ring buffer buf
+    auto dma_data = [&](int kt, int buf, int j) {
+        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
+        if (j < 4) dma16(dst + j * 1024, dvoff[j], pbase_e + kt * TKB);
+        else dma16(dst + OPB + (j - 4) * 1024, dvoff[j], reinterpret_cast<const char*>(qdata) + kt * TKB);
+    };
+    // scale words of the stage pair holding stage kt (blocks 2 (kt & ~1) .. +3) into
+    // scale slot `slot`
+    auto dma_scales = [&](int kt, int slot) {
+        const uint32_t dst = lsc0 + slot * SCB + 256 * wave;
+        const int kb = 2 * (kt & ~1);
+        dma4(dst, svoffP, psbase_e + kb);
+        dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kb);
+    };
+
+    // ------------------------------------------------------------ fragments and scales
+    // fragment b of P (Q): row wp*128 + 32 b + (lane & 31) (wq*128 + ...). The scaled
+    // 32x32x64 fp8 MFMA takes, in lane half g = lane >> 5, bytes 16g..16g+15 of both MX
+    // blocks of the stage: block 0 in registers 0-3, block 1 in registers 4-7 (chunks g
+    // and 2 + g of the 64-byte row); the scale of (row, block h) sits in lane half h
+    int fragP[4][2], fragQ[4][2];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            fragP[b][h] = lofs(wp * 128 + b * 32 + (lane & 31), (lane >> 5) + 2 * h);
+            fragQ[b][h] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), (lane >> 5) + 2 * h);
+        }
+    auto read_frag = [&](const char* base, int off0, int off1) {
+        const uint4 x = *reinterpret_cast<const uint4*>(base + off0);
+        const uint4 y = *reinterpret_cast<const uint4*>(base + off1);
+        i32x8_t v;
+        v[0] = (int)x.x; v[1] = (int)x.y; v[2] = (int)x.z; v[3] = (int)x.w;
+        v[4] = (int)y.x; v[5] = (int)y.y; v[6] = (int)y.z; v[7] = (int)y.w;
+        return v;
+    };
+    // this lane's scale words of its four P and four Q row blocks, from scale slot
+    // `slot`, shifted so that byte 0 / byte 2 are its blocks of the pair's two stages
+    auto read_scales = [&](int slot, int sp[4], int sq[4]) {
+        const char* base = lsc + slot * SCB;
+        const int sh = 8 * (lane >> 5);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            sp[b] = (int)(*reinterpret_cast<const uint32_t*>(base + 4 * (wp * 128 + b * 32 + (lane & 31))) >> sh);
+            sq[b] = (int)(*reinterpret_cast<const uint32_t*>(base + 1024 + 4 * (wq * 128 + b * 32 + (lane & 31))) >> sh);
+        }
+    };
+
+    f32x16_t acc[4][4];
+    // One stage: 16 scaled MFMAs in four groups (row block a); each group also reads
+    // P and Q fragment a of the next stage (from ring buffer nbuf) and issues data copies
+    // 2a and 2a + 1 of the stage being prefetched.  OPSEL picks the scale byte.
+    auto stage = [&](auto opsel_tag, const i32x8_t pf[4], const i32x8_t qf[4], const int sp[4], const int sq[4],
+                     int nbuf, i32x8_t npf[4], i32x8_t nqf[4], int dma_kt, int dma_buf) {
+        constexpr int OPSEL = decltype(opsel_tag)::value;
+        const char* nb = lds + nbuf * BUFB;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[0], acc[a][0], 0, 0, OPSEL, sp[a], OPSEL, sq[0]);
+            npf[a] = read_frag(nb, fragP[a][0], fragP[a][1]);
+            acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[1], acc[a][1], 0, 0, OPSEL, sp[a], OPSEL, sq[1]);
+            nqf[a] = read_frag(nb, fragQ[a][0], fragQ[a][1]);
+            acc[a][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[2], acc[a][2], 0, 0, OPSEL, sp[a], OPSEL, sq[2]);
+            acc[a][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[3], acc[a][3], 0, 0, OPSEL, sp[a], OPSEL, sq[3]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            dma_data(dma_kt, dma_buf, 2 * a);
+            dma_data(dma_kt, dma_buf, 2 * a + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ------------------------------------------------------------ epilogue
+    const int q_in = lane & 31;
+    const int p_sub = 4 * (lane >> 5);
+    auto epilogue = [&](const TileCtx& c, int buf) {
+        if constexpr (MODE == MX_W13) {
+            // a = silu(g) * u for i = pt*128 + wp*64 + 32 a + (0..31): one MX block per
+            // (row, a), split over lanes l and l ^ 32; amax, E8M0 scale and E4M3 codes
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
+                const bool live = rr < c.rows;
+                const size_t r = (size_t)c.mb + (live ? rr : 0);
+#pragma unroll
+                for (int a = 0; a < 2; ++a) {
+                    float av[16];
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int grp = 0; grp < 4; ++grp)
+#pragma unroll
+                        for (int z = 0; z < 4; ++z) {
+                            const float gv = acc[a][b][4 * grp + z], uv = acc[a + 2][b][4 * grp + z];
+                            av[4 * grp + z] = silu_f(gv) * uv;
+                            amax = __builtin_fmaxf(amax, __builtin_fabsf(av[4 * grp + z]));
+                        }
+                    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+                    const uint32_t sb = e8m0_scale(amax);
+                    const int sh = 127 - (int)sb;
+                    const int i0 = c.pt * 128 + wp * 64 + a * 32;
+                    if (live && i0 < g.I) {
+#pragma unroll
+                        for (int grp = 0; grp < 4; ++grp) {
+                            uint32_t w = 0;
+#pragma unroll
+                            for (int z = 0; z < 4; ++z)
+                                w |= e4m3_code(__builtin_ldexpf(av[4 * grp + z], sh)) << (8 * z);
+                            *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 8 * grp + p_sub) = w;
+                        }
+                        if (lane < 32) g.as[r * (g.I / 32) + i0 / 32] = (uint8_t)sb;
+                    }
+                }
+            }
+        } else {
+            // o [R, d] in BF16 through LDS (this wave's 8 KiB of the stage buffer just
+            // consumed), stored as whole 256-byte row segments
+            char* stg = lds + buf * BUFB + wave * 8192;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int grp = 0; grp < 4; ++grp) {
+                        const int c16 = 4 * a + grp;
+                        uint2 v;
+                        v.x = pack_bf16(acc[a][b][4 * grp + 0], acc[a][b][4 * grp + 1]);
+                        v.y = pack_bf16(acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]);
+                        *reinterpret_cast<uint2*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4) + (p_sub << 1)) = v;
+                    }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+#pragma unroll
+                for (int it = 0; it < 8; ++it) {
+                    const int row = 4 * it + (lane >> 4);
+                    const int c16 = lane & 15;
+                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
+                    const int p = c.pt * TP + wp * 128 + 8 * c16;
+                    if (rr < c.rows && p < g.d) *reinterpret_cast<uint4*>(g.o + ((size_t)c.mb + rr) * g.d + p) = v;
+                }
+                __builtin_amdgcn_s_waitcnt(0xc07f);
+            }
+        }
+    };
+
+    // ------------------------------------------------------------ stage stream
+    // As in the BF16 kernel: during stage s the data copies of stage s + 3 are issued
+    // (and, when s + 3 starts a stage pair, its scale words first), the barrier ending
+    // stage s publishes stage s + 2.  Copies issued after those of stage s + 2 are the
+    // 8 data copies of stage s + 3, plus the 2 scale copies when s is odd.
+    int l_tile = vid, l_kt = 0;
+    TileCtx lc = coords(l_tile);
+    copy_offsets(lc);
+    auto advance_load = [&]() {
+        if (++l_kt < lc.nk) return;
+        if (l_tile + G >= total) { l_kt = lc.nk - 1; return; }   // past the end: repeat the last stage
+        l_kt = 0;
+        l_tile += G;
+        lc = coords(l_tile);
+        copy_offsets(lc);
+    };
+    auto issue_stage = [&](int buf, int pair_slot) {
+        if (pair_slot >= 0) dma_scales(l_kt, pair_slot);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma_data(l_kt, buf, j);
+    };
+
+    // prologue: stages 0, 1, 2, with the scale words of pairs 0 and 1
+    issue_stage(0, 0);
+    advance_load();
+    issue_stage(1, -1);
+    advance_load();
+    issue_stage(2, 1);
+    advance_load();
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");   // stages 0, 1 and pair 0's scales landed
+    __syncthreads();
+
+    i32x8_t pa[4], qa[4], pb[4], qb[4];
+    int spa[4], sqa[4], spb[4], sqb[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        pa[b] = read_frag(lds, fragP[b][0], fragP[b][1]);
+        qa[b] = read_frag(lds, fragQ[b][0], fragQ[b][1]);
+    }
+    read_scales(0, spa, sqa);
+
+    int c_tile = vid;
+    TileCtx cc = coords(c_tile);
+    int gs = 0;
+    while (true) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+        for (int kt = 0; kt < cc.nk; kt += 2, gs += 2) {
+            const int pair = gs >> 1;
+            // even stage gs: fragments (pa, qa), scale byte 0; copies of stage gs + 3
+            // (odd: no scales)
+            stage(std::integral_constant<int, 0>(), pa, qa, spa, sqa, (gs + 1) & 3, pb, qb, l_kt, (gs + 3) & 3);
+            advance_load();
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            __syncthreads();
+            // odd stage gs + 1: fragments (pb, qb), scale byte 2; copies of stage gs + 4
+            // after the scale words of the pair it starts; the next pair's scale words
+            // (copied one pair ahead) are read for the next even stage
+            read_scales((pair + 1) % NSC, spb, sqb);
+            dma_scales(l_kt, (pair + 2) % NSC);
+            stage(std::integral_constant<int, 2>(), pb, qb, spa, sqa, (gs + 2) & 3, pa, qa, l_kt, (gs + 4) & 3);
+            advance_load();
+            asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < 4; ++b) { spa[b] = spb[b]; sqa[b] = sqb[b]; }
+        }
+        epilogue(cc, (gs - 1) & 3);
+        c_tile += G;
+        if (c_tile >= total) break;
+        __syncthreads();               // the staging slots are copied into again from the next stage
+        cc = coords(c_tile);
+    }
+}
+
+template <int MODE>
+hipError_t launch_mx_mode(const MxGemmArgs& g, int num_cu, hipStream_t s) {
+    const int64_t R = (int64_t)g.T * g.k;
+    const int64_t tiles = (R / TQ + g.E) * (MODE == MX_W13 ? g.I / 128 : g.d / TP);
+    int64_t grid = tiles < num_cu ? tiles : num_cu;
+    if (grid >= 8) grid -= grid % 8;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(grouped_gemm_mx<MODE>, dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipStream_t s) {
+    switch (mode) {
+        case MX_W13: return launch_mx_mode<MX_W13>(g, num_cu, s);
+        case MX_W2: return launch_mx_mode<MX_W2>(g, num_cu, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -40,6 +40,26 @@ struct GemmArgs {
 
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
 
+// MXFP8 forward products (OCP E4M3 codes, E8M0 scale per 32 along K).
+enum MxMode { MX_W13 = 0, MX_W2 = 1 };
+
+struct MxGemmArgs {
+    int T, d, I, E, k;
+    const int32_t* m_indptr;
+    const int32_t* gather;
+    const uint8_t* xq;    // [T, d]      codes of x
+    const uint8_t* xs;    // [T, d/32]   scales of x
+    const uint8_t* w13q;  // [E, 2I, d]
+    const uint8_t* w13s;  // [E, 2I, d/32]
+    const uint8_t* w2q;   // [E, d, I]
+    const uint8_t* w2s;   // [E, d, I/32]
+    uint8_t* aq;          // [R, I]      SwiGLU output, re-quantized (MX_W13 output, MX_W2 input)
+    uint8_t* as;          // [R, I/32]
+    uint16_t* o;          // [R, d]      BF16 expert outputs (MX_W2 output)
+};
+
+hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipStream_t s);
+
 // y[t] = sum_j w[t][j] * src[slots[t][j]] (w = NULL means weight 1; slots = NULL means
 // row t*k + j), FP32, j ascending.
 hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,

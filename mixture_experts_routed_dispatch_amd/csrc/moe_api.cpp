@@ -101,7 +101,14 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (c.E > kMaxExperts || c.k > c.E || c.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)c.T * c.k;
     if (R > kMaxRoutedRows) return MOE_ERR_UNSUPPORTED;
-    if (c.precision == MOE_MXFP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward added below
+    // MXFP8 runs forward only (the blog post's MXFP8 training path is not built here);
+    // its kernels take K in stages of 64 codes and P tiles of 256 rows
+    if (c.precision == MOE_MXFP8_E4M3 && (c.training || c.d % 256 != 0 || c.I % 128 != 0))
+        return MOE_ERR_UNSUPPORTED;
+    // 32-bit byte offsets inside x, the routed intermediates and one expert's weights
+    if ((int64_t)c.T * c.d * 2 >= (1LL << 31) || R * 2 * c.I * 2 >= (1LL << 31) ||
+        (int64_t)2 * c.I * c.d * 2 >= (1LL << 31))
+        return MOE_ERR_UNSUPPORTED;
     // small-batch inference runs the weight-streaming kernels (nvfp4moe README,
     // "MoE layer": batch-one and small-batch decode get their own launch grid)
     const bool decode_ok = c.training == 0 && c.precision == MOE_BF16 && R > 0 &&
@@ -122,12 +129,16 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_gather = take(sizeof(int32_t) * (size_t)R);
     p->off_slots = take(sizeof(int32_t) * (size_t)R);
     p->off_probs = take(sizeof(float) * (size_t)R);
-    p->off_a = take(2 * (size_t)R * c.I);
+    const bool mx = c.precision == MOE_MXFP8_E4M3;
+    p->off_a = mx ? 0 : take(2 * (size_t)R * c.I);
     p->off_o = take(2 * (size_t)R * c.d);
     p->off_h = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
     p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
     p->off_dxp = c.training ? take(2 * (size_t)R * c.d) : 0;
-    p->off_xq = p->off_xs = p->off_aq = p->off_as = 0;
+    p->off_xq = mx ? take((size_t)c.T * c.d) : 0;
+    p->off_xs = mx ? take((size_t)c.T * c.d / 32) : 0;
+    p->off_aq = mx ? take((size_t)R * c.I) : 0;
+    p->off_as = mx ? take((size_t)R * c.I / 32) : 0;
     p->ws_bytes = off;
     p->ws = nullptr;
     p->ws_size = 0;
@@ -196,6 +207,8 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     if (!p || !w) return MOE_ERR_INVALID_ARG;
     const moe_config_t& c = p->cfg;
     if (c.T > 0 && (!x || !ids || !scores || !y || !w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+    if (c.T > 0 && c.precision == MOE_MXFP8_E4M3 && (!w->w13_scale || !w->w2_scale))
+        return MOE_ERR_INVALID_ARG;
     if (!p->ws) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     p->have_saved_forward = false;
@@ -233,6 +246,34 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
 
+    if (c.precision == MOE_MXFP8_E4M3) {
+        // MXFP8 (blog post "What it is selling": activations quantized after routing,
+        // prepared weights): x is quantized per token row, which equals quantizing the
+        // gathered rows since every MX block lies inside one row
+        uint8_t* xq = p->at<uint8_t>(p->off_xq);
+        uint8_t* xs = p->at<uint8_t>(p->off_xs);
+        e = staged(p, MOE_STAGE_QUANT_X, s, [&] {
+            return launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        MxGemmArgs mg{};
+        mg.T = c.T; mg.d = c.d; mg.I = c.I; mg.E = c.E; mg.k = c.k;
+        mg.m_indptr = m_indptr; mg.gather = gather;
+        mg.xq = xq; mg.xs = xs;
+        mg.w13q = static_cast<const uint8_t*>(w->w13); mg.w13s = w->w13_scale;
+        mg.w2q = static_cast<const uint8_t*>(w->w2); mg.w2s = w->w2_scale;
+        mg.aq = p->at<uint8_t>(p->off_aq); mg.as = p->at<uint8_t>(p->off_as);
+        mg.o = p->at<uint16_t>(p->off_o);
+        e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm_mxfp8(MX_W13, mg, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_W2, s, [&] { return launch_gemm_mxfp8(MX_W2, mg, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_COMBINE, s, [&] {
+            return launch_combine(p->at<uint16_t>(p->off_o), slots, scores, c.T, c.k, c.d,
+                                  static_cast<uint16_t*>(y), s);
+        });
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
     g.m_indptr = m_indptr; g.gather = gather; g.probs = probs;

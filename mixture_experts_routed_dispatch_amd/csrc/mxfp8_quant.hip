@@ -16,30 +16,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// E4M3 (OCP "E4M3FN") code of a finite float, nearest even, saturating.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = __builtin_fabsf(v);
-    if (a >= 448.0f) return sign | 0x7Eu;
-    if (a < 0.015625f) {                                   // below 2^-6: steps of 2^-9
-        const float m = __builtin_rintf(a * 512.0f);        // exact scaling, ties to even
-        return sign | (uint32_t)m;                          // 8 steps is code 0x08 = 2^-6
-    }
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127; // a is normal here
-    float m = __builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 8.0f);
-    if (m == 8.0f) { m = 0.0f; e += 1; }
-    return sign | (uint32_t)(((e + 7) << 3) | (int)m);
-}
-
-// E8M0 byte of a block whose largest magnitude is amax (a BF16 value in FP32)
-__device__ __forceinline__ uint32_t e8m0_scale(float amax) {
-    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);   // 0 for zero / subnormal
-    if (ef == 0) return 0u;
-    int b = ef - 8;                      // (ef - 127) - 8 + 127
-    b = b < 0 ? 0 : (b > 254 ? 254 : b);
-    return (uint32_t)b;
-}
-
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __restrict__ v,
                                                             int64_t nblocks,
                                                             uint8_t* __restrict__ codes,

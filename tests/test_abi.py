@@ -57,6 +57,11 @@ def test_status_strings(L):
     (dict(T=8, d=256, I=128, E=8, k=2, training=2), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, path=9), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, precision=1, training=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d=256, I=128, E=8, k=2, precision=1), moe.MOE_OK),            # MXFP8 forward
+    (dict(T=16384, d=4096, I=2048, E=64, k=8, precision=1), moe.MOE_OK),     # the MXFP8 workload
+    (dict(T=8, d=192, I=128, E=8, k=2, precision=1), moe.MOE_ERR_UNSUPPORTED),  # d % 256
+    (dict(T=8, d=256, I=192, E=8, k=2, precision=1), moe.MOE_ERR_UNSUPPORTED),  # I % 128
+    (dict(T=8, d=32768, I=16384, E=8, k=2), moe.MOE_ERR_UNSUPPORTED),      # 32-bit offsets
     (dict(T=32, d=2048, I=768, E=128, k=8, path=2), moe.MOE_OK),      # decode: T*k <= 256
     (dict(T=33, d=2048, I=768, E=128, k=8, path=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=1, d=256, I=128, E=8, k=2, path=2, training=1), moe.MOE_ERR_UNSUPPORTED),

@@ -424,3 +424,73 @@ def test_prepare_weights_bit_exact(torch_cuda):
     assert np.array_equal(w13_q.cpu().numpy(), r13[0]) and np.array_equal(w13_s.cpu().numpy(), r13[1])
     assert np.array_equal(w2_q.cpu().numpy(), r2[0]) and np.array_equal(w2_s.cpu().numpy(), r2[1])
     layer.close()
+
+
+# ------------------------------------------------------------------ MXFP8 forward
+
+TOL_MX = 6e-2          # against the FP32 oracle on the prepared weights
+TOL_MX_QUANT = 1e-2    # against the oracle that quantizes x and the SwiGLU output at the same points
+
+MX_SHAPES = [
+    # T, d, I, E, k, routing
+    (64, 256, 128, 8, 2, "uniform"),
+    (300, 512, 256, 6, 3, "uniform"),      # ragged row tiles
+    (257, 256, 384, 5, 2, "uniform"),      # three W13 column tiles
+    (200, 256, 128, 64, 8, "zipf"),        # skew and empty experts
+    (130, 256, 128, 1, 1, "uniform"),      # dense layer
+]
+
+
+def _mx_run(torch, inp, t):
+    from mixture_experts_routed_dispatch_amd import moe
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=moe.MOE_MXFP8_E4M3)
+    w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+    y = layer.forward(t["x"], t["ids"], t["scores"], w13q, w2q, w13s, w2s)
+    y2 = layer.forward(t["x"], t["ids"], t["scores"], w13q, w2q, w13s, w2s)
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    assert flags == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # bitwise deterministic
+    layer.close()
+    return y
+
+
+def _prepared_f32(w):
+    return oracle.mx_dequantize(*oracle.mx_quantize(w))
+
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", MX_SHAPES)
+def test_mxfp8_forward_small(torch_cuda, T, d, I, E, k, routing):
+    torch = torch_cuda
+    say("mxfp8 forward small", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=19)
+    t = device_inputs(inp)
+    y = np_of(_mx_run(torch, inp, t))
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f)
+    ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f)
+    e, e_q = rel(y, ref), rel(y, ref_q)
+    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
+    assert e <= TOL_MX
+    assert e_q <= TOL_MX_QUANT
+
+
+def test_mxfp8_forward_full_size_sampled(torch_cuda):
+    torch = torch_cuda
+    say("mxfp8 forward full size: T=16384 d=4096 I=2048 E=64 k=8")
+    inp = inputs.generate_config("mxfp8", seed=0)
+    t = device_inputs(inp)
+    y = np_of(_mx_run(torch, inp, t))
+    del t
+    torch.cuda.empty_cache()
+    rng = np.random.default_rng(9)
+    toks = np.sort(rng.choice(inp.T, size=24, replace=False)).astype(np.int32)
+    toks[0] = 0
+    toks[-1] = inp.T - 1
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f, toks=toks)
+    ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f, toks=toks)
+    e, e_q = rel(y[toks], ref), rel(y[toks], ref_q)
+    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
+    assert e <= TOL_MX
+    assert e_q <= TOL_MX_QUANT
