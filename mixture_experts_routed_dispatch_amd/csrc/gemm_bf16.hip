@@ -109,13 +109,26 @@ struct TileCtx {
     int e, mb, rows, pt, qt, nk;
 };
 
-template <int MODE>
+// kSaveH (FWD_W13 only): also store h = (g, u) for backward.  A separate instantiation
+// rather than a runtime branch: accumulators live into two branches of the epilogue
+// are copied out to scratch by the register allocator.
+template <int MODE, bool kSaveH = false>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ int cum[257];
     __shared__ int wtot[NTHR / MOE_WAVE];
 
     const int tid = threadIdx.x, lane = tid & 63;
+    // The lane id recomputed on the spot (inline mbcnt, which the compiler cannot fold
+    // into `lane`).  Code that runs once per tile (copy offsets, epilogue) derives its
+    // lane-dependent offsets from it, so that none of them is hoisted out of the tile
+    // loop: held across the main loop they would be spilled, and a scratch reload waits
+    // on vmcnt, i.e. on every copy still in flight.
+    auto fresh_lane = []() {
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        return l;
+    };
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wp = wave & 1, wq = wave >> 1;
     const int E = g.E;
@@ -181,20 +194,22 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // barrier leaves exactly the younger copies outstanding).
     constexpr int kDmaOps = (kPk ? 4 : 0) + (kQk ? 4 : 0);     // copies per wave per stage
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
-    const int drow_in_blk = lane >> 2;
     // byte offsets of this lane's rows: P blocks (j = 0..3), then Q blocks
     uint32_t dvoff[8];
     const char* pbase_e = nullptr;        // P base of the load cursor's expert
     auto dma_offsets = [&](const TileCtx& c, const int src[4]) {
+        const int drow_in_blk = fresh_lane() >> 2;
+        const int lane = drow_in_blk * 4 + (fresh_lane() & 3);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = (4 * wave + j) * 16 + drow_in_blk;       // row of the stage tile
             const int cl = (lane & 3) ^ swz(r);                   // logical chunk it holds
             if constexpr (MODE == FWD_W13) {
-                // rows [0,64) gate i0.., [64,128) up i0.., [128,192) gate i0+64.., [192,256) up i0+64..
-                int ii = c.pt * 128 + (r >> 7) * 64 + (r & 63);
+                // 32-row block j of the tile: gate rows i0 + 16 j + (0..15), then the up rows of
+                // the same i, so that an MFMA tile holds both halves of its 16 outputs
+                int ii = c.pt * 128 + (r >> 5) * 16 + (r & 15);
                 if (ii >= g.I) ii = g.I - 1;
-                const int wrow = ((r >> 6) & 1) ? g.I + ii : ii;
+                const int wrow = (r & 16) ? g.I + ii : ii;
                 dvoff[j] = (uint32_t)(wrow * g.d + 8 * cl) * 2u;
             } else if constexpr (MODE == FWD_W2) {
                 int pr = c.pt * TP + r;
@@ -219,6 +234,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // source rows (token or routed row) of this lane's 4 Q block rows in tile c
     auto q_src = [&](const TileCtx& c, int src[4]) {
         if constexpr (kQk) {
+            const int drow_in_blk = fresh_lane() >> 2;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 int rr = c.qt * TQ + (4 * wave + j) * 16 + drow_in_blk;
@@ -380,15 +396,18 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
 
     // ------------------------------------------------------------ epilogue
-    // lane holds D[q][p .. p+3] for q = q0 + 32 b + (lane & 31), p = p0 + 32 a + 8 grp + p_sub
-    const int q_in = lane & 31;
-    const int p_sub = 4 * (lane >> 5);
+    // lane holds D[q][p .. p+3] for q = q0 + 32 b + (lane & 31), p = p0 + 32 a + 8 grp + p_sub.
+    // The epilogue computes its lane index `ln` afresh (mbcnt, as inline assembly the
+    // compiler cannot fold into the kernel's lane id), so that none of the lane-derived offsets is hoisted out of the tile
+    // loop: held across the main loop they would be spilled, and each scratch reload
+    // waits on vmcnt, i.e. on every copy still in flight for the next stages.
     // Plain BF16 outputs go through LDS (this wave's 8 KiB of the stage buffer just
     // consumed) so that each store instruction writes whole 256-byte row segments:
     // per block b, 32 rows x 128 columns are written as 8-byte pieces (16-byte chunk
     // slot c ^ (row & 15)), read back as 16-byte chunks and stored row-contiguously.
-    auto store_rows_bf16 = [&](char* stg, int b, uint16_t* out, size_t ld, int q_first, int q_limit,
+    auto store_rows_bf16 = [&](int ln, char* stg, int b, uint16_t* out, size_t ld, int q_first, int q_limit,
                                int p_first, int p_limit) {
+        const int q_in = ln & 31, p_sub = 4 * (ln >> 5);
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -402,8 +421,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the wave's own LDS writes are done
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
-            const int row = 4 * it + (lane >> 4);
-            const int c16 = lane & 15;
+            const int row = 4 * it + (ln >> 4);
+            const int c16 = ln & 15;
             const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
             const int q = q_first + row;
             const int p = p_first + 8 * c16;
@@ -413,29 +432,36 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
     auto epilogue = [&](const TileCtx& c, int buf) {
         char* stg = lds + buf * BUFB + wave * 8192;
+        const int ln = fresh_lane();
+        const int q_in = ln & 31, p_sub = 4 * (ln >> 5);
         if constexpr (MODE == FWD_W13) {
-            // a[r][i] for i = pt*128 + wp*64 + (0..63): 64 columns, 128-byte row segments
+            // a[r][i] for i = pt*128 + wp*64 + (0..63): 64 columns, 128-byte row segments.
+            // MFMA tile (a, b) holds gate values in element groups 0, 1 and the matching up
+            // values in groups 2, 3: outputs i = 16 a + 8 grp + p_sub + z of the wave's 64.
+            // One row block b at a time (the fences keep the scheduler from overlapping
+            // the blocks).
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int a = 0; a < 2; ++a)
+                for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        const int c8 = 4 * a + grp;
+                    for (int grp = 0; grp < 2; ++grp) {
+                        const int c8 = 2 * a + grp;
                         float gv[4], uv[4], av[4];
 #pragma unroll
                         for (int z = 0; z < 4; ++z) {
                             gv[z] = acc[a][b][4 * grp + z];
-                            uv[z] = acc[a + 2][b][4 * grp + z];
+                            uv[z] = acc[a][b][4 * (grp + 2) + z];
                             av[z] = silu_f(gv[z]) * uv[z];
                         }
                         uint2 v;
                         v.x = pack_bf16(av[0], av[1]);
                         v.y = pack_bf16(av[2], av[3]);
                         *reinterpret_cast<uint2*>(stg + q_in * 128 + ((c8 ^ (q_in & 7)) << 4) + (p_sub << 1)) = v;
-                        if (g.out_h) {
+                        if constexpr (kSaveH) {
                             const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                            const int i = c.pt * 128 + wp * 64 + a * 32 + 8 * grp + p_sub;
+                            const int i = c.pt * 128 + wp * 64 + a * 16 + 8 * grp + p_sub;
                             if (rr < c.rows && i < g.I) {
                                 const size_t r = (size_t)c.mb + rr;
                                 uint2 hg, hu;
@@ -449,8 +475,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 __builtin_amdgcn_s_waitcnt(0xc07f);
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
-                    const int row = 8 * it + (lane >> 3);
-                    const int c8 = lane & 7;
+                    const int row = 8 * it + (ln >> 3);
+                    const int c8 = ln & 7;
                     const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c8 ^ (row & 7)) << 4));
                     const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
                     const int i = c.pt * 128 + wp * 64 + 8 * c8;
@@ -463,7 +489,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             // o [R, d] or dxp [R, d]
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                store_rows_bf16(stg, b, g.out + (size_t)c.mb * g.d, g.d, c.qt * TQ + wq * 128 + b * 32,
+                store_rows_bf16(ln, stg, b, g.out + (size_t)c.mb * g.d, g.d, c.qt * TQ + wq * 128 + b * 32,
                                 c.rows, c.pt * TP + wp * 128, g.d);
         } else if constexpr (MODE == DGRAD_W2) {
             // dA = probs[r] * acc; dg = dA u s(g)(1 + g(1 - s(g))), du = dA g s(g)
@@ -505,7 +531,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             const int Qsz = (MODE == WGRAD_W2) ? g.d : 2 * g.I;
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                store_rows_bf16(stg, b, g.out + (size_t)c.e * Qsz * Psz, Psz, c.qt * TQ + wq * 128 + b * 32,
+                store_rows_bf16(ln, stg, b, g.out + (size_t)c.e * Qsz * Psz, Psz, c.qt * TQ + wq * 128 + b * 32,
                                 Qsz, c.pt * TP + wp * 128, Psz);
         }
     };
@@ -603,7 +629,13 @@ hipError_t launch_mode(const GemmArgs& g, int num_cu, hipStream_t s) {
     int64_t grid = tiles < num_cu ? tiles : num_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(grouped_gemm<MODE>, dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+    if constexpr (MODE == FWD_W13) {
+        if (g.out_h) {
+            hipLaunchKernelGGL((grouped_gemm<MODE, true>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((grouped_gemm<MODE, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
     return hipGetLastError();
 }
 
