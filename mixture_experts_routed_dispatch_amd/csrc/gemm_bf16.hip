@@ -20,24 +20,26 @@
 //   WGRAD_W13  x[gather]^T (MN-major)       dh^T                      R_e    dW13_e [2I, d]
 //
 // Workgroup tile 256 (p) x 256 (q), four waves of 128 x 128 (4 x 4 MFMA blocks
-// of 32 x 32, 256 FP32 accumulators per lane).  K advances in stages of 32
-// through a ring of four LDS buffers (32 KiB each: both operands, rows of 64
-// bytes whose 16-byte chunks are XOR-swizzled so fragment reads and chunk writes
-// are bank-conflict free).  A workgroup walks its tiles as one continuous stream
-// of stages; during stage s it
-//   * computes stage s from buffer s % 4 (two k steps of 16 MFMAs; the fragments
-//     of the second step are read in the shadow of the first step's MFMAs, and
-//     those of stage s + 1's first step in the shadow of the second step's),
-//   * writes the global data of stage s + 2 (held in registers) into buffer
-//     (s + 2) % 4 and issues the global loads of stage s + 3 into those
-//     registers,
-// and ends with one barrier.  Buffer s + 1 was completed before the previous
-// barrier, so the barrier is never waited on for fresh data and the stream does
-// not stall at tile boundaries.  K-major operands are copied as 16-byte chunks;
-// MN-major ones (the transposed products of backward) as 8 x 8 blocks transposed
-// in registers.  The tile list is built on the device from m_indptr, so the host
-// never reads routing counts; consecutive tile ids go to workgroups of one XCD
-// so that the operand slices they share stay in that XCD's L2.
+// of 32 x 32, 256 FP32 accumulators per lane), one workgroup per CU, persistent
+// over a tile list built on the device from m_indptr (the host never reads routing
+// counts).  K advances in stages of 32 through a ring of four LDS buffers (32 KiB
+// each: both operands, rows of 64 bytes whose 16-byte chunks are XOR-swizzled so
+// fragment reads and chunk writes are bank-conflict free).  A workgroup walks its
+// tiles as one continuous stream of stages; during stage s it
+//   * computes stage s from buffer s % 4: two k steps of 16 MFMAs, the fragments of
+//     the second step read in the shadow of the first step's MFMAs, those of stage
+//     s + 1's first step in the shadow of the second step's;
+//   * K-major operands: issues the direct global-to-LDS copies of stage s + 3, one
+//     1 KiB copy after each group of four MFMAs (a burst of copies stalls the MFMA
+//     issue), waited for with explicit vmcnt counts one stage later;
+//   * MN-major operands (the transposed products of backward): writes the registers
+//     of stage s + 2 into LDS as 8 x 8 blocks transposed on the way, and loads
+//     stage s + 3 into them;
+// and ends with one barrier.  The tile walk keeps the expert offsets and the next
+// tiles' gather indices in LDS (the latter fetched by an LDS copy a tile ahead), so
+// the main loop issues no global load the compiler would have to wait for: such a
+// wait would also wait for every copy in flight.  Consecutive tile ids go to
+// workgroups of one XCD so that the operand slices they share stay in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -116,6 +118,8 @@ template <int MODE, bool kSaveH = false>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ int cum[257];
+    __shared__ int mptr[257];          // m_indptr, so that the tile walk reads no global memory
+    __shared__ int gsrc[2][TQ];        // gather indices of the next two load-cursor tiles
     __shared__ int wtot[NTHR / MOE_WAVE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -152,6 +156,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             if (lane >= off) incl += v;
         }
         if (lane == MOE_WAVE - 1) wtot[wave] = incl;
+        for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
         __syncthreads();
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wtot[w];
@@ -165,16 +170,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     if (vid >= total) return;
 
     auto coords = [&](int tile) {
-        int lo = 0, hi = E - 1;                   // largest e with cum[e] <= tile
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cum[mid] <= tile) lo = mid; else hi = mid - 1;
+        // largest e with cum[e] <= tile: cum is non-decreasing and cum[0] = 0, so it is
+        // the number of e in [1, E) with cum[e] <= tile (one ballot per 64 experts)
+        const int fl = fresh_lane();
+        int lo = 0;
+#pragma unroll
+        for (int base = 1; base < 257; base += 64) {
+            const int e = base + fl;
+            lo += __builtin_popcountll(__ballot(e < E && cum[e] <= tile));
         }
+        lo = __builtin_amdgcn_readfirstlane(lo);
         TileCtx c;
         c.e = lo;
         const int local = tile - cum[lo];
-        c.mb = g.m_indptr[lo];
-        c.rows = g.m_indptr[lo + 1] - c.mb;
+        c.mb = mptr[lo];
+        c.rows = mptr[lo + 1] - c.mb;
         c.qt = local / nPt;
         c.pt = local - c.qt * nPt;
         const int nk = (k_size<MODE>(g, c.rows) + TK - 1) / TK;
@@ -231,17 +241,36 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     if constexpr (MODE == DGRAD_W2) qbase = reinterpret_cast<const char*>(g.dy);
     if constexpr (MODE == FWD_W2) qbase = reinterpret_cast<const char*>(g.a);
     if constexpr (MODE == DGRAD_W13) qbase = reinterpret_cast<const char*>(g.dh);
-    // source rows (token or routed row) of this lane's 4 Q block rows in tile c
-    auto q_src = [&](const TileCtx& c, int src[4]) {
+    // source rows (token or routed row) of this lane's 4 Q block rows in tile c; the
+    // gathered modes take the token ids from gsrc[slot], where gather_dma put them
+    constexpr bool kGather = (MODE == FWD_W13 || MODE == DGRAD_W2);
+    auto q_src = [&](const TileCtx& c, int slot, int src[4]) {
         if constexpr (kQk) {
             const int drow_in_blk = fresh_lane() >> 2;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                int rr = c.qt * TQ + (4 * wave + j) * 16 + drow_in_blk;
-                if (rr >= c.rows) rr = c.rows > 0 ? c.rows - 1 : 0;   // ragged tail: a row of the expert
-                if constexpr (MODE == FWD_W13 || MODE == DGRAD_W2) src[j] = g.gather[c.mb + rr];
-                else src[j] = c.mb + rr;
+                if constexpr (kGather) {
+                    src[j] = gsrc[slot][(4 * wave + j) * 16 + drow_in_blk];
+                } else {
+                    int rr = c.qt * TQ + (4 * wave + j) * 16 + drow_in_blk;
+                    if (rr >= c.rows) rr = c.rows > 0 ? c.rows - 1 : 0;   // ragged tail: a row of the expert
+                    src[j] = c.mb + rr;
+                }
             }
+        }
+    };
+    // Gather indices of tile c into gsrc[slot]: wave w copies entries 64 w .. 64 w + 63
+    // (the rows of its own copy blocks, so it later reads only what it copied itself)
+    // with one global_load_lds_dword, issued a tile ahead and counted like the stage
+    // copies; a plain load would make the compiler wait for every copy in flight.
+    auto gather_dma = [&](const TileCtx& c, int slot) {
+        if constexpr (kGather) {
+            int rr = c.qt * TQ + 64 * wave + fresh_lane();
+            if (rr >= c.rows) rr = c.rows - 1;                    // tiles exist only for rows >= 1
+            const uint32_t voff = (uint32_t)(c.mb + rr) * 4u;
+            const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)&gsrc[slot][64 * wave];
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                         :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(g.gather) : "memory");
         }
     };
     auto dma1 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
@@ -547,21 +576,30 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // stage reads.
     int l_tile = vid, l_kt = 0;
     TileCtx lc = coords(l_tile);
-    int n_src[4] = {0, 0, 0, 0};
+    int gslot = 0;                     // gsrc slot of the load cursor's tile
+    TileCtx nc = lc;                   // coordinates of the load cursor's next tile
+    gather_dma(lc, 0);
+    if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, 1); }
+    if constexpr (kGather) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     {
         int src[4] = {0, 0, 0, 0};
-        q_src(lc, src);
+        q_src(lc, 0, src);
         dma_offsets(lc, src);
     }
-    if (l_tile + G < total) q_src(coords(l_tile + G), n_src);
     auto advance_load = [&]() {
         if (++l_kt < lc.nk) return;
         if (l_tile + G >= total) { l_kt = lc.nk - 1; return; }
+        // the indices of the new tile were copied at the previous switch, lc.nk stages
+        // ago; with fewer than 3 stages per tile the stage waits need not cover them
+        if constexpr (kGather) if (lc.nk < 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         l_kt = 0;
         l_tile += G;
-        lc = coords(l_tile);
-        dma_offsets(lc, n_src);
-        if (l_tile + G < total) q_src(coords(l_tile + G), n_src);   // lands during this tile
+        gslot ^= 1;
+        lc = nc;
+        int src[4] = {0, 0, 0, 0};
+        q_src(lc, gslot, src);
+        dma_offsets(lc, src);
+        if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, gslot ^ 1); }
     };
 
     // prologue: stages 0, 1, 2
