@@ -70,6 +70,21 @@ __device__ __forceinline__ Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
 __device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
 
+// Order of an expert's tiles: groups of kQGroup q-tiles (token rows), and inside a
+// group the p-tiles (weight rows) with the group's q-tiles fastest.  The 32 tiles one
+// XCD runs at a time (consecutive ids) then span about 6 q-tiles x 5 p-tiles, which
+// share far more operand data in that XCD's L2 than 32 tiles of one q-tile row or
+// one p-tile column.
+constexpr int kQGroup = 6;
+__device__ __forceinline__ void tile_order(int local, int nQt, int nPt, int& pt, int& qt) {
+    const int gi = local / (kQGroup * nPt);
+    const int rem = local - gi * kQGroup * nPt;
+    const int left = nQt - gi * kQGroup;
+    const int gsz = left < kQGroup ? left : kQGroup;
+    pt = rem / gsz;
+    qt = gi * kQGroup + (rem - pt * gsz);
+}
+
 // out[m] holds element m of each in[k] (k = 0..7): the 8 x 8 BF16 transpose.
 __device__ __forceinline__ void transpose8x8(const Chunk in[8], Chunk out[8]) {
 #pragma unroll
@@ -185,8 +200,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         const int local = tile - cum[lo];
         c.mb = mptr[lo];
         c.rows = mptr[lo + 1] - c.mb;
-        c.qt = local / nPt;
-        c.pt = local - c.qt * nPt;
+        if constexpr (Traits<MODE>::kRaggedK) {
+            c.qt = local / nPt;
+            c.pt = local - c.qt * nPt;
+        } else {
+            tile_order(local, (c.rows + TQ - 1) / TQ, nPt, c.pt, c.qt);
+        }
         const int nk = (k_size<MODE>(g, c.rows) + TK - 1) / TK;
         c.nk = nk > 0 ? nk : 1;                   // an empty expert still runs one all-zero stage
         return c;

@@ -50,6 +50,21 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | ((r >> 1) & 2); }
 __device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ swz(r)) << 4); }
 
+// Order of an expert's tiles: groups of kQGroup q-tiles (token rows), and inside a
+// group the p-tiles (weight rows) with the group's q-tiles fastest.  The 32 tiles one
+// XCD runs at a time (consecutive ids) then span about 6 q-tiles x 5 p-tiles, which
+// share far more operand data in that XCD's L2 than 32 tiles of one q-tile row or
+// one p-tile column.
+constexpr int kQGroup = 6;
+__device__ __forceinline__ void tile_order(int local, int nQt, int nPt, int& pt, int& qt) {
+    const int gi = local / (kQGroup * nPt);
+    const int rem = local - gi * kQGroup * nPt;
+    const int left = nQt - gi * kQGroup;
+    const int gsz = left < kQGroup ? left : kQGroup;
+    pt = rem / gsz;
+    qt = gi * kQGroup + (rem - pt * gsz);
+}
+
 struct TileCtx {
     int e, mb, rows, pt, qt, nk;
 };
@@ -59,10 +74,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ __attribute__((aligned(1024))) char lsc[NSC * SCB];
     __shared__ int cum[257];
+    __shared__ int mptr[257];          // m_indptr, so that the tile walk reads no global memory
+    __shared__ int gsrc[2][TQ];        // token ids (MX_W13) of the next two load-cursor tiles
     __shared__ int wtot[NTHR / MOE_WAVE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The lane id recomputed on the spot (inline mbcnt, which the compiler cannot fold
+    // into `lane`), for the code that runs once per tile: lane-dependent offsets hoisted
+    // out of the tile loop would be spilled, and a scratch reload waits on vmcnt, i.e.
+    // on every copy in flight.
+    auto fresh_lane = []() {
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        return l;
+    };
     const int wp = wave & 1, wq = wave >> 1;
     const int E = g.E;
     const int K = MODE == MX_W13 ? g.d : g.I;          // K of the product (bytes per row)
@@ -82,6 +108,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
             if (lane >= off) incl += v;
         }
         if (lane == MOE_WAVE - 1) wtot[wave] = incl;
+        for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
         __syncthreads();
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wtot[w];
@@ -95,18 +122,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     if (vid >= total) return;
 
     auto coords = [&](int tile) {
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cum[mid] <= tile) lo = mid; else hi = mid - 1;
+        // largest e with cum[e] <= tile = number of e in [1, E) with cum[e] <= tile
+        const int fl = fresh_lane();
+        int lo = 0;
+#pragma unroll
+        for (int base = 1; base < 257; base += 64) {
+            const int e = base + fl;
+            lo += __builtin_popcountll(__ballot(e < E && cum[e] <= tile));
         }
+        lo = __builtin_amdgcn_readfirstlane(lo);
         TileCtx c;
         c.e = lo;
         const int local = tile - cum[lo];
-        c.mb = g.m_indptr[lo];
-        c.rows = g.m_indptr[lo + 1] - c.mb;
-        c.qt = local / nPt;
-        c.pt = local - c.qt * nPt;
+        c.mb = mptr[lo];
+        c.rows = mptr[lo + 1] - c.mb;
+        tile_order(local, (c.rows + TQ - 1) / TQ, nPt, c.pt, c.qt);
         c.nk = K / TKB;                               // even: K is a multiple of 128
         return c;
     };
@@ -114,21 +144,41 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     // row of the P operand (weight row of expert e) behind P tile row r
     auto p_row = [&](const TileCtx& c, int r) {
         if constexpr (MODE == MX_W13) {
-            // rows [0,64) gate i0.., [64,128) up i0.., [128,192) gate i0+64.., [192,256) up i0+64..
-            int ii = c.pt * 128 + (r >> 7) * 64 + (r & 63);
+            // 32-row block j of the tile: gate rows i0 + 16 j + (0..15), then the up rows of
+            // the same i, so that an MFMA tile holds both halves of its 16 outputs
+            int ii = c.pt * 128 + (r >> 5) * 16 + (r & 15);
             if (ii >= g.I) ii = g.I - 1;
-            return ((r >> 6) & 1) ? g.I + ii : ii;
+            return (r & 16) ? g.I + ii : ii;
         } else {
             const int pr = c.pt * TP + r;
             return pr < g.d ? pr : g.d - 1;
         }
     };
-    // row of the Q operand (token of xq, or routed row of aq) behind Q tile row r
-    auto q_row = [&](const TileCtx& c, int r) {
-        int rr = c.qt * TQ + r;
-        if (rr >= c.rows) rr = c.rows - 1;            // ragged tail: a row of the expert
-        if constexpr (MODE == MX_W13) return (int)g.gather[c.mb + rr];
-        else return c.mb + rr;
+    // row of the Q operand (token of xq, or routed row of aq) behind Q tile row r, for
+    // the rows r = 64 w .. 64 w + 63 of wave w only: the token ids come from gsrc[slot],
+    // where gather_dma put them
+    auto q_row = [&](const TileCtx& c, int slot, int r) {
+        if constexpr (MODE == MX_W13) {
+            return gsrc[slot][r];
+        } else {
+            int rr = c.qt * TQ + r;
+            if (rr >= c.rows) rr = c.rows - 1;        // ragged tail: a row of the expert
+            return c.mb + rr;
+        }
+    };
+    // Token ids of tile c into gsrc[slot]: wave w copies entries 64 w .. 64 w + 63 (the
+    // rows of its own data and scale copies) with one global_load_lds_dword, issued a
+    // tile ahead and counted like the stage copies; a plain load would make the
+    // compiler wait for every copy in flight.
+    auto gather_dma = [&](const TileCtx& c, int slot) {
+        if constexpr (MODE == MX_W13) {
+            int rr = c.qt * TQ + 64 * wave + fresh_lane();
+            if (rr >= c.rows) rr = c.rows - 1;                    // tiles exist only for rows >= 1
+            const uint32_t voff = (uint32_t)(c.mb + rr) * 4u;
+            const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)&gsrc[slot][64 * wave];
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                         :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(g.gather) : "memory");
+        }
     };
     const uint8_t* pdata = MODE == MX_W13 ? g.w13q : g.w2q;
     const uint8_t* pscale = MODE == MX_W13 ? g.w13s : g.w2s;
@@ -148,17 +198,18 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     uint32_t svoffP = 0, svoffQ = 0;
     const char* pbase_e = nullptr;
     const char* psbase_e = nullptr;
-    auto copy_offsets = [&](const TileCtx& c) {
+    auto copy_offsets = [&](const TileCtx& c, int slot) {
+        const int fl = fresh_lane();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = (4 * wave + j) * 16 + (lane >> 2);
-            const int cl = (lane & 3) ^ swz(r);
+            const int r = (4 * wave + j) * 16 + (fl >> 2);
+            const int cl = (fl & 3) ^ swz(r);
             dvoff[j] = (uint32_t)(p_row(c, r) * K + 16 * cl);
-            dvoff[4 + j] = (uint32_t)(q_row(c, r) * K + 16 * cl);
+            dvoff[4 + j] = (uint32_t)(q_row(c, slot, r) * K + 16 * cl);
         }
-        const int rs = 64 * wave + lane;
+        const int rs = 64 * wave + fl;
         svoffP = (uint32_t)(p_row(c, rs) * KB);
-        svoffQ = (uint32_t)(q_row(c, rs) * KB);
+        svoffQ = (uint32_t)(q_row(c, slot, rs) * KB);
         pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
         psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * KB);
     };
@@ -228,61 +279,78 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
         const char* nb = lds + nbuf * BUFB;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
+            // The scaled MFMAs have no ordering edge to anything here, and instruction
+            // selection would otherwise emit all of them after the stage's reads and
+            // copies; an empty asm that takes the accumulators just written keeps them
+            // in front of the next copy.  One copy after every two MFMAs: copies issued
+            // back to back queue in the texture unit and hold up the MFMA issue.
             acc[a][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[0], acc[a][0], 0, 0, OPSEL, sp[a], OPSEL, sq[0]);
             npf[a] = read_frag(nb, fragP[a][0], fragP[a][1]);
             acc[a][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[1], acc[a][1], 0, 0, OPSEL, sp[a], OPSEL, sq[1]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            asm volatile("" :: "a"(acc[a][0]), "a"(acc[a][1]));
+            dma_data(dma_kt, dma_buf, 2 * a);
+            __builtin_amdgcn_sched_barrier(0);
             nqf[a] = read_frag(nb, fragQ[a][0], fragQ[a][1]);
             acc[a][2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[2], acc[a][2], 0, 0, OPSEL, sp[a], OPSEL, sq[2]);
             acc[a][3] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(pf[a], qf[3], acc[a][3], 0, 0, OPSEL, sp[a], OPSEL, sq[3]);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            dma_data(dma_kt, dma_buf, 2 * a);
+            asm volatile("" :: "a"(acc[a][2]), "a"(acc[a][3]));
             dma_data(dma_kt, dma_buf, 2 * a + 1);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // ------------------------------------------------------------ epilogue
-    const int q_in = lane & 31;
-    const int p_sub = 4 * (lane >> 5);
     auto epilogue = [&](const TileCtx& c, int buf) {
+        const int ln = fresh_lane();
+        const int q_in = ln & 31, p_sub = 4 * (ln >> 5);
         if constexpr (MODE == MX_W13) {
-            // a = silu(g) * u for i = pt*128 + wp*64 + 32 a + (0..31): one MX block per
-            // (row, a), split over lanes l and l ^ 32; amax, E8M0 scale and E4M3 codes
+            // a = silu(g) * u for i = pt*128 + wp*64 + 32 m + (0..31): one MX block per
+            // (row, m), from MFMA tiles a = 2 m and 2 m + 1, whose element groups 0, 1 hold
+            // gate values and 2, 3 the matching up values (outputs 16 a + 8 grp + p_sub + z),
+            // split over lanes l and l ^ 32; amax, E8M0 scale and E4M3 codes
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
+                __builtin_amdgcn_sched_barrier(0);
                 const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
                 const bool live = rr < c.rows;
                 const size_t r = (size_t)c.mb + (live ? rr : 0);
 #pragma unroll
-                for (int a = 0; a < 2; ++a) {
+                for (int m = 0; m < 2; ++m) {
                     float av[16];
                     float amax = 0.0f;
 #pragma unroll
-                    for (int grp = 0; grp < 4; ++grp)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                        for (int z = 0; z < 4; ++z) {
-                            const float gv = acc[a][b][4 * grp + z], uv = acc[a + 2][b][4 * grp + z];
-                            av[4 * grp + z] = silu_f(gv) * uv;
-                            amax = __builtin_fmaxf(amax, __builtin_fabsf(av[4 * grp + z]));
-                        }
+                        for (int grp = 0; grp < 2; ++grp)
+#pragma unroll
+                            for (int z = 0; z < 4; ++z) {
+                                const float gv = acc[2 * m + h][b][4 * grp + z];
+                                const float uv = acc[2 * m + h][b][4 * (grp + 2) + z];
+                                const float v = silu_f(gv) * uv;
+                                av[8 * h + 4 * grp + z] = v;
+                                amax = __builtin_fmaxf(amax, __builtin_fabsf(v));
+                            }
                     amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
                     const uint32_t sb = e8m0_scale(amax);
                     const int sh = 127 - (int)sb;
-                    const int i0 = c.pt * 128 + wp * 64 + a * 32;
+                    const int i0 = c.pt * 128 + wp * 64 + m * 32;
                     if (live && i0 < g.I) {
 #pragma unroll
-                        for (int grp = 0; grp < 4; ++grp) {
-                            uint32_t w = 0;
+                        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                            for (int z = 0; z < 4; ++z)
-                                w |= e4m3_code(__builtin_ldexpf(av[4 * grp + z], sh)) << (8 * z);
-                            *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 8 * grp + p_sub) = w;
-                        }
-                        if (lane < 32) g.as[r * (g.I / 32) + i0 / 32] = (uint8_t)sb;
+                            for (int grp = 0; grp < 2; ++grp) {
+                                uint32_t w = 0;
+#pragma unroll
+                                for (int z = 0; z < 4; ++z)
+                                    w |= e4m3_code(__builtin_ldexpf(av[8 * h + 4 * grp + z], sh)) << (8 * z);
+                                *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 16 * h + 8 * grp + p_sub) = w;
+                            }
+                        if (ln < 32) g.as[r * (g.I / 32) + i0 / 32] = (uint8_t)sb;
                     }
                 }
             }
@@ -305,8 +373,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                 __builtin_amdgcn_s_waitcnt(0xc07f);
 #pragma unroll
                 for (int it = 0; it < 8; ++it) {
-                    const int row = 4 * it + (lane >> 4);
-                    const int c16 = lane & 15;
+                    const int row = 4 * it + (ln >> 4);
+                    const int c16 = ln & 15;
                     const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
                     const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
                     const int p = c.pt * TP + wp * 128 + 8 * c16;
@@ -324,14 +392,25 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     // 8 data copies of stage s + 3, plus the 2 scale copies when s is odd.
     int l_tile = vid, l_kt = 0;
     TileCtx lc = coords(l_tile);
-    copy_offsets(lc);
+    TileCtx nc = lc;                   // coordinates of the load cursor's next tile
+    int gslot = 0;                     // gsrc slot of the load cursor's tile
+    gather_dma(lc, 0);
+    if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, 1); }
+    if constexpr (MODE == MX_W13) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    copy_offsets(lc, 0);
+    // The token ids of a new tile were copied at the previous switch, a whole tile of
+    // at least 2 stages earlier (K is a multiple of 128), and every stage ends with a
+    // wait that retires all copies issued before the previous stage.
     auto advance_load = [&]() {
         if (++l_kt < lc.nk) return;
         if (l_tile + G >= total) { l_kt = lc.nk - 1; return; }   // past the end: repeat the last stage
+        if constexpr (MODE == MX_W13) if (lc.nk < 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         l_kt = 0;
         l_tile += G;
-        lc = coords(l_tile);
-        copy_offsets(lc);
+        gslot ^= 1;
+        lc = nc;
+        copy_offsets(lc, gslot);
+        if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, gslot ^ 1); }
     };
     auto issue_stage = [&](int buf, int pair_slot) {
         if (pair_slot >= 0) dma_scales(l_kt, pair_slot);
