@@ -57,11 +57,14 @@ def parse():
 
 KERNEL_OF_STAGE = {
     # stage name (library event pairs) -> substring of the kernel symbol rocprofv3 reports
-    "dispatch": "dispatch_place", "w13": "grouped_gemm<0>", "w2": "grouped_gemm<1>",
+    "dispatch": "dispatch_place", "w13": "grouped_gemm<0,", "w2": "grouped_gemm<1,",
     "combine": "combine_kernel", "score_grad": "score_grad_kernel",
-    "dgrad_w2": "grouped_gemm<2>", "dgrad_w13": "grouped_gemm<3>",
-    "wgrad_w2": "grouped_gemm<4>", "wgrad_w13": "grouped_gemm<5>",
+    "dgrad_w2": "grouped_gemm<2,", "dgrad_w13": "grouped_gemm<3,",
+    "wgrad_w2": "grouped_gemm<4,", "wgrad_w13": "grouped_gemm<5,",
+    "quant_x": "quantize_kernel", "decode_w13": "decode_w13", "decode_w2": "decode_w2",
 }
+# the MXFP8 workload's GEMM stages run the block-scaled kernels
+KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13="grouped_gemm_mx<0>", w2="grouped_gemm_mx<1>")
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -77,17 +80,26 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(stage: str, workload: str):
-    """HBM bytes (read + written) per launch of the stage's kernel, from the committed
-    rocprofv3 counter summary, if it was taken on the current sources and workload."""
+def kernel_of_stage(workload: str):
+    return KERNEL_OF_STAGE_MX if workload == "mxfp8" else KERNEL_OF_STAGE
+
+
+def _load_traffic():
     try:
         with open(TRAFFIC_PATH) as f:
-            tab = json.load(f)
+            return json.load(f)
     except (OSError, ValueError):
+        return {}
+
+
+def traffic_for(stage: str, workload: str):
+    """HBM bytes (read + written) per launch of the stage's kernel, from the committed
+    rocprofv3 counter summary, if it was taken on the current sources for this workload."""
+    tab = _load_traffic()
+    if tab.get("source_hash") != source_hash():
         return None
-    if tab.get("source_hash") != source_hash() or tab.get("workload") != workload:
-        return None
-    ent = tab.get("kernels", {}).get(KERNEL_OF_STAGE.get(stage, "?"))
+    ent = tab.get("workloads", {}).get(workload, {}).get("kernels", {}).get(
+        kernel_of_stage(workload).get(stage, "?"))
     return None if ent is None else ent["read_bytes"] + ent["write_bytes"]
 
 
@@ -118,15 +130,19 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
     fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
     write = {k: sum(v) / len(v) for k, v in write.items()}
     kernels = {}
-    for stage, sub in KERNEL_OF_STAGE.items():
+    for stage, sub in kernel_of_stage(workload).items():
         names = [k for k in fetch if sub in k]
         if names and names[0] in write:
             kernels[sub] = {"read_bytes": fetch[names[0]] * 1024.0 * f_fetch,
                             "write_bytes": write[names[0]] * 1024.0 * f_write,
                             "fetch_kib_raw": fetch[names[0]], "write_kib_raw": write[names[0]]}
-    tab = {"workload": workload, "source_hash": source_hash(), "copy_kernel": ck,
-           "copy_bytes": copy_bytes, "fetch_factor": f_fetch, "write_factor": f_write,
-           "kernels": kernels}
+    # one file for every workload measured on the same sources
+    tab = _load_traffic()
+    if tab.get("source_hash") != source_hash():
+        tab = {"source_hash": source_hash(), "workloads": {}}
+    tab.setdefault("workloads", {})[workload] = {
+        "copy_kernel": ck, "copy_bytes": copy_bytes, "fetch_factor": f_fetch,
+        "write_factor": f_write, "kernels": kernels}
     with open(TRAFFIC_PATH, "w") as f:
         json.dump(tab, f, indent=1)
     return tab
