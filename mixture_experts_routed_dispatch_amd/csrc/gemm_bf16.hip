@@ -221,7 +221,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // explicit vmcnt counts (issued as inline assembly, so the compiler neither
     // tracks nor waits for them: loads complete in issue order, and the wait before a
     // barrier leaves exactly the younger copies outstanding).
-    constexpr int kDmaOps = (kPk ? 4 : 0) + (kQk ? 4 : 0);     // copies per wave per stage
+    // The MN-major P of the DGRAD products (a weight matrix read transposed) is copied
+    // too, into an MN-major stage (see read_p_tr below).
+    constexpr bool kPmn = (MODE == DGRAD_W2 || MODE == DGRAD_W13);
+    constexpr bool kPcopy = kPk || kPmn;
+    constexpr int kDmaOps = (kPcopy ? 4 : 0) + (kQk ? 4 : 0);  // copies per wave per stage
+    // row length (elements) of the MN-major P: W2_e [d, I] for DGRAD_W2, W13_e [2I, d]
+    // for DGRAD_W13; a stage holds 32 of its rows (k) x 256 columns (p)
+    const int pmn_ld = MODE == DGRAD_W2 ? g.I : g.d;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
     // byte offsets of this lane's rows: P blocks (j = 0..3), then Q blocks
     uint32_t dvoff[8];
@@ -244,6 +251,16 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 int pr = c.pt * TP + r;
                 if (pr >= g.d) pr = g.d - 1;
                 dvoff[j] = (uint32_t)(pr * g.I + 8 * cl) * 2u;
+            } else if constexpr (kPmn) {
+                // MN-major stage: 32 rows (k) of 512 bytes; copy j of wave w fills rows
+                // 8 w + 2 j + L / 32, 16-byte slot L % 32, which holds logical chunk
+                // (L % 32) ^ ((row & 3) << 2) (columns p = 8 chunk ..)
+                const int L = fresh_lane();
+                const int kr = 8 * wave + 2 * j + (L >> 5);
+                const int ch = (L & 31) ^ ((kr & 3) << 2);
+                int col = c.pt * TP + 8 * ch;
+                if (col > pmn_ld - 8) col = pmn_ld - 8;           // past the matrix: any valid column
+                dvoff[j] = (uint32_t)(kr * pmn_ld + col) * 2u;
             }
             if constexpr (kQk) {
                 const int qs = src[j];
@@ -253,7 +270,13 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             }
         }
         if constexpr (MODE == FWD_W13) pbase_e = reinterpret_cast<const char*>(g.w13 + (size_t)c.e * 2 * g.I * g.d);
-        if constexpr (MODE == FWD_W2) pbase_e = reinterpret_cast<const char*>(g.w2 + (size_t)c.e * g.d * g.I);
+        if constexpr (MODE == FWD_W2 || MODE == DGRAD_W2) pbase_e = reinterpret_cast<const char*>(g.w2 + (size_t)c.e * g.d * g.I);
+        if constexpr (MODE == DGRAD_W13) pbase_e = reinterpret_cast<const char*>(g.w13 + (size_t)c.e * 2 * g.I * g.d);
+    };
+    // byte offset of stage kt inside the P rows of the load cursor's expert
+    auto p_stage_bytes = [&](int kt) {
+        if constexpr (kPmn) return (size_t)kt * TK * pmn_ld * 2;
+        else return (size_t)kt * TK * 2;
     };
     const char* qbase = nullptr;
     if constexpr (MODE == FWD_W13) qbase = reinterpret_cast<const char*>(g.x);
@@ -300,8 +323,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     auto dma_stage = [&](int kt, int buf) {
         const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
         const int kbytes = kt * TK * 2;
-        if constexpr (kPk) {
-            const char* b = pbase_e + kbytes;
+        if constexpr (kPcopy) {
+            const char* b = pbase_e + p_stage_bytes(kt);
 #pragma unroll
             for (int j = 0; j < 4; ++j) dma1(dst + j * 1024, dvoff[j], b);
         }
@@ -315,8 +338,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     auto dma_one = [&](int kt, int buf, int j) {
         const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
         const int kbytes = kt * TK * 2;
-        if constexpr (kPk && kQk) {
-            if (j < 4) dma1(dst + j * 1024, dvoff[j], pbase_e + kbytes);
+        if constexpr (kPcopy && kQk) {
+            if (j < 4) dma1(dst + j * 1024, dvoff[j], pbase_e + p_stage_bytes(kt));
             else dma1(dst + OPB + (j - 4) * 1024, dvoff[j], qbase + kbytes);
         } else if constexpr (kQk) {
             if (j < 4) dma1(dst + OPB + j * 1024, dvoff[4 + j], qbase + kbytes);
@@ -332,7 +355,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // One 8 (k) x 8 (mn) block per thread: threads 0..127 own a P block; with an
     // MN-major Q too (weight gradients), threads 128..255 own a Q block.  Loaded one
     // stage before it is written, transposed in registers on the way to LDS.
-    constexpr bool kStaged = !kPk;
+    constexpr bool kStaged = !kPcopy;
     Chunk st[8];
     auto load_stage = [&](const TileCtx& c, int kt) {
         if constexpr (kStaged) {
@@ -404,12 +427,37 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         fragP[b] = lofs(wp * 128 + b * 32 + (lane & 31), lane >> 5);
         fragQ[b] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), lane >> 5);
     }
+    // MN-major P fragments (kPmn) with ds_read_b64_tr_b16: within a 16-lane group, lane j
+    // reads 4 consecutive p of row k0 + j / 4 at column n0 + 4 (j % 4), and lane i
+    // receives rows k0 .. k0 + 3 of column n0 + i.  Lane l = 16 g + j of fragment a, k
+    // step ks, read t (k 4t .. 4t + 3 of its 8) takes row 16 ks + 8 (g >> 1) + 4 t +
+    // (j >> 2) and column p0 + 16 (g & 1) + 4 (j & 3), p0 = wp 128 + 32 a: the result is
+    // the MFMA A operand (p = l & 31, k = 8 (l >> 5) ..).  The chunk swizzle puts the 32
+    // (row, chunk) pairs one read touches on every bank group exactly twice.
+    int trbase = 0, trxa[4] = {0, 0, 0, 0};
+    if constexpr (kPmn) {
+        const int gq = lane >> 4, jj = lane & 15;
+        trbase = (8 * (gq >> 1) + (jj >> 2)) * 512 + (wp * 16 + 2 * (gq & 1) + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) trxa[a] = (a ^ (jj >> 2)) << 6;
+    }
+    auto read_p_tr = [&](const char* base, int a, int ks) {
+        typedef short i16x4_t __attribute__((ext_vector_type(4)));
+        typedef short i16x8_t __attribute__((ext_vector_type(8)));
+        typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+        const char* p0 = base + trbase + trxa[a] + ks * 16 * 512;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)p0);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)(p0 + 4 * 512));
+        const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8_t, v);
+    };
     auto read_frags = [&](int buf, int ks, bf16x8_t pf[4], bf16x8_t qf[4]) {
         const char* base = lds + buf * BUFB;
         const int x = ks ? 32 : 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            pf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragP[b] ^ x));
+            if constexpr (kPmn) pf[b] = read_p_tr(base, b, ks);
+            else pf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragP[b] ^ x));
             qf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragQ[b] ^ x));
         }
     };
@@ -428,13 +476,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[0], acc[a][0], 0, 0, 0);
-            npf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[a] ^ x));
+            if constexpr (kPmn) npf[a] = read_p_tr(rbase, a, rks);
+            else npf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[a] ^ x));
             acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[1], acc[a][1], 0, 0, 0);
             nqf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[a] ^ x));
             acc[a][2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[2], acc[a][2], 0, 0, 0);
             acc[a][3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[3], acc[a][3], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x100, kPmn ? 2 : 1, 0);   // LDS read(s) of P
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
