@@ -62,6 +62,7 @@ KERNEL_OF_STAGE = {
     "dgrad_w2": "grouped_gemm<2,", "dgrad_w13": "grouped_gemm<3,",
     "wgrad_w2": "grouped_gemm<4,", "wgrad_w13": "grouped_gemm<5,",
     "quant_x": "quantize_kernel", "decode_w13": "decode_w13", "decode_w2": "decode_w2",
+    "wgrad_rows": "wgrad_rows_kernel",
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels
 KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13="grouped_gemm_mx<0>", w2="grouped_gemm_mx<1>")
@@ -322,6 +323,7 @@ def main():
                  "dgrad_w13": 4.0 * R * I * d, "wgrad_w13": 4.0 * R * I * d}
     # bytes each stage must move at least once
     min_bytes = {"combine": 2.0 * R * d + 2.0 * T * d + 8.0 * R,
+                 "wgrad_rows": 4.0 * R * d + 4.0 * T * d + 8.0 * R,
                  "dispatch": 8.0 * R + 4.0 * (E + 1) + 12.0 * R,
                  "quant_x": T * d * (2.0 + 1.0 + 1.0 / 32),
                  "decode_w13": n_active_mean * 2 * I * d * 2.0 + 2.0 * T * d + 2.0 * R * I + 4.0 * R,

@@ -188,7 +188,8 @@ const char* moe_status_string(moe_status_t status);
 #define MOE_STAGE_DX_COMBINE 10
 #define MOE_STAGE_DECODE_W13 11
 #define MOE_STAGE_DECODE_W2 12
-#define MOE_STAGE_COUNT 13
+#define MOE_STAGE_WGRAD_ROWS 13
+#define MOE_STAGE_COUNT 14
 
 /* Per-stage timing with HIP events, for measurement only.  While enabled,
  * moe_forward and moe_backward record a pair of HIP events around each kernel

@@ -101,7 +101,43 @@ __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __
     }
 }
 
+// Row-major operands of the weight-gradient products: xg[r] = x[gather[r]] and
+// dys[r] = bf16(probs[r] * dy[gather[r]]) for routed rows r.  One workgroup per row
+// (grid-strided), one 16-byte chunk of each per thread.
+__global__ __launch_bounds__(kThreads) void wgrad_rows_kernel(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ dy,
+                                                              const int32_t* __restrict__ gather,
+                                                              const float* __restrict__ probs,
+                                                              int64_t R, int d,
+                                                              uint16_t* __restrict__ xg,
+                                                              uint16_t* __restrict__ dys) {
+    for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
+        const size_t t = (size_t)gather[r];
+        const float sc = probs[r];
+        for (int n = threadIdx.x * 8; n < d; n += kThreads * 8) {
+            const uint4 xv = *reinterpret_cast<const uint4*>(x + t * d + n);
+            const uint4 gv = *reinterpret_cast<const uint4*>(dy + t * d + n);
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+            uint32_t ow[4];
+#pragma unroll
+            for (int z = 0; z < 4; ++z) ow[z] = pack_bf16(sc * bf16lo(gw[z]), sc * bf16hi(gw[z]));
+            *reinterpret_cast<uint4*>(xg + (size_t)r * d + n) = xv;
+            *reinterpret_cast<uint4*>(dys + (size_t)r * d + n) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, const int32_t* gather,
+                             const float* probs, int64_t R, int d, uint16_t* xg, uint16_t* dys,
+                             hipStream_t s) {
+    if (R == 0) return hipSuccess;
+    const int64_t grid = R < 65536 ? R : 65536;
+    hipLaunchKernelGGL(wgrad_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, dy, gather,
+                       probs, R, d, xg, dys);
+    return hipGetLastError();
+}
 
 hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,
                           int d, uint16_t* y, hipStream_t s) {

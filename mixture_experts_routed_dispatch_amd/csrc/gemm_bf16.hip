@@ -29,13 +29,12 @@
 //   * computes stage s from buffer s % 4: two k steps of 16 MFMAs, the fragments of
 //     the second step read in the shadow of the first step's MFMAs, those of stage
 //     s + 1's first step in the shadow of the second step's;
-//   * K-major operands: issues the direct global-to-LDS copies of stage s + 3, one
-//     1 KiB copy after each group of four MFMAs (a burst of copies stalls the MFMA
-//     issue), waited for with explicit vmcnt counts one stage later;
-//   * MN-major operands (the transposed products of backward): writes the registers
-//     of stage s + 2 into LDS as 8 x 8 blocks transposed on the way, and loads
-//     stage s + 3 into them;
-// and ends with one barrier.  The tile walk keeps the expert offsets and the next
+//   * issues the direct global-to-LDS copies of stage s + 3, one 1 KiB copy after
+//     each group of four MFMAs (a burst of copies stalls the MFMA issue), waited for
+//     with explicit vmcnt counts one stage later;
+// and ends with one barrier.  K-major operands are staged as rows of K; MN-major
+// operands (the transposed products of backward) as rows of M or N, read into MFMA
+// fragments with the transposing LDS read ds_read_b64_tr_b16.  The tile walk keeps the expert offsets and the next
 // tiles' gather indices in LDS (the latter fetched by an LDS copy a tile ahead), so
 // the main loop issues no global load the compiler would have to wait for: such a
 // wait would also wait for every copy in flight.  Consecutive tile ids go to
@@ -51,15 +50,6 @@ constexpr int NBUF = 4;
 constexpr int NTHR = 256;
 constexpr int OPB = TP * TK * 2;          // one operand of one stage: 16 KiB
 constexpr int BUFB = 2 * OPB;             // one stage buffer (P then Q): 32 KiB
-
-struct __attribute__((aligned(16))) Chunk { uint32_t w[4]; };
-
-__device__ __forceinline__ Chunk ld16(const uint16_t* p) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    Chunk c; c.w[0] = v.x; c.w[1] = v.y; c.w[2] = v.z; c.w[3] = v.w;
-    return c;
-}
-__device__ __forceinline__ Chunk zero_chunk() { Chunk c; c.w[0] = c.w[1] = c.w[2] = c.w[3] = 0; return c; }
 
 // Byte offset of logical 16-byte chunk c (k = 8c .. 8c+7 of the stage) of row r in
 // an operand tile: 64-byte rows, chunk slot c ^ swz(r).  swz maps bits (2, 3) of r
@@ -83,18 +73,6 @@ __device__ __forceinline__ void tile_order(int local, int nQt, int nPt, int& pt,
     const int gsz = left < kQGroup ? left : kQGroup;
     pt = rem / gsz;
     qt = gi * kQGroup + (rem - pt * gsz);
-}
-
-// out[m] holds element m of each in[k] (k = 0..7): the 8 x 8 BF16 transpose.
-__device__ __forceinline__ void transpose8x8(const Chunk in[8], Chunk out[8]) {
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = in[2 * j].w[m >> 1], hi = in[2 * j + 1].w[m >> 1];
-            out[m].w[j] = (m & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-        }
-    }
 }
 
 template <int MODE> struct Traits;
@@ -221,19 +199,35 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // explicit vmcnt counts (issued as inline assembly, so the compiler neither
     // tracks nor waits for them: loads complete in issue order, and the wait before a
     // barrier leaves exactly the younger copies outstanding).
-    // The MN-major P of the DGRAD products (a weight matrix read transposed) is copied
-    // too, into an MN-major stage (see read_p_tr below).
-    constexpr bool kPmn = (MODE == DGRAD_W2 || MODE == DGRAD_W13);
-    constexpr bool kPcopy = kPk || kPmn;
-    constexpr int kDmaOps = (kPcopy ? 4 : 0) + (kQk ? 4 : 0);  // copies per wave per stage
-    // row length (elements) of the MN-major P: W2_e [d, I] for DGRAD_W2, W13_e [2I, d]
-    // for DGRAD_W13; a stage holds 32 of its rows (k) x 256 columns (p)
-    const int pmn_ld = MODE == DGRAD_W2 ? g.I : g.d;
+    // MN-major operands (the transposed products of backward) are copied the same way
+    // into MN-major stages: 32 rows (k) x 256 columns, read as MFMA fragments with
+    // transposing LDS reads (read_tr below).
+    constexpr bool kPmn = !kPk, kQmn = !kQk;
+    constexpr bool kRagged = Traits<MODE>::kRaggedK;
+    // row length (elements) of an MN-major operand, which is also its column count:
+    // P = W2_e [d, I] (DGRAD_W2), W13_e [2I, d] (DGRAD_W13), a [R, I] (WGRAD_W2),
+    // xg [R, d] (WGRAD_W13); Q = dys [R, d] (WGRAD_W2), dh [R, 2I] (WGRAD_W13)
+    const int pmn_ld = (MODE == DGRAD_W2 || MODE == WGRAD_W2) ? g.I : g.d;
+    const int qmn_ld = MODE == WGRAD_W13 ? 2 * g.I : g.d;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds;
     // byte offsets of this lane's rows: P blocks (j = 0..3), then Q blocks
     uint32_t dvoff[8];
     const char* pbase_e = nullptr;        // P base of the load cursor's expert
+    const char* qbase_e = nullptr;        // Q base of the load cursor's expert (weight gradients)
+    int lc_rows = 0;                      // routed rows of the load cursor's expert
+    // MN-major copy j of wave w fills stage rows 8 w + 2 j + L / 32, 16-byte slot L % 32,
+    // which holds logical chunk (L % 32) ^ ((row & 3) << 2), i.e. columns
+    // col0 + 8 chunk .. + 7 of that k row; columns past the matrix read any valid column
+    auto mn_offset = [&](int j, int col0, int ld) {
+        const int L = fresh_lane();
+        const int kr = 8 * wave + 2 * j + (L >> 5);
+        const int ch = (L & 31) ^ ((kr & 3) << 2);
+        int col = col0 + 8 * ch;
+        if (col > ld - 8) col = ld - 8;
+        return (uint32_t)(kr * ld + col) * 2u;
+    };
     auto dma_offsets = [&](const TileCtx& c, const int src[4]) {
+        lc_rows = c.rows;
         const int drow_in_blk = fresh_lane() >> 2;
         const int lane = drow_in_blk * 4 + (fresh_lane() & 3);
 #pragma unroll
@@ -251,18 +245,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 int pr = c.pt * TP + r;
                 if (pr >= g.d) pr = g.d - 1;
                 dvoff[j] = (uint32_t)(pr * g.I + 8 * cl) * 2u;
-            } else if constexpr (kPmn) {
-                // MN-major stage: 32 rows (k) of 512 bytes; copy j of wave w fills rows
-                // 8 w + 2 j + L / 32, 16-byte slot L % 32, which holds logical chunk
-                // (L % 32) ^ ((row & 3) << 2) (columns p = 8 chunk ..)
-                const int L = fresh_lane();
-                const int kr = 8 * wave + 2 * j + (L >> 5);
-                const int ch = (L & 31) ^ ((kr & 3) << 2);
-                int col = c.pt * TP + 8 * ch;
-                if (col > pmn_ld - 8) col = pmn_ld - 8;           // past the matrix: any valid column
-                dvoff[j] = (uint32_t)(kr * pmn_ld + col) * 2u;
+            } else {
+                dvoff[j] = mn_offset(j, c.pt * TP, pmn_ld);
             }
-            if constexpr (kQk) {
+            if constexpr (kQmn) {
+                dvoff[4 + j] = mn_offset(j, c.qt * TQ, qmn_ld);
+            } else {
                 const int qs = src[j];
                 if constexpr (MODE == FWD_W13 || MODE == DGRAD_W2) dvoff[4 + j] = (uint32_t)(qs * g.d + 8 * cl) * 2u;
                 else if constexpr (MODE == FWD_W2) dvoff[4 + j] = (uint32_t)(qs * g.I + 8 * cl) * 2u;
@@ -272,6 +260,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         if constexpr (MODE == FWD_W13) pbase_e = reinterpret_cast<const char*>(g.w13 + (size_t)c.e * 2 * g.I * g.d);
         if constexpr (MODE == FWD_W2 || MODE == DGRAD_W2) pbase_e = reinterpret_cast<const char*>(g.w2 + (size_t)c.e * g.d * g.I);
         if constexpr (MODE == DGRAD_W13) pbase_e = reinterpret_cast<const char*>(g.w13 + (size_t)c.e * 2 * g.I * g.d);
+        if constexpr (MODE == WGRAD_W2) {
+            pbase_e = reinterpret_cast<const char*>(g.a + (size_t)c.mb * g.I);
+            qbase_e = reinterpret_cast<const char*>(g.dys + (size_t)c.mb * g.d);
+        }
+        if constexpr (MODE == WGRAD_W13) {
+            pbase_e = reinterpret_cast<const char*>(g.xg + (size_t)c.mb * g.d);
+            qbase_e = reinterpret_cast<const char*>(g.dh + (size_t)c.mb * 2 * g.I);
+        }
     };
     // byte offset of stage kt inside the P rows of the load cursor's expert
     auto p_stage_bytes = [&](int kt) {
@@ -319,105 +315,41 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                      :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(base) : "memory");
     };
-    // copies of stage kt of the load cursor's tile into ring buffer buf
-    auto dma_stage = [&](int kt, int buf) {
-        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
-        const int kbytes = kt * TK * 2;
-        if constexpr (kPcopy) {
-            const char* b = pbase_e + p_stage_bytes(kt);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dma1(dst + j * 1024, dvoff[j], b);
-        }
-        if constexpr (kQk) {
-            const char* b = qbase + kbytes;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) dma1(dst + OPB + j * 1024, dvoff[4 + j], b);
-        }
+    // The weight gradients run K over an expert's routed rows, which end at any row:
+    // their copies are buffer loads whose resource covers only the stage's rows inside
+    // the expert, so that the rows past its end land in LDS as zeros.
+    auto bcopy = [&](uint32_t lds_addr, uint32_t voff, __amdgpu_buffer_rsrc_t rs) {
+        asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rs) : "memory");
     };
-    // copy j of stage kt (j < 4: P block j, else Q block j - 4; only K-major operands)
+    auto stage_rsrc = [&](const char* base_e, int ld, int kt) {
+        const int left = lc_rows - kt * TK;
+        const int n = left < 0 ? 0 : (left > TK ? TK : left);
+        // the values are uniform; say so, so that the resource is built in SGPRs
+        const uint64_t b = (uint64_t)(uintptr_t)(base_e + (size_t)kt * TK * ld * 2);
+        const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(b >> 32)) << 32) |
+                            (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)bu, (short)0,
+                                                 __builtin_amdgcn_readfirstlane(n * ld * 2), 0x00020000);
+    };
+    // copy j of stage kt of the load cursor's tile into ring buffer buf (j < 4: P
+    // block j, else Q block j - 4)
     auto dma_one = [&](int kt, int buf, int j) {
-        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
-        const int kbytes = kt * TK * 2;
-        if constexpr (kPcopy && kQk) {
-            if (j < 4) dma1(dst + j * 1024, dvoff[j], pbase_e + p_stage_bytes(kt));
-            else dma1(dst + OPB + (j - 4) * 1024, dvoff[j], qbase + kbytes);
-        } else if constexpr (kQk) {
-            if (j < 4) dma1(dst + OPB + j * 1024, dvoff[4 + j], qbase + kbytes);
+        const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024 + (j < 4 ? j * 1024 : OPB + (j - 4) * 1024);
+        if constexpr (kRagged) {
+            if (j < 4) bcopy(dst, dvoff[j], stage_rsrc(pbase_e, pmn_ld, kt));
+            else bcopy(dst, dvoff[j], stage_rsrc(qbase_e, qmn_ld, kt));
+        } else {
+            if (j < 4) dma1(dst, dvoff[j], pbase_e + p_stage_bytes(kt));
+            else dma1(dst, dvoff[j], qbase + kt * TK * 2);
         }
     };
-    // wait until at most n of this wave's copies are outstanding
-    auto wait_dma = [&]() {
-        if constexpr (kDmaOps == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if constexpr (kDmaOps == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    auto dma_stage = [&](int kt, int buf) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma_one(kt, buf, j);
     };
-
-    // ------------------------------------------------------------ MN-major operands: via registers
-    // One 8 (k) x 8 (mn) block per thread: threads 0..127 own a P block; with an
-    // MN-major Q too (weight gradients), threads 128..255 own a Q block.  Loaded one
-    // stage before it is written, transposed in registers on the way to LDS.
-    constexpr bool kStaged = !kPcopy;
-    Chunk st[8];
-    auto load_stage = [&](const TileCtx& c, int kt) {
-        if constexpr (kStaged) {
-            const int k0 = kt * TK;
-            const int bt = tid & 127;
-            const int mnb = bt & 31, kb = bt >> 5;
-            if (tid < 128) {
-                const int pcol = c.pt * TP + mnb * 8;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int k = k0 + kb * 8 + kk;
-                    Chunk v = zero_chunk();
-                    if constexpr (MODE == DGRAD_W2) {
-                        if (pcol < g.I) v = ld16(g.w2 + ((size_t)c.e * g.d + k) * g.I + pcol);
-                    } else if constexpr (MODE == DGRAD_W13) {
-                        if (pcol < g.d) v = ld16(g.w13 + ((size_t)c.e * 2 * g.I + k) * g.d + pcol);
-                    } else if constexpr (MODE == WGRAD_W2) {
-                        if (k < c.rows && pcol < g.I) v = ld16(g.a + (size_t)(c.mb + k) * g.I + pcol);
-                    } else {  // WGRAD_W13
-                        if (k < c.rows && pcol < g.d) v = ld16(g.x + (size_t)g.gather[c.mb + k] * g.d + pcol);
-                    }
-                    st[kk] = v;
-                }
-            } else if constexpr (!kQk) {
-                const int qcol = c.qt * TQ + mnb * 8;
-#pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int k = k0 + kb * 8 + kk;
-                    Chunk v = zero_chunk();
-                    if constexpr (MODE == WGRAD_W2) {
-                        if (k < c.rows && qcol < g.d) {
-                            const int r = c.mb + k;
-                            const Chunk dv = ld16(g.dy + (size_t)g.gather[r] * g.d + qcol);
-                            const float sc = g.probs[r];
-#pragma unroll
-                            for (int w = 0; w < 4; ++w)
-                                v.w[w] = pack_bf16(bf16lo(dv.w[w]) * sc, bf16hi(dv.w[w]) * sc);
-                        }
-                    } else {  // WGRAD_W13
-                        if (k < c.rows && qcol < 2 * g.I) v = ld16(g.dh + (size_t)(c.mb + k) * 2 * g.I + qcol);
-                    }
-                    st[kk] = v;
-                }
-            }
-        }
-    };
-    auto store_stage = [&](int buf) {
-        if constexpr (kStaged) {
-            const int bt = tid & 127;
-            const int mnb = bt & 31, kb = bt >> 5;
-            if (tid < 128 || !kQk) {
-                char* dst = lds + buf * BUFB + (tid < 128 ? 0 : OPB);
-                Chunk t[8];
-                transpose8x8(st, t);
-#pragma unroll
-                for (int m = 0; m < 8; ++m)
-                    *reinterpret_cast<uint4*>(dst + lofs(mnb * 8 + m, kb)) =
-                        make_uint4(t[m].w[0], t[m].w[1], t[m].w[2], t[m].w[3]);
-            }
-        }
-    };
-
+    // wait until at most one stage (8 copies) of this wave's copies is outstanding
+    auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
     // ------------------------------------------------------------ fragments
     // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
     // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
@@ -427,25 +359,28 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         fragP[b] = lofs(wp * 128 + b * 32 + (lane & 31), lane >> 5);
         fragQ[b] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), lane >> 5);
     }
-    // MN-major P fragments (kPmn) with ds_read_b64_tr_b16: within a 16-lane group, lane j
-    // reads 4 consecutive p of row k0 + j / 4 at column n0 + 4 (j % 4), and lane i
+    // MN-major fragments with ds_read_b64_tr_b16: within a 16-lane group, lane j reads 4
+    // consecutive columns of row k0 + j / 4 at column n0 + 4 (j % 4), and lane i
     // receives rows k0 .. k0 + 3 of column n0 + i.  Lane l = 16 g + j of fragment a, k
     // step ks, read t (k 4t .. 4t + 3 of its 8) takes row 16 ks + 8 (g >> 1) + 4 t +
-    // (j >> 2) and column p0 + 16 (g & 1) + 4 (j & 3), p0 = wp 128 + 32 a: the result is
-    // the MFMA A operand (p = l & 31, k = 8 (l >> 5) ..).  The chunk swizzle puts the 32
-    // (row, chunk) pairs one read touches on every bank group exactly twice.
-    int trbase = 0, trxa[4] = {0, 0, 0, 0};
-    if constexpr (kPmn) {
+    // (j >> 2) and column c0 + 16 (g & 1) + 4 (j & 3), c0 = 128 wp (P) or 128 wq (Q)
+    // + 32 a: the result is the MFMA operand (column l & 31, k = 8 (l >> 5) ..), as a
+    // K-major fragment read would give it.  The chunk swizzle puts the 32 (row, chunk)
+    // pairs one read touches on every bank group exactly twice.
+    int trbase = 0, trbaseQ = OPB, trxa[4] = {0, 0, 0, 0};
+    if constexpr (kPmn || kQmn) {
         const int gq = lane >> 4, jj = lane & 15;
-        trbase = (8 * (gq >> 1) + (jj >> 2)) * 512 + (wp * 16 + 2 * (gq & 1) + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+        const int rowpart = (8 * (gq >> 1) + (jj >> 2)) * 512 + (2 * (gq & 1) + ((jj & 3) >> 1)) * 16 + (jj & 1) * 8;
+        trbase = rowpart + wp * 16 * 16;
+        trbaseQ = OPB + rowpart + wq * 16 * 16;
 #pragma unroll
         for (int a = 0; a < 4; ++a) trxa[a] = (a ^ (jj >> 2)) << 6;
     }
-    auto read_p_tr = [&](const char* base, int a, int ks) {
+    auto read_tr = [&](const char* base, int tb, int a, int ks) {
         typedef short i16x4_t __attribute__((ext_vector_type(4)));
         typedef short i16x8_t __attribute__((ext_vector_type(8)));
         typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-        const char* p0 = base + trbase + trxa[a] + ks * 16 * 512;
+        const char* p0 = base + tb + trxa[a] + ks * 16 * 512;
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)p0);
         const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)(p0 + 4 * 512));
         const i16x8_t v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -456,9 +391,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         const int x = ks ? 32 : 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if constexpr (kPmn) pf[b] = read_p_tr(base, b, ks);
+            if constexpr (kPmn) pf[b] = read_tr(base, trbase, b, ks);
             else pf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragP[b] ^ x));
-            qf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragQ[b] ^ x));
+            if constexpr (kQmn) qf[b] = read_tr(base, trbaseQ, b, ks);
+            else qf[b] = *reinterpret_cast<const bf16x8_t*>(base + (fragQ[b] ^ x));
         }
     };
 
@@ -476,18 +412,19 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[0], acc[a][0], 0, 0, 0);
-            if constexpr (kPmn) npf[a] = read_p_tr(rbase, a, rks);
+            if constexpr (kPmn) npf[a] = read_tr(rbase, trbase, a, rks);
             else npf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[a] ^ x));
             acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[1], acc[a][1], 0, 0, 0);
-            nqf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[a] ^ x));
+            if constexpr (kQmn) nqf[a] = read_tr(rbase, trbaseQ, a, rks);
+            else nqf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[a] ^ x));
             acc[a][2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[2], acc[a][2], 0, 0, 0);
             acc[a][3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[3], acc[a][3], 0, 0, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, kPmn ? 2 : 1, 0);   // LDS read(s) of P
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kQmn ? 2 : 1, 0);   // LDS read(s) of Q
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            if constexpr (kDmaOps > 0) dma_one(dma_kt, dma_buf, dma_first + a);
+            dma_one(dma_kt, dma_buf, dma_first + a);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -635,8 +572,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 
     // ------------------------------------------------------------ stage stream
     // Stage s of the stream lives in ring buffer s % 4.  During stage s the copies
-    // of stage s + 3 are issued (K-major) and the registers of stage s + 2 are
-    // written (MN-major); the barrier ending stage s publishes stage s + 2 (its
+    // of stage s + 3 are issued; the barrier ending stage s publishes stage s + 2 (its
     // copies, issued during stage s - 1, are waited for) and ring buffer s + 1 was
     // published one barrier earlier, so the first fragments of stage s + 1 are read
     // before it.  The load cursor runs three stages ahead of the compute cursor;
@@ -671,16 +607,11 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
 
     // prologue: stages 0, 1, 2
-    if constexpr (kDmaOps > 0) {
-        dma_stage(l_kt, 0);
-    }
-    if constexpr (kStaged) { load_stage(lc, l_kt); store_stage(0); }
+    dma_stage(l_kt, 0);
     advance_load();
-    if constexpr (kDmaOps > 0) dma_stage(l_kt, 1);
-    if constexpr (kStaged) { load_stage(lc, l_kt); store_stage(1); }
+    dma_stage(l_kt, 1);
     advance_load();
-    if constexpr (kDmaOps > 0) dma_stage(l_kt, 2);
-    if constexpr (kStaged) load_stage(lc, l_kt);
+    dma_stage(l_kt, 2);
     advance_load();
     wait_dma();                        // stages 0 and 1 copied (stage 2 may be in flight)
     __syncthreads();
@@ -699,15 +630,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
         for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
-            // k step 0: MFMAs on (fa, fc); meanwhile read step 1's fragments, issue the
-            // copies of stage gs + 3, write the registers of stage gs + 2
-            // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd),
-            // issuing the copies of stage gs + 3 and writing the registers of stage gs + 2
-            if constexpr (kStaged) store_stage((gs + 2) & 3);
+            // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd) and
+            // issuing the first half of the copies of stage gs + 3
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fa, fc, gs & 3, 1, fb, fd, l_kt, (gs + 3) & 3, 0);
-            if constexpr (kStaged) load_stage(lc, l_kt);
-            // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments
+            // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments and
+            // issuing the rest of the copies of stage gs + 3
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, l_kt, (gs + 3) & 3, 4);
             advance_load();

@@ -34,6 +34,8 @@ struct GemmArgs {
     const uint16_t* h;    // [R, 2I]  saved gate/up pre-activations
     const uint16_t* dy;   // [T, d]
     const uint16_t* dh;   // [R, 2I]  gradient w.r.t. (gate, up)
+    const uint16_t* xg;   // [R, d]   x[gather[r]]              (weight gradients)
+    const uint16_t* dys;  // [R, d]   bf16(probs[r] * dy[gather[r]])  (weight gradients)
     uint16_t* out;        // mode output
     uint16_t* out_h;      // FWD_W13 with save: h
 };
@@ -67,6 +69,12 @@ hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float
 // ds[t][j] = <dy[t], o[slots[t][j]]> in FP32.
 hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_t* slots, int T,
                              int k, int d, float* ds, hipStream_t s);
+
+// Operands of the weight gradients: xg[r] = x[gather[r]], dys[r] = bf16(probs[r] *
+// dy[gather[r]]), both [R, d].
+hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, const int32_t* gather,
+                             const float* probs, int64_t R, int d, uint16_t* xg, uint16_t* dys,
+                             hipStream_t s);
 
 // Small-batch (decode) path: T*k <= kMaxDecodeRows routed entries, E <= 256.
 constexpr int kMaxDecodeRows = 256;

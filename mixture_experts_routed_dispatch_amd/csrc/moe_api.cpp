@@ -34,7 +34,7 @@ struct moe_plan_s {
     bool decode;
     // workspace offsets (bytes)
     size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
-    size_t off_a, off_o, off_h, off_dh, off_dxp, off_xq, off_xs, off_aq, off_as;
+    size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_aq, off_as;
     size_t ws_bytes;
     char* ws;
     size_t ws_size;
@@ -135,6 +135,8 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_h = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
     p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
     p->off_dxp = c.training ? take(2 * (size_t)R * c.d) : 0;
+    p->off_xg = c.training ? take(2 * (size_t)R * c.d) : 0;
+    p->off_dys = c.training ? take(2 * (size_t)R * c.d) : 0;
     p->off_xq = mx ? take((size_t)c.T * c.d) : 0;
     p->off_xs = mx ? take((size_t)c.T * c.d / 32) : 0;
     p->off_aq = mx ? take((size_t)R * c.I) : 0;
@@ -329,6 +331,8 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     g.h = p->at<uint16_t>(p->off_h);
     g.dy = static_cast<const uint16_t*>(dy);
     g.dh = p->at<uint16_t>(p->off_dh);
+    g.xg = p->at<uint16_t>(p->off_xg);
+    g.dys = p->at<uint16_t>(p->off_dys);
     if (c.T == 0) {
         // no routed rows: every expert gradient is +0 (the weight-gradient kernels write them)
         g.m_indptr = p->at<int32_t>(p->off_m_indptr);
@@ -339,6 +343,11 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     } else {
         g.out = p->at<uint16_t>(p->off_dh);
         e = staged(p, MOE_STAGE_DGRAD_W2, s, [&] { return launch_gemm(DGRAD_W2, g, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_WGRAD_ROWS, s, [&] {
+            return launch_wgrad_rows(g.x, g.dy, g.gather, g.probs, p->R, c.d, p->at<uint16_t>(p->off_xg),
+                                     p->at<uint16_t>(p->off_dys), s);
+        });
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     g.out = static_cast<uint16_t*>(dw2);

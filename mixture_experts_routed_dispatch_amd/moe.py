@@ -41,7 +41,7 @@ EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_de
            "moe_profile_read")
 
 STAGES = ("dispatch", "quant_x", "w13", "w2", "combine", "score_grad", "dgrad_w2", "wgrad_w2",
-          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2")
+          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows")
 
 
 class MoeError(RuntimeError):
