@@ -66,6 +66,11 @@ __device__ __forceinline__ int lofs(int r, int c) { return r * 64 + ((c ^ swz(r)
 // share far more operand data in that XCD's L2 than 32 tiles of one q-tile row or
 // one p-tile column.
 constexpr int kQGroup = 6;
+// Longest weight-gradient tile (in K stages) computed in one piece.
+#ifndef MOE_WGRAD_CHUNK
+#define MOE_WGRAD_CHUNK 192
+#endif
+constexpr int kChunk = MOE_WGRAD_CHUNK;
 __device__ __forceinline__ void tile_order(int local, int nQt, int nPt, int& pt, int& qt) {
     const int gi = local / (kQGroup * nPt);
     const int rem = local - gi * kQGroup * nPt;
@@ -100,8 +105,14 @@ template <int MODE> __device__ __forceinline__ int k_size(const GemmArgs& g, int
     else return rows_e;
 }
 
+// One work item of a workgroup: stages k0 .. k0 + nk - 1 of tile (e, pt, qt).  A
+// weight-gradient tile cut into np > 1 pieces along K has its pieces' partial sums in
+// slots pslot0 + i * pstride (i = 0 .. np - 1; this piece's is `slot`) and its piece
+// counter at cslot.
 struct TileCtx {
-    int e, mb, rows, pt, qt, nk;
+    int e, mb, rows, pt, qt;
+    int k0, nk;
+    int np, slot, pslot0, pstride, cslot;
 };
 
 // kSaveH (FWD_W13 only): also store h = (g, u) for backward.  A separate instantiation
@@ -110,8 +121,11 @@ struct TileCtx {
 template <int MODE, bool kSaveH = false>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
-    __shared__ int cum[257];
+    __shared__ int cum[257];           // prefix over experts of their tiles (work items)
     __shared__ int mptr[257];          // m_indptr, so that the tile walk reads no global memory
+    // weight gradients only: experts in work order, their K stages and chunk counts, and
+    // prefixes (in work order) of partial-sum slots and split tiles
+    __shared__ int worder[256], wnk[256], wnch[256], pcum[257], tcum[257];
     __shared__ int gsrc[2][TQ];        // gather indices of the next two load-cursor tiles
     __shared__ int wtot[NTHR / MOE_WAVE];
 
@@ -132,60 +146,127 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     const int nPt = num_p_tiles<MODE>(g);
     constexpr bool kPk = Traits<MODE>::kP_kmajor, kQk = Traits<MODE>::kQ_kmajor;
 
-    // ---- tile list: tiles of expert e are cum[e] .. cum[e+1]-1
-    {
-        int cnt = 0;
-        if (tid < E) {
-            if constexpr (Traits<MODE>::kRaggedK) {
-                cnt = nPt * num_q_tiles_fixed<MODE>(g);
-            } else {
-                const int rows = g.m_indptr[tid + 1] - g.m_indptr[tid];
-                cnt = ((rows + TQ - 1) / TQ) * nPt;
-            }
-        }
-        int incl = cnt;
+    // ---- work list
+    // Tiles are numbered expert by expert; workgroup v takes items v, v + G, ... (the
+    // weight gradients snake: odd rounds run v = G - 1 .. 0).  Consecutive items run at
+    // the same time on consecutive workgroups of one XCD, so the tiles of one expert
+    // share their operand slices in its L2.
+    // The weight gradients' K is the expert's routed rows, which skewed routing makes a
+    // hundred times larger for some experts than for others.  There the experts are
+    // taken in decreasing order of work per tile, and a tile longer than C stages is cut
+    // into ceil(nk / C) equal pieces along K (C = kChunk stages, doubled until at most
+    // kMaxPieces pieces result), each piece a work item of its own: all pieces i of an
+    // expert's tiles follow each other in the list (they share K, like whole tiles).
+    // Each piece stores its FP32 partial sums; the last piece of a tile to finish adds
+    // them up in piece order (a fixed order: the result does not depend on timing).
+    constexpr bool kRagged = Traits<MODE>::kRaggedK;
+    const int kTPE = kRagged ? nPt * num_q_tiles_fixed<MODE>(g) : 0;   // tiles per expert (weight gradients)
+    auto nk_of = [&](int rows) {
+        const int nk = (k_size<MODE>(g, rows) + TK - 1) / TK;
+        return nk > 0 ? nk : 1;                   // an empty expert still runs one all-zero stage
+    };
+    // exclusive prefix over threads 0 .. E-1 of v (threads >= E pass 0); returns the
+    // block total.  Ends with a barrier.
+    auto block_scan = [&](int v, int* out) {
+        int incl = v;
         for (int off = 1; off < MOE_WAVE; off <<= 1) {
-            const int v = __shfl_up(incl, off, MOE_WAVE);
-            if (lane >= off) incl += v;
+            const int u = __shfl_up(incl, off, MOE_WAVE);
+            if (lane >= off) incl += u;
         }
         if (lane == MOE_WAVE - 1) wtot[wave] = incl;
-        for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
         __syncthreads();
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wtot[w];
-        if (tid < E) cum[tid + 1] = pre + incl;
-        if (tid == 0) cum[0] = 0;
+        if (tid < E) out[tid + 1] = pre + incl;
+        if (tid == 0) out[0] = 0;
+        const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
         __syncthreads();
+        return tot;
+    };
+    for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
+    __syncthreads();
+    if constexpr (kRagged) {
+        const int nk = tid < E ? nk_of(mptr[tid + 1] - mptr[tid]) : 0;
+        // chunk size C = kChunk << ci: the smallest with at most kMaxPieces pieces
+        int ci = 0;
+        for (; ci < 7; ++ci) {
+            const int C = kChunk << ci;
+            const int pc = (tid < E && nk > C) ? kTPE * ((nk + C - 1) / C) : 0;
+            if (block_scan(pc, pcum) <= kMaxPieces) break;
+        }
+        const int C = kChunk << ci;
+        const int nch = tid < E ? (nk + C - 1) / C : 0;
+        const int csz = tid < E ? (nk + nch - 1) / nch : 0;
+        if (tid < E) { wnk[tid] = nk; wnch[tid] = csz; }
+        __syncthreads();
+        // work order: decreasing piece length, then expert id
+        int rank = 0;
+        if (tid < E)
+            for (int e2 = 0; e2 < E; ++e2) rank += (wnch[e2] > csz || (wnch[e2] == csz && e2 < tid)) ? 1 : 0;
+        __syncthreads();
+        if (tid < E) { worder[rank] = tid; wnch[tid] = nch; }
+        __syncthreads();
+        const int e = tid < E ? worder[tid] : 0;            // expert at work position tid
+        const int nche = tid < E ? wnch[e] : 0;
+        block_scan(tid < E ? nche * kTPE : 0, cum);
+        block_scan((tid < E && nche > 1) ? nche * kTPE : 0, pcum);
+        block_scan((tid < E && nche > 1) ? kTPE : 0, tcum);
+    } else {
+        const int rows = tid < E ? mptr[tid + 1] - mptr[tid] : 0;
+        block_scan(tid < E ? ((rows + TQ - 1) / TQ) * nPt : 0, cum);
     }
-    const int total = cum[E];
     const int G = gridDim.x;
     const int vid = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
-    if (vid >= total) return;
-
-    auto coords = [&](int tile) {
-        // largest e with cum[e] <= tile: cum is non-decreasing and cum[0] = 0, so it is
-        // the number of e in [1, E) with cum[e] <= tile (one ballot per 64 experts)
+    const int total = cum[E];
+    int n_items;
+    {
+        const int F = total / G, rem = total - F * G;
+        const int pos = (kRagged && (F & 1)) ? G - 1 - vid : vid;
+        n_items = F + (pos < rem ? 1 : 0);
+    }
+    if (n_items == 0) return;
+    // largest s with cum[s] <= x: cum is non-decreasing and cum[0] = 0, so it is the
+    // number of s in [1, E) with cum[s] <= x (one ballot per 64 entries)
+    auto expert_at = [&](int x) {
         const int fl = fresh_lane();
         int lo = 0;
 #pragma unroll
         for (int base = 1; base < 257; base += 64) {
             const int e = base + fl;
-            lo += __builtin_popcountll(__ballot(e < E && cum[e] <= tile));
+            lo += __builtin_popcountll(__ballot(e < E && cum[e] <= x));
         }
-        lo = __builtin_amdgcn_readfirstlane(lo);
+        return __builtin_amdgcn_readfirstlane(lo);
+    };
+    // work item k of this workgroup
+    auto coords = [&](int k) {
+        const int item = k * G + ((kRagged && (k & 1)) ? G - 1 - vid : vid);
         TileCtx c;
-        c.e = lo;
-        const int local = tile - cum[lo];
-        c.mb = mptr[lo];
-        c.rows = mptr[lo + 1] - c.mb;
-        if constexpr (Traits<MODE>::kRaggedK) {
-            c.qt = local / nPt;
-            c.pt = local - c.qt * nPt;
+        const int sp = expert_at(item);
+        const int local = item - cum[sp];
+        if constexpr (kRagged) {
+            const int e = worder[sp];
+            const int nk = wnk[e], nch = wnch[e];
+            const int ch = local / kTPE, j = local - ch * kTPE;
+            c.e = e;
+            c.qt = j / nPt;
+            c.pt = j - c.qt * nPt;
+            c.k0 = nk * ch / nch;
+            c.nk = nk * (ch + 1) / nch - c.k0;
+            c.np = nch;
+            c.pslot0 = pcum[sp] + j;
+            c.pstride = kTPE;
+            c.slot = c.pslot0 + ch * kTPE;
+            c.cslot = tcum[sp] + j;
         } else {
-            tile_order(local, (c.rows + TQ - 1) / TQ, nPt, c.pt, c.qt);
+            c.e = sp;
+            tile_order(local, (mptr[sp + 1] - mptr[sp] + TQ - 1) / TQ, nPt, c.pt, c.qt);
+            c.k0 = 0;
+            c.nk = nk_of(0);
+            c.np = 1;
+            c.pslot0 = c.pstride = c.slot = c.cslot = 0;
         }
-        const int nk = (k_size<MODE>(g, c.rows) + TK - 1) / TK;
-        c.nk = nk > 0 ? nk : 1;                   // an empty expert still runs one all-zero stage
+        c.mb = mptr[c.e];
+        c.rows = mptr[c.e + 1] - c.mb;
         return c;
     };
 
@@ -203,7 +284,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // into MN-major stages: 32 rows (k) x 256 columns, read as MFMA fragments with
     // transposing LDS reads (read_tr below).
     constexpr bool kPmn = !kPk, kQmn = !kQk;
-    constexpr bool kRagged = Traits<MODE>::kRaggedK;
     // row length (elements) of an MN-major operand, which is also its column count:
     // P = W2_e [d, I] (DGRAD_W2), W13_e [2I, d] (DGRAD_W13), a [R, I] (WGRAD_W2),
     // xg [R, d] (WGRAD_W13); Q = dys [R, d] (WGRAD_W2), dh [R, 2I] (WGRAD_W13)
@@ -578,12 +658,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // before it.  The load cursor runs three stages ahead of the compute cursor;
     // once the stream is exhausted it repeats its last stage into buffers no later
     // stage reads.
-    int l_tile = vid, l_kt = 0;
-    TileCtx lc = coords(l_tile);
+    int l_item = 0, l_kt = 0;          // load cursor: work item, stage within it
+    TileCtx lc = coords(0);
     int gslot = 0;                     // gsrc slot of the load cursor's tile
-    TileCtx nc = lc;                   // coordinates of the load cursor's next tile
+    TileCtx nc = lc;                   // coordinates of the load cursor's next item
     gather_dma(lc, 0);
-    if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, 1); }
+    if (n_items > 1) { nc = coords(1); gather_dma(nc, 1); }
     if constexpr (kGather) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     {
         int src[4] = {0, 0, 0, 0};
@@ -592,26 +672,26 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     }
     auto advance_load = [&]() {
         if (++l_kt < lc.nk) return;
-        if (l_tile + G >= total) { l_kt = lc.nk - 1; return; }
+        if (l_item + 1 >= n_items) { l_kt = lc.nk - 1; return; }
         // the indices of the new tile were copied at the previous switch, lc.nk stages
         // ago; with fewer than 3 stages per tile the stage waits need not cover them
         if constexpr (kGather) if (lc.nk < 3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         l_kt = 0;
-        l_tile += G;
+        ++l_item;
         gslot ^= 1;
         lc = nc;
         int src[4] = {0, 0, 0, 0};
         q_src(lc, gslot, src);
         dma_offsets(lc, src);
-        if (l_tile + G < total) { nc = coords(l_tile + G); gather_dma(nc, gslot ^ 1); }
+        if (l_item + 1 < n_items) { nc = coords(l_item + 1); gather_dma(nc, gslot ^ 1); }
     };
 
     // prologue: stages 0, 1, 2
-    dma_stage(l_kt, 0);
+    dma_stage(lc.k0 + l_kt, 0);
     advance_load();
-    dma_stage(l_kt, 1);
+    dma_stage(lc.k0 + l_kt, 1);
     advance_load();
-    dma_stage(l_kt, 2);
+    dma_stage(lc.k0 + l_kt, 2);
     advance_load();
     wait_dma();                        // stages 0 and 1 copied (stage 2 may be in flight)
     __syncthreads();
@@ -619,8 +699,36 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     bf16x8_t fa[4], fb[4], fc[4], fd[4];
     read_frags(0, 0, fa, fc);
 
-    int c_tile = vid;
-    TileCtx cc = coords(c_tile);
+    // A piece of a split weight-gradient tile stores its partial sums: thread t, float4
+    // j at (j * 256 + t) * 4 of its slot, j = (a * 4 + b) * 4 + z holding acc[a][b][4 z ..
+    // 4 z + 3].  The first piece also describes the tile for wgrad_fixup, which adds up
+    // the pieces after this kernel (the kernel boundary makes them visible; a device-wide
+    // fence per piece would write back and invalidate an XCD's whole L2).
+    constexpr int kPartFloats = NTHR * 256;
+    auto store_piece = [&](const TileCtx& c) {
+        const int t = fresh_lane() + 64 * wave;
+        float* mine = g.part + (size_t)c.slot * kPartFloats;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    const int j = (a * 4 + b) * 4 + z;
+                    const f32x4_t v = {acc[a][b][4 * z], acc[a][b][4 * z + 1], acc[a][b][4 * z + 2], acc[a][b][4 * z + 3]};
+                    *reinterpret_cast<f32x4_t*>(mine + ((size_t)j * NTHR + t) * 4) = v;
+                }
+        if (t == 0 && c.slot == c.pslot0) {
+            int4 dsc;
+            dsc.x = c.e; dsc.y = c.qt * 65536 + c.pt; dsc.z = c.np; dsc.w = c.pslot0 * 65536 + c.pstride;
+            g.split[c.cslot] = dsc;
+        }
+    };
+    if constexpr (kRagged)
+        if (vid == 0 && tid == 0) *g.nsplit = tcum[E];
+
+    int c_item = 0;
+    TileCtx cc = coords(0);
     int gs = 0;
     while (true) {
 #pragma unroll
@@ -633,20 +741,67 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd) and
             // issuing the first half of the copies of stage gs + 3
             __builtin_amdgcn_sched_barrier(0);
-            mfma_step(fa, fc, gs & 3, 1, fb, fd, l_kt, (gs + 3) & 3, 0);
+            mfma_step(fa, fc, gs & 3, 1, fb, fd, lc.k0 + l_kt, (gs + 3) & 3, 0);
             // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments and
             // issuing the rest of the copies of stage gs + 3
             __builtin_amdgcn_sched_barrier(0);
-            mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, l_kt, (gs + 3) & 3, 4);
+            mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
             advance_load();
             wait_dma();                // this wave's copies of stage gs + 2 have landed
             __syncthreads();
         }
-        epilogue(cc, (gs - 1) & 3);
-        c_tile += G;
-        if (c_tile >= total) break;
+        if (!kRagged || cc.np == 1) epilogue(cc, (gs - 1) & 3);
+        else store_piece(cc);
+        if (++c_item >= n_items) break;
         __syncthreads();               // the staging slots are copied into again from the next stage
-        cc = coords(c_tile);
+        cc = coords(c_item);
+    }
+}
+
+// Weight-gradient tiles cut into pieces along K: out = ((piece 0 + piece 1) + ...) in
+// BF16, one workgroup per quarter of a tile.  Thread t of the tile owns the elements thread t of
+// grouped_gemm held (wave w = t / 64 covers p in [128 (w & 1), +128), q in
+// [128 (w >> 1), +128) of the tile).
+template <int MODE>
+__global__ __launch_bounds__(NTHR) void wgrad_fixup(GemmArgs g) {
+    constexpr int kPartFloats = NTHR * 256;
+    const int n = *g.nsplit;
+    const int t = threadIdx.x, ln = t & 63, wave = t >> 6, wp = wave & 1, wq = wave >> 1;
+    const int Psz = (MODE == WGRAD_W2) ? g.I : g.d;
+    const int Qsz = (MODE == WGRAD_W2) ? g.d : 2 * g.I;
+    for (int bi = blockIdx.x; bi < 4 * n; bi += gridDim.x) {
+        const int ts = bi >> 2, j0 = 16 * (bi & 3);     // tile, quarter of its elements
+        const int4 dsc = g.split[ts];
+        const int e = dsc.x, qt = dsc.y >> 16, pt = dsc.y & 0xFFFF, np = dsc.z;
+        const int pslot0 = dsc.w >> 16, pstride = dsc.w & 0xFFFF;
+        // element (a, b, z, 0..3): q = q0 + 32 b + (ln & 31), p = p0 + 32 a + 8 z + 4 (ln >> 5)
+        const int q0 = qt * TQ + wq * 128 + (ln & 31), p0 = pt * TP + wp * 128 + 4 * (ln >> 5);
+        uint16_t* out = g.out + (size_t)e * Qsz * Psz;
+        {
+            f32x4_t sum[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                sum[i] = *reinterpret_cast<const f32x4_t*>(g.part + (size_t)pslot0 * kPartFloats + ((size_t)(j0 + i) * NTHR + t) * 4);
+            for (int w = 1; w < np; ++w) {
+                const float* src = g.part + (size_t)(pslot0 + w * pstride) * kPartFloats;
+                f32x4_t v[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const f32x4_t*>(src + ((size_t)(j0 + i) * NTHR + t) * 4);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sum[i] += v[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int j = j0 + i, a = j >> 4, b = (j >> 2) & 3, z = j & 3;
+                const int q = q0 + 32 * b, p = p0 + 32 * a + 8 * z;
+                if (q < Qsz && p < Psz) {
+                    uint2 o;
+                    o.x = pack_bf16(sum[i][0], sum[i][1]);
+                    o.y = pack_bf16(sum[i][2], sum[i][3]);
+                    *reinterpret_cast<uint2*>(out + (size_t)q * Psz + p) = o;
+                }
+            }
+        }
     }
 }
 
@@ -670,6 +825,10 @@ hipError_t launch_mode(const GemmArgs& g, int num_cu, hipStream_t s) {
         }
     }
     hipLaunchKernelGGL((grouped_gemm<MODE, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+    if constexpr (MODE == WGRAD_W2 || MODE == WGRAD_W13) {
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((wgrad_fixup<MODE>), dim3(2 * kMaxPieces), dim3(NTHR), 0, s, g);
+    }
     return hipGetLastError();
 }
 

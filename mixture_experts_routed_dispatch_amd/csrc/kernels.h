@@ -38,7 +38,14 @@ struct GemmArgs {
     const uint16_t* dys;  // [R, d]   bf16(probs[r] * dy[gather[r]])  (weight gradients)
     uint16_t* out;        // mode output
     uint16_t* out_h;      // FWD_W13 with save: h
+    float* part;          // [kMaxPieces, 256 * 256] FP32 partial sums of split weight-gradient tiles
+    int4* split;          // [kMaxPieces / 2] split tiles: (e, qt << 16 | pt, pieces, slot0 << 16 | stride)
+    int32_t* nsplit;      // number of split tiles of the last weight-gradient launch
 };
+
+// Pieces of split weight-gradient tiles in one launch (sizes their FP32 partial sums).
+constexpr int kMaxPieces = 512;
+constexpr size_t kGemmPartBytes = (size_t)kMaxPieces * 256 * 256 * sizeof(float);
 
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
 

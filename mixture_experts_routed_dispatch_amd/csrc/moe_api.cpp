@@ -35,6 +35,7 @@ struct moe_plan_s {
     // workspace offsets (bytes)
     size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
     size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_aq, off_as;
+    size_t off_part, off_split;        // split weight-gradient tiles: partial sums, descriptors
     size_t ws_bytes;
     char* ws;
     size_t ws_size;
@@ -141,6 +142,9 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_xs = mx ? take((size_t)c.T * c.d / 32) : 0;
     p->off_aq = mx ? take((size_t)R * c.I) : 0;
     p->off_as = mx ? take((size_t)R * c.I / 32) : 0;
+    const bool gemms = !mx && !p->decode;
+    p->off_split = take(sizeof(int32_t) * 4 * (kMaxPieces / 2 + 1));
+    p->off_part = gemms && c.training ? take(kGemmPartBytes) : 0;
     p->ws_bytes = off;
     p->ws = nullptr;
     p->ws_size = 0;
@@ -278,6 +282,9 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.part = p->at<float>(p->off_part);
+    g.split = p->at<int4>(p->off_split);
+    g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));
     g.m_indptr = m_indptr; g.gather = gather; g.probs = probs;
     g.x = static_cast<const uint16_t*>(x);
     g.w13 = static_cast<const uint16_t*>(w->w13);
@@ -321,6 +328,9 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.part = p->at<float>(p->off_part);
+    g.split = p->at<int4>(p->off_split);
+    g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));
     g.m_indptr = p->at<int32_t>(p->off_m_indptr);
     g.gather = p->at<int32_t>(p->off_gather);
     g.probs = p->at<float>(p->off_probs);

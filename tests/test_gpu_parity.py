@@ -349,6 +349,40 @@ def test_backward_small(torch_cuda, T, d, I, E, k, routing):
     layer.close()
 
 
+@pytest.mark.parametrize("T,d,I,E,k,hot", [(13000, 320, 192, 3, 1, 12500), (7000, 256, 128, 4, 2, 6600)])
+def test_backward_split_weight_gradient_tiles(torch_cuda, T, d, I, E, k, hot):
+    """An expert with more than 192 stages of 32 routed rows (12500 rows: 3 pieces, 6600
+    rows: 2 pieces) has its weight-gradient tiles cut along K into pieces whose FP32
+    partial sums are added up in piece order after the product; the result must match
+    the oracle and repeat bitwise."""
+    import dataclasses
+    torch = torch_cuda
+    say("backward split tiles", T, d, I, E, k, hot)
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=21, with_dy=True)
+    rng = np.random.default_rng(5)
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        if t < hot:
+            ids[t] = np.concatenate([[0], 1 + rng.permutation(E - 1)[:k - 1]])
+        else:
+            ids[t] = 1 + rng.permutation(E - 1)[:k]
+    inp = dataclasses.replace(inp, ids=ids)
+    t = device_inputs(inp)
+    layer = make_layer(inp, training=True)
+    layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    _, dw13b, dw2b, _ = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert torch.equal(dw13.view(torch.int16), dw13b.view(torch.int16))
+    assert torch.equal(dw2.view(torch.int16), dw2b.view(torch.int16))
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    dw13_ref = dw13_ref.reshape(E, 2 * I, d)
+    e_w2, e_w13 = rel(np_of(dw2), dw2_ref), rel(np_of(dw13), dw13_ref)
+    say("  dw2 %.3e dw13 %.3e" % (e_w2, e_w13))
+    assert max(e_w2, e_w13) <= TOL_BF16
+    layer.close()
+
+
 def test_backward_full_size_sampled(torch_cuda):
     torch = torch_cuda
     say("backward full size: train workload")
