@@ -14,12 +14,16 @@
 //     streams 16 rows of W2_e over K = I and writes o[t*k + j][n] in BF16.
 //   combine: y[t] = sum_j s[t][j] * o[t*k + j], FP32, j ascending from +0.0 (the
 //     prefill combine kernel, reading the rows in entry order).
-// A wave owns its item from the first load to the last store: no K split, no
-// reduction and no barrier between waves, so every wave of a CU streams on its own,
-// and the result does not depend on timing.  Items go to waves round-robin.
+// With many items (small batches) a wave owns its item from the first load to the last
+// store: no K split, no reduction and no barrier between waves, so every wave of a CU
+// streams on its own.  Items go to waves round-robin.  With fewer items than wave
+// slots on the chip (one token: k experts x 96 blocks) that would leave CUs idle and
+// each wave streaming its rows in several dependent load batches, so there the four
+// waves of a workgroup share one item, each streaming a quarter of K, and add their
+// partial sums through LDS in wave order (fixed: the result does not depend on timing).
 //
 // With one token the experts are the k ids themselves (distinct by the layer's
-// precondition).  With more tokens every workgroup first sorts the routed entries by
+// precondition), and the W2 products and the combine are one launch (decode_w2_one).  With more tokens every workgroup first sorts the routed entries by
 // expert in LDS (counts, their prefix over the expert ids, the active experts in
 // ascending id, and each expert's entries in ascending (t, j) order).
 //
@@ -162,21 +166,57 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& g, const DecodeSmem&
     return true;
 }
 
-// Walks this wave's items: its global wave id, then every (number of waves)-th item
-// after it.  For each item, f(slot, block).  (A shared work counter would balance
-// better, but one atomic per item on one address serialises: thousands per launch.)
-template <class F>
-__device__ __forceinline__ void for_wave_items(int items, int nblk, F f) {
-    const int nw = (int)gridDim.x * kWaves;
-    for (int item = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6); item < items; item += nw) {
+// Walks this wave's items (kSplit: this workgroup's): its global wave (workgroup) id,
+// then every (number of waves (workgroups))-th item after it.  For each item,
+// f(slot, block).  (A shared work counter would balance better, but one atomic per
+// item on one address serialises: thousands per launch.)
+template <bool kSplit, class F>
+__device__ __forceinline__ void for_items(int items, int nblk, F f) {
+    const int nw = kSplit ? (int)gridDim.x : (int)gridDim.x * kWaves;
+    const int first = kSplit ? (int)blockIdx.x : (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    for (int item = first; item < items; item += nw) {
         const int slot = item / nblk;
         f(slot, item - slot * nblk);
     }
 }
 
+// K split: wave w takes steps [S w / 4, S (w + 1) / 4) of the S steps of 32.
+template <bool kSplit>
+__device__ __forceinline__ void wave_steps(int S, int& s0, int& s1) {
+    if (kSplit) {
+        const int w = threadIdx.x >> 6;
+        s0 = S * w / kWaves;
+        s1 = S * (w + 1) / kWaves;
+    } else {
+        s0 = 0;
+        s1 = S;
+    }
+}
+
+// K split: the four waves' partial sums added in wave order; the total is valid in
+// wave 0.  red is double-buffered by the caller (`par`), so one barrier per call
+// suffices: a buffer is rewritten only after the next call's barrier, which wave 0
+// reaches after it has read the buffer.
+template <bool kSplit>
+__device__ __forceinline__ f32x4_t reduce_waves(f32x4_t acc, f32x4_t (*red)[kWaves][MOE_WAVE], int& par) {
+    if (!kSplit) return acc;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    red[par][wave][lane] = acc;
+    __syncthreads();
+    f32x4_t s = red[par][0][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += red[par][w][lane];
+    par ^= 1;
+    return s;
+}
+
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
     __shared__ DecodeSmem sm;
+    __shared__ f32x4_t red[2][kWaves][MOE_WAVE];
+    int par = 0;
     const int lane = threadIdx.x & 63;
+    const bool lead = !kSplit || threadIdx.x < MOE_WAVE;   // the wave that stores
     const int n = lane & 15, kq = lane >> 4;
     const int d = g.d, I = g.I, k = g.k;
     const int nIB = I / 8;
@@ -189,7 +229,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
         decode_setup(sm, g.ids, g.T, k, g.E, g.status, blockIdx.x == 0);
         items = sm.n_active * nIB;
     }
-    for_wave_items(items, nIB, [&](int slot, int ib) {
+    int s0, s1;
+    wave_steps<kSplit>(d / 32, s0, s1);
+    for_items<kSplit>(items, nIB, [&](int slot, int ib) {
         int e, M, e0;
         if (!slot_info(g, sm, one, slot, e, M, e0)) return;
         auto entry = [&](int m) { return one ? e0 : sm.ent[e0 + m]; };
@@ -201,13 +243,14 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
             const int m = m0 + n;
             const bool mv = m < M;
             const int tok = mv ? entry(m) / k : 0;
-            const f32x4_t acc = mma_row_block(wp, g.x + (size_t)tok * d + 8 * kq, mv, d / 32);
+            const f32x4_t acc = reduce_waves<kSplit>(
+                mma_row_block(wp + 32 * s0, g.x + (size_t)tok * d + 8 * kq + 32 * s0, mv, s1 - s0), red, par);
             // lane l holds rows 4 kq + z of column n; the up value of gate column c < 8
             // sits in lane l + 8 of the same 16-lane group
             float up[4];
 #pragma unroll
             for (int z = 0; z < 4; ++z) up[z] = __shfl_down(acc[z], 8, 16);
-            if (n < 8) {
+            if (lead && n < 8) {
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
                     const int mm = m0 + 4 * kq + z;
@@ -219,9 +262,13 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
     });
 }
 
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
     __shared__ DecodeSmem sm;
+    __shared__ f32x4_t red[2][kWaves][MOE_WAVE];
+    int par = 0;
     const int lane = threadIdx.x & 63;
+    const bool lead = !kSplit || threadIdx.x < MOE_WAVE;
     const int n = lane & 15, kq = lane >> 4;
     const int d = g.d, I = g.I, k = g.k;
     const int nNB = d / 16;
@@ -233,7 +280,9 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
         decode_setup(sm, g.ids, g.T, k, g.E, g.status, false);
         items = sm.n_active * nNB;
     }
-    for_wave_items(items, nNB, [&](int slot, int nb) {
+    int s0, s1;
+    wave_steps<kSplit>(I / 32, s0, s1);
+    for_items<kSplit>(items, nNB, [&](int slot, int nb) {
         int e, M, e0;
         if (!slot_info(g, sm, one, slot, e, M, e0)) return;
         auto entry = [&](int m) { return one ? e0 : sm.ent[e0 + m]; };
@@ -243,38 +292,97 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
             const int m = m0 + n;
             const bool mv = m < M;
             const uint16_t* ap = g.a + (size_t)(mv ? entry(m) : 0) * I + 8 * kq;
-            const f32x4_t acc = mma_row_block(wp, ap, mv, I / 32);
+            const f32x4_t acc = reduce_waves<kSplit>(mma_row_block(wp + 32 * s0, ap + 32 * s0, mv, s1 - s0), red, par);
+            if (lead) {
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                const int mm = m0 + 4 * kq + z;
-                if (mm < M) g.o[(size_t)entry(mm) * d + n0 + n] = (uint16_t)f32_to_bf16(acc[z]);
+                for (int z = 0; z < 4; ++z) {
+                    const int mm = m0 + 4 * kq + z;
+                    if (mm < M) g.o[(size_t)entry(mm) * d + n0 + n] = (uint16_t)f32_to_bf16(acc[z]);
+                }
             }
         }
     });
 }
 
+// One token: the W2 products of all k experts and the combine, 8 output features per
+// workgroup: y[n] = sum_j s_j * bf16(W2_{e_j}[n] . a_j) in FP32, j ascending from +0.0
+// (the combine kernel's order and rounding, so the result equals the three-launch
+// path's).  Experts 2p and 2p + 1 share one MFMA: its columns 0..7 are rows n0 .. n0 + 7
+// of W2 of expert 2p, columns 8..15 the same rows of expert 2p + 1, A row 0 is a_2p and
+// row 1 is a_2p+1, so D[0][c] and D[1][8 + c] are the two experts' outputs.  Wave w takes
+// the pairs w, w + 4, ...; an invalid expert id contributes 0.
+__global__ __launch_bounds__(kThreads, 3) void decode_w2_one(DecodeArgs g) {
+    __shared__ float ov[kMaxTopK][8];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int d = g.d, I = g.I, k = g.k;
+    const int npair = (k + 1) / 2;
+    auto valid = [&](int j) { return j < k && (unsigned)g.ids[j] < (unsigned)g.E; };
+    for (int nb = blockIdx.x; nb < d / 8; nb += gridDim.x) {
+        const int n0 = nb * 8;
+        for (int p = wave; p < npair; p += kWaves) {
+            const int jc = 2 * p + (n >> 3);               // expert slot of B column n
+            const int ec = valid(jc) ? g.ids[jc] : 0;
+            const uint16_t* wp = g.w2 + ((size_t)ec * d + n0 + (n & 7)) * I + 8 * kq;
+            const int jr = 2 * p + n;                       // expert slot of A row n (rows 0, 1)
+            const bool rv = n < 2 && valid(jr);
+            const uint16_t* ap = g.a + (size_t)(rv ? jr : 0) * I + 8 * kq;
+            const f32x4_t acc = mma_row_block(wp, ap, rv, I / 32);
+            // lanes with kq = 0 hold rows 0..3 of column n
+            if (kq == 0) {
+                if (n < 8 && 2 * p < k) ov[2 * p][n] = valid(2 * p) ? acc[0] : 0.f;
+                if (n >= 8 && 2 * p + 1 < k) ov[2 * p + 1][n - 8] = valid(2 * p + 1) ? acc[1] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (tid < 8) {
+            float y = 0.f;
+            for (int j = 0; j < k; ++j) y = __builtin_fmaf(g.scores[j], bf16_to_f32(f32_to_bf16(ov[j][tid])), y);
+            g.y[n0 + tid] = (uint16_t)f32_to_bf16(y);
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
-hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
-    const int R = g.T * g.k;
-    if (R <= 0) return hipSuccess;
-    const int slots = R < g.E ? R : g.E;                  // active experts at most
-    const int cap = 3 * num_cu;                           // resident workgroups
-    int grid = (slots * (g.I / 8) + kWaves - 1) / kWaves;
+hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s) {
+    if (g.T != 1 || g.k > kMaxTopK) return hipErrorInvalidValue;
+    const int cap = 3 * num_cu;
+    int grid = g.d / 8;
     grid = grid < cap ? grid : cap;
-    hipLaunchKernelGGL(decode_w13, dim3(grid), dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL(decode_w2_one, dim3(grid), dim3(kThreads), 0, s, g);
     return hipGetLastError();
 }
 
-hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s) {
+// Items of a launch with `slots` active experts at most and `nblk` items per expert:
+// one wave per item while that fills the resident wave slots, else one workgroup
+// (four waves splitting K) per item.
+template <class K1, class K2>
+hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, int nblk, int num_cu,
+                         hipStream_t s) {
     const int R = g.T * g.k;
     if (R <= 0) return hipSuccess;
-    const int slots = R < g.E ? R : g.E;
-    const int cap = 3 * num_cu;
-    int grid = (slots * (g.d / 16) + kWaves - 1) / kWaves;
-    grid = grid < cap ? grid : cap;
-    hipLaunchKernelGGL(decode_w2, dim3(grid), dim3(kThreads), 0, s, g);
+    const int slots = R < g.E ? R : g.E;                  // active experts at most
+    const int items = slots * nblk;
+    const int cap = 3 * num_cu;                           // resident workgroups
+    if (items < cap * kWaves) {
+        const int grid = items < cap ? items : cap;
+        hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kThreads), 0, s, g);
+    } else {
+        int grid = (items + kWaves - 1) / kWaves;
+        grid = grid < cap ? grid : cap;
+        hipLaunchKernelGGL(wave_kernel, dim3(grid), dim3(kThreads), 0, s, g);
+    }
     return hipGetLastError();
+}
+
+hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
+    return launch_decode(decode_w13<false>, decode_w13<true>, g, g.I / 8, num_cu, s);
+}
+
+hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s) {
+    return launch_decode(decode_w2<false>, decode_w2<true>, g, g.d / 16, num_cu, s);
 }
 
 }  // namespace moe

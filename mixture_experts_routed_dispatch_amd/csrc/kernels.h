@@ -101,6 +101,10 @@ struct DecodeArgs {
 
 hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s);
+// One token: W2 of all k experts and the score-weighted combine into y (a launch in place
+// of decode_w2 and combine).
+constexpr int kMaxTopK = 32;
+hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
 
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, hipStream_t s);

@@ -20,7 +20,6 @@ namespace {
 
 constexpr int64_t kMaxRoutedRows = 131072;   // nvfp4moe README, "Limits"
 constexpr int kMaxExperts = 256;             // nvfp4moe README, "Limits"
-constexpr int kMaxTopK = 32;
 constexpr size_t kMaxProfileRecords = 4096;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -235,6 +234,10 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         dg.status = p->at<int32_t>(p->off_status);
         hipError_t e = staged(p, MOE_STAGE_DECODE_W13, s, [&] { return launch_decode_w13(dg, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
+        if (c.T == 1) {
+            e = staged(p, MOE_STAGE_DECODE_W2, s, [&] { return launch_decode_w2_one(dg, p->num_cu, s); });
+            return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        }
         e = staged(p, MOE_STAGE_DECODE_W2, s, [&] { return launch_decode_w2(dg, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
         e = staged(p, MOE_STAGE_COMBINE, s, [&] {

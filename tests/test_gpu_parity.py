@@ -221,6 +221,7 @@ DECODE_SHAPES = [
     (8, 320, 192, 64, 32, "uniform"),      # k = 32
     (30, 256, 128, 128, 8, "zipf"),        # skewed, some experts with many rows, most empty
     (256, 128, 64, 200, 1, "uniform"),     # T*k at the decode limit
+    (32, 1024, 512, 64, 8, "uniform"),     # enough items for one wave per item (no K split)
 ]
 
 
