@@ -606,39 +606,72 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 store_rows_bf16(ln, stg, b, g.out + (size_t)c.mb * g.d, g.d, c.qt * TQ + wq * 128 + b * 32,
                                 c.rows, c.pt * TP + wp * 128, g.d);
         } else if constexpr (MODE == DGRAD_W2) {
-            // dA = probs[r] * acc; dg = dA u s(g)(1 + g(1 - s(g))), du = dA g s(g)
+            // dA = probs[r] * acc; dg = dA u s(g)(1 + g(1 - s(g))), du = dA g s(g).  Per half
+            // row block (32 rows x 64 columns of the wave) the FP32 accumulators go through
+            // LDS (16-byte chunk c of row q at slot c ^ (q & 15)) so that each lane then owns
+            // 8 consecutive columns of one row: h is read and dh written in 16-byte row
+            // pieces (8-byte pieces of 32 rows per instruction cost about 40k cycles per
+            // tile each way).  The h loads of a half block are issued before its staging.
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                if (rr >= c.rows) continue;
-                const size_t r = (size_t)c.mb + rr;
-                const float sc = g.probs[r];
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
+                for (int ah = 0; ah < 2; ++ah) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int i0 = c.pt * TP + wp * 128 + 64 * ah + 8 * (ln & 7);   // this lane's 8 columns
+                    const int ic = i0 < g.I ? i0 : g.I - 8;
+                    uint4 hg[4], hu[4];
+                    float sc[4];
 #pragma unroll
-                    for (int grp = 0; grp < 4; ++grp) {
-                        const int i = c.pt * TP + wp * 128 + a * 32 + 8 * grp + p_sub;
-                        if (i >= g.I) continue;
-                        const uint2 hg = *reinterpret_cast<const uint2*>(g.h + r * 2 * g.I + i);
-                        const uint2 hu = *reinterpret_cast<const uint2*>(g.h + r * 2 * g.I + g.I + i);
-                        const float gv[4] = {bf16lo(hg.x), bf16hi(hg.x), bf16lo(hg.y), bf16hi(hg.y)};
-                        const float uv[4] = {bf16lo(hu.x), bf16hi(hu.x), bf16lo(hu.y), bf16hi(hu.y)};
-                        float dg[4], du[4];
+                    for (int it = 0; it < 4; ++it) {
+                        const int rr = c.qt * TQ + wq * 128 + b * 32 + 8 * it + (ln >> 3);
+                        const size_t r = (size_t)c.mb + (rr < c.rows ? rr : c.rows - 1);
+                        hg[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + ic);
+                        hu[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + g.I + ic);
+                        sc[it] = g.probs[r];
+                    }
+#pragma unroll
+                    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                        for (int grp = 0; grp < 4; ++grp) {
+                            const int c16 = (32 * a2 + 8 * grp + p_sub) >> 2;
+                            const int a = 2 * ah + a2;
+                            f32x4_t v = {acc[a][b][4 * grp], acc[a][b][4 * grp + 1], acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]};
+                            *reinterpret_cast<f32x4_t*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4)) = v;
+                        }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own LDS writes are done
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int row = 8 * it + (ln >> 3), c8 = ln & 7;
+                        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8) ^ (row & 15)) << 4));
+                        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4));
+                        const float av[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        const uint32_t gw[4] = {hg[it].x, hg[it].y, hg[it].z, hg[it].w};
+                        const uint32_t uw[4] = {hu[it].x, hu[it].y, hu[it].z, hu[it].w};
+                        uint32_t og[4], ou[4];
 #pragma unroll
                         for (int z = 0; z < 4; ++z) {
-                            const float dA = sc * acc[a][b][4 * grp + z];
-                            const float sg = sigmoid_f(gv[z]);
-                            dg[z] = dA * uv[z] * sg * (1.0f + gv[z] * (1.0f - sg));
-                            du[z] = dA * gv[z] * sg;
+                            float dg2[2], du2[2];
+#pragma unroll
+                            for (int h2 = 0; h2 < 2; ++h2) {
+                                const float gv = h2 ? bf16hi(gw[z]) : bf16lo(gw[z]);
+                                const float uv = h2 ? bf16hi(uw[z]) : bf16lo(uw[z]);
+                                const float dA = sc[it] * av[2 * z + h2];
+                                const float sg = sigmoid_f(gv);
+                                dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
+                                du2[h2] = dA * gv * sg;
+                            }
+                            og[z] = pack_bf16(dg2[0], dg2[1]);
+                            ou[z] = pack_bf16(du2[0], du2[1]);
                         }
-                        uint2 og, ou;
-                        og.x = pack_bf16(dg[0], dg[1]); og.y = pack_bf16(dg[2], dg[3]);
-                        ou.x = pack_bf16(du[0], du[1]); ou.y = pack_bf16(du[2], du[3]);
-                        *reinterpret_cast<uint2*>(g.out + r * 2 * g.I + i) = og;
-                        *reinterpret_cast<uint2*>(g.out + r * 2 * g.I + g.I + i) = ou;
+                        const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
+                        if (rr < c.rows && i0 < g.I) {
+                            const size_t r = (size_t)c.mb + rr;
+                            *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + i0) = make_uint4(og[0], og[1], og[2], og[3]);
+                            *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + g.I + i0) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+                        }
                     }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the slots are rewritten
                 }
-            }
         } else {
             // weight gradients: out[e][q][p], q < Qsz rows, p < Psz columns
             const int Psz = (MODE == WGRAD_W2) ? g.I : g.d;
