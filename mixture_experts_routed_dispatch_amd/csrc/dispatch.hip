@@ -35,22 +35,44 @@ __global__ __launch_bounds__(kThreads) void dispatch_count(const int32_t* __rest
                                                            int k, int E, int32_t* __restrict__ hist,
                                                            int32_t* __restrict__ status) {
     __shared__ int h[256];
+    __shared__ int sid[kDispatchChunk];   // the chunk's ids, for the repeated-id check
     for (int e = threadIdx.x; e < 256; e += kThreads) h[e] = 0;
-    __syncthreads();
     const int64_t R = (int64_t)T * k;
     const int64_t q0 = (int64_t)blockIdx.x * kDispatchChunk;
     const int64_t q1 = q0 + kDispatchChunk < R ? q0 + kDispatchChunk : R;
+    const int n = (int)(q1 - q0);
+    // all loads of the chunk in flight at once (a loop whose trip count the compiler
+    // cannot see would wait for each one)
+    int ev[kDispatchChunk / kThreads];
+#pragma unroll
+    for (int s = 0; s < kDispatchChunk / kThreads; ++s) {
+        const int i = s * kThreads + (int)threadIdx.x;
+        ev[s] = i < n ? ids[q0 + i] : 0;
+    }
+#pragma unroll
+    for (int s = 0; s < kDispatchChunk / kThreads; ++s) {
+        const int i = s * kThreads + (int)threadIdx.x;
+        if (i < n) sid[i] = ev[s];
+    }
+    __syncthreads();
     int bad = 0;
-    for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
-        const int e = ids[q];
+#pragma unroll
+    for (int s = 0; s < kDispatchChunk / kThreads; ++s) {
+        const int i = s * kThreads + (int)threadIdx.x;
+        if (i >= n) continue;
+        const int64_t q = q0 + i;
+        const int e = ev[s];
         if ((unsigned)e >= (unsigned)E) {
             bad |= 1;
             continue;
         }
         const int64_t t = q / k;
         const int j = (int)(q - t * k);
-        for (int jj = 0; jj < j; ++jj)
-            if (ids[t * k + jj] == e) bad |= 2;
+        for (int jj = 0; jj < j; ++jj) {
+            const int64_t qq = t * k + jj;          // an earlier entry of the same token
+            const int e2 = qq >= q0 ? sid[qq - q0] : ids[qq];
+            if (e2 == e) bad |= 2;
+        }
         atomicAdd(&h[e], 1);
     }
     if (bad) atomicOr(status, bad);
@@ -72,10 +94,16 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
     // 1. per expert: total count and count in earlier chunks (thread e owns expert e)
     int tot = 0, before = 0;
     if (tid < E) {
-        for (int b = 0; b < nchunks; ++b) {
-            const int v = hist[(int64_t)b * E + tid];
-            tot += v;
-            before += (b < (int)blockIdx.x) ? v : 0;
+        // eight chunk histograms in flight at a time
+        for (int b0 = 0; b0 < nchunks; b0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = b0 + u < nchunks ? hist[(int64_t)(b0 + u) * E + tid] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                tot += v[u];
+                before += (b0 + u < (int)blockIdx.x) ? v[u] : 0;
+            }
         }
     }
     // 2. exclusive scan of the totals over experts (wave scan + wave offsets)
@@ -101,15 +129,14 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
     int ev[kSteps];
     float sv[kSteps];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+    for (int s = 0; s < kSteps; ++s) {                   // all loads first, then the counts
         const int64_t q = qw + s * MOE_WAVE + lane;
-        ev[s] = -1;
-        sv[s] = 0.f;
-        if (q < R) {
-            const int e = ids[q];
-            sv[s] = scores[q];
-            if ((unsigned)e < (unsigned)E) ev[s] = e;
-        }
+        ev[s] = q < R ? ids[q] : -1;
+        sv[s] = q < R ? scores[q] : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        if ((unsigned)ev[s] >= (unsigned)E) ev[s] = -1;
         if (ev[s] >= 0) atomicAdd(&start[wave][ev[s]], 1);
     }
     __syncthreads();
