@@ -14,13 +14,14 @@
 //     streams 16 rows of W2_e over K = I and writes o[t*k + j][n] in BF16.
 //   combine: y[t] = sum_j s[t][j] * o[t*k + j], FP32, j ascending from +0.0 (the
 //     prefill combine kernel, reading the rows in entry order).
-// With many items (small batches) a wave owns its item from the first load to the last
-// store: no K split, no reduction and no barrier between waves, so every wave of a CU
-// streams on its own.  Items go to waves round-robin.  With fewer items than wave
-// slots on the chip (one token: k experts x 96 blocks) that would leave CUs idle and
-// each wave streaming its rows in several dependent load batches, so there the four
-// waves of a workgroup share one item, each streaming a quarter of K, and add their
-// partial sums through LDS in wave order (fixed: the result does not depend on timing).
+// Either the four waves of a workgroup share an item, each streaming a quarter of K,
+// and add their partial sums through LDS in wave order (fixed: the result does not
+// depend on timing); or a wave owns its item from the first load to the last store,
+// with no reduction and no barrier between waves.  The first is used when the items
+// are fewer than the wave slots on the chip (one token: k experts x 96 blocks) or when
+// a quarter of K still fills a wave's load batch (W13, K = d = 2048: 10,752 items at 32
+// tokens are 14 per workgroup, where one wave per item leaves the last of 4 rounds half
+// empty); the second for short K (W2 at 32 tokens, K = I = 768).
 //
 // With one token the experts are the k ids themselves (distinct by the layer's
 // precondition), and the W2 products and the combine are one launch (decode_w2_one).  With more tokens every workgroup first sorts the routed entries by
@@ -355,18 +356,20 @@ hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s) 
     return hipGetLastError();
 }
 
-// Items of a launch with `slots` active experts at most and `nblk` items per expert:
-// one wave per item while that fills the resident wave slots, else one workgroup
-// (four waves splitting K) per item.
+// Items of a launch with `slots` active experts at most, `nblk` items per expert and
+// `ksteps` K steps of 32 per item: one workgroup (four waves splitting K) per item when
+// the items do not fill the resident wave slots, or when each wave still streams a full
+// batch of loads (the items then divide evenly over workgroups instead of leaving the
+// last round of waves half empty); else one wave per item.
 template <class K1, class K2>
-hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, int nblk, int num_cu,
-                         hipStream_t s) {
+hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, int nblk, int ksteps,
+                         int num_cu, hipStream_t s) {
     const int R = g.T * g.k;
     if (R <= 0) return hipSuccess;
     const int slots = R < g.E ? R : g.E;                  // active experts at most
     const int items = slots * nblk;
     const int cap = 3 * num_cu;                           // resident workgroups
-    if (items < cap * kWaves) {
+    if (items < cap * kWaves || ksteps >= kWaves * kBatch) {
         const int grid = items < cap ? items : cap;
         hipLaunchKernelGGL(split_kernel, dim3(grid), dim3(kThreads), 0, s, g);
     } else {
@@ -378,11 +381,11 @@ hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, i
 }
 
 hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
-    return launch_decode(decode_w13<false>, decode_w13<true>, g, g.I / 8, num_cu, s);
+    return launch_decode(decode_w13<false>, decode_w13<true>, g, g.I / 8, g.d / 32, num_cu, s);
 }
 
 hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s) {
-    return launch_decode(decode_w2<false>, decode_w2<true>, g, g.d / 16, num_cu, s);
+    return launch_decode(decode_w2<false>, decode_w2<true>, g, g.d / 16, g.I / 32, num_cu, s);
 }
 
 }  // namespace moe
