@@ -174,9 +174,9 @@ moe_status_t moe_get_status(moe_plan_t plan, int32_t* device_flags, int32_t clea
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t status);
 
-/* Kernel stages of moe_forward / moe_backward (in launch order, except WGRAD_ROWS, which
- * runs between DGRAD_W2 and WGRAD_W2; the one-token decode runs W2 and the combine as
- * one kernel, recorded as DECODE_W2). */
+/* Kernel stages of moe_forward / moe_backward.  moe_backward launches SCORE_GRAD,
+ * DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order; the
+ * one-token decode runs W2 and the combine as one kernel, recorded as DECODE_W2. */
 #define MOE_STAGE_DISPATCH 0
 #define MOE_STAGE_QUANT_X 1
 #define MOE_STAGE_W13 2

@@ -354,8 +354,18 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
                                  p->at<int32_t>(p->off_status), s)) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
+        // input gradients first, each consumer right after its producer, so that dh and
+        // dxp are still in the memory-side cache when they are read back
         g.out = p->at<uint16_t>(p->off_dh);
         e = staged(p, MOE_STAGE_DGRAD_W2, s, [&] { return launch_gemm(DGRAD_W2, g, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        g.out = p->at<uint16_t>(p->off_dxp);
+        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm(DGRAD_W13, g, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_DX_COMBINE, s, [&] {
+            return launch_combine(p->at<uint16_t>(p->off_dxp), slots, nullptr, c.T, c.k, c.d,
+                                  static_cast<uint16_t*>(dx), s);
+        });
         if (e != hipSuccess) return MOE_ERR_HIP;
         e = staged(p, MOE_STAGE_WGRAD_ROWS, s, [&] {
             return launch_wgrad_rows(g.x, g.dy, g.gather, g.probs, p->R, c.d, p->at<uint16_t>(p->off_xg),
@@ -366,21 +376,9 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     g.out = static_cast<uint16_t*>(dw2);
     e = staged(p, MOE_STAGE_WGRAD_W2, s, [&] { return launch_gemm(WGRAD_W2, g, p->num_cu, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
-    if (c.T > 0) {
-        g.out = p->at<uint16_t>(p->off_dxp);
-        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm(DGRAD_W13, g, p->num_cu, s); });
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
     g.out = static_cast<uint16_t*>(dw13);
     e = staged(p, MOE_STAGE_WGRAD_W13, s, [&] { return launch_gemm(WGRAD_W13, g, p->num_cu, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
-    if (c.T > 0) {
-        e = staged(p, MOE_STAGE_DX_COMBINE, s, [&] {
-            return launch_combine(p->at<uint16_t>(p->off_dxp), slots, nullptr, c.T, c.k, c.d,
-                                  static_cast<uint16_t*>(dx), s);
-        });
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
     return MOE_OK;
 }
 
