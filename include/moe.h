@@ -135,8 +135,12 @@ moe_status_t moe_quantize_mxfp8(const void* v_bf16, int64_t rows, int32_t K,
 /* Prepare BF16 weights for the MXFP8 pipeline (blog post, "What it is
  * selling": MXFP8 accepts prepared weights): quantize w13 [E,2I,d] and
  * w2 [E,d,I] along their K (last) dimension with moe_quantize_mxfp8's rule.
- * Outputs are caller-owned: w13_q [E,2I,d], w13_s [E,2I,d/32], w2_q [E,d,I],
- * w2_s [E,d,I/32].  Meant to run outside any timed region. */
+ * Outputs are caller-owned: codes w13_q [E,2I,d] and w2_q [E,d,I] as
+ * moe_quantize_mxfp8 writes them; scales block-major: viewing w13 as
+ * N = E*2I rows of length K = d (w2: N = E*d rows of length K = I), the four
+ * scale bytes of blocks 4g .. 4g+3 of row n are bytes [4 (g N + n), +4), i.e.
+ * uint8 [K/128, N, 4] (E*2I*d/32 and E*d*I/32 bytes).  Needs d and I multiples
+ * of 128 (else MOE_ERR_UNSUPPORTED).  Meant to run outside any timed region. */
 moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const void* w2_bf16,
                                  uint8_t* w13_q, uint8_t* w13_s, uint8_t* w2_q, uint8_t* w2_s,
                                  void* stream);

@@ -23,7 +23,10 @@
 // Scales travel as direct copies too: the 4 bytes (blocks 2 kt .. 2 kt + 3) of a
 // row cover a pair of stages; per stage pair, each wave copies the words of 64 P
 // rows and 64 Q rows into one of three 2 KiB scale slots, together with the data
-// copies of the pair's first stage.  A lane then reads the words of its four row
+// copies of the pair's first stage.  The weight scales and the scales of a are
+// stored block-major (the words of one stage pair for consecutive rows are
+// contiguous), so those copies read 256 contiguous bytes; the scales of x are gathered
+// by token, a word per row.  A lane then reads the words of its four row
 // blocks once per pair and shifts them by 8 (lane >> 5) bits, so that byte 0 holds
 // its scale for the first stage of the pair and byte 2 for the second (the MFMA's
 // op_sel picks the byte).
@@ -93,6 +96,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     const int E = g.E;
     const int K = MODE == MX_W13 ? g.d : g.I;          // K of the product (bytes per row)
     const int KB = K / 32;                             // scale bytes per row
+    const size_t R = (size_t)g.T * g.k;                // routed rows
     const int nPt = MODE == MX_W13 ? g.I / 128 : g.d / TP;
 
     // ---- tile list: tiles of expert e are cum[e] .. cum[e+1]-1
@@ -208,10 +212,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
             dvoff[4 + j] = (uint32_t)(q_row(c, slot, r) * K + 16 * cl);
         }
         const int rs = 64 * wave + fl;
-        svoffP = (uint32_t)(p_row(c, rs) * KB);
-        svoffQ = (uint32_t)(q_row(c, slot, rs) * KB);
+        svoffP = (uint32_t)(p_row(c, rs) * 4);
+        svoffQ = (uint32_t)(q_row(c, slot, rs) * (MODE == MX_W13 ? KB : 4));
         pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
-        psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * KB);
+        psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * 4);
     };
     auto dma16 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -231,9 +235,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     // scale slot `slot`
     auto dma_scales = [&](int kt, int slot) {
         const uint32_t dst = lsc0 + slot * SCB + 256 * wave;
-        const int kb = 2 * (kt & ~1);
-        dma4(dst, svoffP, psbase_e + kb);
-        dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kb);
+        const size_t kp = (size_t)(kt >> 1);                  // stage pair = group of 4 blocks
+        dma4(dst, svoffP, psbase_e + kp * E * prows_e * 4);
+        if constexpr (MODE == MX_W13) dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + 4 * kp);
+        else dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kp * R * 4);
     };
 
     // ------------------------------------------------------------ fragments and scales
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                                     w |= e4m3_code(__builtin_ldexpf(av[8 * h + 4 * grp + z], sh)) << (8 * z);
                                 *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 16 * h + 8 * grp + p_sub) = w;
                             }
-                        if (ln < 32) g.as[r * (g.I / 32) + i0 / 32] = (uint8_t)sb;
+                        if (ln < 32) g.as[((size_t)(i0 >> 7) * R + r) * 4 + ((i0 >> 5) & 3)] = (uint8_t)sb;
                     }
                 }
             }

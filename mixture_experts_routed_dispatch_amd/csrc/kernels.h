@@ -59,11 +59,11 @@ struct MxGemmArgs {
     const uint8_t* xq;    // [T, d]      codes of x
     const uint8_t* xs;    // [T, d/32]   scales of x
     const uint8_t* w13q;  // [E, 2I, d]
-    const uint8_t* w13s;  // [E, 2I, d/32]
+    const uint8_t* w13s;  // block-major words: (g, row) at (g * E 2I + row) * 4, row = e 2I + n
     const uint8_t* w2q;   // [E, d, I]
-    const uint8_t* w2s;   // [E, d, I/32]
+    const uint8_t* w2s;   // block-major words: (g, row) at (g * E d + row) * 4, row = e d + n
     uint8_t* aq;          // [R, I]      SwiGLU output, re-quantized (MX_W13 output, MX_W2 input)
-    uint8_t* as;          // [R, I/32]
+    uint8_t* as;          // block-major words: (g, r) at (g * R + r) * 4
     uint16_t* o;          // [R, d]      BF16 expert outputs (MX_W2 output)
 };
 
@@ -106,7 +106,9 @@ hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s);
 constexpr int kMaxTopK = 32;
 hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
 
+// block_major: scale word (g, row) (bytes of blocks 4 g .. 4 g + 3) at (g * rows + row) * 4
+// (K a multiple of 128); else scales [rows, K/32].
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s);
+                                 uint8_t* scales, bool block_major, hipStream_t s);
 
 }  // namespace moe

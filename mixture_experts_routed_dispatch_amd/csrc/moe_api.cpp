@@ -193,7 +193,7 @@ moe_status_t moe_quantize_mxfp8(const void* v, int64_t rows, int32_t K, uint8_t*
                                 uint8_t* scales, void* stream) {
     if (rows < 0 || K <= 0 || K % 32 != 0) return MOE_ERR_INVALID_ARG;
     if (rows > 0 && (!v || !codes || !scales)) return MOE_ERR_INVALID_ARG;
-    hipError_t e = launch_quantize_mxfp8(static_cast<const uint16_t*>(v), rows, K, codes, scales,
+    hipError_t e = launch_quantize_mxfp8(static_cast<const uint16_t*>(v), rows, K, codes, scales, false,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -202,9 +202,16 @@ moe_status_t moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, 
                                  uint8_t* w13_s, uint8_t* w2_q, uint8_t* w2_s, void* stream) {
     if (!p || !w13 || !w2 || !w13_q || !w13_s || !w2_q || !w2_s) return MOE_ERR_INVALID_ARG;
     const moe_config_t& c = p->cfg;
-    moe_status_t st = moe_quantize_mxfp8(w13, (int64_t)c.E * 2 * c.I, c.d, w13_q, w13_s, stream);
-    if (st != MOE_OK) return st;
-    return moe_quantize_mxfp8(w2, (int64_t)c.E * c.d, c.I, w2_q, w2_s, stream);
+    if (c.d % 128 != 0 || c.I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // block-major scales (the layout the MXFP8 GEMMs copy from)
+    if (launch_quantize_mxfp8(static_cast<const uint16_t*>(w13), (int64_t)c.E * 2 * c.I, c.d, w13_q, w13_s,
+                              true, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_quantize_mxfp8(static_cast<const uint16_t*>(w2), (int64_t)c.E * c.d, c.I, w2_q, w2_s, true,
+                              s) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
 }
 
 moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const float* scores,
@@ -262,7 +269,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         uint8_t* xq = p->at<uint8_t>(p->off_xq);
         uint8_t* xs = p->at<uint8_t>(p->off_xs);
         e = staged(p, MOE_STAGE_QUANT_X, s, [&] {
-            return launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, s);
+            return launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, false, s);
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
         MxGemmArgs mg{};

@@ -8,6 +8,11 @@
 // v / 2^(shared) rounded to nearest even on the E4M3 grid and clamped to
 // +-448.  Inputs are BF16, so v / 2^(shared) is exact in FP32 and the
 // codes are a deterministic function of the input bits.
+//
+// Scales are stored row-major ([rows, K/32]) or block-major: the four bytes of blocks
+// 4 g .. 4 g + 3 of a row form one word, and word (g, row) sits at (g * rows + row) * 4,
+// so that the words of consecutive rows for one group of 128 K elements are contiguous
+// (the MXFP8 GEMMs copy them 64 rows at a time).
 #include "common.h"
 #include "kernels.h"
 
@@ -17,7 +22,8 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __restrict__ v,
-                                                            int64_t nblocks,
+                                                            int64_t nblocks, int kb_row, int64_t rows,
+                                                            bool block_major,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
     for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
@@ -47,20 +53,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __re
         uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
         dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
         dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-        scales[b] = (uint8_t)sb;
+        int64_t si = b;
+        if (block_major) {
+            const int64_t row = b / kb_row;
+            const int kb = (int)(b - row * kb_row);
+            si = ((int64_t)(kb >> 2) * rows + row) * 4 + (kb & 3);
+        }
+        scales[si] = (uint8_t)sb;
     }
 }
 
 }  // namespace
 
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, hipStream_t s) {
+                                 uint8_t* scales, bool block_major, hipStream_t s) {
+    if (block_major && K % 128 != 0) return hipErrorInvalidValue;
     const int64_t nblocks = rows * (K / 32);
     if (nblocks == 0) return hipSuccess;
     int64_t grid = (nblocks + kThreads - 1) / kThreads;
     if (grid > 65536) grid = 65536;
-    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, v, nblocks,
-                       codes, scales);
+    hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, v, nblocks, K / 32,
+                       rows, block_major, codes, scales);
     return hipGetLastError();
 }
 

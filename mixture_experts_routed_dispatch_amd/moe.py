@@ -259,9 +259,10 @@ class Layer:
         dev = w13.device
         E, I, d = self.E, self.I, self.d
         w13_q = torch.empty((E, 2 * I, d), dtype=torch.uint8, device=dev)
-        w13_s = torch.empty((E, 2 * I, d // 32), dtype=torch.uint8, device=dev)
+        # scales block-major: [K/128, rows, 4] (see moe_prepare_weights in include/moe.h)
+        w13_s = torch.empty((d // 128, E * 2 * I, 4), dtype=torch.uint8, device=dev)
         w2_q = torch.empty((E, d, I), dtype=torch.uint8, device=dev)
-        w2_s = torch.empty((E, d, I // 32), dtype=torch.uint8, device=dev)
+        w2_s = torch.empty((I // 128, E * d, 4), dtype=torch.uint8, device=dev)
         moe_prepare_weights(self.plan, _ptr(w13), _ptr(w2), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q),
                             _ptr(w2_s), _stream(stream))
         return w13_q, w13_s, w2_q, w2_s

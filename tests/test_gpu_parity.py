@@ -456,8 +456,16 @@ def test_prepare_weights_bit_exact(torch_cuda):
     torch.cuda.synchronize()
     r13 = oracle.mx_quantize(inp.w13)
     r2 = oracle.mx_quantize(inp.w2)
-    assert np.array_equal(w13_q.cpu().numpy(), r13[0]) and np.array_equal(w13_s.cpu().numpy(), r13[1])
-    assert np.array_equal(w2_q.cpu().numpy(), r2[0]) and np.array_equal(w2_s.cpu().numpy(), r2[1])
+
+    def row_major(s_bm, shape):
+        # block-major [K/128, N, 4] -> [N, K/32], N = all rows of the weight
+        g, n, _ = s_bm.shape
+        return s_bm.transpose(1, 0, 2).reshape(n, 4 * g).reshape(shape)
+
+    assert np.array_equal(w13_q.cpu().numpy(), r13[0])
+    assert np.array_equal(row_major(w13_s.cpu().numpy(), r13[1].shape), r13[1])
+    assert np.array_equal(w2_q.cpu().numpy(), r2[0])
+    assert np.array_equal(row_major(w2_s.cpu().numpy(), r2[1].shape), r2[1])
     layer.close()
 
 
