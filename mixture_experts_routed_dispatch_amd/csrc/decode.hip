@@ -130,14 +130,15 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 // acc(16 rows x 16 cols) = A * B over K steps 0 .. S - 1 (32 each): B column (l & 15)
 // from wrow (already offset by 8 (l >> 4) elements), A row (l & 15) from arow at the
 // same offset, or zeros when the row is absent.
+template <int B = kBatch>
 __device__ __forceinline__ f32x4_t mma_row_block(const uint16_t* wrow, const uint16_t* arow,
                                                  bool arow_valid, int S) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const bf16x8_t zero = {};
-    for (int base = 0; base < S; base += kBatch) {
-        bf16x8_t wb[kBatch], xa[kBatch];
+    for (int base = 0; base < S; base += B) {
+        bf16x8_t wb[B], xa[B];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < B; ++j) {
             const int s = base + j;
             if (s < S) {
                 wb[j] = ld_bf16x8(wrow + 32 * s);
@@ -145,7 +146,7 @@ __device__ __forceinline__ f32x4_t mma_row_block(const uint16_t* wrow, const uin
             }
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j)
+        for (int j = 0; j < B; ++j)
             if (base + j < S) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], wb[j], acc, 0, 0, 0);
     }
     return acc;
@@ -311,8 +312,10 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
 // path's).  Experts 2p and 2p + 1 share one MFMA: its columns 0..7 are rows n0 .. n0 + 7
 // of W2 of expert 2p, columns 8..15 the same rows of expert 2p + 1, A row 0 is a_2p and
 // row 1 is a_2p+1, so D[0][c] and D[1][8 + c] are the two experts' outputs.  Wave w takes
-// the pairs w, w + 4, ...; an invalid expert id contributes 0.
-__global__ __launch_bounds__(kThreads, 3) void decode_w2_one(DecodeArgs g) {
+// the pairs w, w + 4, ...; an invalid expert id contributes 0.  One workgroup per CU (d / 8
+// of them), each wave loading 24 K steps at once: at K = I = 768 its whole pair in one
+// round trip.
+__global__ __launch_bounds__(kThreads, 1) void decode_w2_one(DecodeArgs g) {
     __shared__ float ov[kMaxTopK][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kq = lane >> 4;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2_one(DecodeArgs g) {
             const int jr = 2 * p + n;                       // expert slot of A row n (rows 0, 1)
             const bool rv = n < 2 && valid(jr);
             const uint16_t* ap = g.a + (size_t)(rv ? jr : 0) * I + 8 * kq;
-            const f32x4_t acc = mma_row_block(wp, ap, rv, I / 32);
+            const f32x4_t acc = mma_row_block<24>(wp, ap, rv, I / 32);
             // lanes with kq = 0 hold rows 0..3 of column n
             if (kq == 0) {
                 if (n < 8 && 2 * p < k) ov[2 * p][n] = valid(2 * p) ? acc[0] : 0.f;
