@@ -16,8 +16,11 @@
 //   FWD_W2     W2_e rows                    a[r]                      I      o [R, d]
 //   DGRAD_W2   W2_e^T  (MN-major)           dy[gather[r]]             d      dh = SwiGLU'(h) * probs * W2^T dy
 //   DGRAD_W13  W13_e^T (MN-major)           dh[r]                     2I     dxp [R, d]
-//   WGRAD_W2   a^T     (MN-major)           (probs * dy[gather])^T    R_e    dW2_e [d, I]
-//   WGRAD_W13  x[gather]^T (MN-major)       dh^T                      R_e    dW13_e [2I, d]
+//   WGRAD_W2   a^T     (MN-major)           dys^T (MN-major)          R_e    dW2_e [d, I]
+//   WGRAD_W13  xg^T    (MN-major)           dh^T  (MN-major)          R_e    dW13_e [2I, d]
+//
+// (xg = x[gather], dys = bf16(probs * dy[gather]): row-major copies made once before
+// the weight gradients, so that every operand is a plain slab the copies can move.)
 //
 // Workgroup tile 256 (p) x 256 (q), four waves of 128 x 128 (4 x 4 MFMA blocks
 // of 32 x 32, 256 FP32 accumulators per lane), one workgroup per CU, persistent
@@ -34,11 +37,13 @@
 //     with explicit vmcnt counts one stage later;
 // and ends with one barrier.  K-major operands are staged as rows of K; MN-major
 // operands (the transposed products of backward) as rows of M or N, read into MFMA
-// fragments with the transposing LDS read ds_read_b64_tr_b16.  The tile walk keeps the expert offsets and the next
-// tiles' gather indices in LDS (the latter fetched by an LDS copy a tile ahead), so
-// the main loop issues no global load the compiler would have to wait for: such a
-// wait would also wait for every copy in flight.  Consecutive tile ids go to
-// workgroups of one XCD so that the operand slices they share stay in its L2.
+// fragments with the transposing LDS read ds_read_b64_tr_b16.  The tile walk keeps
+// the expert offsets and the next tiles' gather indices in LDS (the latter fetched by
+// an LDS copy a tile ahead), so the main loop issues no global load the compiler would
+// have to wait for: such a wait would also wait for every copy in flight.  Consecutive
+// work items go to workgroups of one XCD so that the operand slices they share stay
+// in its L2.  The weight gradients order and cut their tiles for balance (see the
+// work list below) and add split tiles up in wgrad_fixup.
 #include "common.h"
 #include "kernels.h"
 
