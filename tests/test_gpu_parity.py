@@ -384,6 +384,30 @@ def test_backward_split_weight_gradient_tiles(torch_cuda, T, d, I, E, k, hot):
     layer.close()
 
 
+def test_no_tokens(torch_cuda):
+    """T = 0: the forward writes nothing and succeeds; the backward gives all-zero weight
+    gradients (every expert is empty)."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("no tokens: T=0 d=256 I=128 E=8 k=2")
+    d, I, E, k = 256, 128, 8, 2
+    layer = moe.Layer(0, d, I, E, k, training=True)
+    x = torch.empty((0, d), dtype=torch.bfloat16, device=dev())
+    ids = torch.empty((0, k), dtype=torch.int32, device=dev())
+    scores = torch.empty((0, k), dtype=torch.float32, device=dev())
+    w13 = torch.randn((E, 2 * I, d), device=dev()).to(torch.bfloat16)
+    w2 = torch.randn((E, d, I), device=dev()).to(torch.bfloat16)
+    y = layer.forward(x, ids, scores, w13, w2)
+    dw13 = torch.full((E, 2 * I, d), 7.0, dtype=torch.bfloat16, device=dev())
+    dw2 = torch.full((E, d, I), 7.0, dtype=torch.bfloat16, device=dev())
+    dx, dw13, dw2, ds = layer.backward(x, x, w13, w2, dw13=dw13, dw2=dw2)
+    torch.cuda.synchronize()
+    assert y.shape == (0, d) and dx.shape == (0, d) and ds.shape == (0, k)
+    assert not torch.any(dw13.view(torch.int16) != 0)
+    assert not torch.any(dw2.view(torch.int16) != 0)
+    layer.close()
+
+
 def test_backward_full_size_sampled(torch_cuda):
     torch = torch_cuda
     say("backward full size: train workload")
