@@ -62,6 +62,15 @@ __device__ __forceinline__ uint32_t e8m0_scale(float amax) {
     return (uint32_t)b;
 }
 
+// Streaming (non-temporal) store of 16 bytes, for whole-line outputs no nearby kernel
+// reads back from cache: written through L2 as ordinary stores, they evict operand
+// lines the other workgroups of the XCD are still reading.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt(void* p, uint4 v) {
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     uint32_t l = __lane_id();
     return l == 0 ? 0ull : (~0ull >> (64 - l));

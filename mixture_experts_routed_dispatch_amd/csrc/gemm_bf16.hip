@@ -524,6 +524,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // consumed) so that each store instruction writes whole 256-byte row segments:
     // per block b, 32 rows x 128 columns are written as 8-byte pieces (16-byte chunk
     // slot c ^ (row & 15)), read back as 16-byte chunks and stored row-contiguously.
+    // These outputs (o, dxp, the weight gradients) are streamed out with non-temporal
+    // stores of whole lines: written as ordinary stores they evicted the operand slices
+    // the XCD's workgroups share in L2 (W2 main loop 31k cycles per tile without its
+    // stores, 38-45k with ordinary ones).  a and dh, read back by the next product while
+    // still cached, are stored normally, and so are stores of 8-byte pieces (the saved
+    // h): non-temporal partial lines are written one by one, which made W13 35 % slower.
     auto store_rows_bf16 = [&](int ln, char* stg, int b, uint16_t* out, size_t ld, int q_first, int q_limit,
                                int p_first, int p_limit) {
         const int q_in = ln & 31, p_sub = 4 * (ln >> 5);
@@ -545,7 +551,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
             const int q = q_first + row;
             const int p = p_first + 8 * c16;
-            if (q < q_limit && p < p_limit) *reinterpret_cast<uint4*>(out + (size_t)q * ld + p) = v;
+            if (q < q_limit && p < p_limit) store_nt(out + (size_t)q * ld + p, v);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);      // reads done before the slot is rewritten
     };
