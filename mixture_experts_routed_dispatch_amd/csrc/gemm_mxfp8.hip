@@ -361,7 +361,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
             }
         } else {
             // o [R, d] in BF16 through LDS (this wave's 8 KiB of the stage buffer just
-            // consumed), stored as whole 256-byte row segments
+            // consumed), stored as whole 256-byte row segments with non-temporal stores
+            // (ordinary ones evict the operands the XCD's workgroups share in L2)
             char* stg = lds + buf * BUFB + wave * 8192;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                     const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
                     const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
                     const int p = c.pt * TP + wp * 128 + 8 * c16;
-                    if (rr < c.rows && p < g.d) *reinterpret_cast<uint4*>(g.o + ((size_t)c.mb + rr) * g.d + p) = v;
+                    if (rr < c.rows && p < g.d) store_nt(g.o + ((size_t)c.mb + rr) * g.d + p, v);
                 }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
             }
