@@ -50,22 +50,28 @@ def parse():
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="before warm-up, run one plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="time the vendor library's BF16 GEMMs (hipBLASLt through torch) on the "
+                         "workload's expert-product shapes with uniform rows per expert, and a "
+                         "square 8192 GEMM, then exit (context for the roofline)")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc csv files and exit")
     return ap.parse_args()
 
 
 KERNEL_OF_STAGE = {
-    # stage name (library event pairs) -> substring of the kernel symbol rocprofv3 reports
-    "dispatch": "dispatch_place", "w13": "grouped_gemm<0,", "w2": "grouped_gemm<1,",
-    "combine": "combine_kernel", "score_grad": "score_grad_kernel",
-    "dgrad_w2": "grouped_gemm<2,", "dgrad_w13": "grouped_gemm<3,",
-    "wgrad_w2": "grouped_gemm<4,", "wgrad_w13": "grouped_gemm<5,",
-    "quant_x": "quantize_kernel", "decode_w13": "decode_w13", "decode_w2": "decode_w2",
-    "wgrad_rows": "wgrad_rows_kernel",
+    # stage name (library event pairs) -> substrings of the symbols (as rocprofv3 reports
+    # them) of every kernel the stage launches
+    "dispatch": ("dispatch_count", "dispatch_place"),
+    "w13": ("grouped_gemm<0,", "fwd_fixup<0,"), "w2": ("grouped_gemm<1,", "fwd_fixup<1,"),
+    "combine": ("combine_kernel",), "score_grad": ("score_grad_kernel",),
+    "dgrad_w2": ("grouped_gemm<2,",), "dgrad_w13": ("grouped_gemm<3,",),
+    "wgrad_w2": ("grouped_gemm<4,", "wgrad_fixup<4>"), "wgrad_w13": ("grouped_gemm<5,", "wgrad_fixup<5>"),
+    "quant_x": ("quantize_kernel",), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),
+    "wgrad_rows": ("wgrad_rows_kernel",),
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels
-KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13="grouped_gemm_mx<0>", w2="grouped_gemm_mx<1>")
+KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0>",), w2=("grouped_gemm_mx<1>",))
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -94,13 +100,13 @@ def _load_traffic():
 
 
 def traffic_for(stage: str, workload: str):
-    """HBM bytes (read + written) per launch of the stage's kernel, from the committed
-    rocprofv3 counter summary, if it was taken on the current sources for this workload."""
+    """HBM bytes (read + written) per call of the stage (all its kernels), from the
+    committed rocprofv3 counter summary, if it was taken on the current sources for this
+    workload."""
     tab = _load_traffic()
     if tab.get("source_hash") != source_hash():
         return None
-    ent = tab.get("workloads", {}).get(workload, {}).get("kernels", {}).get(
-        kernel_of_stage(workload).get(stage, "?"))
+    ent = tab.get("workloads", {}).get(workload, {}).get("stages", {}).get(stage)
     return None if ent is None else ent["read_bytes"] + ent["write_bytes"]
 
 
@@ -130,20 +136,25 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
     f_write = copy_bytes / (max(write[ck]) * 1024.0)
     fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
     write = {k: sum(v) / len(v) for k, v in write.items()}
-    kernels = {}
-    for stage, sub in kernel_of_stage(workload).items():
-        names = [k for k in fetch if sub in k]
-        if names and names[0] in write:
-            kernels[sub] = {"read_bytes": fetch[names[0]] * 1024.0 * f_fetch,
-                            "write_bytes": write[names[0]] * 1024.0 * f_write,
-                            "fetch_kib_raw": fetch[names[0]], "write_kib_raw": write[names[0]]}
+    kernels, stages = {}, {}
+    for stage, subs in kernel_of_stage(workload).items():
+        names = sorted(k for k in fetch if k in write and any(sub in k for sub in subs))
+        if not names:
+            continue
+        for k in names:
+            kernels[k] = {"read_bytes": fetch[k] * 1024.0 * f_fetch, "write_bytes": write[k] * 1024.0 * f_write,
+                          "fetch_kib_raw": fetch[k], "write_kib_raw": write[k]}
+        # every kernel of the stage runs once per call of the stage
+        stages[stage] = {"kernels": names,
+                         "read_bytes": sum(kernels[k]["read_bytes"] for k in names),
+                         "write_bytes": sum(kernels[k]["write_bytes"] for k in names)}
     # one file for every workload measured on the same sources
     tab = _load_traffic()
     if tab.get("source_hash") != source_hash():
         tab = {"source_hash": source_hash(), "workloads": {}}
     tab.setdefault("workloads", {})[workload] = {
         "copy_kernel": ck, "copy_bytes": copy_bytes, "fetch_factor": f_fetch,
-        "write_factor": f_write, "kernels": kernels}
+        "write_factor": f_write, "stages": stages, "kernels": kernels}
     with open(TRAFFIC_PATH, "w") as f:
         json.dump(tab, f, indent=1)
     return tab
@@ -192,8 +203,51 @@ def cpu_baseline(inp, training: bool, target_s: float):
     }
 
 
+def library_gemm(workload: str):
+    """hipBLASLt (torch.bmm / torch.matmul, contiguous BF16 operands) on the shapes of the
+    workload's two forward expert products with R / E rows per expert: no gather, no
+    SwiGLU, no ragged tails, i.e. the plain batched GEMM the grouped kernels generalise;
+    and one square 8192 GEMM, the chip's dense BF16 rate under its power limit."""
+    import torch
+    from mixture_experts_routed_dispatch_amd import inputs
+    cfg = inputs.CONFIGS[WORKLOADS[workload][0]]
+    E, d, I = cfg["E"], cfg["d"], cfg["I"]
+    M = cfg["T"] * cfg["k"] // E
+
+    def timed(fn, flop, n=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / n
+        return {"us": round(us, 1), "tflops": round(flop / (us * 1e-6) / 1e12, 1)}
+
+    g = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda *shape: torch.randn(*shape, device="cuda", generator=g).to(torch.bfloat16).contiguous()
+    out = {"library": "hipBLASLt via torch %s" % torch.__version__, "workload": workload,
+           "rows_per_expert": M, "E": E, "d": d, "I": I}
+    x, w13 = rnd(E, M, d), rnd(E, d, 2 * I)
+    out["w13_bmm"] = timed(lambda: torch.bmm(x, w13), 2.0 * E * M * d * 2 * I)
+    del x, w13
+    a, w2 = rnd(E, M, I), rnd(E, I, d)
+    out["w2_bmm"] = timed(lambda: torch.bmm(a, w2), 2.0 * E * M * I * d)
+    del a, w2
+    A, B = rnd(8192, 8192), rnd(8192, 8192)
+    out["square_8192"] = timed(lambda: torch.matmul(A, B), 2.0 * 8192 ** 3, n=10)
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
+    if args.library_gemm:
+        library_gemm(args.workload)
+        return
     if args.traffic:
         tab = write_traffic(args.traffic[0], args.traffic[1], args.workload,
                             args.copy_probe or (1 << 30))

@@ -180,6 +180,72 @@ def test_forward_full_size_sampled(torch_cuda, name, path):
     layer.close()
 
 
+def _counts_routing(counts, k, seed):
+    """ids [T, k] with exactly counts[e] rows per expert (distinct per token), T = sum / k:
+    the expert-sorted slot list is cut into k columns T apart (no expert has T rows, so a
+    token's experts differ), then tokens and columns are shuffled."""
+    counts = np.asarray(counts)
+    T = int(counts.sum()) // k
+    assert T * k == counts.sum() and counts.max() < T
+    flat = np.repeat(np.arange(len(counts), dtype=np.int32), counts)
+    ids = np.stack([flat[j * T:(j + 1) * T] for j in range(k)], axis=1)
+    rng = np.random.default_rng(seed)
+    ids = ids[rng.permutation(T)]
+    for t in range(T):
+        ids[t] = ids[t, rng.permutation(k)]
+    return ids
+
+
+@pytest.mark.parametrize("training", [False, True])
+def test_forward_ragged_expert_tails(torch_cuda, training):
+    """Experts with a few rows (1 to 60) past four whole 256-row tiles, one with exactly
+    1024 rows and one empty: the partly filled last tiles load clamped rows and mask their
+    stores.  Every token that has a row in such a tile (plus 32 others) is checked
+    against the oracle, in forward and, when training, through dx (which reads the saved
+    h of those rows)."""
+    import dataclasses
+    torch = torch_cuda
+    d, I, E, k = 1024, 512, 16, 2
+    rng = np.random.default_rng(8)
+    counts = 1024 + rng.integers(1, 61, size=E)
+    counts[3] = 1024             # an exact multiple of the tile: no partial tile
+    counts[7] = 0                # an empty expert
+    if counts.sum() % k:
+        counts[0] += 1
+    say("ragged expert tails: d=%d I=%d E=%d k=%d training=%s counts %s" % (d, I, E, k, training, counts.tolist()))
+    ids = _counts_routing(counts, k, seed=9)
+    T = ids.shape[0]
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=23, with_dy=training)
+    inp = dataclasses.replace(inp, ids=ids)
+    t = device_inputs(inp)
+    layer = make_layer(inp, training=training, path=1)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    y2 = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    if training:
+        dx = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])[0]
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # bitwise deterministic
+    # tokens of the experts' rows past their last whole tile (rows are in token order)
+    toks = set()
+    for e in range(E):
+        te = np.nonzero((ids == e).any(axis=1))[0]
+        toks.update(te[(len(te) // 256) * 256:].tolist())
+    toks.update(rng.choice(T, size=32, replace=False).tolist())
+    toks = np.array(sorted(toks), np.int32)
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
+    got = np_of(y)[toks]
+    e_y = rel(got, ref)
+    say("  %d tokens: y rel %.3e maxrel %.3e" % (len(toks), e_y, maxrel(got, ref)))
+    assert e_y <= TOL_BF16
+    if training:
+        dx_ref, _ = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, toks=toks)
+        e_dx = rel(np_of(dx)[toks], dx_ref)
+        say("  dx rel %.3e" % e_dx)
+        assert e_dx <= TOL_BF16
+    layer.close()
+
+
 def test_graph_replay_matches_eager(torch_cuda):
     torch = torch_cuda
     inp = inputs.generate(512, 512, 256, 8, 4, seed=4)
