@@ -530,6 +530,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // stores, 38-45k with ordinary ones).  a and dh, read back by the next product while
     // still cached, are stored normally, and so are stores of 8-byte pieces (the saved
     // h): non-temporal partial lines are written one by one, which made W13 35 % slower.
+    // The staged rows are read back all at once and then stored: the empty asm consumes
+    // every loaded value before the stores' bounds checks, so that the compiler issues the
+    // reads together and waits once, instead of sinking each read into its store's branch
+    // (a read, a wait and a store per row piece, one LDS latency each).  Once the values
+    // are in registers the staging slot may be rewritten.
+    auto lds_values_ready = [](auto& v) {
+#pragma unroll
+        for (auto& x : v) asm volatile("" : "+v"(x));
+    };
     auto store_rows_bf16 = [&](int ln, char* stg, int b, uint16_t* out, size_t ld, int q_first, int q_limit,
                                int p_first, int p_limit) {
         const int q_in = ln & 31, p_sub = 4 * (ln >> 5);
@@ -544,16 +553,19 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 *reinterpret_cast<uint2*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4) + (p_sub << 1)) = v;
             }
         __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the wave's own LDS writes are done
+        u32x4_t v[8];
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int row = 4 * it + (ln >> 4);
-            const int c16 = ln & 15;
-            const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
-            const int q = q_first + row;
-            const int p = p_first + 8 * c16;
-            if (q < q_limit && p < p_limit) store_nt(out + (size_t)q * ld + p, v);
+            v[it] = *reinterpret_cast<const u32x4_t*>(stg + row * 256 + (((ln & 15) ^ (row & 15)) << 4));
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);      // reads done before the slot is rewritten
+        lds_values_ready(v);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int q = q_first + 4 * it + (ln >> 4);
+            const int p = p_first + 8 * (ln & 15);
+            if (q < q_limit && p < p_limit) store_nt(out + (size_t)q * ld + p, make_uint4(v[it][0], v[it][1], v[it][2], v[it][3]));
+        }
     };
     auto epilogue = [&](const TileCtx& c, int buf) {
         char* stg = lds + buf * BUFB + wave * 8192;
@@ -598,17 +610,20 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                         }
                     }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
+                u32x4_t v[4];
 #pragma unroll
                 for (int it = 0; it < 4; ++it) {
                     const int row = 8 * it + (ln >> 3);
-                    const int c8 = ln & 7;
-                    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c8 ^ (row & 7)) << 4));
-                    const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
-                    const int i = c.pt * 128 + wp * 64 + 8 * c8;
-                    if (rr < c.rows && i < g.I)
-                        *reinterpret_cast<uint4*>(g.out + ((size_t)c.mb + rr) * g.I + i) = v;
+                    v[it] = *reinterpret_cast<const u32x4_t*>(stg + row * 128 + (((ln & 7) ^ (row & 7)) << 4));
                 }
-                __builtin_amdgcn_s_waitcnt(0xc07f);
+                lds_values_ready(v);
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + 8 * it + (ln >> 3);
+                    const int i = c.pt * 128 + wp * 64 + 8 * (ln & 7);
+                    if (rr < c.rows && i < g.I)
+                        *reinterpret_cast<u32x4_t*>(g.out + ((size_t)c.mb + rr) * g.I + i) = v[it];
+                }
             }
         } else if constexpr (MODE == FWD_W2 || MODE == DGRAD_W13) {
             // o [R, d] or dxp [R, d]
@@ -650,11 +665,18 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                             *reinterpret_cast<f32x4_t*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4)) = v;
                         }
                     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own LDS writes are done
+                    f32x4_t sv[8];
 #pragma unroll
                     for (int it = 0; it < 4; ++it) {
                         const int row = 8 * it + (ln >> 3), c8 = ln & 7;
-                        const f32x4_t v0 = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8) ^ (row & 15)) << 4));
-                        const f32x4_t v1 = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4));
+                        sv[2 * it] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8) ^ (row & 15)) << 4));
+                        sv[2 * it + 1] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4));
+                    }
+                    lds_values_ready(sv);
+#pragma unroll
+                    for (int it = 0; it < 4; ++it) {
+                        const int row = 8 * it + (ln >> 3);
+                        const f32x4_t v0 = sv[2 * it], v1 = sv[2 * it + 1];
                         const float av[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                         const uint32_t gw[4] = {hg[it].x, hg[it].y, hg[it].z, hg[it].w};
                         const uint32_t uw[4] = {hu[it].x, hu[it].y, hu[it].z, hu[it].w};
@@ -681,7 +703,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                             *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + g.I + i0) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
                         }
                     }
-                    __builtin_amdgcn_s_waitcnt(0xc07f);   // reads done before the slots are rewritten
                 }
         } else {
             // weight gradients: out[e][q][p], q < Qsz rows, p < Psz columns
