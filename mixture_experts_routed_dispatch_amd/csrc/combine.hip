@@ -3,8 +3,9 @@
 // nvfp4moe README, "MoE layer": the timed path ends with probability weighting
 // and a deterministic combine; "Training": router gradients.  Both are
 // HBM-streaming gathers: each thread owns 8 consecutive features (one 16-byte
-// load per routed row) and sums the k rows of its token in FP32 with j
-// ascending from +0.0, so the result does not depend on the launch shape.
+// load per routed row, non-temporal in the combine: 53.5 against 57 us at the
+// prefill size) and sums the k rows of its token in FP32 with j ascending from
+// +0.0, so the result does not depend on the launch shape.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,6 +13,13 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+
+// A gathered row piece, read non-temporally: each routed row is read once (by its
+// token), and the producers stream these rows out with non-temporal stores.
+__device__ __forceinline__ uint4 ld_row_nt(const uint16_t* p) {
+    const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __restrict__ src,
                                                            const int32_t* __restrict__ slots,
@@ -32,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
         float s[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            v[u] = *reinterpret_cast<const uint4*>(src + row(j + u) * d + n);
+            v[u] = ld_row_nt(src + row(j + u) * d + n);
             s[u] = wt ? wt[j + u] : 1.0f;
         }
 #pragma unroll
@@ -46,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
         }
     }
     for (; j < k; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src + row(j) * d + n);
+        const uint4 v = ld_row_nt(src + row(j) * d + n);
         const float s = wt ? wt[j] : 1.0f;
         const uint32_t ww[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -64,7 +72,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const uint16_t* __res
 }
 
 // ds[t][j] = <dy[t], o[slots[t][j]]>: one workgroup per token, fixed reduction tree.
+// The token's rows are taken 8 at a time with all their loads in flight (indices past
+// k clamp to row k - 1 and are not used); each j keeps its own chain of FMAs over n, so
+// the sums are those of one row at a time.
 constexpr int kMaxK = 32;
+constexpr int kRowsInFlight = 8;
 
 __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __restrict__ dy,
                                                               const uint16_t* __restrict__ o,
@@ -75,22 +87,36 @@ __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __
     const int t = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int32_t* sl = slots + (size_t)t * k;
-    for (int j = 0; j < k; ++j) {
-        float acc = 0.0f;
-        const size_t r = (size_t)sl[j];
+    for (int j0 = 0; j0 < k; j0 += kRowsInFlight) {
+        size_t r[kRowsInFlight];
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) r[u] = (size_t)sl[j0 + u < k ? j0 + u : k - 1];
+        float acc[kRowsInFlight];
+#pragma unroll
+        for (int u = 0; u < kRowsInFlight; ++u) acc[u] = 0.0f;
         for (int n = threadIdx.x * 8; n < d; n += kThreads * 8) {
             const uint4 a = *reinterpret_cast<const uint4*>(dy + (size_t)t * d + n);
-            const uint4 b = *reinterpret_cast<const uint4*>(o + r * d + n);
-            const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+            uint4 b[kRowsInFlight];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                acc = __builtin_fmaf(bf16lo(aw[z]), bf16lo(bw[z]), acc);
-                acc = __builtin_fmaf(bf16hi(aw[z]), bf16hi(bw[z]), acc);
+            for (int u = 0; u < kRowsInFlight; ++u) b[u] = ld_row_nt(o + r[u] * d + n);
+            const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+            for (int u = 0; u < kRowsInFlight; ++u) {
+                const uint32_t bw[4] = {b[u].x, b[u].y, b[u].z, b[u].w};
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    acc[u] = __builtin_fmaf(bf16lo(aw[z]), bf16lo(bw[z]), acc[u]);
+                    acc[u] = __builtin_fmaf(bf16hi(aw[z]), bf16hi(bw[z]), acc[u]);
+                }
             }
         }
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_down(acc, off, MOE_WAVE);
-        if (lane == 0) part[wave][j] = acc;
+        for (int u = 0; u < kRowsInFlight; ++u) {
+            float v = acc[u];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, MOE_WAVE);
+            if (lane == 0 && j0 + u < k) part[wave][j0 + u] = v;
+        }
     }
     __syncthreads();
     if (threadIdx.x < k) {
