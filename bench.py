@@ -123,8 +123,9 @@ def _pmc_values(path: str, counter: str):
 
 def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) of
-    `bench.py --copy-probe N` into bytes per launch for each kernel.  Each counter is
-    scaled by the factor that makes the plain copy of N bytes read and write N bytes."""
+    `bench.py --copy-probe N` into bytes per launch for each kernel (median over its
+    dispatches).  Each counter is scaled by the factor that makes the plain copy of N
+    bytes read and write N bytes."""
     fetch = _pmc_values(fetch_csv, "FETCH_SIZE")
     write = _pmc_values(write_csv, "WRITE_SIZE")
     copy = [k for k in fetch if "copy" in k.lower() and "moe" not in k and k in write]
@@ -134,8 +135,11 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
     ck = max(copy, key=lambda k: max(fetch[k]))
     f_fetch = copy_bytes / (max(fetch[ck]) * 1024.0)
     f_write = copy_bytes / (max(write[ck]) * 1024.0)
-    fetch = {k: sum(v) / len(v) for k, v in fetch.items()}
-    write = {k: sum(v) / len(v) for k, v in write.items()}
+    # the median over a kernel's dispatches: the calls of one stage are alike, while a
+    # kernel can also run once outside the steps (the quantizer prepares the weights)
+    med = lambda v: sorted(v)[len(v) // 2]
+    fetch = {k: med(v) for k, v in fetch.items()}
+    write = {k: med(v) for k, v in write.items()}
     kernels, stages = {}, {}
     for stage, subs in kernel_of_stage(workload).items():
         names = sorted(k for k in fetch if k in write and any(sub in k for sub in subs))
