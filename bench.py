@@ -50,6 +50,10 @@ def parse():
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="before warm-up, run one plain device copy of BYTES (counter calibration)")
+    ap.add_argument("--routed", action="store_true",
+                    help="time moe_forward_routed instead: the workload's rows put in expert "
+                         "order once outside the timed region, then W13 + SwiGLU and W2 on "
+                         "them (no dispatch, no combine; BF16 forward workloads)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library's BF16 GEMMs (hipBLASLt through torch) on the "
                          "workload's expert-product shapes with uniform rows per expert, and a "
@@ -314,7 +318,20 @@ def main():
              for (a, b), (sa, sb) in zip(w_list, w_scales)]
     state = {"i": 0}
 
+    if args.routed:
+        if training or decode or mx:
+            raise SystemExit("--routed: BF16 forward workloads on the grouped-GEMM path only")
+        # expert-major rows and m_indptr from the library's own dispatch, once
+        m_ind, gath, _, _ = layer.dispatch(t["ids"], t["scores"])
+        x_rows = t["x"][gath.long()].contiguous()
+        out_rows = torch.empty((R, d), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+
     def step():
+        if args.routed:
+            moe.moe_forward_routed(layer.plan, x_rows.data_ptr(), m_ind.data_ptr(), wlist[0],
+                                   out_rows.data_ptr(), sp)
+            return
         i = state["i"]
         state["i"] = i + 1
         ids_dev = ids_list[i % len(ids_list)]
@@ -426,7 +443,8 @@ def main():
                 + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
         "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s" % (
             cfg_name, T, d, I, E, k, "MXFP8-E4M3" if mx else "BF16",
-            "forward+backward" if training else "forward"),
+            "forward+backward" if training else
+            ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward")),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},
         "tokens_per_s": T / (ms_step * 1e-3),

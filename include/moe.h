@@ -68,6 +68,7 @@ typedef enum {
 /* device status bits (moe_get_status) */
 #define MOE_DEV_ID_OUT_OF_RANGE 1
 #define MOE_DEV_ID_DUPLICATE 2
+#define MOE_DEV_BAD_INDPTR 4   /* moe_forward_routed: m_indptr not non-decreasing from 0, or past T*k */
 
 typedef struct {
     int32_t T;          /* physical token count, fixed per plan (blog post, "Caveats", item 2) */
@@ -157,6 +158,25 @@ moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const vo
  * the W2 outputs for moe_backward; a later forward overwrites them. */
 moe_status_t moe_forward(moe_plan_t plan, const void* x, const int32_t* ids, const float* scores,
                          const moe_weights_t* w, void* y, void* stream);
+
+/* Forward of rows already in expert order (nvfp4moe README, "MoE layer": frameworks
+ * that already hold expert-major rows call the layer on them directly).  For each
+ * expert e and row r in [m_indptr[e], m_indptr[e+1]):
+ *   out[r] = W2_e (silu(W1_e x_rows[r]) * (W3_e x_rows[r]))       (BF16, FP32 accumulate)
+ * with no dispatch, no score weighting and no combine: the caller owns the routing.
+ *   x_rows    BF16 [R', d] device, R' = m_indptr[E] <= T*k of the plan
+ *   m_indptr  int32 [E+1] device, m_indptr[0] = 0, non-decreasing (empty experts valid)
+ *   out       BF16 [R', d] device, row r written for every r < m_indptr[E]
+ * The pages also pass padded_offsets, which describe their padded tile layout; these
+ * kernels take ragged expert segments, so only m_indptr is needed.  An m_indptr that is
+ * not non-decreasing from 0, or whose total exceeds T*k, is caught on the device: every
+ * expert is then taken as empty (out is not written) and MOE_DEV_BAD_INDPTR is set
+ * (moe_get_status).  BF16 inference plans on the grouped-GEMM path (cfg.path =
+ * MOE_PATH_PREFILL, or AUTO with T*k > 256) with T*k*d*2 < 2^31; others return
+ * MOE_ERR_UNSUPPORTED.  It uses the plan's dispatch and intermediate workspace, which the
+ * next call overwrites. */
+moe_status_t moe_forward_routed(moe_plan_t plan, const void* x_rows, const int32_t* m_indptr,
+                                const moe_weights_t* w, void* out, void* stream);
 
 /* Backward (DGRAD + WGRAD + router gradient; blog post, "What it is selling";
  * nvfp4moe README, "Training") of the most recent training forward on this

@@ -177,7 +177,42 @@ __global__ __launch_bounds__(kThreads) void dispatch_place(
     }
 }
 
+// Rows already in expert order: workgroup 0 checks the caller's m_indptr (entry 0 is
+// 0, every entry at least the one before and at most R) and copies it, or zeros when it
+// fails; every workgroup writes part of the identity gather, so that the gathered
+// products read row r of the caller's rows for routed row r.
+__global__ __launch_bounds__(kThreads) void routed_prep(const int32_t* __restrict__ m_in, int E, int64_t R,
+                                                        int32_t* __restrict__ m_out,
+                                                        int32_t* __restrict__ gather,
+                                                        int32_t* __restrict__ status) {
+    if (blockIdx.x == 0) {
+        __shared__ int bad;
+        if (threadIdx.x == 0) bad = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i <= E; i += kThreads) {
+            const int v = m_in[i];
+            const bool ok = (i == 0) ? v == 0 : (v >= m_in[i - 1] && (int64_t)v <= R);
+            if (!ok) atomicOr(&bad, 1);
+        }
+        __syncthreads();
+        const bool b = bad != 0;
+        for (int i = threadIdx.x; i <= E; i += kThreads) m_out[i] = b ? 0 : m_in[i];
+        if (b && threadIdx.x == 0) atomicOr(status, kDevBadIndptr);
+    }
+    for (int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x; r < R; r += (int64_t)gridDim.x * kThreads)
+        gather[r] = (int32_t)r;
+}
+
 }  // namespace
+
+hipError_t launch_routed_prep(const int32_t* m_in, int E, int64_t R, int32_t* m_out, int32_t* gather,
+                              int32_t* status, hipStream_t s) {
+    int64_t grid = (R + kThreads - 1) / kThreads;
+    if (grid < 1) grid = 1;
+    if (grid > 1024) grid = 1024;
+    hipLaunchKernelGGL(routed_prep, dim3((unsigned)grid), dim3(kThreads), 0, s, m_in, E, R, m_out, gather, status);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const int32_t* ids, const float* scores, int T, int k, int E,
                            int32_t* hist, int32_t* m_indptr, int32_t* gather, int32_t* slots,

@@ -9,6 +9,7 @@ namespace moe {
 // Device status bits (the MOE_DEV_* values of moe.h).
 constexpr int kDevIdOutOfRange = 1;
 constexpr int kDevIdDuplicate = 2;
+constexpr int kDevBadIndptr = 4;
 
 // Entries (t, j) handled by one dispatch workgroup.
 constexpr int kDispatchChunk = 2048;
@@ -19,6 +20,11 @@ inline int dispatch_chunks(int64_t R) { return (int)((R + kDispatchChunk - 1) / 
 hipError_t launch_dispatch(const int32_t* ids, const float* scores, int T, int k, int E,
                            int32_t* hist, int32_t* m_indptr, int32_t* gather, int32_t* slots,
                            float* probs, int32_t* status, hipStream_t s);
+
+// Pre-dispatched rows: validates a caller's m_indptr [E+1] into m_out (all zeros and
+// kDevBadIndptr when it does not rise from 0 or passes R) and writes gather[r] = r, r < R.
+hipError_t launch_routed_prep(const int32_t* m_in, int E, int64_t R, int32_t* m_out, int32_t* gather,
+                              int32_t* status, hipStream_t s);
 
 enum GemmMode { FWD_W13 = 0, FWD_W2 = 1, DGRAD_W2 = 2, DGRAD_W13 = 3, WGRAD_W2 = 4, WGRAD_W13 = 5 };
 

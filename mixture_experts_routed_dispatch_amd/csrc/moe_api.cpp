@@ -317,6 +317,41 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     return MOE_OK;
 }
 
+moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t* m_indptr,
+                                const moe_weights_t* w, void* out, void* stream) {
+    if (!p || !w) return MOE_ERR_INVALID_ARG;
+    const moe_config_t& c = p->cfg;
+    if (c.precision != MOE_BF16 || c.training || p->decode) return MOE_ERR_UNSUPPORTED;
+    if (p->R * c.d * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;   // 32-bit row offsets into x_rows
+    if (c.T > 0 && (!x_rows || !m_indptr || !out || !w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+    if (!p->ws) return MOE_ERR_WORKSPACE;
+    p->have_saved_forward = false;
+    if (c.T == 0) return MOE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int32_t* mi = p->at<int32_t>(p->off_m_indptr);
+    int32_t* gather = p->at<int32_t>(p->off_gather);
+    hipError_t e = staged(p, MOE_STAGE_DISPATCH, s, [&] {
+        return launch_routed_prep(m_indptr, c.E, p->R, mi, gather, p->at<int32_t>(p->off_status), s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    GemmArgs g{};
+    g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.part = p->at<float>(p->off_part);
+    g.split = p->at<int4>(p->off_split);
+    g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));
+    g.m_indptr = mi; g.gather = gather;
+    g.x = static_cast<const uint16_t*>(x_rows);
+    g.w13 = static_cast<const uint16_t*>(w->w13);
+    g.w2 = static_cast<const uint16_t*>(w->w2);
+    g.out = p->at<uint16_t>(p->off_a);
+    e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm(FWD_W13, g, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    g.a = p->at<uint16_t>(p->off_a);
+    g.out = static_cast<uint16_t*>(out);
+    e = staged(p, MOE_STAGE_W2, s, [&] { return launch_gemm(FWD_W2, g, p->num_cu, s); });
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe_weights_t* w,
                           void* dx, void* dw13, void* dw2, float* dscores, void* stream) {
     if (!p || !w) return MOE_ERR_INVALID_ARG;

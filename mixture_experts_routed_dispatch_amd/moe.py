@@ -33,10 +33,11 @@ MOE_PATH_DECODE = 2
 
 MOE_DEV_ID_OUT_OF_RANGE = 1
 MOE_DEV_ID_DUPLICATE = 2
+MOE_DEV_BAD_INDPTR = 4
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_destroy",
-           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward",
+           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward", "moe_forward_routed",
            "moe_backward", "moe_get_status", "moe_status_string", "moe_profile",
            "moe_profile_read")
 
@@ -89,6 +90,8 @@ def lib():
         L.moe_prepare_weights.restype = ctypes.c_int
         L.moe_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_routed.argtypes = [vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
+        L.moe_forward_routed.restype = ctypes.c_int
         L.moe_backward.argtypes = [vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp]
         L.moe_backward.restype = ctypes.c_int
         L.moe_get_status.argtypes = [vp, ctypes.POINTER(i32), i32, vp]
@@ -153,6 +156,11 @@ def weights(w13, w2, w13_scale=0, w2_scale=0) -> MoeWeights:
 
 def moe_forward(plan, x, ids, scores, w: MoeWeights, y, stream=0):
     _ok(lib().moe_forward(plan, x, ids, scores, ctypes.byref(w), y, stream), "moe_forward")
+
+
+def moe_forward_routed(plan, x_rows, m_indptr, w: MoeWeights, out, stream=0):
+    _ok(lib().moe_forward_routed(plan, x_rows, m_indptr, ctypes.byref(w), out, stream),
+        "moe_forward_routed")
 
 
 def moe_backward(plan, dy, x, w: MoeWeights, dx, dw13, dw2, dscores, stream=0):
@@ -238,6 +246,16 @@ class Layer:
         w = weights(_ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale))
         moe_forward(self.plan, _ptr(x), _ptr(ids), _ptr(scores), w, _ptr(y), _stream(stream))
         return y
+
+    def forward_routed(self, x_rows, m_indptr, w13, w2, out=None, stream=None):
+        """Expert outputs of rows already in expert order (int32 m_indptr [E+1] on the
+        device); out BF16 [T*k, d], of which rows m_indptr[E].. are not written."""
+        import torch
+        if out is None:
+            out = torch.empty((self.T * self.k, self.d), dtype=torch.bfloat16, device=x_rows.device)
+        w = weights(_ptr(w13), _ptr(w2))
+        moe_forward_routed(self.plan, _ptr(x_rows), _ptr(m_indptr), w, _ptr(out), _stream(stream))
+        return out
 
     def backward(self, dy, x, w13, w2, dx=None, dw13=None, dw2=None, dscores=None, stream=None):
         import torch

@@ -246,6 +246,81 @@ def test_forward_ragged_expert_tails(torch_cuda, training):
     layer.close()
 
 
+# ------------------------------------------------------------------ pre-dispatched rows
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", [(600, 512, 384, 6, 3, "uniform"), (3000, 1024, 512, 16, 4, "uniform"),
+                                               (300, 256, 128, 128, 8, "zipf")])
+def test_forward_routed_matches_oracle(torch_cuda, T, d, I, E, k, routing):
+    """Rows put in expert order by the oracle's own dispatch, with its m_indptr: row
+    slots[t][j] of the output is the expert output of (t, j)."""
+    torch = torch_cuda
+    say("forward routed", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=31)
+    m_indptr, gather, slots, _ = oracle.dispatch(inp.ids, inp.scores, E)
+    t = device_inputs(inp)
+    x_rows = t["x"][torch.from_numpy(gather.astype(np.int64)).to(dev())].contiguous()
+    layer = make_layer(inp, path=1)
+    out = layer.forward_routed(x_rows, torch.from_numpy(m_indptr).to(dev()), t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    _, o_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, want_o=True)
+    got = np_of(out)[slots.reshape(-1)].reshape(T, k, d)
+    e = rel(got, o_ref)
+    say("  rel %.3e maxrel %.3e" % (e, maxrel(got, o_ref)))
+    assert e <= TOL_BF16
+    layer.close()
+
+
+def test_forward_routed_ragged_segments(torch_cuda):
+    """Caller-made segments: empty experts (first, middle, last), a segment of one row, and
+    fewer rows than T*k; each row is checked as a one-expert token (k = 1, score 1) of the
+    oracle, and the rows past m_indptr[E] are left as they were."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 400, 512, 256, 8, 2
+    counts = np.array([0, 300, 1, 0, 257, 45, 100, 0])
+    m_indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(m_indptr[-1])
+    assert n < T * k
+    inp = inputs.generate(n, d, I, E, 1, "uniform", seed=32)
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)[:, None]
+    ones = np.ones((n, 1), np.float32)
+    x_rows = bf16_dev(inp.x)
+    w13, w2 = bf16_dev(inp.w13), bf16_dev(inp.w2)
+    layer = moe.Layer(T, d, I, E, k, path=moe.MOE_PATH_PREFILL)
+    out = torch.full((T * k, d), 3.0, dtype=torch.bfloat16, device=dev())
+    layer.forward_routed(x_rows, torch.from_numpy(m_indptr).to(dev()), w13, w2, out=out)
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    _, o_ref = oracle.forward_tokens(inp.x, ids, ones, inp.w13, inp.w2, want_o=True)
+    got = np_of(out)
+    e = rel(got[:n], o_ref[:, 0])
+    say("  ragged segments: rel %.3e" % e)
+    assert e <= TOL_BF16
+    assert np.all(got[n:] == 3.0)
+    layer.close()
+
+
+def test_forward_routed_rejects_bad_indptr(torch_cuda):
+    """A decreasing m_indptr, or one whose total passes T*k, sets MOE_DEV_BAD_INDPTR and
+    leaves the output untouched (every expert taken as empty)."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 256, 256, 128, 4, 2
+    layer = moe.Layer(T, d, I, E, k, path=moe.MOE_PATH_PREFILL)
+    g = torch.Generator(device="cpu").manual_seed(3)
+    x_rows = (torch.randn((T * k, d), generator=g) * 0.5).to(torch.bfloat16).to(dev())
+    w13 = (torch.randn((E, 2 * I, d), generator=g) / 16).to(torch.bfloat16).to(dev())
+    w2 = (torch.randn((E, d, I), generator=g) / 11).to(torch.bfloat16).to(dev())
+    for bad in ([0, 100, 50, 300, 400], [0, 100, 200, 300, T * k + 1], [5, 100, 200, 300, 400]):
+        out = torch.full((T * k, d), 7.0, dtype=torch.bfloat16, device=dev())
+        layer.forward_routed(x_rows, torch.tensor(bad, dtype=torch.int32, device=dev()), w13, w2, out=out)
+        st, flags = layer.status(clear=True)
+        assert st == moe.MOE_ERR_ROUTING and flags == moe.MOE_DEV_BAD_INDPTR, bad
+        assert bool(torch.all(out == 7.0)), bad
+    layer.close()
+
+
 def test_graph_replay_matches_eager(torch_cuda):
     torch = torch_cuda
     inp = inputs.generate(512, 512, 256, 8, 4, seed=4)
