@@ -54,6 +54,9 @@ def parse():
                     help="time moe_forward_routed instead: the workload's rows put in expert "
                          "order once outside the timed region, then W13 + SwiGLU and W2 on "
                          "them (no dispatch, no combine; BF16 forward workloads)")
+    ap.add_argument("--wgrad-accumulate", action="store_true",
+                    help="train workload: the backward adds the weight gradients into the "
+                         "existing dW13 / dW2 (plan option wgrad_accumulate)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library's BF16 GEMMs (hipBLASLt through torch) on the "
                          "workload's expert-product shapes with uniform rows per expert, and a "
@@ -278,8 +281,11 @@ def main():
     t = device_inputs(inp)
     decode = cfg_name.startswith("decode")
     mx = cfg_name == "mxfp8"
+    if args.wgrad_accumulate and not training:
+        raise SystemExit("--wgrad-accumulate: the train workload only")
     layer = moe.Layer(T, d, I, E, k, training=training,
-                      precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16)
+                      precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16,
+                      wgrad_accumulate=args.wgrad_accumulate)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
@@ -443,7 +449,8 @@ def main():
                 + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
         "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s" % (
             cfg_name, T, d, I, E, k, "MXFP8-E4M3" if mx else "BF16",
-            "forward+backward" if training else
+            ("forward+backward (weight gradients accumulated)" if args.wgrad_accumulate else "forward+backward")
+            if training else
             ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward")),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},

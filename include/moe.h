@@ -79,6 +79,9 @@ typedef struct {
     int32_t precision;  /* moe_precision_t */
     int32_t training;   /* 1: forward saves what moe_backward needs (BF16 only) */
     int32_t path;       /* MOE_PATH_* */
+    int32_t wgrad_accumulate;  /* 1: moe_backward adds the weight gradients into dw13 / dw2
+                                  (blog post, "What it is selling": in-place accumulation
+                                  into the parameters' gradients); training plans only */
 } moe_config_t;
 
 typedef struct {
@@ -184,6 +187,9 @@ moe_status_t moe_forward_routed(moe_plan_t plan, const void* x_rows, const int32
  *   dx      BF16 [T, d]   = dL/dx
  *   dw13    BF16 [E,2I,d] = dL/dW13, overwritten (+0.0 for experts with no row)
  *   dw2     BF16 [E,d,I]  = dL/dW2, overwritten
+ *   (with cfg.wgrad_accumulate = 1 instead dw13 = bf16(dw13 + bf16(dL/dW13)), likewise
+ *    dw2: the gradient in BF16 added in FP32 to the value already there, one rounding;
+ *    experts with no row keep their values)
  *   dscores f32  [T, k]   = dL/dscores[t][j] = <dy[t], expert output of (t, j)>
  * Returns MOE_ERR_STATE if no training forward ran since the workspace was
  * bound.  BF16 plans only. */

@@ -560,6 +560,25 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             v[it] = *reinterpret_cast<const u32x4_t*>(stg + row * 256 + (((ln & 15) ^ (row & 15)) << 4));
         }
         lds_values_ready(v);
+        if constexpr (MODE == WGRAD_W2 || MODE == WGRAD_W13) {
+            // accumulate: out = bf16(out + bf16(gradient)); the old values are loaded at
+            // clamped (always valid) addresses, all before the first add
+            if (g.accumulate) {
+                u32x4_t old[8];
+#pragma unroll
+                for (int it = 0; it < 8; ++it) {
+                    const int q = q_first + 4 * it + (ln >> 4);
+                    const int p = p_first + 8 * (ln & 15);
+                    const int qc = q < q_limit ? q : q_limit - 1, pc = p < p_limit ? p : p_limit - 8;
+                    old[it] = *reinterpret_cast<const u32x4_t*>(out + (size_t)qc * ld + pc);
+                }
+#pragma unroll
+                for (int it = 0; it < 8; ++it)
+#pragma unroll
+                    for (int z = 0; z < 4; ++z)
+                        v[it][z] = pack_bf16(bf16lo(old[it][z]) + bf16lo(v[it][z]), bf16hi(old[it][z]) + bf16hi(v[it][z]));
+            }
+        }
 #pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int q = q_first + 4 * it + (ln >> 4);
@@ -824,7 +843,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 }
 
 // Weight-gradient tiles cut into pieces along K: out = ((piece 0 + piece 1) + ...) in
-// BF16, one workgroup per quarter of a tile.  Thread t of the tile owns the elements thread t of
+// BF16 (accumulate: out = bf16(out + that)), one workgroup per quarter of a tile.  Thread t of the tile owns the elements thread t of
 // grouped_gemm held (wave w = t / 64 covers p in [128 (w & 1), +128), q in
 // [128 (w >> 1), +128) of the tile).
 template <int MODE>
@@ -855,6 +874,17 @@ __global__ __launch_bounds__(NTHR) void wgrad_fixup(GemmArgs g) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sum[i] += v[i];
             }
+            // accumulate: the old values, loaded at clamped addresses before any store
+            uint2 old[16];
+            if (g.accumulate) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int j = j0 + i, a = j >> 4, b = (j >> 2) & 3, z = j & 3;
+                    const int q = q0 + 32 * b, p = p0 + 32 * a + 8 * z;
+                    const int qc = q < Qsz ? q : Qsz - 1, pc = p < Psz ? p : Psz - 4;
+                    old[i] = *reinterpret_cast<const uint2*>(out + (size_t)qc * Psz + pc);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int j = j0 + i, a = j >> 4, b = (j >> 2) & 3, z = j & 3;
@@ -863,6 +893,10 @@ __global__ __launch_bounds__(NTHR) void wgrad_fixup(GemmArgs g) {
                     uint2 o;
                     o.x = pack_bf16(sum[i][0], sum[i][1]);
                     o.y = pack_bf16(sum[i][2], sum[i][3]);
+                    if (g.accumulate) {
+                        o.x = pack_bf16(bf16lo(old[i].x) + bf16lo(o.x), bf16hi(old[i].x) + bf16hi(o.x));
+                        o.y = pack_bf16(bf16lo(old[i].y) + bf16lo(o.y), bf16hi(old[i].y) + bf16hi(o.y));
+                    }
                     *reinterpret_cast<uint2*>(out + (size_t)q * Psz + p) = o;
                 }
             }

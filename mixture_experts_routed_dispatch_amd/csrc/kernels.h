@@ -47,6 +47,7 @@ struct GemmArgs {
     float* part;          // [kMaxPieces, 256 * 256] FP32 partial sums of split weight-gradient tiles
     int4* split;          // [kMaxPieces / 2] split tiles: (e, qt << 16 | pt, pieces, slot0 << 16 | stride)
     int32_t* nsplit;      // number of split tiles of the last weight-gradient launch
+    int accumulate;       // weight gradients: add into out instead of overwriting
 };
 
 // Pieces of split weight-gradient tiles in one launch (sizes their FP32 partial sums).

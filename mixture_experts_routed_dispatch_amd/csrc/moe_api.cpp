@@ -95,6 +95,8 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (c.T < 0 || c.d <= 0 || c.I <= 0 || c.E <= 0 || c.k <= 0) return MOE_ERR_INVALID_ARG;
     if (c.precision != MOE_BF16 && c.precision != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
     if (c.training != 0 && c.training != 1) return MOE_ERR_INVALID_ARG;
+    if (c.wgrad_accumulate != 0 && c.wgrad_accumulate != 1) return MOE_ERR_INVALID_ARG;
+    if (c.wgrad_accumulate && !c.training) return MOE_ERR_UNSUPPORTED;
     if (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_PREFILL && c.path != MOE_PATH_DECODE)
         return MOE_ERR_INVALID_ARG;
     if (c.d % 64 != 0 || c.I % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -386,6 +388,7 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     g.h = p->at<uint16_t>(p->off_h);
     g.dy = static_cast<const uint16_t*>(dy);
     g.dh = p->at<uint16_t>(p->off_dh);
+    g.accumulate = c.wgrad_accumulate;
     g.xg = p->at<uint16_t>(p->off_xg);
     g.dys = p->at<uint16_t>(p->off_dys);
     if (c.T == 0) {

@@ -54,7 +54,8 @@ class MoeError(RuntimeError):
 class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("precision", ctypes.c_int32),
-                ("training", ctypes.c_int32), ("path", ctypes.c_int32)]
+                ("training", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("wgrad_accumulate", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -118,8 +119,9 @@ def _ok(status: int, where: str):
         raise MoeError(status, where)
 
 
-def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO) -> int:
-    cfg = MoeConfig(T, d, I, E, k, precision, training, path)
+def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO,
+             wgrad_accumulate=0) -> int:
+    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate)
     h = ctypes.c_void_p()
     _ok(lib().moe_plan(ctypes.byref(cfg), ctypes.byref(h)), "moe_plan")
     return h.value
@@ -207,11 +209,12 @@ class Layer:
     """One plan plus its torch-allocated workspace; all compute goes through libmoe."""
 
     def __init__(self, T, d, I, E, k, precision=MOE_BF16, training=False, path=MOE_PATH_AUTO,
-                 device="cuda"):
+                 device="cuda", wgrad_accumulate=False):
         import torch
         self.T, self.d, self.I, self.E, self.k = T, d, I, E, k
         self.precision = precision
-        self.plan = moe_plan(T, d, I, E, k, precision, int(bool(training)), path)
+        self.plan = moe_plan(T, d, I, E, k, precision, int(bool(training)), path,
+                             int(bool(wgrad_accumulate)))
         nbytes = moe_workspace_bytes(self.plan)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         moe_bind_workspace(self.plan, _ptr(self.workspace), self.workspace.numel())

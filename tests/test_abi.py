@@ -66,10 +66,13 @@ def test_status_strings(L):
     (dict(T=33, d=2048, I=768, E=128, k=8, path=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=1, d=256, I=128, E=8, k=2, path=2, training=1), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=0, d=256, I=128, E=8, k=2, path=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=64, d=256, I=128, E=8, k=2, training=1, wgrad_accumulate=1), moe.MOE_OK),
+    (dict(T=64, d=256, I=128, E=8, k=2, wgrad_accumulate=1), moe.MOE_ERR_UNSUPPORTED),  # no backward
+    (dict(T=64, d=256, I=128, E=8, k=2, training=1, wgrad_accumulate=2), moe.MOE_ERR_INVALID_ARG),
 ])
 def test_plan_validation(L, cfg, expect):
     c = moe.MoeConfig(cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"], cfg.get("precision", 0),
-                      cfg.get("training", 0), cfg.get("path", 0))
+                      cfg.get("training", 0), cfg.get("path", 0), cfg.get("wgrad_accumulate", 0))
     h = ctypes.c_void_p()
     st = L.moe_plan(ctypes.byref(c), ctypes.byref(h))
     assert st == expect

@@ -525,6 +525,47 @@ def test_backward_split_weight_gradient_tiles(torch_cuda, T, d, I, E, k, hot):
     layer.close()
 
 
+@pytest.mark.parametrize("T,d,I,E,k,routing,hot", [(400, 512, 384, 6, 3, "uniform", 0),
+                                                    (300, 256, 128, 128, 8, "zipf", 0),
+                                                    (7000, 256, 128, 4, 2, "uniform", 6600)])
+def test_backward_accumulates_weight_gradients(torch_cuda, T, d, I, E, k, routing, hot):
+    """wgrad_accumulate: dW13 and dW2 start from random values and come back as those
+    values plus the gradient (experts with no row bitwise unchanged); the hot case has an
+    expert of 6600 rows, whose tiles are cut into pieces and summed by the fixup kernel."""
+    import dataclasses
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("backward accumulate", T, d, I, E, k, routing, hot)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=41, with_dy=True)
+    if hot:
+        rng = np.random.default_rng(6)
+        ids = np.empty((T, k), np.int32)
+        for t in range(T):
+            ids[t] = (np.concatenate([[0], 1 + rng.permutation(E - 1)[:k - 1]]) if t < hot
+                      else 1 + rng.permutation(E - 1)[:k])
+        inp = dataclasses.replace(inp, ids=ids)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, training=True, wgrad_accumulate=True)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dw13_0 = (torch.randn((E, 2 * I, d), generator=g) * 0.05).to(torch.bfloat16).to(dev())
+    dw2_0 = (torch.randn((E, d, I), generator=g) * 0.05).to(torch.bfloat16).to(dev())
+    dw13, dw2 = dw13_0.clone(), dw2_0.clone()
+    layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    layer.backward(t["dy"], t["x"], t["w13"], t["w2"], dw13=dw13, dw2=dw2)
+    torch.cuda.synchronize()
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    dw13_ref = dw13_ref.reshape(E, 2 * I, d) + np_of(dw13_0)
+    dw2_ref = dw2_ref + np_of(dw2_0)
+    e13, e2 = rel(np_of(dw13), dw13_ref), rel(np_of(dw2), dw2_ref)
+    say("  dw13 %.3e dw2 %.3e" % (e13, e2))
+    assert max(e13, e2) <= TOL_BF16
+    counts = np.bincount(inp.ids.ravel(), minlength=E)
+    for e in np.nonzero(counts == 0)[0]:
+        assert torch.equal(dw13[e].view(torch.int16), dw13_0[e].view(torch.int16))
+        assert torch.equal(dw2[e].view(torch.int16), dw2_0[e].view(torch.int16))
+    layer.close()
+
+
 def test_no_tokens(torch_cuda):
     """T = 0: the forward writes nothing and succeeds; the backward gives all-zero weight
     gradients (every expert is empty)."""
