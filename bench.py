@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--wgrad-accumulate", action="store_true",
                     help="train workload: the backward adds the weight gradients into the "
                          "existing dW13 / dW2 (plan option wgrad_accumulate)")
+    ap.add_argument("--recompute-h", action="store_true",
+                    help="train workload: the forward keeps no h, the backward recomputes it "
+                         "(plan option recompute_h)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library's BF16 GEMMs (hipBLASLt through torch) on the "
                          "workload's expert-product shapes with uniform rows per expert, and a "
@@ -75,7 +78,7 @@ KERNEL_OF_STAGE = {
     "dgrad_w2": ("grouped_gemm<2,",), "dgrad_w13": ("grouped_gemm<3,",),
     "wgrad_w2": ("grouped_gemm<4,", "wgrad_fixup<4>"), "wgrad_w13": ("grouped_gemm<5,", "wgrad_fixup<5>"),
     "quant_x": ("quantize_kernel",), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),
-    "wgrad_rows": ("wgrad_rows_kernel",),
+    "wgrad_rows": ("wgrad_rows_kernel",), "recompute_h": ("grouped_gemm<0,",),
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels
 KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0>",), w2=("grouped_gemm_mx<1>",))
@@ -281,11 +284,11 @@ def main():
     t = device_inputs(inp)
     decode = cfg_name.startswith("decode")
     mx = cfg_name == "mxfp8"
-    if args.wgrad_accumulate and not training:
-        raise SystemExit("--wgrad-accumulate: the train workload only")
+    if (args.wgrad_accumulate or args.recompute_h) and not training:
+        raise SystemExit("--wgrad-accumulate, --recompute-h: the train workload only")
     layer = moe.Layer(T, d, I, E, k, training=training,
                       precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16,
-                      wgrad_accumulate=args.wgrad_accumulate)
+                      wgrad_accumulate=args.wgrad_accumulate, recompute_h=args.recompute_h)
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
@@ -399,7 +402,7 @@ def main():
 
     # dominant kernel: the longest stage
     dom = max(stage_us, key=stage_us.get)
-    gemm_flop = {"w13": 4.0 * R * I * d, "w2": 2.0 * R * I * d,
+    gemm_flop = {"w13": 4.0 * R * I * d, "w2": 2.0 * R * I * d, "recompute_h": 4.0 * R * I * d,
                  "dgrad_w2": 2.0 * R * I * d, "wgrad_w2": 2.0 * R * I * d,
                  "dgrad_w13": 4.0 * R * I * d, "wgrad_w13": 4.0 * R * I * d}
     # bytes each stage must move at least once
@@ -449,7 +452,8 @@ def main():
                 + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
         "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s" % (
             cfg_name, T, d, I, E, k, "MXFP8-E4M3" if mx else "BF16",
-            ("forward+backward (weight gradients accumulated)" if args.wgrad_accumulate else "forward+backward")
+            ("forward+backward" + (", weight gradients accumulated" if args.wgrad_accumulate else "")
+             + (", h recomputed in the backward" if args.recompute_h else ""))
             if training else
             ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward")),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,

@@ -82,6 +82,10 @@ typedef struct {
     int32_t wgrad_accumulate;  /* 1: moe_backward adds the weight gradients into dw13 / dw2
                                   (blog post, "What it is selling": in-place accumulation
                                   into the parameters' gradients); training plans only */
+    int32_t recompute_h;       /* 1: the training forward does not keep h = (g, u); the
+                                  backward recomputes it first, in memory the backward
+                                  reuses later (blog post, "Caveats": activation-slot
+                                  overflow selects recomputation); training plans only */
 } moe_config_t;
 
 typedef struct {
@@ -105,6 +109,15 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out);
 /* Bytes of device workspace the plan needs (the analogue of planning memory
  * before creating a context; blog post, "Caveats", item 7).  0 on NULL. */
 size_t moe_workspace_bytes(moe_plan_t plan);
+
+/* The plan's memory, as text (blog post, "Caveats" and "Bottom line": plan the memory
+ * and read its explanation before sizing the layer): one line per workspace region with
+ * its bytes, what it holds and whether it is kept from the training forward for the
+ * backward ("saved") or only used within a call ("scratch"), the totals, and the row
+ * limits.  Writes at most len - 1 characters and a terminating NUL into buf (when buf
+ * is not NULL and len > 0) and returns the length of the whole report, like snprintf;
+ * 0 for a NULL plan.  Host only. */
+size_t moe_plan_explain(moe_plan_t plan, char* buf, size_t len);
 
 /* Give the plan a device buffer of at least moe_workspace_bytes bytes,
  * 256-byte aligned; the caller keeps ownership and must keep it alive while
@@ -205,7 +218,7 @@ moe_status_t moe_get_status(moe_plan_t plan, int32_t* device_flags, int32_t clea
 const char* moe_status_string(moe_status_t status);
 
 /* Kernel stages of moe_forward / moe_backward.  moe_backward launches SCORE_GRAD,
- * DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order; the
+ * [RECOMPUTE_H,] DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order; the
  * one-token decode runs W2 and the combine as one kernel, recorded as DECODE_W2. */
 #define MOE_STAGE_DISPATCH 0
 #define MOE_STAGE_QUANT_X 1
@@ -221,7 +234,8 @@ const char* moe_status_string(moe_status_t status);
 #define MOE_STAGE_DECODE_W13 11
 #define MOE_STAGE_DECODE_W2 12
 #define MOE_STAGE_WGRAD_ROWS 13
-#define MOE_STAGE_COUNT 14
+#define MOE_STAGE_RECOMPUTE_H 14
+#define MOE_STAGE_COUNT 15
 
 /* Per-stage timing with HIP events, for measurement only.  While enabled,
  * moe_forward and moe_backward record a pair of HIP events around each kernel

@@ -9,6 +9,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <cstdio>
+#include <string>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -40,6 +42,7 @@ struct moe_plan_s {
     size_t ws_size;
     int num_cu;
     bool have_saved_forward;
+    bool h_aliased;                    // recompute_h: h occupies the dxp / xg / dys region
     // measurement-only event pairs around kernel stages (moe_profile)
     struct ProfRec { int stage; hipEvent_t a, b; };
     bool prof_on = false;
@@ -97,6 +100,8 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (c.training != 0 && c.training != 1) return MOE_ERR_INVALID_ARG;
     if (c.wgrad_accumulate != 0 && c.wgrad_accumulate != 1) return MOE_ERR_INVALID_ARG;
     if (c.wgrad_accumulate && !c.training) return MOE_ERR_UNSUPPORTED;
+    if (c.recompute_h != 0 && c.recompute_h != 1) return MOE_ERR_INVALID_ARG;
+    if (c.recompute_h && !c.training) return MOE_ERR_UNSUPPORTED;
     if (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_PREFILL && c.path != MOE_PATH_DECODE)
         return MOE_ERR_INVALID_ARG;
     if (c.d % 64 != 0 || c.I % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -134,11 +139,23 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     const bool mx = c.precision == MOE_MXFP8_E4M3;
     p->off_a = mx ? 0 : take(2 * (size_t)R * c.I);
     p->off_o = take(2 * (size_t)R * c.d);
-    p->off_h = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
+    const size_t h_bytes = 2 * (size_t)R * 2 * c.I;
+    p->off_h = (c.training && !c.recompute_h) ? take(h_bytes) : 0;
     p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
     p->off_dxp = c.training ? take(2 * (size_t)R * c.d) : 0;
     p->off_xg = c.training ? take(2 * (size_t)R * c.d) : 0;
     p->off_dys = c.training ? take(2 * (size_t)R * c.d) : 0;
+    p->h_aliased = false;
+    if (c.training && c.recompute_h) {
+        // the recomputed h lives from the start of the backward to DGRAD W2; dxp, xg and
+        // dys (consecutive) are first written after that, so h takes their place
+        if (h_bytes <= p->off_dys + 2 * (size_t)R * c.d - p->off_dxp) {
+            p->off_h = p->off_dxp;
+            p->h_aliased = true;
+        } else {
+            p->off_h = take(h_bytes);
+        }
+    }
     p->off_xq = mx ? take((size_t)c.T * c.d) : 0;
     p->off_xs = mx ? take((size_t)c.T * c.d / 32) : 0;
     p->off_aq = mx ? take((size_t)R * c.I) : 0;
@@ -156,6 +173,79 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
 }
 
 size_t moe_workspace_bytes(moe_plan_t p) { return p ? p->ws_bytes : 0; }
+
+size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
+    if (!p) return 0;
+    const moe_config_t& c = p->cfg;
+    const int64_t R = p->R;
+    const bool mx = c.precision == MOE_MXFP8_E4M3;
+    const bool gemms = !mx && !p->decode;
+    std::string out;
+    char line[512];
+    auto add = [&](const char* fmt, auto... args) {
+        std::snprintf(line, sizeof line, fmt, args...);
+        out += line;
+    };
+    add("moe plan: T=%d d=%d I=%d E=%d k=%d, %lld routed rows (T*k), %s, %s, %s path\n", c.T, c.d, c.I, c.E,
+        c.k, (long long)R, mx ? "MXFP8 E4M3" : "BF16", c.training ? "training" : "inference",
+        p->decode ? "decode (weight-streaming)" : "grouped-GEMM");
+    if (c.training)
+        add("options: weight gradients %s; h %s\n", c.wgrad_accumulate ? "accumulated" : "overwritten",
+            c.recompute_h ? (p->h_aliased ? "recomputed in the backward, in the dX / WGRAD-operand region"
+                                          : "recomputed in the backward, in a region of its own")
+                          : "saved by the forward");
+    add("workspace %zu bytes (%.1f MiB):\n", p->ws_bytes, p->ws_bytes / 1048576.0);
+    add("  %-10s %14s  %-8s %s\n", "region", "bytes", "kind", "holds");
+    const char* keep = c.training ? "saved" : "scratch";
+    auto region = [&](const char* name, size_t bytes, const char* kind, const char* what) {
+        if (bytes) add("  %-10s %14zu  %-8s %s\n", name, bytes, kind, what);
+    };
+    size_t saved = 0;
+    auto saved_region = [&](const char* name, size_t bytes, const char* what) {
+        region(name, bytes, keep, what);
+        if (c.training) saved += bytes;
+    };
+    region("status", sizeof(int32_t), "flags", "sticky device routing flags (moe_get_status)");
+    region("hist", sizeof(int32_t) * (size_t)(p->nchunks > 0 ? p->nchunks : 1) * c.E, "scratch",
+           "dispatch: per-chunk expert counts");
+    saved_region("m_indptr", sizeof(int32_t) * (size_t)(c.E + 1), "expert row offsets [E+1]");
+    saved_region("gather", sizeof(int32_t) * (size_t)R, "token of each routed row [R]");
+    saved_region("slots", sizeof(int32_t) * (size_t)R, "routed row of each (t, j) [T, k]");
+    saved_region("probs", sizeof(float) * (size_t)R, "score of each routed row [R]");
+    if (!mx) saved_region("a", 2 * (size_t)R * c.I, "SwiGLU output [R, I] BF16");
+    saved_region("o", 2 * (size_t)R * c.d, "expert outputs [R, d] BF16");
+    if (c.training) {
+        const size_t hb = 2 * (size_t)R * 2 * c.I;
+        if (c.recompute_h)
+            region("h", p->h_aliased ? 0 : hb, "backward", "W13 pre-activations (g, u) [R, 2I] BF16, recomputed");
+        else
+            saved_region("h", hb, "W13 pre-activations (g, u) [R, 2I] BF16");
+        region("dh", 2 * (size_t)R * 2 * c.I, "backward", "gradient w.r.t. (g, u) [R, 2I] BF16");
+        region("dxp", 2 * (size_t)R * c.d, "backward",
+               p->h_aliased ? "per-row input gradients [R, d] BF16 (first h, recomputed, with xg and dys)"
+                            : "per-row input gradients [R, d] BF16");
+        region("xg", 2 * (size_t)R * c.d, "backward", "x[gather] [R, d] BF16 (weight-gradient operand)");
+        region("dys", 2 * (size_t)R * c.d, "backward", "probs * dy[gather] [R, d] BF16 (weight-gradient operand)");
+    }
+    if (mx) {
+        region("xq", (size_t)c.T * c.d, "scratch", "E4M3 codes of x [T, d]");
+        region("xs", (size_t)c.T * c.d / 32, "scratch", "E8M0 scales of x [T, d/32]");
+        region("aq", (size_t)R * c.I, "scratch", "E4M3 codes of a [R, I]");
+        region("as", (size_t)R * c.I / 32, "scratch", "E8M0 scales of a (block-major)");
+    }
+    region("split", sizeof(int32_t) * 4 * (kMaxPieces / 2 + 1), "scratch", "split weight-gradient tiles");
+    if (gemms && c.training)
+        region("part", kGemmPartBytes, "backward", "FP32 partial sums of split weight-gradient tiles");
+    add("kept from the training forward for the backward: %zu bytes (%.1f MiB)\n", saved, saved / 1048576.0);
+    add("limits: T*k <= %lld routed rows, E <= %d, k <= %d, d and I multiples of 64\n",
+        (long long)kMaxRoutedRows, kMaxExperts, kMaxTopK);
+    if (buf && len > 0) {
+        const size_t n = out.size() < len - 1 ? out.size() : len - 1;
+        std::memcpy(buf, out.data(), n);
+        buf[n] = '\0';
+    }
+    return out.size();
+}
 
 moe_status_t moe_bind_workspace(moe_plan_t p, void* dptr, size_t bytes) {
     if (!p || !dptr) return MOE_ERR_INVALID_ARG;
@@ -302,7 +392,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     g.w13 = static_cast<const uint16_t*>(w->w13);
     g.w2 = static_cast<const uint16_t*>(w->w2);
     g.out = p->at<uint16_t>(p->off_a);
-    g.out_h = c.training ? p->at<uint16_t>(p->off_h) : nullptr;
+    g.out_h = (c.training && !c.recompute_h) ? p->at<uint16_t>(p->off_h) : nullptr;
     e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm(FWD_W13, g, p->num_cu, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
     g.a = p->at<uint16_t>(p->off_a);
@@ -399,6 +489,15 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
                                  p->at<int32_t>(p->off_status), s)) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
+        if (c.recompute_h) {
+            // h again from x and W13 (the same kernel and inputs as the forward, so the
+            // same values); a is rewritten with what it holds
+            GemmArgs gr = g;
+            gr.out = p->at<uint16_t>(p->off_a);
+            gr.out_h = p->at<uint16_t>(p->off_h);
+            e = staged(p, MOE_STAGE_RECOMPUTE_H, s, [&] { return launch_gemm(FWD_W13, gr, p->num_cu, s); });
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
         // input gradients first, each consumer right after its producer, so that dh and
         // dxp are still in the memory-side cache when they are read back
         g.out = p->at<uint16_t>(p->off_dh);

@@ -38,11 +38,11 @@ MOE_DEV_BAD_INDPTR = 4
 # every symbol include/moe.h declares
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_destroy",
            "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward", "moe_forward_routed",
-           "moe_backward", "moe_get_status", "moe_status_string", "moe_profile",
+           "moe_backward", "moe_get_status", "moe_status_string", "moe_profile", "moe_plan_explain",
            "moe_profile_read")
 
 STAGES = ("dispatch", "quant_x", "w13", "w2", "combine", "score_grad", "dgrad_w2", "wgrad_w2",
-          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows")
+          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows", "recompute_h")
 
 
 class MoeError(RuntimeError):
@@ -55,7 +55,7 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("training", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("wgrad_accumulate", ctypes.c_int32)]
+                ("wgrad_accumulate", ctypes.c_int32), ("recompute_h", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -79,6 +79,8 @@ def lib():
         L.moe_plan.restype = ctypes.c_int
         L.moe_workspace_bytes.argtypes = [vp]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_plan_explain.argtypes = [vp, ctypes.c_char_p, ctypes.c_size_t]
+        L.moe_plan_explain.restype = ctypes.c_size_t
         L.moe_bind_workspace.argtypes = [vp, vp, ctypes.c_size_t]
         L.moe_bind_workspace.restype = ctypes.c_int
         L.moe_plan_destroy.argtypes = [vp]
@@ -120,8 +122,8 @@ def _ok(status: int, where: str):
 
 
 def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO,
-             wgrad_accumulate=0) -> int:
-    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate)
+             wgrad_accumulate=0, recompute_h=0) -> int:
+    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate, recompute_h)
     h = ctypes.c_void_p()
     _ok(lib().moe_plan(ctypes.byref(cfg), ctypes.byref(h)), "moe_plan")
     return h.value
@@ -129,6 +131,13 @@ def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO,
 
 def moe_workspace_bytes(plan: int) -> int:
     return int(lib().moe_workspace_bytes(plan))
+
+
+def moe_plan_explain(plan: int) -> str:
+    n = int(lib().moe_plan_explain(plan, None, 0))
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().moe_plan_explain(plan, buf, n + 1)
+    return buf.value.decode()
 
 
 def moe_bind_workspace(plan: int, ptr: int, nbytes: int):
@@ -209,15 +218,18 @@ class Layer:
     """One plan plus its torch-allocated workspace; all compute goes through libmoe."""
 
     def __init__(self, T, d, I, E, k, precision=MOE_BF16, training=False, path=MOE_PATH_AUTO,
-                 device="cuda", wgrad_accumulate=False):
+                 device="cuda", wgrad_accumulate=False, recompute_h=False):
         import torch
         self.T, self.d, self.I, self.E, self.k = T, d, I, E, k
         self.precision = precision
         self.plan = moe_plan(T, d, I, E, k, precision, int(bool(training)), path,
-                             int(bool(wgrad_accumulate)))
+                             int(bool(wgrad_accumulate)), int(bool(recompute_h)))
         nbytes = moe_workspace_bytes(self.plan)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         moe_bind_workspace(self.plan, _ptr(self.workspace), self.workspace.numel())
+
+    def explain(self) -> str:
+        return moe_plan_explain(self.plan)
 
     def close(self):
         if self.plan:

@@ -69,10 +69,14 @@ def test_status_strings(L):
     (dict(T=64, d=256, I=128, E=8, k=2, training=1, wgrad_accumulate=1), moe.MOE_OK),
     (dict(T=64, d=256, I=128, E=8, k=2, wgrad_accumulate=1), moe.MOE_ERR_UNSUPPORTED),  # no backward
     (dict(T=64, d=256, I=128, E=8, k=2, training=1, wgrad_accumulate=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=64, d=256, I=128, E=8, k=2, training=1, recompute_h=1), moe.MOE_OK),
+    (dict(T=64, d=256, I=128, E=8, k=2, recompute_h=1), moe.MOE_ERR_UNSUPPORTED),     # nothing to recompute
+    (dict(T=64, d=256, I=128, E=8, k=2, training=1, recompute_h=-1), moe.MOE_ERR_INVALID_ARG),
 ])
 def test_plan_validation(L, cfg, expect):
     c = moe.MoeConfig(cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"], cfg.get("precision", 0),
-                      cfg.get("training", 0), cfg.get("path", 0), cfg.get("wgrad_accumulate", 0))
+                      cfg.get("training", 0), cfg.get("path", 0), cfg.get("wgrad_accumulate", 0),
+                      cfg.get("recompute_h", 0))
     h = ctypes.c_void_p()
     st = L.moe_plan(ctypes.byref(c), ctypes.byref(h))
     assert st == expect
@@ -148,3 +152,39 @@ def test_oracle_and_library_share_nothing():
     with open(os.path.join(ROOT, "oracle", "__init__.py")) as f:
         src = f.read()
     assert "mixture_experts_routed_dispatch_amd" not in src
+
+
+def test_plan_explain_and_recompute_workspace(L):
+    """The report names every region with its bytes and the total the plan asks for; a
+    training plan that recomputes h needs R * 2I * 2 bytes less (h takes the place of the
+    backward's dX / weight-gradient operands), which the report says."""
+    T, d, I, E, k = 8192, 2048, 768, 128, 8
+    keep = moe.moe_plan(T, d, I, E, k, training=1)
+    rec = moe.moe_plan(T, d, I, E, k, training=1, recompute_h=1)
+    inf = moe.moe_plan(T, d, I, E, k, training=0)
+    try:
+        R = T * k
+        assert moe.moe_workspace_bytes(keep) - moe.moe_workspace_bytes(rec) == 2 * R * 2 * I
+        for plan in (keep, rec, inf):
+            text = moe.moe_plan_explain(plan)
+            assert ("workspace %d bytes" % moe.moe_workspace_bytes(plan)) in text
+            for name in ("m_indptr", "gather", "slots", "probs", "o"):
+                assert "\n  %s " % name in text
+            assert "limits: T*k <= 131072" in text
+            assert len(text) == int(L.moe_plan_explain(ctypes.c_void_p(plan), None, 0))
+        t_keep, t_rec = moe.moe_plan_explain(keep), moe.moe_plan_explain(rec)
+        assert "h saved by the forward" in t_keep and "\n  h " in t_keep
+        assert "h recomputed in the backward, in the dX / WGRAD-operand region" in t_rec
+        assert "\n  h " not in t_rec
+        # saved bytes: the dispatch, a and o (and h unless recomputed)
+        saved = lambda t: int(t.split("kept from the training forward for the backward: ")[1].split(" ")[0])
+        assert saved(t_keep) - saved(t_rec) == 2 * R * 2 * I
+        assert saved(moe.moe_plan_explain(inf)) == 0
+        # truncation: at most len - 1 characters and a NUL
+        buf = ctypes.create_string_buffer(20)
+        n = L.moe_plan_explain(ctypes.c_void_p(keep), buf, 20)
+        assert n == len(t_keep) and buf.value.decode() == t_keep[:19]
+        assert L.moe_plan_explain(None, None, 0) == 0
+    finally:
+        for plan in (keep, rec, inf):
+            moe.moe_plan_destroy(plan)

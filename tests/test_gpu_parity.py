@@ -566,6 +566,32 @@ def test_backward_accumulates_weight_gradients(torch_cuda, T, d, I, E, k, routin
     layer.close()
 
 
+@pytest.mark.parametrize("T,d,I,E,k,routing", [(400, 512, 384, 6, 3, "uniform"),     # h in the dX region
+                                               (300, 128, 256, 8, 2, "uniform"),     # 2I > 3d: own region
+                                               (300, 256, 128, 128, 8, "zipf")])
+def test_backward_recompute_h_matches_saved(torch_cuda, T, d, I, E, k, routing):
+    """recompute_h: the forward keeps no h and the backward recomputes it with the same
+    kernel from the same x and W13, so every gradient equals, bit for bit, that of a plan
+    that saved h (which the other backward tests check against the oracle)."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("backward recompute h", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=43, with_dy=True)
+    t = device_inputs(inp)
+    outs = []
+    for rec in (False, True):
+        layer = moe.Layer(T, d, I, E, k, training=True, recompute_h=rec)
+        y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+        assert layer.status()[1] == 0
+        outs.append([v.clone() for v in (y, dx, dw13, dw2, ds)])
+        layer.close()
+    for name, a, b in zip(("y", "dx", "dw13", "dw2", "ds"), outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b), name
+
+
 def test_no_tokens(torch_cuda):
     """T = 0: the forward writes nothing and succeeds; the backward gives all-zero weight
     gradients (every expert is empty)."""
