@@ -51,9 +51,9 @@ def _L():
         lib.orc_num_threads.restype = ctypes.c_int
         lib.orc_check_routing.argtypes = [i32, i32, i32, vp]
         lib.orc_dispatch.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp]
-        lib.orc_forward_tokens.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, vp, vp]
-        lib.orc_backward_tokens.argtypes = [i32] * 5 + [vp] * 6 + [i32, vp, vp, vp]
-        lib.orc_wgrad_cols.argtypes = [i32] * 5 + [vp] * 6 + [i32, vp, vp, vp]
+        lib.orc_forward_tokens.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, vp, vp, i32]
+        lib.orc_backward_tokens.argtypes = [i32] * 5 + [vp] * 6 + [i32, vp, vp, vp, i32]
+        lib.orc_wgrad_cols.argtypes = [i32] * 5 + [vp] * 6 + [i32, vp, vp, vp, i32]
         lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.orc_e4m3_decode.restype = ctypes.c_double
         lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
@@ -62,7 +62,7 @@ def _L():
         lib.orc_mx_scale_byte.restype = ctypes.c_uint8
         lib.orc_mx_quantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         lib.orc_mx_dequantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
-        lib.orc_forward_tokens_mx.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp]
+        lib.orc_forward_tokens_mx.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, i32]
         _lib = lib
     return _lib
 
@@ -127,8 +127,12 @@ def _shapes(x, w13, w2, ids):
     return T, d, I, E, ids.shape[1]
 
 
-def forward_tokens(x, ids, scores, w13, w2, toks=None, want_o=False, want_a=False):
-    """y for the listed tokens ([ntok, d] float64); optionally o [ntok,k,d] and a [ntok,k,I]."""
+ACT_SWIGLU, ACT_GEGLU, ACT_REGLU = 0, 1, 2
+
+
+def forward_tokens(x, ids, scores, w13, w2, toks=None, want_o=False, want_a=False, act=ACT_SWIGLU):
+    """y for the listed tokens ([ntok, d] float64); optionally o [ntok,k,d] and a [ntok,k,I].
+    act: the gated activation (0 SwiGLU, 1 GeGLU with the exact GELU, 2 ReGLU)."""
     xf, w13f, w2f = _f32(x), _f32(w13), _f32(w2)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     scores = np.ascontiguousarray(scores, dtype=np.float32)
@@ -140,7 +144,7 @@ def forward_tokens(x, ids, scores, w13, w2, toks=None, want_o=False, want_a=Fals
     a = np.zeros((n, k, I), np.float64) if want_a else None
     _check(_L().orc_forward_tokens(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f), _p(w2f),
                                    n, _p(toks), _p(y), _p(o) if o is not None else None,
-                                   _p(a) if a is not None else None))
+                                   _p(a) if a is not None else None, int(act)))
     out = [y]
     if want_o:
         out.append(o)
@@ -149,7 +153,7 @@ def forward_tokens(x, ids, scores, w13, w2, toks=None, want_o=False, want_a=Fals
     return out[0] if len(out) == 1 else tuple(out)
 
 
-def backward_tokens(x, ids, scores, w13, w2, dy, toks=None):
+def backward_tokens(x, ids, scores, w13, w2, dy, toks=None, act=ACT_SWIGLU):
     """(dX [ntok, d], dS [ntok, k]) in float64 for the listed tokens."""
     xf, w13f, w2f, dyf = _f32(x), _f32(w13), _f32(w2), _f32(dy)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
@@ -160,11 +164,11 @@ def backward_tokens(x, ids, scores, w13, w2, dy, toks=None):
     dx = np.zeros((n, d), np.float64)
     ds = np.zeros((n, k), np.float64)
     _check(_L().orc_backward_tokens(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f), _p(w2f),
-                                    _p(dyf), n, _p(toks), _p(dx), _p(ds)))
+                                    _p(dyf), n, _p(toks), _p(dx), _p(ds), int(act)))
     return dx, ds
 
 
-def wgrad_cols(x, ids, scores, w13, w2, dy, icols=None):
+def wgrad_cols(x, ids, scores, w13, w2, dy, icols=None, act=ACT_SWIGLU):
     """Weight gradients on intermediate columns icols (all by default).
 
     Returns (dW2[:, :, icols] as [E, d, ni], dW13 rows (icols, I+icols) as [E, 2, ni, d]).
@@ -178,7 +182,7 @@ def wgrad_cols(x, ids, scores, w13, w2, dy, icols=None):
     dw2 = np.zeros((E, d, ni), np.float64)
     dw13 = np.zeros((E, 2, ni, d), np.float64)
     _check(_L().orc_wgrad_cols(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f), _p(w2f),
-                               _p(dyf), ni, _p(icols), _p(dw2), _p(dw13)))
+                               _p(dyf), ni, _p(icols), _p(dw2), _p(dw13), int(act)))
     return dw2, dw13
 
 
@@ -217,8 +221,8 @@ def mx_dequantize(codes, scales) -> np.ndarray:
     return out
 
 
-def forward_tokens_mx(x, ids, scores, w13, w2, toks=None):
-    """y with x and the SwiGLU output passed through MX block-32 quantize/dequantize."""
+def forward_tokens_mx(x, ids, scores, w13, w2, toks=None, act=ACT_SWIGLU):
+    """y with x and the gated-activation output passed through MX block-32 quantize/dequantize."""
     xf, w13f, w2f = _f32(x), _f32(w13), _f32(w2)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     scores = np.ascontiguousarray(scores, dtype=np.float32)
@@ -227,5 +231,5 @@ def forward_tokens_mx(x, ids, scores, w13, w2, toks=None):
     n = len(toks)
     y = np.zeros((n, d), np.float64)
     _check(_L().orc_forward_tokens_mx(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f),
-                                      _p(w2f), n, _p(toks), _p(y)))
+                                      _p(w2f), n, _p(toks), _p(y), int(act)))
     return y

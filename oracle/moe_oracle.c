@@ -33,6 +33,7 @@
  *     (a stable counting sort of the flattened (t, j) list by expert id);
  *   - W13 is [E, 2I, d]: gate rows [0, I), up rows [I, 2I);
  *   - SwiGLU is silu(gate) * up with silu(z) = z / (1 + exp(-z)), no clamp;
+ *     GeGLU uses the exact (erf) GELU, ReGLU max(z, 0);
  *   - scores weight the expert outputs in the combine, without renormalising;
  *   - dS[t][j] = <dY[t], o_(t,j)> with o the unscaled expert output.
  */
@@ -52,6 +53,33 @@ int orc_num_threads(void) { return omp_get_max_threads(); }
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* Gated activations of the W13 output ([NV] "Supported kernel surface": SwiGLU,
+ * GeGLU and ReGLU FC1 epilogues): a = f(g) * u with
+ *   act 0 (SwiGLU): f(z) = silu(z) = z / (1 + e^-z)
+ *   act 1 (GeGLU):  f(z) = gelu(z) = z Phi(z) = z (1 + erf(z / sqrt 2)) / 2   (exact GELU)
+ *   act 2 (ReGLU):  f(z) = relu(z) = max(z, 0)
+ * and f' for the backward:
+ *   silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *   gelu'(z) = Phi(z) + z phi(z), phi(z) = e^(-z^2/2) / sqrt(2 pi)
+ *   relu'(z) = 1 for z > 0, else 0. */
+#define ORC_ACT_SWIGLU 0
+#define ORC_ACT_GEGLU 1
+#define ORC_ACT_REGLU 2
+static double act_f(int act, double z)
+{
+    if (act == ORC_ACT_GEGLU) return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+    if (act == ORC_ACT_REGLU) return z > 0.0 ? z : 0.0;
+    return silu(z);
+}
+static double act_df(int act, double z)
+{
+    if (act == ORC_ACT_GEGLU)
+        return 0.5 * (1.0 + erf(z / sqrt(2.0))) + z * exp(-0.5 * z * z) / sqrt(2.0 * acos(-1.0));
+    if (act == ORC_ACT_REGLU) return z > 0.0 ? 1.0 : 0.0;
+    const double sg = sigmoid(z);
+    return sg * (1.0 + z * (1.0 - sg));
+}
 
 /* Routing precondition ([NV] "MoE layer": each token row holds distinct expert
  * indices, all in [0, E)).  Returns ORC_OK, ORC_ERR_RANGE or ORC_ERR_DUPLICATE. */
@@ -106,9 +134,9 @@ int orc_dispatch(int T, int E, int k, const int32_t* ids, const float* scores,
 }
 
 /* One expert MLP applied to one token ([DM] "What it is selling": W13 ->
- * SwiGLU -> W2).  g[i] = W1_e[i].x, u[i] = W3_e[i].x, a = silu(g)*u,
+ * SwiGLU -> W2).  g[i] = W1_e[i].x, u[i] = W3_e[i].x, a = f(g)*u (act_f),
  * o[n] = W2_e[n].a.  Any of g/u/a may be used by the caller afterwards. */
-static void expert_mlp(int d, int I, const float* x_t, const float* w13_e, const float* w2_e,
+static void expert_mlp(int act, int d, int I, const float* x_t, const float* w13_e, const float* w2_e,
                        double* g, double* u, double* a, double* o)
 {
     for (int i = 0; i < I; ++i) {
@@ -121,7 +149,7 @@ static void expert_mlp(int d, int I, const float* x_t, const float* w13_e, const
         }
         g[i] = sg;
         u[i] = su;
-        a[i] = silu(sg) * su;
+        a[i] = act_f(act, sg) * su;
     }
     if (o) {
         for (int n = 0; n < d; ++n) {
@@ -143,7 +171,7 @@ int orc_forward_tokens(int T, int d, int I, int E, int k,
                        const float* x, const int32_t* ids, const float* scores,
                        const float* w13, const float* w2,
                        int ntok, const int32_t* toks,
-                       double* y, double* o_out, double* a_out)
+                       double* y, double* o_out, double* a_out, int act)
 {
     int rc = orc_check_routing(T, E, k, ids);
     if (rc != ORC_OK) return rc;
@@ -164,7 +192,7 @@ int orc_forward_tokens(int T, int d, int I, int E, int k,
         for (int j = 0; j < k; ++j) {
             int e = ids[(size_t)t * k + j];
             double s = (double)scores[(size_t)t * k + j];
-            expert_mlp(d, I, x_t, w13 + (size_t)e * 2 * I * d, w2 + (size_t)e * d * I, g, u, a, o);
+            expert_mlp(act, d, I, x_t, w13 + (size_t)e * 2 * I * d, w2 + (size_t)e * d * I, g, u, a, o);
             for (int n = 0; n < d; ++n) y_t[n] += s * o[n];
             if (o_out) memcpy(o_out + ((size_t)q * k + j) * d, o, sizeof(double) * (size_t)d);
             if (a_out) memcpy(a_out + ((size_t)q * k + j) * I, a, sizeof(double) * (size_t)I);
@@ -180,14 +208,14 @@ int orc_forward_tokens(int T, int d, int I, int E, int k,
  *   dS[t][j] = <dY[t], o>                       (y is linear in s)
  *   dO       = s * dY[t]
  *   dA[i]    = sum_n W2_e[n][i] dO[n]
- *   dg[i]    = dA[i] * u[i] * sigmoid(g[i]) * (1 + g[i] (1 - sigmoid(g[i])))
- *   du[i]    = dA[i] * silu(g[i])
+ *   dg[i]    = dA[i] * u[i] * f'(g[i])      (SwiGLU: f' = sigmoid (1 + g (1 - sigmoid)))
+ *   du[i]    = dA[i] * f(g[i])
  *   dX[t]   += W1_e^T dg + W3_e^T du
  * dx is [ntok, d], ds is [ntok, k]. */
 int orc_backward_tokens(int T, int d, int I, int E, int k,
                         const float* x, const int32_t* ids, const float* scores,
                         const float* w13, const float* w2, const float* dy,
-                        int ntok, const int32_t* toks, double* dx, double* ds)
+                        int ntok, const int32_t* toks, double* dx, double* ds, int act)
 {
     int rc = orc_check_routing(T, E, k, ids);
     if (rc != ORC_OK) return rc;
@@ -211,7 +239,7 @@ int orc_backward_tokens(int T, int d, int I, int E, int k,
             double s = (double)scores[(size_t)t * k + j];
             const float* w13_e = w13 + (size_t)e * 2 * I * d;
             const float* w2_e = w2 + (size_t)e * d * I;
-            expert_mlp(d, I, x_t, w13_e, w2_e, g, u, a, o);
+            expert_mlp(act, d, I, x_t, w13_e, w2_e, g, u, a, o);
             double dot = 0.0;
             for (int n = 0; n < d; ++n) dot += (double)dy_t[n] * o[n];
             ds[(size_t)q * k + j] = dot;
@@ -219,9 +247,8 @@ int orc_backward_tokens(int T, int d, int I, int E, int k,
                 double dA = 0.0;
                 for (int n = 0; n < d; ++n)
                     dA += (double)w2_e[(size_t)n * I + i] * (s * (double)dy_t[n]);
-                double sg = sigmoid(g[i]);
-                dg[i] = dA * u[i] * sg * (1.0 + g[i] * (1.0 - sg));
-                du[i] = dA * silu(g[i]);
+                dg[i] = dA * u[i] * act_df(act, g[i]);
+                du[i] = dA * act_f(act, g[i]);
             }
             for (int c = 0; c < d; ++c) {
                 double acc = 0.0;
@@ -247,7 +274,7 @@ int orc_backward_tokens(int T, int d, int I, int E, int k,
 int orc_wgrad_cols(int T, int d, int I, int E, int k,
                    const float* x, const int32_t* ids, const float* scores,
                    const float* w13, const float* w2, const float* dy,
-                   int ni, const int32_t* icols, double* dw2, double* dw13)
+                   int ni, const int32_t* icols, double* dw2, double* dw13, int act)
 {
     int rc = orc_check_routing(T, E, k, ids);
     if (rc != ORC_OK) return rc;
@@ -283,12 +310,11 @@ int orc_wgrad_cols(int T, int d, int I, int E, int k,
                         sg += (double)wg[c] * (double)x_t[c];
                         su += (double)wu[c] * (double)x_t[c];
                     }
-                    aq[q] = silu(sg) * su;
+                    aq[q] = act_f(act, sg) * su;
                     double dA = 0.0;
                     for (int n = 0; n < d; ++n) dA += (double)w2_e[(size_t)n * I + i] * dO[n];
-                    double sgm = sigmoid(sg);
-                    dgq[q] = dA * su * sgm * (1.0 + sg * (1.0 - sgm));
-                    duq[q] = dA * silu(sg);
+                    dgq[q] = dA * su * act_df(act, sg);
+                    duq[q] = dA * act_f(act, sg);
                 }
                 for (int n = 0; n < d; ++n)
                     for (int q = 0; q < ni; ++q) dw2_e[(size_t)n * ni + q] += dO[n] * aq[q];
@@ -397,7 +423,7 @@ void orc_mx_dequantize(int64_t rows, int K, const uint8_t* codes, const uint8_t*
 int orc_forward_tokens_mx(int T, int d, int I, int E, int k,
                           const float* x, const int32_t* ids, const float* scores,
                           const float* w13, const float* w2,
-                          int ntok, const int32_t* toks, double* y)
+                          int ntok, const int32_t* toks, double* y, int act)
 {
     int rc = orc_check_routing(T, E, k, ids);
     if (rc != ORC_OK) return rc;
@@ -431,7 +457,7 @@ int orc_forward_tokens_mx(int T, int d, int I, int E, int k,
             double s = (double)scores[(size_t)t * k + j];
             const float* w13_e = w13 + (size_t)e * 2 * I * d;
             const float* w2_e = w2 + (size_t)e * d * I;
-            expert_mlp(d, I, xq, w13_e, w2_e, g, u, a, NULL);
+            expert_mlp(act, d, I, xq, w13_e, w2_e, g, u, a, NULL);
             for (int b = 0; b < I / 32; ++b) {
                 uint8_t sb = orc_mx_scale_byte(a + b * 32, 32);
                 double X = ldexp(1.0, (int)sb - 127);

@@ -29,12 +29,12 @@ def small_case(seed, T=12, d=64, I=32, E=5, k=2, routing="uniform"):
     return inp
 
 
-def loss(orc, x, ids, s, w13, w2, dy):
-    y = orc.forward_tokens(x, ids, s, w13, w2)
+def loss(orc, x, ids, s, w13, w2, dy, act=0):
+    y = orc.forward_tokens(x, ids, s, w13, w2, act=act)
     return float((y * dy.astype(np.float64)).sum())
 
 
-def fd(orc, inp, which, v):
+def fd(orc, inp, which, v, act=0):
     base = dict(x=f32(inp.x), s=inp.scores, w13=f32(inp.w13), w2=f32(inp.w2))
     dyf = f32(inp.dy)
     vals = []
@@ -43,28 +43,44 @@ def fd(orc, inp, which, v):
         pert = (base[which].astype(np.float64) + sign * H * v)
         assert np.array_equal(pert.astype(np.float32).astype(np.float64), pert)  # exact in f32
         args[which] = pert.astype(np.float32)
-        vals.append(loss(orc, args["x"], inp.ids, args["s"], args["w13"], args["w2"], dyf))
+        vals.append(loss(orc, args["x"], inp.ids, args["s"], args["w13"], args["w2"], dyf, act))
     return (vals[0] - vals[1]) / (2 * H)
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_finite_differences(orc, seed):
+@pytest.mark.parametrize("seed,act", [(0, 0), (1, 0), (0, 1), (1, 2)])
+def test_finite_differences(orc, seed, act):
     inp = small_case(seed)
     rng = np.random.default_rng(100 + seed)
-    dx, ds = orc.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
-    dw2, dw13 = orc.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    if act == 2:
+        # relu has a kink at 0: no routed gate may cross it under the perturbations, whose
+        # effect on a gate is at most h * sum|w| (x moved) or h * sum|x| (W1 moved)
+        x64, w64 = f32(inp.x).astype(np.float64), f32(inp.w13).astype(np.float64)
+        g = np.einsum("td,eid->tei", x64, w64[:, :inp.I])
+        gmin = min(np.abs(g[t, e]).min() for t in range(inp.T) for e in inp.ids[t])
+        step = H * max(np.abs(w64[:, :inp.I]).sum(axis=2).max(), np.abs(x64).sum(axis=1).max())
+        assert gmin > 2 * step, (gmin, step)
+    dx, ds = orc.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
+    dw2, dw13 = orc.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
     E, d, I = inp.E, inp.d, inp.I
     dw13_full = dw13.reshape(E, 2 * I, d)          # [E, 2, I, d] with all columns = [E, 2I, d]
     grads = {"x": dx, "s": ds, "w13": dw13_full, "w2": dw2}
     shapes = {"x": inp.x.shape, "s": inp.scores.shape, "w13": inp.w13.shape, "w2": inp.w2.shape}
     for which in ("x", "s", "w13", "w2"):
         v = rng.integers(-1, 2, size=shapes[which]).astype(np.float64)
-        num = fd(orc, inp, which, v)
+        num = fd(orc, inp, which, v, act)
         ana = float((grads[which] * v).sum())
         assert abs(num - ana) <= 1e-6 * max(1.0, abs(ana)), (which, num, ana)
 
 
-def test_dense_case_against_torch_autograd(orc):
+ACT_TORCH = {0: torch.nn.functional.silu,
+             1: lambda z: torch.nn.functional.gelu(z, approximate="none"),
+             2: torch.nn.functional.relu}
+
+
+@pytest.mark.parametrize("act", [0, 1, 2])
+def test_dense_case_against_torch_autograd(orc, act):
+    """E = 1, k = 1: the layer is a dense gated MLP; torch float64 autograd (silu, the
+    exact gelu, relu) gives every gradient."""
     inp = small_case(3, T=9, d=64, I=32, E=1, k=1)
     s = np.ones((inp.T, 1), np.float32) * np.float32(0.625)
     xf, w13f, w2f, dyf = f32(inp.x), f32(inp.w13[0]), f32(inp.w2[0]), f32(inp.dy)
@@ -73,11 +89,11 @@ def test_dense_case_against_torch_autograd(orc):
     W3 = torch.tensor(w13f[32:], dtype=torch.float64, requires_grad=True)
     W2 = torch.tensor(w2f, dtype=torch.float64, requires_grad=True)
     S = torch.tensor(s[:, 0].astype(np.float64), requires_grad=True)
-    o = (torch.nn.functional.silu(X @ W1.T) * (X @ W3.T)) @ W2.T
+    o = (ACT_TORCH[act](X @ W1.T) * (X @ W3.T)) @ W2.T
     y = S[:, None] * o
     (y * torch.tensor(dyf, dtype=torch.float64)).sum().backward()
-    dx, ds = orc.backward_tokens(inp.x, inp.ids, s, inp.w13, inp.w2, inp.dy)
-    dw2, dw13 = orc.wgrad_cols(inp.x, inp.ids, s, inp.w13, inp.w2, inp.dy)
+    dx, ds = orc.backward_tokens(inp.x, inp.ids, s, inp.w13, inp.w2, inp.dy, act=act)
+    dw2, dw13 = orc.wgrad_cols(inp.x, inp.ids, s, inp.w13, inp.w2, inp.dy, act=act)
     np.testing.assert_allclose(dx, X.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(ds[:, 0], S.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dw2[0], W2.grad.numpy(), rtol=1e-11, atol=1e-12)

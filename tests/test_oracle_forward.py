@@ -112,6 +112,36 @@ def test_silu_closed_forms(orc):
     assert abs(run(-64.0, 1.0)) < 1e-25
 
 
+@pytest.mark.parametrize("act", [1, 2])
+def test_gated_activation_closed_forms(orc, act):
+    """d = I = 1, W3 = W2 = 1, x = 1: y = f(w1).  GeGLU (act 1) takes the exact GELU,
+    f(z) = z Phi(z) with Phi the standard normal CDF (scipy); ReGLU (act 2) max(z, 0)."""
+    from scipy.stats import norm
+    def run(w1):
+        xb = inputs.to_bf16_bits(np.array([[1.0]], np.float32))
+        w13 = inputs.to_bf16_bits(np.array([[[w1], [1.0]]], np.float32))
+        w2 = inputs.to_bf16_bits(np.array([[[1.0]]], np.float32))
+        return orc.forward_tokens(xb, np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32),
+                                  w13, w2, act=act)[0, 0]
+    for z in (-4.0, -2.5, -1.0, -0.375, 0.0, 0.25, 1.0, 1.5, 3.0):
+        want = z * norm.cdf(z) if act == 1 else max(z, 0.0)
+        assert abs(run(z) - want) <= 1e-15 * max(1.0, abs(want)), (z, run(z), want)
+
+
+@pytest.mark.parametrize("act,fn", [(1, lambda z: torch.nn.functional.gelu(z, approximate="none")),
+                                    (2, torch.nn.functional.relu)])
+def test_dense_identity_other_activations(orc, act, fn):
+    # E = 1, k = 1, s = 1 with GeGLU / ReGLU: the dense gated MLP in torch float64
+    inp = inputs.generate(T=37, d=96, I=40, E=1, k=1, seed=3)
+    scores = np.ones((inp.T, 1), np.float32)
+    y = orc.forward_tokens(inp.x, inp.ids, scores, inp.w13, inp.w2, act=act)
+    w13 = f32(inp.w13[0])
+    x = torch.from_numpy(f32(inp.x)).double()
+    ref = (fn(x @ torch.from_numpy(w13[:40]).double().T) * (x @ torch.from_numpy(w13[40:]).double().T)) \
+        @ torch.from_numpy(f32(inp.w2[0])).double().T
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def test_golden_hand_example(orc):
     with open(os.path.join(GOLDEN, "forward_tiny.json")) as f:
         g = json.load(f)
