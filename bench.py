@@ -60,6 +60,8 @@ def parse():
     ap.add_argument("--recompute-h", action="store_true",
                     help="train workload: the forward keeps no h, the backward recomputes it "
                          "(plan option recompute_h)")
+    ap.add_argument("--activation", default="swiglu", choices=("swiglu", "geglu", "reglu"),
+                    help="gated activation of the W13 output (plan option activation)")
     ap.add_argument("--library-gemm", action="store_true",
                     help="time the vendor library's BF16 GEMMs (hipBLASLt through torch) on the "
                          "workload's expert-product shapes with uniform rows per expert, and a "
@@ -288,7 +290,8 @@ def main():
         raise SystemExit("--wgrad-accumulate, --recompute-h: the train workload only")
     layer = moe.Layer(T, d, I, E, k, training=training,
                       precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16,
-                      wgrad_accumulate=args.wgrad_accumulate, recompute_h=args.recompute_h)
+                      wgrad_accumulate=args.wgrad_accumulate, recompute_h=args.recompute_h,
+                      activation=("swiglu", "geglu", "reglu").index(args.activation))
     stream = torch.cuda.current_stream()
     sp = int(stream.cuda_stream)
     y = torch.empty((T, d), dtype=torch.bfloat16, device="cuda")
@@ -450,12 +453,13 @@ def main():
                 + ", softmax-of-normal scores"
                 + ("; 16 routings over disjoint expert groups, cycled" if cfg_name == "decode1" else "")
                 + ("; 4 copies of the weights, rotated" if cfg_name == "decode32" else ""),
-        "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s" % (
+        "config": {"workload": "%s: T=%d d=%d I=%d E=%d k=%d %s %s%s" % (
             cfg_name, T, d, I, E, k, "MXFP8-E4M3" if mx else "BF16",
             ("forward+backward" + (", weight gradients accumulated" if args.wgrad_accumulate else "")
              + (", h recomputed in the backward" if args.recompute_h else ""))
             if training else
-            ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward")),
+            ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward"),
+            "" if args.activation == "swiglu" else ", %s" % {"geglu": "GeGLU", "reglu": "ReGLU"}[args.activation]),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},
         "tokens_per_s": T / (ms_step * 1e-3),

@@ -65,6 +65,12 @@ typedef enum {
 #define MOE_PATH_PREFILL 1     /* grouped-GEMM path */
 #define MOE_PATH_DECODE 2      /* weight-streaming path; requires T*k <= 256, inference, BF16 */
 
+/* gated activation of the W13 output (moe_config_t.activation; nvfp4moe README,
+ * "Supported kernel surface": SwiGLU, GeGLU and ReGLU FC1 epilogues): a = f(g) * u */
+#define MOE_ACT_SWIGLU 0       /* f = silu(z) = z / (1 + e^-z) */
+#define MOE_ACT_GEGLU 1        /* f = gelu(z) = z Phi(z), the exact (erf) GELU */
+#define MOE_ACT_REGLU 2        /* f = max(z, 0) */
+
 /* device status bits (moe_get_status) */
 #define MOE_DEV_ID_OUT_OF_RANGE 1
 #define MOE_DEV_ID_DUPLICATE 2
@@ -86,6 +92,7 @@ typedef struct {
                                   backward recomputes it first, in memory the backward
                                   reuses later (blog post, "Caveats": activation-slot
                                   overflow selects recomputation); training plans only */
+    int32_t activation;        /* MOE_ACT_*; every path and precision */
 } moe_config_t;
 
 typedef struct {

@@ -34,6 +34,42 @@ __device__ __forceinline__ float sigmoid_f(float z) {
 }
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
+// Gated activations of the W13 output (nvfp4moe README, "Supported kernel surface":
+// SwiGLU, GeGLU and ReGLU FC1 epilogues): a = f(g) * u with f = silu, the exact (erf)
+// GELU z Phi(z), or max(z, 0); act_df is f' for the backward (Phi(z) + z phi(z) for the
+// GELU, with the device library's erff and the hardware exp2).
+constexpr int kActSwiGLU = 0, kActGeGLU = 1, kActReGLU = 2;
+template <int kAct> __device__ __forceinline__ float act_f(float z) {
+    if constexpr (kAct == kActGeGLU) return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+    else if constexpr (kAct == kActReGLU) return z > 0.0f ? z : 0.0f;
+    else return silu_f(z);
+}
+// f and f' together (the GELU's Phi computed once)
+template <int kAct> __device__ __forceinline__ void act_f_df(float z, float& f, float& df) {
+    if constexpr (kAct == kActGeGLU) {
+        const float cdf = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+        f = z * cdf;
+        df = cdf + z * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z);
+    } else if constexpr (kAct == kActReGLU) {
+        f = z > 0.0f ? z : 0.0f;
+        df = z > 0.0f ? 1.0f : 0.0f;
+    } else {
+        const float sg = sigmoid_f(z);
+        f = z * sg;
+        df = sg * (1.0f + z * (1.0f - sg));
+    }
+}
+template <int kAct> __device__ __forceinline__ float act_df(float z) {
+    if constexpr (kAct == kActGeGLU)
+        return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+               z * 0.39894228040143268f * __builtin_amdgcn_exp2f(-0.72134752044448170f * z * z);
+    else if constexpr (kAct == kActReGLU) return z > 0.0f ? 1.0f : 0.0f;
+    else {
+        const float sg = sigmoid_f(z);
+        return sg * (1.0f + z * (1.0f - sg));
+    }
+}
+
 // OCP MX conversion (E4M3 elements, E8M0 block scale) shared by the quantizer and
 // the MXFP8 W13 epilogue.
 // E4M3 (OCP "E4M3FN") code of a finite float, nearest even, saturating.

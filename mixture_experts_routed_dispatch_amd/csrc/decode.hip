@@ -212,7 +212,7 @@ __device__ __forceinline__ f32x4_t reduce_waves(f32x4_t acc, f32x4_t (*red)[kWav
     return s;
 }
 
-template <bool kSplit>
+template <bool kSplit, int kAct = kActSwiGLU>
 __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
     __shared__ DecodeSmem sm;
     __shared__ f32x4_t red[2][kWaves][MOE_WAVE];
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
                 for (int z = 0; z < 4; ++z) {
                     const int mm = m0 + 4 * kq + z;
                     if (mm < M)
-                        g.a[(size_t)entry(mm) * I + i0 + n] = (uint16_t)f32_to_bf16(silu_f(acc[z]) * up[z]);
+                        g.a[(size_t)entry(mm) * I + i0 + n] = (uint16_t)f32_to_bf16(act_f<kAct>(acc[z]) * up[z]);
                 }
             }
         }
@@ -384,6 +384,10 @@ hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, i
 }
 
 hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
+    if (g.act == kActGeGLU)
+        return launch_decode(decode_w13<false, kActGeGLU>, decode_w13<true, kActGeGLU>, g, g.I / 8, g.d / 32, num_cu, s);
+    if (g.act == kActReGLU)
+        return launch_decode(decode_w13<false, kActReGLU>, decode_w13<true, kActReGLU>, g, g.I / 8, g.d / 32, num_cu, s);
     return launch_decode(decode_w13<false>, decode_w13<true>, g, g.I / 8, g.d / 32, num_cu, s);
 }
 

@@ -123,7 +123,9 @@ struct TileCtx {
 // kSaveH (FWD_W13 only): also store h = (g, u) for backward.  A separate instantiation
 // rather than a runtime branch: accumulators live into two branches of the epilogue
 // are copied out to scratch by the register allocator.
-template <int MODE, bool kSaveH = false>
+// kAct (FWD_W13 and DGRAD_W2): the gated activation, a template parameter so that the
+// SwiGLU kernels stay as they are.
+template <int MODE, bool kSaveH = false, int kAct = kActSwiGLU>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ int cum[257];           // prefix over experts of their tiles (work items)
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                         for (int z = 0; z < 4; ++z) {
                             gv[z] = acc[a][b][4 * grp + z];
                             uv[z] = acc[a][b][4 * (grp + 2) + z];
-                            av[z] = silu_f(gv[z]) * uv[z];
+                            av[z] = act_f<kAct>(gv[z]) * uv[z];
                         }
                         uint2 v;
                         v.x = pack_bf16(av[0], av[1]);
@@ -708,9 +710,16 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                                 const float gv = h2 ? bf16hi(gw[z]) : bf16lo(gw[z]);
                                 const float uv = h2 ? bf16hi(uw[z]) : bf16lo(uw[z]);
                                 const float dA = sc[it] * av[2 * z + h2];
-                                const float sg = sigmoid_f(gv);
-                                dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
-                                du2[h2] = dA * gv * sg;
+                                if constexpr (kAct == kActSwiGLU) {
+                                    const float sg = sigmoid_f(gv);
+                                    dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
+                                    du2[h2] = dA * gv * sg;
+                                } else {
+                                    float f, df;
+                                    act_f_df<kAct>(gv, f, df);
+                                    dg2[h2] = dA * uv * df;
+                                    du2[h2] = dA * f;
+                                }
                             }
                             og[z] = pack_bf16(dg2[0], dg2[1]);
                             ou[z] = pack_bf16(du2[0], du2[1]);
@@ -917,13 +926,26 @@ hipError_t launch_mode(const GemmArgs& g, int num_cu, hipStream_t s) {
     int64_t grid = tiles < num_cu ? tiles : num_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
+    const dim3 gd((unsigned)grid), bd(NTHR);
     if constexpr (MODE == FWD_W13) {
         if (g.out_h) {
-            hipLaunchKernelGGL((grouped_gemm<MODE, true>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+            if (g.act == kActGeGLU) hipLaunchKernelGGL((grouped_gemm<MODE, true, kActGeGLU>), gd, bd, 0, s, g);
+            else if (g.act == kActReGLU) hipLaunchKernelGGL((grouped_gemm<MODE, true, kActReGLU>), gd, bd, 0, s, g);
+            else hipLaunchKernelGGL((grouped_gemm<MODE, true>), gd, bd, 0, s, g);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((grouped_gemm<MODE, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+    if constexpr (MODE == FWD_W13 || MODE == DGRAD_W2) {
+        if (g.act == kActGeGLU) {
+            hipLaunchKernelGGL((grouped_gemm<MODE, false, kActGeGLU>), gd, bd, 0, s, g);
+            return hipGetLastError();
+        }
+        if (g.act == kActReGLU) {
+            hipLaunchKernelGGL((grouped_gemm<MODE, false, kActReGLU>), gd, bd, 0, s, g);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((grouped_gemm<MODE, false>), gd, bd, 0, s, g);
     if constexpr (MODE == WGRAD_W2 || MODE == WGRAD_W13) {
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL((wgrad_fixup<MODE>), dim3(2 * kMaxPieces), dim3(NTHR), 0, s, g);

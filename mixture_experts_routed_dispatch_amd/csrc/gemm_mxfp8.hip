@@ -72,7 +72,7 @@ struct TileCtx {
     int e, mb, rows, pt, qt, nk;
 };
 
-template <int MODE>
+template <int MODE, int kAct = kActSwiGLU>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ __attribute__((aligned(1024))) char lsc[NSC * SCB];
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                             for (int z = 0; z < 4; ++z) {
                                 const float gv = acc[2 * m + h][b][4 * grp + z];
                                 const float uv = acc[2 * m + h][b][4 * (grp + 2) + z];
-                                const float v = silu_f(gv) * uv;
+                                const float v = act_f<kAct>(gv) * uv;
                                 av[8 * h + 4 * grp + z] = v;
                                 amax = __builtin_fmaxf(amax, __builtin_fabsf(v));
                             }
@@ -488,6 +488,16 @@ hipError_t launch_mx_mode(const MxGemmArgs& g, int num_cu, hipStream_t s) {
     int64_t grid = tiles < num_cu ? tiles : num_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
+    if constexpr (MODE == MX_W13) {
+        if (g.act == kActGeGLU) {
+            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kActGeGLU>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+            return hipGetLastError();
+        }
+        if (g.act == kActReGLU) {
+            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kActReGLU>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL(grouped_gemm_mx<MODE>, dim3((unsigned)grid), dim3(NTHR), 0, s, g);
     return hipGetLastError();
 }

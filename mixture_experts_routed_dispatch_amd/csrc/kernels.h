@@ -48,6 +48,7 @@ struct GemmArgs {
     int4* split;          // [kMaxPieces / 2] split tiles: (e, qt << 16 | pt, pieces, slot0 << 16 | stride)
     int32_t* nsplit;      // number of split tiles of the last weight-gradient launch
     int accumulate;       // weight gradients: add into out instead of overwriting
+    int act;              // gated activation (kActSwiGLU / kActGeGLU / kActReGLU)
 };
 
 // Pieces of split weight-gradient tiles in one launch (sizes their FP32 partial sums).
@@ -72,6 +73,7 @@ struct MxGemmArgs {
     uint8_t* aq;          // [R, I]      SwiGLU output, re-quantized (MX_W13 output, MX_W2 input)
     uint8_t* as;          // block-major words: (g, r) at (g * R + r) * 4
     uint16_t* o;          // [R, d]      BF16 expert outputs (MX_W2 output)
+    int act;              // gated activation of the W13 epilogue
 };
 
 hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipStream_t s);
@@ -104,6 +106,7 @@ struct DecodeArgs {
     uint16_t* o;           // [T*k, d]  expert output of entry t*k + j
     uint16_t* y;           // [T, d]
     int32_t* status;       // sticky routing flags
+    int act;               // gated activation of decode W13
 };
 
 hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s);

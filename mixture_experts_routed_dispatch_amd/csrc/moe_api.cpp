@@ -102,6 +102,7 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (c.wgrad_accumulate && !c.training) return MOE_ERR_UNSUPPORTED;
     if (c.recompute_h != 0 && c.recompute_h != 1) return MOE_ERR_INVALID_ARG;
     if (c.recompute_h && !c.training) return MOE_ERR_UNSUPPORTED;
+    if (c.activation < MOE_ACT_SWIGLU || c.activation > MOE_ACT_REGLU) return MOE_ERR_INVALID_ARG;
     if (c.path != MOE_PATH_AUTO && c.path != MOE_PATH_PREFILL && c.path != MOE_PATH_DECODE)
         return MOE_ERR_INVALID_ARG;
     if (c.d % 64 != 0 || c.I % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -323,6 +324,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     if (p->decode) {
         DecodeArgs dg{};
         dg.T = c.T; dg.d = c.d; dg.I = c.I; dg.E = c.E; dg.k = c.k;
+        dg.act = c.activation;
         dg.ids = ids; dg.scores = scores;
         dg.x = static_cast<const uint16_t*>(x);
         dg.w13 = static_cast<const uint16_t*>(w->w13);
@@ -366,6 +368,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         if (e != hipSuccess) return MOE_ERR_HIP;
         MxGemmArgs mg{};
         mg.T = c.T; mg.d = c.d; mg.I = c.I; mg.E = c.E; mg.k = c.k;
+        mg.act = c.activation;
         mg.m_indptr = m_indptr; mg.gather = gather;
         mg.xq = xq; mg.xs = xs;
         mg.w13q = static_cast<const uint8_t*>(w->w13); mg.w13s = w->w13_scale;
@@ -384,6 +387,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.act = c.activation;
     g.part = p->at<float>(p->off_part);
     g.split = p->at<int4>(p->off_split);
     g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));
@@ -428,6 +432,7 @@ moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t*
     if (e != hipSuccess) return MOE_ERR_HIP;
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.act = c.activation;
     g.part = p->at<float>(p->off_part);
     g.split = p->at<int4>(p->off_split);
     g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));
@@ -465,6 +470,7 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
+    g.act = c.activation;
     g.part = p->at<float>(p->off_part);
     g.split = p->at<int4>(p->off_split);
     g.nsplit = p->at<int32_t>(p->off_split + sizeof(int32_t) * 4 * (kMaxPieces / 2));

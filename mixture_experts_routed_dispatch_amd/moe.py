@@ -34,6 +34,7 @@ MOE_PATH_DECODE = 2
 MOE_DEV_ID_OUT_OF_RANGE = 1
 MOE_DEV_ID_DUPLICATE = 2
 MOE_DEV_BAD_INDPTR = 4
+MOE_ACT_SWIGLU, MOE_ACT_GEGLU, MOE_ACT_REGLU = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_destroy",
@@ -55,7 +56,8 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("training", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("wgrad_accumulate", ctypes.c_int32), ("recompute_h", ctypes.c_int32)]
+                ("wgrad_accumulate", ctypes.c_int32), ("recompute_h", ctypes.c_int32),
+                ("activation", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -122,8 +124,8 @@ def _ok(status: int, where: str):
 
 
 def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO,
-             wgrad_accumulate=0, recompute_h=0) -> int:
-    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate, recompute_h)
+             wgrad_accumulate=0, recompute_h=0, activation=MOE_ACT_SWIGLU) -> int:
+    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate, recompute_h, activation)
     h = ctypes.c_void_p()
     _ok(lib().moe_plan(ctypes.byref(cfg), ctypes.byref(h)), "moe_plan")
     return h.value
@@ -218,12 +220,12 @@ class Layer:
     """One plan plus its torch-allocated workspace; all compute goes through libmoe."""
 
     def __init__(self, T, d, I, E, k, precision=MOE_BF16, training=False, path=MOE_PATH_AUTO,
-                 device="cuda", wgrad_accumulate=False, recompute_h=False):
+                 device="cuda", wgrad_accumulate=False, recompute_h=False, activation=MOE_ACT_SWIGLU):
         import torch
         self.T, self.d, self.I, self.E, self.k = T, d, I, E, k
         self.precision = precision
         self.plan = moe_plan(T, d, I, E, k, precision, int(bool(training)), path,
-                             int(bool(wgrad_accumulate)), int(bool(recompute_h)))
+                             int(bool(wgrad_accumulate)), int(bool(recompute_h)), int(activation))
         nbytes = moe_workspace_bytes(self.plan)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         moe_bind_workspace(self.plan, _ptr(self.workspace), self.workspace.numel())

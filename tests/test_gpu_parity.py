@@ -769,3 +769,81 @@ def test_mxfp8_forward_full_size_sampled(torch_cuda):
     say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
     assert e <= TOL_MX
     assert e_q <= TOL_MX_QUANT
+
+
+# ------------------------------------------------------------------ GeGLU / ReGLU
+
+ACTS = [(1, "geglu"), (2, "reglu")]
+
+
+@pytest.mark.parametrize("act,name", ACTS)
+@pytest.mark.parametrize("T,d,I,E,k,routing,path", [(600, 512, 384, 6, 3, "uniform", 1),
+                                                    (257, 320, 192, 5, 2, "uniform", 1),
+                                                    (1, 256, 128, 16, 4, "uniform", 2),
+                                                    (7, 512, 384, 16, 4, "uniform", 2)])
+def test_forward_gated_activations(torch_cuda, act, name, T, d, I, E, k, routing, path):
+    """GeGLU (exact GELU) and ReGLU W13 epilogues on the grouped-GEMM path (1) and the
+    decode path (2, one and seven tokens) against the oracle with the same activation."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("forward", name, T, d, I, E, k, routing, "path", path)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=51)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, path=path, activation=act)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, act=act)
+    e = rel(np_of(y), ref)
+    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
+    assert e <= TOL_BF16
+    layer.close()
+
+
+@pytest.mark.parametrize("act,name", ACTS)
+@pytest.mark.parametrize("T,d,I,E,k,routing", [(400, 512, 384, 6, 3, "uniform"), (300, 256, 128, 128, 8, "zipf")])
+def test_backward_gated_activations(torch_cuda, act, name, T, d, I, E, k, routing):
+    """The backward of GeGLU / ReGLU (f'(g) in the W2 DGRAD epilogue, f(g) in du and in
+    the saved a) against the oracle's gradients with the same activation."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("backward", name, T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=53, with_dy=True)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, training=True, activation=act)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    y_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, act=act)
+    dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
+    errs = dict(y=rel(np_of(y), y_ref), dx=rel(np_of(dx), dx_ref), ds=rel(np_of(ds), ds_ref),
+                dw2=rel(np_of(dw2), dw2_ref), dw13=rel(np_of(dw13), dw13_ref.reshape(E, 2 * I, d)))
+    say("  " + " ".join("%s %.3e" % kv for kv in errs.items()))
+    for kname, v in errs.items():
+        assert v <= TOL_BF16, kname
+    layer.close()
+
+
+@pytest.mark.parametrize("act,name", ACTS)
+def test_mxfp8_forward_gated_activations(torch_cuda, act, name):
+    """The MXFP8 W13 epilogue with GeGLU / ReGLU before the E4M3 re-quantization."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 300, 512, 256, 6, 3
+    say("mxfp8 forward", name, T, d, I, E, k)
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=57)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3, activation=act)
+    w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+    y = np_of(layer.forward(t["x"], t["ids"], t["scores"], w13q, w2q, w13s, w2s))
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f, act=act)
+    ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f, act=act)
+    e, e_q = rel(y, ref), rel(y, ref_q)
+    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
+    assert e <= TOL_MX
+    assert e_q <= TOL_MX_QUANT
+    layer.close()
