@@ -83,7 +83,7 @@ KERNEL_OF_STAGE = {
     "wgrad_rows": ("wgrad_rows_kernel",), "recompute_h": ("grouped_gemm<0,",),
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels
-KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0>",), w2=("grouped_gemm_mx<1>",))
+KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0,",), w2=("grouped_gemm_mx<1,",))
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 
 
