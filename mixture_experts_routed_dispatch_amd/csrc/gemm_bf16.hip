@@ -272,8 +272,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             c.np = 1;
             c.pslot0 = c.pstride = c.slot = c.cslot = 0;
         }
-        c.mb = mptr[c.e];
-        c.rows = mptr[c.e + 1] - c.mb;
+        // uniform: kept in SGPRs
+        c.mb = __builtin_amdgcn_readfirstlane(mptr[c.e]);
+        c.rows = __builtin_amdgcn_readfirstlane(mptr[c.e + 1]) - c.mb;
         return c;
     };
 
@@ -440,12 +441,18 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     // ------------------------------------------------------------ fragments
     // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
     // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
+    // (recomputed at every tile start from the lane id read afresh, so that they are not
+    // held across the epilogue, where the kernels that save h run short of registers)
     int fragP[4], fragQ[4];
+    auto frag_offsets = [&]() {
+        const int fl = fresh_lane();
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        fragP[b] = lofs(wp * 128 + b * 32 + (lane & 31), lane >> 5);
-        fragQ[b] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), lane >> 5);
-    }
+        for (int b = 0; b < 4; ++b) {
+            fragP[b] = lofs(wp * 128 + b * 32 + (fl & 31), fl >> 5);
+            fragQ[b] = OPB + lofs(wq * 128 + b * 32 + (fl & 31), fl >> 5);
+        }
+    };
+    frag_offsets();
     // MN-major fragments with ds_read_b64_tr_b16: within a 16-lane group, lane j reads 4
     // consecutive columns of row k0 + j / 4 at column n0 + 4 (j % 4), and lane i
     // receives rows k0 .. k0 + 3 of column n0 + i.  Lane l = 16 g + j of fragment a, k
@@ -848,6 +855,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         if (++c_item >= n_items) break;
         __syncthreads();               // the staging slots are copied into again from the next stage
         cc = coords(c_item);
+        frag_offsets();
     }
 }
 
