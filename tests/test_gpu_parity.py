@@ -350,6 +350,90 @@ def test_graph_replay_matches_eager(torch_cuda):
     layer.close()
 
 
+@pytest.mark.parametrize("acc,rec", [(False, False), (True, True)])
+def test_training_graph_replay_matches_eager(torch_cuda, acc, rec):
+    """Forward + backward of a training plan captured in one HIP graph: every replay (the
+    gradient buffers reset first, eager work of the same plan between replays) gives the
+    eager results bit for bit; with wgrad_accumulate and recompute_h as well."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 400, 512, 384, 6, 3
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=61, with_dy=True)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, training=True, wgrad_accumulate=acc, recompute_h=rec)
+    g0 = torch.Generator(device="cpu").manual_seed(11)
+    dw13_0 = (torch.randn((E, 2 * I, d), generator=g0) * 0.05).to(torch.bfloat16).to(dev())
+    dw2_0 = (torch.randn((E, d, I), generator=g0) * 0.05).to(torch.bfloat16).to(dev())
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev())
+    dx = torch.empty_like(y)
+    ds = torch.empty((T, k), dtype=torch.float32, device=dev())
+    dw13, dw2 = dw13_0.clone(), dw2_0.clone()
+
+    def step():
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y)
+        layer.backward(t["dy"], t["x"], t["w13"], t["w2"], dx=dx, dw13=dw13, dw2=dw2, dscores=ds)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [v.clone() for v in (y, dx, dw13, dw2, ds)]
+    gr = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                             # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        step()
+    for rep in range(3):
+        dw13.copy_(dw13_0)
+        dw2.copy_(dw2_0)
+        for v in (y, dx, ds):
+            v.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("y", "dx", "dw13", "dw2", "ds"), (y, dx, dw13, dw2, ds), ref):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b), (rep, name)
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])   # eager work between replays
+        torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    layer.close()
+
+
+def test_routed_graph_replay_matches_eager(torch_cuda):
+    """moe_forward_routed captured in a HIP graph replays to the eager result."""
+    torch = torch_cuda
+    T, d, I, E, k = 600, 512, 384, 6, 3
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=63)
+    m_indptr, gather, _, _ = oracle.dispatch(inp.ids, inp.scores, E)
+    t = device_inputs(inp)
+    x_rows = t["x"][torch.from_numpy(gather.astype(np.int64)).to(dev())].contiguous()
+    mi = torch.from_numpy(m_indptr).to(dev())
+    layer = make_layer(inp, path=1)
+    ref = layer.forward_routed(x_rows, mi, t["w13"], t["w2"]).clone()
+    out = torch.empty_like(ref)
+    gr = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.forward_routed(x_rows, mi, t["w13"], t["w2"], out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        layer.forward_routed(x_rows, mi, t["w13"], t["w2"], out=out)
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+    layer.close()
+
+
 # ------------------------------------------------------------------ decode path
 
 DECODE_SHAPES = [
