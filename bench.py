@@ -79,7 +79,7 @@ KERNEL_OF_STAGE = {
     "combine": ("combine_kernel",), "score_grad": ("score_grad_kernel",),
     "dgrad_w2": ("grouped_gemm<2,",), "dgrad_w13": ("grouped_gemm<3,",),
     "wgrad_w2": ("grouped_gemm<4,", "wgrad_fixup<4>"), "wgrad_w13": ("grouped_gemm<5,", "wgrad_fixup<5>"),
-    "quant_x": ("quantize_kernel",), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),
+    "quant_x": ("quantize_kernel", "route_scales_kernel"), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),
     "wgrad_rows": ("wgrad_rows_kernel",), "recompute_h": ("grouped_gemm<0,",),
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels

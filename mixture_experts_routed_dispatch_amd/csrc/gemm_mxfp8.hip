@@ -95,7 +95,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     const int wp = wave & 1, wq = wave >> 1;
     const int E = g.E;
     const int K = MODE == MX_W13 ? g.d : g.I;          // K of the product (bytes per row)
-    const int KB = K / 32;                             // scale bytes per row
     const size_t R = (size_t)g.T * g.k;                // routed rows
     const int nPt = MODE == MX_W13 ? g.I / 128 : g.d / TP;
 
@@ -161,14 +160,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     // row of the Q operand (token of xq, or routed row of aq) behind Q tile row r, for
     // the rows r = 64 w .. 64 w + 63 of wave w only: the token ids come from gsrc[slot],
     // where gather_dma put them
+    auto routed_row = [&](const TileCtx& c, int r) {
+        int rr = c.qt * TQ + r;
+        if (rr >= c.rows) rr = c.rows - 1;            // ragged tail: a row of the expert
+        return c.mb + rr;
+    };
     auto q_row = [&](const TileCtx& c, int slot, int r) {
-        if constexpr (MODE == MX_W13) {
-            return gsrc[slot][r];
-        } else {
-            int rr = c.qt * TQ + r;
-            if (rr >= c.rows) rr = c.rows - 1;        // ragged tail: a row of the expert
-            return c.mb + rr;
-        }
+        if constexpr (MODE == MX_W13) return gsrc[slot][r];
+        else return routed_row(c, r);
     };
     // Token ids of tile c into gsrc[slot]: wave w copies entries 64 w .. 64 w + 63 (the
     // rows of its own data and scale copies) with one global_load_lds_dword, issued a
@@ -213,7 +212,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
         }
         const int rs = 64 * wave + fl;
         svoffP = (uint32_t)(p_row(c, rs) * 4);
-        svoffQ = (uint32_t)(q_row(c, slot, rs) * (MODE == MX_W13 ? KB : 4));
+        svoffQ = (uint32_t)(routed_row(c, rs) * 4);          // Q scales are in routed order in both modes
         pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
         psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * 4);
     };
@@ -237,8 +236,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
         const uint32_t dst = lsc0 + slot * SCB + 256 * wave;
         const size_t kp = (size_t)(kt >> 1);                  // stage pair = group of 4 blocks
         dma4(dst, svoffP, psbase_e + kp * E * prows_e * 4);
-        if constexpr (MODE == MX_W13) dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + 4 * kp);
-        else dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kp * R * 4);
+        dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kp * R * 4);
     };
 
     // ------------------------------------------------------------ fragments and scales

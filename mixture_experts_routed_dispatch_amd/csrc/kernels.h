@@ -65,7 +65,7 @@ struct MxGemmArgs {
     const int32_t* m_indptr;
     const int32_t* gather;
     const uint8_t* xq;    // [T, d]      codes of x
-    const uint8_t* xs;    // [T, d/32]   scales of x
+    const uint8_t* xs;    // scales of x[gather], block-major words: (g, r) at (g * R + r) * 4
     const uint8_t* w13q;  // [E, 2I, d]
     const uint8_t* w13s;  // block-major words: (g, row) at (g * E 2I + row) * 4, row = e 2I + n
     const uint8_t* w2q;   // [E, d, I]
@@ -120,5 +120,9 @@ hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
 // (K a multiple of 128); else scales [rows, K/32].
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, bool block_major, hipStream_t s);
+// block-major scale words of the routed rows x[gather[r]], r < R, from row-major
+// [rows, K/32] scales; K a multiple of 128, gather entries valid rows of the source
+hipError_t launch_route_scales(const uint8_t* scales, const int32_t* gather, int64_t R, int K,
+                               uint8_t* out, hipStream_t s);
 
 }  // namespace moe

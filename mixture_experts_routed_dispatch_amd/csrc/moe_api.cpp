@@ -35,7 +35,7 @@ struct moe_plan_s {
     bool decode;
     // workspace offsets (bytes)
     size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
-    size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_aq, off_as;
+    size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_xsr, off_aq, off_as;
     size_t off_part, off_split;        // split weight-gradient tiles: partial sums, descriptors
     size_t ws_bytes;
     char* ws;
@@ -159,6 +159,7 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     }
     p->off_xq = mx ? take((size_t)c.T * c.d) : 0;
     p->off_xs = mx ? take((size_t)c.T * c.d / 32) : 0;
+    p->off_xsr = mx ? take((size_t)R * c.d / 32) : 0;
     p->off_aq = mx ? take((size_t)R * c.I) : 0;
     p->off_as = mx ? take((size_t)R * c.I / 32) : 0;
     const bool gemms = !mx && !p->decode;
@@ -231,6 +232,7 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
     if (mx) {
         region("xq", (size_t)c.T * c.d, "scratch", "E4M3 codes of x [T, d]");
         region("xs", (size_t)c.T * c.d / 32, "scratch", "E8M0 scales of x [T, d/32]");
+        region("xs_routed", (size_t)R * c.d / 32, "scratch", "scales of x[gather], block-major [d/128, R, 4]");
         region("aq", (size_t)R * c.I, "scratch", "E4M3 codes of a [R, I]");
         region("as", (size_t)R * c.I / 32, "scratch", "E8M0 scales of a (block-major)");
     }
@@ -359,18 +361,22 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     if (c.precision == MOE_MXFP8_E4M3) {
         // MXFP8 (blog post "What it is selling": activations quantized after routing,
         // prepared weights): x is quantized per token row, which equals quantizing the
-        // gathered rows since every MX block lies inside one row
+        // gathered rows since every MX block lies inside one row; the scales are then
+        // copied out per routed row, block-major, so that a W13 tile's scale words for one
+        // K group are contiguous
         uint8_t* xq = p->at<uint8_t>(p->off_xq);
         uint8_t* xs = p->at<uint8_t>(p->off_xs);
+        uint8_t* xsr = p->at<uint8_t>(p->off_xsr);
         e = staged(p, MOE_STAGE_QUANT_X, s, [&] {
-            return launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, false, s);
+            hipError_t qe = launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, false, s);
+            return qe != hipSuccess ? qe : launch_route_scales(xs, gather, p->R, c.d, xsr, s);
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
         MxGemmArgs mg{};
         mg.T = c.T; mg.d = c.d; mg.I = c.I; mg.E = c.E; mg.k = c.k;
         mg.act = c.activation;
         mg.m_indptr = m_indptr; mg.gather = gather;
-        mg.xq = xq; mg.xs = xs;
+        mg.xq = xq; mg.xs = xsr;
         mg.w13q = static_cast<const uint8_t*>(w->w13); mg.w13s = w->w13_scale;
         mg.w2q = static_cast<const uint8_t*>(w->w2); mg.w2s = w->w2_scale;
         mg.aq = p->at<uint8_t>(p->off_aq); mg.as = p->at<uint8_t>(p->off_as);

@@ -63,7 +63,52 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __re
     }
 }
 
+// Scales of gathered rows, block-major: word (g, r) of out, the four scale bytes of K
+// group g (blocks 4 g .. 4 g + 3) of routed row r, is word g of source row gather[r].
+// A workgroup transposes 256 routed rows x 16 groups through LDS: 16 lanes read the 64
+// bytes of one source row, and each store of a wave covers 64 consecutive words of one
+// group.  Row stride 17 words in LDS: the column reads hit 64 different banks.
+constexpr int kRouteRows = 256, kRouteGroups = 16;
+__global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* __restrict__ src,
+                                                                const int32_t* __restrict__ gather,
+                                                                int64_t R, int groups,
+                                                                uint32_t* __restrict__ out) {
+    static_assert(kThreads == kRouteRows, "one thread per routed row in the stores");
+    __shared__ uint32_t tile[kRouteRows * (kRouteGroups + 1)];
+    const int t = threadIdx.x;
+    const int g0 = blockIdx.y * kRouteGroups;
+    const int w = t % kRouteGroups;
+    for (int64_t r0 = (int64_t)blockIdx.x * kRouteRows; r0 < R; r0 += (int64_t)gridDim.x * kRouteRows) {
+#pragma unroll
+        for (int i = 0; i < kRouteGroups; ++i) {
+            const int row = t / kRouteGroups + i * (kThreads / kRouteGroups);
+            if (r0 + row < R && g0 + w < groups)
+                tile[row * (kRouteGroups + 1) + w] = src[(int64_t)gather[r0 + row] * groups + g0 + w];
+        }
+        __syncthreads();
+        if (r0 + t < R) {
+            for (int gi = 0; gi < kRouteGroups && g0 + gi < groups; ++gi)
+                out[(int64_t)(g0 + gi) * R + r0 + t] = tile[t * (kRouteGroups + 1) + gi];
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
+
+hipError_t launch_route_scales(const uint8_t* scales, const int32_t* gather, int64_t R, int K,
+                               uint8_t* out, hipStream_t s) {
+    if (K % 128 != 0) return hipErrorInvalidValue;
+    if (R == 0) return hipSuccess;
+    const int chunks = (K / 128 + kRouteGroups - 1) / kRouteGroups;
+    if (chunks > 65535) return hipErrorInvalidValue;
+    int64_t grid = (R + kRouteRows - 1) / kRouteRows;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(route_scales_kernel, dim3((unsigned)grid, (unsigned)chunks), dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint32_t*>(scales), gather, R, K / 128,
+                       reinterpret_cast<uint32_t*>(out));
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, bool block_major, hipStream_t s) {
