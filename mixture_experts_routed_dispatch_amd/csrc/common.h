@@ -90,19 +90,23 @@ template <int kAct> __device__ __forceinline__ float act_df(float z) {
 
 // OCP MX conversion (E4M3 elements, E8M0 block scale) shared by the quantizer and
 // the MXFP8 W13 epilogue.
-// E4M3 (OCP "E4M3FN") code of a finite float, nearest even, saturating.
+// E4M3 (OCP "E4M3FN") code of a finite float, nearest even, saturating, without
+// branches.  From 2^-6 up, the FP32 pattern is rounded to 3 mantissa bits in the
+// integer domain (adding 2^19 - 1 plus the lowest kept bit rounds to nearest even, and
+// a carry out of the mantissa steps the exponent), the exponent is rebiased from 127 to
+// 7, and codes past 0x7E (448) saturate to it.  Below 2^-6 the code is the number of
+// 2^-9 steps, nearest even: adding 2^23 to |v| 2^9 in one FMA leaves that integer in
+// the low mantissa bits.  Code 0x08 (2^-6) is reached from both sides.  Equal to the
+// plain definition (exponent, rint of the scaled mantissa, carry, clamp at 448) on
+// every finite float.
 __device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-    const float a = __builtin_fabsf(v);
-    if (a >= 448.0f) return sign | 0x7Eu;
-    if (a < 0.015625f) {                                   // below 2^-6: steps of 2^-9
-        const float m = __builtin_rintf(a * 512.0f);        // exact scaling, ties to even
-        return sign | (uint32_t)m;                          // 8 steps is code 0x08 = 2^-6
-    }
-    int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127; // a is normal here
-    float m = __builtin_rintf((__builtin_ldexpf(a, -e) - 1.0f) * 8.0f);
-    if (m == 8.0f) { m = 0.0f; e += 1; }
-    return sign | (uint32_t)(((e + 7) << 3) | (int)m);
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    uint32_t code = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+    code = code < 0x7Eu ? code : 0x7Eu;
+    const uint32_t sub = __float_as_uint(__builtin_fmaf(__uint_as_float(mag), 512.0f, 8388608.0f)) & 0xFFu;
+    return sign | (mag < 0x3C800000u ? sub : code);
 }
 
 // E8M0 byte of a block whose largest magnitude is amax (any finite float):

@@ -763,6 +763,45 @@ def test_quantize_bit_exact(torch_cuda):
     assert np.array_equal(codes.cpu().numpy(), rc)
 
 
+def test_quantize_every_bf16_value(torch_cuda):
+    """Every finite BF16 value through the device E4M3/E8M0 conversion at 18 block scales:
+    the values, sorted by magnitude, fill blocks 31 at a time behind an anchor element of
+    2^j times the group's largest magnitude (j = 0..17), so each value is converted at
+    scaled magnitudes from the top of the E4M3 range down through its subnormal steps
+    to zero.  Codes and scale bytes must equal the oracle's bit for bit."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    allbits = np.arange(65536, dtype=np.uint32)
+    vals = (allbits << 16).view(np.float32)
+    fin = allbits[np.isfinite(vals)].astype(np.uint16)
+    fin = fin[np.argsort(np.abs((fin.astype(np.uint32) << 16).view(np.float32)), kind="stable")]
+    groups = -(-fin.size // 31)
+    fin = np.concatenate([fin, np.zeros(groups * 31 - fin.size, np.uint16)]).reshape(groups, 31)
+    gmax = np.abs((fin.astype(np.uint32) << 16).view(np.float32)).max(axis=1)
+    blocks = []
+    for j in range(18):
+        anchor = gmax.astype(np.float64) * 2.0 ** j
+        ok = anchor < 3.0e38
+        a_bits = inputs.to_bf16_bits(anchor[ok].astype(np.float32))
+        assert np.array_equal((a_bits.astype(np.uint32) << 16).view(np.float32), anchor[ok])   # exact
+        blocks.append(np.concatenate([a_bits[:, None], fin[ok]], axis=1))
+    blocks = np.concatenate(blocks)
+    pad = -len(blocks) % 8
+    blocks = np.concatenate([blocks, np.zeros((pad, 32), np.uint16)])
+    bits = np.ascontiguousarray(blocks.reshape(-1, 256))
+    rows, K = bits.shape
+    say("quantize every finite bf16 value: %d blocks" % (rows * K // 32))
+    src = bf16_dev(bits)
+    codes = torch.empty((rows, K), dtype=torch.uint8, device=dev())
+    scales = torch.empty((rows, K // 32), dtype=torch.uint8, device=dev())
+    moe.moe_quantize_mxfp8(src.data_ptr(), rows, K, codes.data_ptr(), scales.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rc, rs = oracle.mx_quantize(bits)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(codes.cpu().numpy(), rc)
+
+
 def test_prepare_weights_bit_exact(torch_cuda):
     torch = torch_cuda
     inp = inputs.generate(16, 256, 128, 4, 2, seed=3)
@@ -797,6 +836,7 @@ MX_SHAPES = [
     (257, 256, 384, 5, 2, "uniform"),      # three W13 column tiles
     (200, 256, 128, 64, 8, "zipf"),        # skew and empty experts
     (130, 256, 128, 1, 1, "uniform"),      # dense layer
+    (100, 2304, 128, 4, 2, "uniform"),     # 18 scale words per row: a partial second group chunk
 ]
 
 
