@@ -152,7 +152,10 @@ moe_status_t moe_dispatch(moe_plan_t plan, const int32_t* ids, const float* scor
  * per block of 32 consecutive elements the E8M0 byte is
  * clamp(floor(log2(max|v|)) - 8 + 127, 0, 254) (0 for an all-zero block) and
  * each element is E4M3(v / 2^(byte - 127)), nearest-even, clamped to +-448.
- * codes uint8 [rows, K]; scales uint8 [rows, K/32].  Needs no plan. */
+ * codes uint8 [rows, K]; scales uint8 [rows, K/32].  Needs no plan.
+ * Inputs are meant to be finite.  An infinite or NaN element is encoded as
+ * 448 with its sign bit (E4M3's NaN codes are never written), and the scale
+ * byte of its block is then not specified. */
 moe_status_t moe_quantize_mxfp8(const void* v_bf16, int64_t rows, int32_t K,
                                 uint8_t* codes, uint8_t* scales, void* stream);
 
