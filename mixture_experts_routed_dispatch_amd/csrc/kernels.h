@@ -121,8 +121,8 @@ hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
                                  uint8_t* scales, bool block_major, hipStream_t s);
 // block-major scale words of the routed rows x[gather[r]], r < R, from row-major
-// [rows, K/32] scales; K a multiple of 128, gather entries valid rows of the source
-hipError_t launch_route_scales(const uint8_t* scales, const int32_t* gather, int64_t R, int K,
-                               uint8_t* out, hipStream_t s);
+// [rows, K/32] scales; K a multiple of 128; gather entries outside [0, rows) read row 0
+hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_t* gather, int64_t R,
+                               int K, uint8_t* out, hipStream_t s);
 
 }  // namespace moe

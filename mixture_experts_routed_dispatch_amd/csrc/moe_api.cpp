@@ -369,7 +369,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         uint8_t* xsr = p->at<uint8_t>(p->off_xsr);
         e = staged(p, MOE_STAGE_QUANT_X, s, [&] {
             hipError_t qe = launch_quantize_mxfp8(static_cast<const uint16_t*>(x), c.T, c.d, xq, xs, false, s);
-            return qe != hipSuccess ? qe : launch_route_scales(xs, gather, p->R, c.d, xsr, s);
+            return qe != hipSuccess ? qe : launch_route_scales(xs, c.T, gather, p->R, c.d, xsr, s);
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
         MxGemmArgs mg{};

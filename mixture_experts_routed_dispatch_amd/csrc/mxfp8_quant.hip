@@ -68,10 +68,12 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __re
 // A workgroup transposes 256 routed rows x 16 groups through LDS: 16 lanes read the 64
 // bytes of one source row, and each store of a wave covers 64 consecutive words of one
 // group.  Row stride 17 words in LDS: the column reads hit 64 different banks.
+// Entries of gather past the routed count (left unwritten by the dispatch when routes
+// carry invalid expert ids) are read clamped to row 0; no product reads their words.
 constexpr int kRouteRows = 256, kRouteGroups = 16;
 __global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* __restrict__ src,
                                                                 const int32_t* __restrict__ gather,
-                                                                int64_t R, int groups,
+                                                                int64_t R, int groups, uint32_t src_rows,
                                                                 uint32_t* __restrict__ out) {
     static_assert(kThreads == kRouteRows, "one thread per routed row in the stores");
     __shared__ uint32_t tile[kRouteRows * (kRouteGroups + 1)];
@@ -82,8 +84,11 @@ __global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* 
 #pragma unroll
         for (int i = 0; i < kRouteGroups; ++i) {
             const int row = t / kRouteGroups + i * (kThreads / kRouteGroups);
-            if (r0 + row < R && g0 + w < groups)
-                tile[row * (kRouteGroups + 1) + w] = src[(int64_t)gather[r0 + row] * groups + g0 + w];
+            if (r0 + row < R && g0 + w < groups) {
+                uint32_t t = (uint32_t)gather[r0 + row];
+                if (t >= src_rows) t = 0;
+                tile[row * (kRouteGroups + 1) + w] = src[(int64_t)t * groups + g0 + w];
+            }
         }
         __syncthreads();
         if (r0 + t < R) {
@@ -96,16 +101,16 @@ __global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* 
 
 }  // namespace
 
-hipError_t launch_route_scales(const uint8_t* scales, const int32_t* gather, int64_t R, int K,
-                               uint8_t* out, hipStream_t s) {
-    if (K % 128 != 0) return hipErrorInvalidValue;
+hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_t* gather, int64_t R,
+                               int K, uint8_t* out, hipStream_t s) {
+    if (K % 128 != 0 || rows <= 0 || rows > 0xFFFFFFFFll) return hipErrorInvalidValue;
     if (R == 0) return hipSuccess;
     const int chunks = (K / 128 + kRouteGroups - 1) / kRouteGroups;
     if (chunks > 65535) return hipErrorInvalidValue;
     int64_t grid = (R + kRouteRows - 1) / kRouteRows;
     if (grid > 65536) grid = 65536;
     hipLaunchKernelGGL(route_scales_kernel, dim3((unsigned)grid, (unsigned)chunks), dim3(kThreads), 0, s,
-                       reinterpret_cast<const uint32_t*>(scales), gather, R, K / 128,
+                       reinterpret_cast<const uint32_t*>(scales), gather, R, K / 128, (uint32_t)rows,
                        reinterpret_cast<uint32_t*>(out));
     return hipGetLastError();
 }

@@ -538,6 +538,47 @@ def test_decode_flags_invalid_routing(torch_cuda):
     layer.close()
 
 
+@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
+def test_forward_flags_invalid_routing(torch_cuda, mx):
+    """A grouped-GEMM forward whose routing holds an out-of-range id flags it and stays
+    in bounds: the dispatch leaves the routed rows past the valid count unwritten (the
+    workspace is filled with 0xFF bytes first, so their indices read as -1), and the next
+    call with valid routing matches a fresh layer bit for bit."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    inp = inputs.generate(300, 256, 128, 8, 2, "uniform", seed=23)
+    t = device_inputs(inp)
+    prec = moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16
+
+    def run(layer, ids):
+        if mx:
+            w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+            return layer.forward(t["x"], ids, t["scores"], w13q, w2q, w13s, w2s)
+        return layer.forward(t["x"], ids, t["scores"], t["w13"], t["w2"])
+
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, path=1)
+    layer.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    layer.status(clear=True)            # the fill set every status bit too
+    bad = inp.ids.copy()
+    bad[5, 0] = inp.E
+    bad[17, 1] = -2
+    run(layer, torch.from_numpy(bad).to(dev()))
+    torch.cuda.synchronize()
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags & moe.MOE_DEV_ID_OUT_OF_RANGE
+    y = run(layer, t["ids"]).clone()
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    assert st == moe.MOE_OK and flags == 0
+    layer.close()
+    fresh = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, path=1)
+    y2 = run(fresh, t["ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    fresh.close()
+
+
 # ------------------------------------------------------------------ backward
 
 BWD_SHAPES = [
