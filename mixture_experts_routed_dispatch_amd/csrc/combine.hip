@@ -129,16 +129,20 @@ __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __
 
 // Row-major operands of the weight-gradient products: xg[r] = x[gather[r]] and
 // dys[r] = bf16(probs[r] * dy[gather[r]]) for routed rows r.  One workgroup per row
-// (grid-strided), one 16-byte chunk of each per thread.
+// (grid-strided), one 16-byte chunk of each per thread.  Entries of gather past the
+// routed count (left unwritten by the dispatch for invalid expert ids) are read clamped
+// to token 0; the products read only the rows of their experts.
 __global__ __launch_bounds__(kThreads) void wgrad_rows_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ dy,
                                                               const int32_t* __restrict__ gather,
                                                               const float* __restrict__ probs,
-                                                              int64_t R, int d,
+                                                              int64_t R, int d, uint32_t T,
                                                               uint16_t* __restrict__ xg,
                                                               uint16_t* __restrict__ dys) {
     for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-        const size_t t = (size_t)gather[r];
+        uint32_t tu = (uint32_t)gather[r];
+        if (tu >= T) tu = 0;
+        const size_t t = tu;
         const float sc = probs[r];
         for (int n = threadIdx.x * 8; n < d; n += kThreads * 8) {
             const uint4 xv = *reinterpret_cast<const uint4*>(x + t * d + n);
@@ -155,13 +159,14 @@ __global__ __launch_bounds__(kThreads) void wgrad_rows_kernel(const uint16_t* __
 
 }  // namespace
 
-hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, const int32_t* gather,
+hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, int T, const int32_t* gather,
                              const float* probs, int64_t R, int d, uint16_t* xg, uint16_t* dys,
                              hipStream_t s) {
     if (R == 0) return hipSuccess;
+    if (T <= 0) return hipErrorInvalidValue;
     const int64_t grid = R < 65536 ? R : 65536;
     hipLaunchKernelGGL(wgrad_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, dy, gather,
-                       probs, R, d, xg, dys);
+                       probs, R, d, (uint32_t)T, xg, dys);
     return hipGetLastError();
 }
 

@@ -538,25 +538,33 @@ def test_decode_flags_invalid_routing(torch_cuda):
     layer.close()
 
 
-@pytest.mark.parametrize("mx", [False, True], ids=["bf16", "mxfp8"])
-def test_forward_flags_invalid_routing(torch_cuda, mx):
-    """A grouped-GEMM forward whose routing holds an out-of-range id flags it and stays
-    in bounds: the dispatch leaves the routed rows past the valid count unwritten (the
-    workspace is filled with 0xFF bytes first, so their indices read as -1), and the next
-    call with valid routing matches a fresh layer bit for bit."""
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "bf16-train"])
+def test_forward_flags_invalid_routing(torch_cuda, mode):
+    """A grouped-GEMM call (forward, or forward + backward) whose routing holds
+    out-of-range ids flags them and stays in bounds: the dispatch leaves the routed rows
+    past the valid count unwritten (the workspace is filled with 0xFF bytes first, so
+    their indices read as -1), and the next call with valid routing matches a fresh
+    layer bit for bit."""
     torch = torch_cuda
     from mixture_experts_routed_dispatch_amd import moe
-    inp = inputs.generate(300, 256, 128, 8, 2, "uniform", seed=23)
+    mx, train = mode == "mxfp8", mode == "bf16-train"
+    inp = inputs.generate(300, 256, 128, 8, 2, "uniform", seed=23, with_dy=train)
     t = device_inputs(inp)
     prec = moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16
 
     def run(layer, ids):
         if mx:
             w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
-            return layer.forward(t["x"], ids, t["scores"], w13q, w2q, w13s, w2s)
-        return layer.forward(t["x"], ids, t["scores"], t["w13"], t["w2"])
+            return [layer.forward(t["x"], ids, t["scores"], w13q, w2q, w13s, w2s)]
+        y = layer.forward(t["x"], ids, t["scores"], t["w13"], t["w2"])
+        if not train:
+            return [y]
+        return [y] + list(layer.backward(t["dy"], t["x"], t["w13"], t["w2"]))
 
-    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, path=1)
+    def bits(v):
+        return v.view(torch.int32) if v.dtype == torch.float32 else v.view(torch.int16)
+
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, training=train, path=1)
     layer.workspace.fill_(0xFF)
     torch.cuda.synchronize()
     layer.status(clear=True)            # the fill set every status bit too
@@ -567,15 +575,16 @@ def test_forward_flags_invalid_routing(torch_cuda, mx):
     torch.cuda.synchronize()
     st, flags = layer.status(clear=True)
     assert st == moe.MOE_ERR_ROUTING and flags & moe.MOE_DEV_ID_OUT_OF_RANGE
-    y = run(layer, t["ids"]).clone()
+    out = [v.clone() for v in run(layer, t["ids"])]
     torch.cuda.synchronize()
     st, flags = layer.status()
     assert st == moe.MOE_OK and flags == 0
     layer.close()
-    fresh = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, path=1)
-    y2 = run(fresh, t["ids"])
+    fresh = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=prec, training=train, path=1)
+    ref = run(fresh, t["ids"])
     torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    for a, b in zip(out, ref):
+        assert torch.equal(bits(a), bits(b))
     fresh.close()
 
 
