@@ -90,23 +90,19 @@ template <int kAct> __device__ __forceinline__ float act_df(float z) {
 
 // OCP MX conversion (E4M3 elements, E8M0 block scale) shared by the quantizer and
 // the MXFP8 W13 epilogue.
-// E4M3 (OCP "E4M3FN") code of a finite float, nearest even, saturating, without
-// branches.  From 2^-6 up, the FP32 pattern is rounded to 3 mantissa bits in the
-// integer domain (adding 2^19 - 1 plus the lowest kept bit rounds to nearest even, and
-// a carry out of the mantissa steps the exponent), the exponent is rebiased from 127 to
-// 7, and codes past 0x7E (448) saturate to it.  Below 2^-6 the code is the number of
-// 2^-9 steps, nearest even: adding 2^23 to |v| 2^9 in one FMA leaves that integer in
-// the low mantissa bits.  Code 0x08 (2^-6) is reached from both sides.  Equal to the
-// plain definition (exponent, rint of the scaled mantissa, carry, clamp at 448) on
-// every finite float.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-    const uint32_t bits = __float_as_uint(v);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const uint32_t mag = bits & 0x7FFFFFFFu;
-    uint32_t code = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
-    code = code < 0x7Eu ? code : 0x7Eu;
-    const uint32_t sub = __float_as_uint(__builtin_fmaf(__uint_as_float(mag), 512.0f, 8388608.0f)) & 0xFFu;
-    return sign | (mag < 0x3C800000u ? sub : code);
+// E4M3 (OCP "E4M3FN") codes of four finite floats, nearest even, saturating at +-448,
+// packed little-endian (a in bits 0..7): gfx950's f32 -> FP8 conversion (OCP E4M3 on
+// this target), two values per instruction, after a med3 clamp to +-448.  The plain
+// definition it stands for: from 2^-6 up, round the mantissa to 3 bits (a carry steps
+// the exponent) and rebias the exponent from 127 to 7, saturating past 448; below 2^-6,
+// the nearest-even count of 2^-9 steps; the sign bit is kept, also on zero.  The two
+// agree on every finite float (all 2^32 patterns were compared on the GPU, with this
+// library's compile flags, against that definition written out in integer arithmetic).
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    auto sat = [](float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+    return (uint32_t)w;
 }
 
 // E8M0 byte of a block whose largest magnitude is amax (any finite float):

@@ -347,10 +347,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                         for (int h = 0; h < 2; ++h)
 #pragma unroll
                             for (int grp = 0; grp < 2; ++grp) {
-                                uint32_t w = 0;
-#pragma unroll
-                                for (int z = 0; z < 4; ++z)
-                                    w |= e4m3_code(__builtin_ldexpf(av[8 * h + 4 * grp + z], sh)) << (8 * z);
+                                const float* q = &av[8 * h + 4 * grp];
+                                const uint32_t w = e4m3_pack4(__builtin_ldexpf(q[0], sh), __builtin_ldexpf(q[1], sh),
+                                                              __builtin_ldexpf(q[2], sh), __builtin_ldexpf(q[3], sh));
                                 *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 16 * h + 8 * grp + p_sub) = w;
                             }
                         if (ln < 32) g.as[((size_t)(i0 >> 7) * R + r) * 4 + ((i0 >> 5) & 3)] = (uint8_t)sb;

@@ -44,11 +44,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __re
         uint32_t out[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t c0 = e4m3_code(__builtin_ldexpf(bf16lo(w[2 * i]), sh));
-            const uint32_t c1 = e4m3_code(__builtin_ldexpf(bf16hi(w[2 * i]), sh));
-            const uint32_t c2 = e4m3_code(__builtin_ldexpf(bf16lo(w[2 * i + 1]), sh));
-            const uint32_t c3 = e4m3_code(__builtin_ldexpf(bf16hi(w[2 * i + 1]), sh));
-            out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+            out[i] = e4m3_pack4(__builtin_ldexpf(bf16lo(w[2 * i]), sh), __builtin_ldexpf(bf16hi(w[2 * i]), sh),
+                                __builtin_ldexpf(bf16lo(w[2 * i + 1]), sh), __builtin_ldexpf(bf16hi(w[2 * i + 1]), sh));
         }
         uint4* dst = reinterpret_cast<uint4*>(codes + b * 32);
         dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
@@ -85,9 +82,9 @@ __global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* 
         for (int i = 0; i < kRouteGroups; ++i) {
             const int row = t / kRouteGroups + i * (kThreads / kRouteGroups);
             if (r0 + row < R && g0 + w < groups) {
-                uint32_t t = (uint32_t)gather[r0 + row];
-                if (t >= src_rows) t = 0;
-                tile[row * (kRouteGroups + 1) + w] = src[(int64_t)t * groups + g0 + w];
+                uint32_t tok = (uint32_t)gather[r0 + row];
+                if (tok >= src_rows) tok = 0;
+                tile[row * (kRouteGroups + 1) + w] = src[(int64_t)tok * groups + g0 + w];
             }
         }
         __syncthreads();
