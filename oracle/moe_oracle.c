@@ -28,7 +28,7 @@
  *         nearest even and clamped to the largest normal), which the blog
  *         post's "MXFP8 E4M3" mode names.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent or leave a step open:
  *   - within one expert, routed rows are ordered by ascending token index
  *     (a stable counting sort of the flattened (t, j) list by expert id);
  *   - W13 is [E, 2I, d]: gate rows [0, I), up rows [I, 2I);
