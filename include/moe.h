@@ -197,9 +197,11 @@ moe_status_t moe_forward(moe_plan_t plan, const void* x, const int32_t* ids, con
  * kernels take ragged expert segments, so only m_indptr is needed.  An m_indptr that is
  * not non-decreasing from 0, or whose total exceeds T*k, is caught on the device: every
  * expert is then taken as empty (out is not written) and MOE_DEV_BAD_INDPTR is set
- * (moe_get_status).  BF16 inference plans on the grouped-GEMM path (cfg.path =
+ * (moe_get_status).  Inference plans on the grouped-GEMM path (cfg.path =
  * MOE_PATH_PREFILL, or AUTO with T*k > 256) with T*k*d*2 < 2^31; others return
- * MOE_ERR_UNSUPPORTED.  It uses the plan's dispatch and intermediate workspace, which the
+ * MOE_ERR_UNSUPPORTED.  MXFP8 plans take prepared weights with their scales (as
+ * moe_forward does) and quantize the m_indptr[E] rows of x_rows as they stand, with
+ * moe_quantize_mxfp8's rule, before W13.  It uses the plan's dispatch and intermediate workspace, which the
  * next call overwrites. */
 moe_status_t moe_forward_routed(moe_plan_t plan, const void* x_rows, const int32_t* m_indptr,
                                 const moe_weights_t* w, void* out, void* stream);

@@ -119,8 +119,11 @@ hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
 
 // block_major: scale word (g, row) (bytes of blocks 4 g .. 4 g + 3) at (g * rows + row) * 4
 // (K a multiple of 128); else scales [rows, K/32].
+// rows_dev (optional, device): convert only the first min(rows, *rows_dev) rows; the
+// block-major layout keeps `rows` as its plane stride
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, bool block_major, hipStream_t s);
+                                 uint8_t* scales, bool block_major, hipStream_t s,
+                                 const int32_t* rows_dev = nullptr);
 // block-major scale words of the routed rows x[gather[r]], r < R, from row-major
 // [rows, K/32] scales; K a multiple of 128; gather entries outside [0, rows) read row 0
 hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_t* gather, int64_t R,

@@ -423,9 +423,11 @@ moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t*
                                 const moe_weights_t* w, void* out, void* stream) {
     if (!p || !w) return MOE_ERR_INVALID_ARG;
     const moe_config_t& c = p->cfg;
-    if (c.precision != MOE_BF16 || c.training || p->decode) return MOE_ERR_UNSUPPORTED;
+    const bool mx = c.precision == MOE_MXFP8_E4M3;
+    if (c.training || p->decode) return MOE_ERR_UNSUPPORTED;
     if (p->R * c.d * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;   // 32-bit row offsets into x_rows
     if (c.T > 0 && (!x_rows || !m_indptr || !out || !w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+    if (c.T > 0 && mx && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
     if (!p->ws) return MOE_ERR_WORKSPACE;
     p->have_saved_forward = false;
     if (c.T == 0) return MOE_OK;
@@ -436,6 +438,31 @@ moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t*
         return launch_routed_prep(m_indptr, c.E, p->R, mi, gather, p->at<int32_t>(p->off_status), s);
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
+    if (mx) {
+        // the m_indptr[E] rows are quantized as they stand, their scales written
+        // block-major over the routed rows (the layout W13 copies); the codes take the
+        // `o` region, which W2 does not use here since it writes the caller's rows
+        uint8_t* xq = p->at<uint8_t>(p->off_o);
+        uint8_t* xsr = p->at<uint8_t>(p->off_xsr);
+        e = staged(p, MOE_STAGE_QUANT_X, s, [&] {
+            return launch_quantize_mxfp8(static_cast<const uint16_t*>(x_rows), p->R, c.d, xq, xsr, true, s,
+                                         mi + c.E);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        MxGemmArgs mg{};
+        mg.T = c.T; mg.d = c.d; mg.I = c.I; mg.E = c.E; mg.k = c.k;
+        mg.act = c.activation;
+        mg.m_indptr = mi; mg.gather = gather;
+        mg.xq = xq; mg.xs = xsr;
+        mg.w13q = static_cast<const uint8_t*>(w->w13); mg.w13s = w->w13_scale;
+        mg.w2q = static_cast<const uint8_t*>(w->w2); mg.w2s = w->w2_scale;
+        mg.aq = p->at<uint8_t>(p->off_aq); mg.as = p->at<uint8_t>(p->off_as);
+        mg.o = static_cast<uint16_t*>(out);
+        e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm_mxfp8(MX_W13, mg, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_W2, s, [&] { return launch_gemm_mxfp8(MX_W2, mg, p->num_cu, s); });
+        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+    }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
     g.act = c.activation;

@@ -23,9 +23,14 @@ constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint16_t* __restrict__ v,
                                                             int64_t nblocks, int kb_row, int64_t rows,
+                                                            const int32_t* __restrict__ rows_dev,
                                                             bool block_major,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
+    if (rows_dev) {                       // only the first *rows_dev rows (at most rows)
+        const int64_t n = *rows_dev;
+        if (n < rows) nblocks = (n > 0 ? n : 0) * kb_row;
+    }
     for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks;
          b += (int64_t)gridDim.x * kThreads) {
         const uint4* src = reinterpret_cast<const uint4*>(v + b * 32);
@@ -113,14 +118,15 @@ hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_
 }
 
 hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t* codes,
-                                 uint8_t* scales, bool block_major, hipStream_t s) {
+                                 uint8_t* scales, bool block_major, hipStream_t s,
+                                 const int32_t* rows_dev) {
     if (block_major && K % 128 != 0) return hipErrorInvalidValue;
     const int64_t nblocks = rows * (K / 32);
     if (nblocks == 0) return hipSuccess;
     int64_t grid = (nblocks + kThreads - 1) / kThreads;
     if (grid > 65536) grid = 65536;
     hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, v, nblocks, K / 32,
-                       rows, block_major, codes, scales);
+                       rows, rows_dev, block_major, codes, scales);
     return hipGetLastError();
 }
 

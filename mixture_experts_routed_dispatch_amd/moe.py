@@ -264,13 +264,15 @@ class Layer:
         moe_forward(self.plan, _ptr(x), _ptr(ids), _ptr(scores), w, _ptr(y), _stream(stream))
         return y
 
-    def forward_routed(self, x_rows, m_indptr, w13, w2, out=None, stream=None):
+    def forward_routed(self, x_rows, m_indptr, w13, w2, w13_scale=None, w2_scale=None, out=None,
+                       stream=None):
         """Expert outputs of rows already in expert order (int32 m_indptr [E+1] on the
-        device); out BF16 [T*k, d], of which rows m_indptr[E].. are not written."""
+        device); out BF16 [T*k, d], of which rows m_indptr[E].. are not written.  MXFP8
+        plans take the prepared weights and their scales."""
         import torch
         if out is None:
             out = torch.empty((self.T * self.k, self.d), dtype=torch.bfloat16, device=x_rows.device)
-        w = weights(_ptr(w13), _ptr(w2))
+        w = weights(_ptr(w13), _ptr(w2), _ptr(w13_scale), _ptr(w2_scale))
         moe_forward_routed(self.plan, _ptr(x_rows), _ptr(m_indptr), w, _ptr(out), _stream(stream))
         return out
 

@@ -301,6 +301,68 @@ def test_forward_routed_ragged_segments(torch_cuda):
     layer.close()
 
 
+def test_forward_routed_mxfp8_ragged_segments(torch_cuda):
+    """MXFP8 on caller-made segments (empty experts first, middle and last, a one-row
+    segment, fewer rows than T*k, and an x_rows buffer of exactly m_indptr[E] rows): each
+    row against the oracle as a one-expert token (k = 1, score 1), on the prepared
+    weights, both with FP32 activations and quantizing x and the SwiGLU output as the
+    kernels do; rows past m_indptr[E] stay as they were."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 400, 512, 256, 8, 2
+    counts = np.array([0, 300, 1, 0, 257, 45, 100, 0])
+    m_indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    n = int(m_indptr[-1])
+    assert n < T * k
+    inp = inputs.generate(n, d, I, E, 1, "uniform", seed=33)
+    ids = np.repeat(np.arange(E, dtype=np.int32), counts)[:, None]
+    ones = np.ones((n, 1), np.float32)
+    layer = moe.Layer(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3, path=moe.MOE_PATH_PREFILL)
+    w13q, w13s, w2q, w2s = layer.prepare_weights(bf16_dev(inp.w13), bf16_dev(inp.w2))
+    out = torch.full((T * k, d), 3.0, dtype=torch.bfloat16, device=dev())
+    layer.forward_routed(bf16_dev(inp.x), torch.from_numpy(m_indptr).to(dev()), w13q, w2q, w13s, w2s, out=out)
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    got = np_of(out)
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    ref = oracle.forward_tokens(inp.x, ids, ones, w13f, w2f)
+    ref_q = oracle.forward_tokens_mx(inp.x, ids, ones, w13f, w2f)
+    e, e_q = rel(got[:n], ref), rel(got[:n], ref_q)
+    say("  mxfp8 ragged segments: rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
+    assert e <= TOL_MX
+    assert e_q <= TOL_MX_QUANT
+    assert np.all(got[n:] == 3.0)
+    layer.close()
+
+
+def test_forward_routed_mxfp8_matches_oracle(torch_cuda):
+    """MXFP8: rows put in expert order by the oracle's dispatch give, row for row, the
+    expert outputs of the token-routed forward's quantizing oracle, and the status stays
+    clear."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 600, 512, 384, 6, 3
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=34)
+    m_indptr, gather, slots, _ = oracle.dispatch(inp.ids, inp.scores, E)
+    t = device_inputs(inp)
+    x_rows = t["x"][torch.from_numpy(gather.astype(np.int64)).to(dev())].contiguous()
+    layer = moe.Layer(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3, path=moe.MOE_PATH_PREFILL)
+    w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+    out = layer.forward_routed(x_rows, torch.from_numpy(m_indptr).to(dev()), w13q, w2q, w13s, w2s)
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    ids_rows = np.zeros((T * k, 1), np.int32)
+    for e in range(E):
+        ids_rows[m_indptr[e]:m_indptr[e + 1], 0] = e
+    x_bits = inp.x[gather]
+    ref_q = oracle.forward_tokens_mx(x_bits, ids_rows, np.ones((T * k, 1), np.float32), w13f, w2f)
+    e_q = rel(np_of(out), ref_q)
+    say("  mxfp8 routed: rel %.3e (quantizing oracle)" % e_q)
+    assert e_q <= TOL_MX_QUANT
+    layer.close()
+
+
 def test_forward_routed_rejects_bad_indptr(torch_cuda):
     """A decreasing m_indptr, or one whose total passes T*k, sets MOE_DEV_BAD_INDPTR and
     leaves the output untouched (every expert taken as empty)."""
