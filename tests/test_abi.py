@@ -157,6 +157,29 @@ def test_oracle_and_library_share_nothing():
     assert "mixture_experts_routed_dispatch_amd" not in src
 
 
+def test_plan_explain_mxfp8_regions(L):
+    """An MXFP8 plan's report lists the conversion regions with the sizes the layouts
+    fix: codes of x [T, d], its scales [T, d/32], their routed block-major copy
+    [d/128, R, 4], codes of a [R, I] and their scales; the BF16 `a` region is absent."""
+    T, d, I, E, k = 16384, 4096, 2048, 64, 8
+    plan = moe.moe_plan(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3)
+    try:
+        R = T * k
+        text = moe.moe_plan_explain(plan)
+        sizes = {}
+        for line in text.splitlines():
+            f = line.split()
+            if line.startswith("  ") and len(f) >= 3 and f[1].isdigit():
+                sizes[f[0]] = int(f[1])
+        assert sizes["xq"] == T * d and sizes["xs"] == T * d // 32
+        assert sizes["xs_routed"] == R * d // 32
+        assert sizes["aq"] == R * I and sizes["as"] == R * I // 32
+        assert sizes["o"] == 2 * R * d and "a" not in sizes
+        assert sum(sizes.values()) <= moe.moe_workspace_bytes(plan)
+    finally:
+        moe.moe_plan_destroy(plan)
+
+
 def test_plan_explain_and_recompute_workspace(L):
     """The report names every region with its bytes and the total the plan asks for; a
     training plan that recomputes h needs R * 2I * 2 bytes less (h takes the place of the
