@@ -412,6 +412,41 @@ def test_graph_replay_matches_eager(torch_cuda):
     layer.close()
 
 
+def test_mxfp8_graph_replay_matches_eager(torch_cuda):
+    """The MXFP8 forward (dispatch, x conversion and its routed scale copy, both FP8
+    products, combine) captured in one HIP graph: every replay, with eager calls of the
+    same plan between replays, equals the eager result bit for bit."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    inp = inputs.generate(512, 512, 256, 8, 4, seed=8)
+    t = device_inputs(inp)
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, precision=moe.MOE_MXFP8_E4M3, path=1)
+    w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+    fwd = lambda y=None: layer.forward(t["x"], t["ids"], t["scores"], w13q, w2q, w13s, w2s, y=y)
+    y_eager = fwd()
+    torch.cuda.synchronize()
+    y_out = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(y_out)                                   # warm
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fwd(y_out)
+    for rep in range(4):
+        y_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_out.view(torch.int16), y_eager.view(torch.int16)), rep
+        fwd()                                        # eager work between replays
+        torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    layer.close()
+
+
 @pytest.mark.parametrize("acc,rec", [(False, False), (True, True)])
 def test_training_graph_replay_matches_eager(torch_cuda, acc, rec):
     """Forward + backward of a training plan captured in one HIP graph: every replay (the
