@@ -53,7 +53,7 @@ def parse():
     ap.add_argument("--routed", action="store_true",
                     help="time moe_forward_routed instead: the workload's rows put in expert "
                          "order once outside the timed region, then W13 + SwiGLU and W2 on "
-                         "them (no dispatch, no combine; BF16 forward workloads)")
+                         "them (no dispatch, no combine; forward workloads, BF16 or MXFP8)")
     ap.add_argument("--wgrad-accumulate", action="store_true",
                     help="train workload: the backward adds the weight gradients into the "
                          "existing dW13 / dW2 (plan option wgrad_accumulate)")
@@ -331,8 +331,8 @@ def main():
     state = {"i": 0}
 
     if args.routed:
-        if training or decode or mx:
-            raise SystemExit("--routed: BF16 forward workloads on the grouped-GEMM path only")
+        if training or decode:
+            raise SystemExit("--routed: forward workloads on the grouped-GEMM path only")
         # expert-major rows and m_indptr from the library's own dispatch, once
         m_ind, gath, _, _ = layer.dispatch(t["ids"], t["scores"])
         x_rows = t["x"][gath.long()].contiguous()
