@@ -98,8 +98,14 @@ typedef struct {
 typedef struct {
     const void* w13;          /* BF16 [E, 2I, d], or E4M3 codes (uint8) [E, 2I, d] */
     const void* w2;           /* BF16 [E, d, I],  or E4M3 codes (uint8) [E, d, I]  */
-    const uint8_t* w13_scale; /* MXFP8 only: E8M0 [E, 2I, d/32]; NULL for BF16 */
-    const uint8_t* w2_scale;  /* MXFP8 only: E8M0 [E, d, I/32];  NULL for BF16 */
+    /* MXFP8 only (NULL for BF16): E8M0 scale bytes in the block-major layout that
+     * moe_prepare_weights writes, uint8 [K/128, N, 4] with the expert matrices stacked
+     * as N rows: w13_scale has N = E*2I rows of K = d, w2_scale N = E*d rows of K = I.
+     * Byte 4 (g N + n) + j is the scale of elements [32 (4 g + j), +32) of row n.  The
+     * row-major [rows, K/32] scales of moe_quantize_mxfp8 are NOT this layout and give
+     * wrong results here; prepare weights with moe_prepare_weights. */
+    const uint8_t* w13_scale;
+    const uint8_t* w2_scale;
 } moe_weights_t;
 
 /* Validate cfg against the limits (K = d and I multiples of 64, at most 256
@@ -127,13 +133,18 @@ size_t moe_workspace_bytes(moe_plan_t plan);
 size_t moe_plan_explain(moe_plan_t plan, char* buf, size_t len);
 
 /* Give the plan a device buffer of at least moe_workspace_bytes bytes,
- * 256-byte aligned; the caller keeps ownership and must keep it alive while
- * the plan is used.  Clears the device status word (synchronously, with a
+ * 256-byte aligned (blog post, "Caveats", item 7 and the "Dist-MoE" README intro:
+ * the library owns its temporary memory, sized before the context exists; here the
+ * caller allocates it, so that the calls themselves never allocate, as the nvfp4moe
+ * README, "MoE layer", asks of a warmed plan); the caller keeps ownership and must
+ * keep it alive while the plan is used.  Clears the device status word (synchronously, with a
  * plain memset: call it outside graph capture).  Rebinding forgets the saved
  * forward state. */
 moe_status_t moe_bind_workspace(moe_plan_t plan, void* dptr, size_t bytes);
 
-/* Release the host plan (not the caller's workspace).  NULL is accepted. */
+/* Release the host plan (not the caller's workspace; blog post, "Caveats": one
+ * context per stream, so a plan is released by its one owner).  Returns MOE_OK;
+ * NULL is accepted. */
 moe_status_t moe_plan_destroy(moe_plan_t plan);
 
 /* Deterministic dispatch (nvfp4moe README, "Grouped GEMM" and "Training"):
@@ -226,7 +237,9 @@ moe_status_t moe_backward(moe_plan_t plan, const void* dy, const void* x, const 
  * MOE_ERR_ROUTING when a bit is set, MOE_OK otherwise. */
 moe_status_t moe_get_status(moe_plan_t plan, int32_t* device_flags, int32_t clear, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code (blog post, "What it is selling": unsupported
+ * modes are refused when the context is created, with a reason).  Never NULL; an
+ * unknown code gives "unknown status". */
 const char* moe_status_string(moe_status_t status);
 
 /* Kernel stages of moe_forward / moe_backward.  moe_backward launches SCORE_GRAD,

@@ -10,6 +10,18 @@ MXFP8 E4M3 with prepared weights; the OCP MX v1.0 conversion rule).
 * The shared exponent of a block is floor(log2(amax)) - 8 as a biased E8M0
   byte, clamped to [0, 254]; the dequantized block is within half an E4M3
   step of the input (or saturates at the top).
+
+The quantization-aware forward (x and the gated-activation output a passed
+through the block-32 quantize->dequantize image) is pinned by:
+* two hand-derived cases (tests/golden/mx_forward_requant.json) in which the
+  re-quantization of a, the quantization of x, the floor scale rule and the
+  block boundaries each change the result;
+* reduction to the plain forward: when the re-quantization of a is the identity
+  (selector weights put every a on its grid), the quantized forward of x equals
+  the plain forward of x's quantize->dequantize image bit for bit;
+* the a step alone: with x on its grid, y equals W2 applied to the image of the
+  plain forward's a under an independent quantizer (torch's float8_e4m3fn cast
+  after the floor rule's power-of-two scaling).
 """
 import math
 
@@ -86,15 +98,106 @@ def test_block_quantize_error_bound(orc):
     assert np.array_equal(orc.mx_dequantize(c2, s2)[0], blk)
 
 
-def test_mx_forward_reduces_to_plain_on_grid_values(orc):
-    # When x and every SwiGLU output already sit on their MX grids the quantized
-    # forward equals the plain one; with I = 32 and a single token we can force
-    # that by making W2 and everything downstream irrelevant: zero scores give +0.
+def _unpack(entries, n):
+    v = np.zeros(n, np.float64)
+    for idx, m, e in entries:
+        v[idx] = m * 2.0 ** e
+    return v
+
+
+def test_mx_forward_golden(orc):
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "mx_forward_requant.json")) as f:
+        gold = json.load(f)
+    d = I = 64
+    ids = np.zeros((1, 1), np.int32)
+    scores = np.full((1, 1), 0.5, np.float32)
+    w2 = np.eye(d, I, dtype=np.float32)[None]
+    for case in gold["cases"]:
+        w13 = np.zeros((1, 2 * I, d), np.float32)
+        if case.get("x_ones"):
+            x = np.ones((1, d), np.float32)
+            w13[0, :I] = np.diag(_unpack(case["w1_diag"], I)).astype(np.float32)
+        else:
+            x = _unpack(case["x"], d).astype(np.float32)[None]
+            w13[0, :I] = np.eye(I, d, dtype=np.float32)
+        w13[0, I:] = np.eye(I, d, dtype=np.float32)
+        want = _unpack(case["y"], d)
+        got = orc.forward_tokens_mx(x, ids, scores, w13, w2, act=orc.ACT_REGLU)[0]
+        assert np.array_equal(got, want), (case["name"], np.nonzero(got != want), got[got != want])
+        # the same inputs without any quantization give another result: each listed
+        # derivation step matters
+        plain = orc.forward_tokens(x, ids, scores, w13, w2, act=orc.ACT_REGLU)[0]
+        assert not np.array_equal(plain, want)
+
+
+def _selector_layer(seed, T=6, d=64, I=64, E=3, k=2):
+    """Off-grid x; W1 rows pick one column of x, W3 rows pick the all-ones column 0 times
+    2^-4, except rows 0 and 32 of each expert, which pick column 0 twice (a = 1, the
+    block maximum).  With ReGLU every a is then x_q[c] 2^-4 (or 0, or 1): a 3-bit mantissa
+    within 2^10 of the block's power-of-two maximum, i.e. already on its MX grid."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-3.9, 3.9, (T, d))
+    x[np.abs(x) < 2.0 ** -5] = 0.0
+    x[:, 0] = 1.0
+    x = x.astype(np.float32)
+    w13 = np.zeros((E, 2 * I, d), np.float32)
+    for e in range(E):
+        cols = rng.integers(1, d, I)
+        for i in range(I):
+            if i % 32 == 0:
+                w13[e, i, 0] = 1.0
+                w13[e, I + i, 0] = 1.0
+            else:
+                w13[e, i, cols[i]] = 1.0
+                w13[e, I + i, 0] = 2.0 ** -4
+    w2 = (rng.standard_normal((E, d, I)) / np.sqrt(I)).astype(np.float32)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    scores = rng.uniform(0.1, 1.0, (T, k)).astype(np.float32)
+    return x, ids, scores, w13, w2
+
+
+def test_mx_forward_equals_plain_forward_of_quantized_x(orc):
+    x, ids, scores, w13, w2 = _selector_layer(3)
+    xq = orc.mx_dequantize(*orc.mx_quantize(x))
+    assert not np.array_equal(xq, x)                        # x is off its grid
+    got = orc.forward_tokens_mx(x, ids, scores, w13, w2, act=orc.ACT_REGLU)
+    want = orc.forward_tokens(xq, ids, scores, w13, w2, act=orc.ACT_REGLU)
+    assert np.array_equal(got, want)
+    # and the quantization of x is visible in the result
+    assert not np.array_equal(got, orc.forward_tokens(x, ids, scores, w13, w2, act=orc.ACT_REGLU))
+
+
+def _dq_torch(v):
+    """Quantize->dequantize along the last axis in blocks of 32, written independently
+    of the oracle: scale 2^(floor(log2 amax) - 8) from numpy's frexp, elements through
+    torch's float8_e4m3fn cast after clamping to +-448."""
+    v = np.asarray(v, np.float64)
+    blk = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
+    amax = np.abs(blk).max(-1, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    X = np.where(amax > 0, np.ldexp(1.0, np.clip(ex - 1 - 8, -127, 127)), 1.0)
+    q = np.clip(blk / X, -448.0, 448.0)
+    q8 = torch.from_numpy(q.copy()).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return (q8 * X).reshape(v.shape)
+
+
+def test_mx_forward_requantizes_a(orc):
     from mixture_experts_routed_dispatch_amd import inputs
-    inp = inputs.generate(T=4, d=64, I=32, E=2, k=1, seed=9)
-    y = orc.forward_tokens_mx(inp.x, inp.ids, np.zeros_like(inp.scores), inp.w13, inp.w2)
-    assert np.all(y == 0.0)
-    yq = orc.forward_tokens_mx(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
-    yp = orc.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
-    rel = np.linalg.norm(yq - yp) / np.linalg.norm(yp)
-    assert 1e-3 < rel < 0.1                                  # quantization noise, not a bug
+    inp = inputs.generate(T=5, d=64, I=64, E=4, k=2, seed=11)
+    x = orc.mx_dequantize(*orc.mx_quantize(inp.x))        # x already on its grid
+    w13, w2 = orc._f32(inp.w13), orc._f32(inp.w2)
+    for act in (orc.ACT_SWIGLU, orc.ACT_REGLU):
+        _, a = orc.forward_tokens(x, inp.ids, inp.scores, w13, w2, want_a=True, act=act)
+        aq = _dq_torch(a)
+        assert not np.array_equal(aq, a)
+        want = np.zeros((inp.T, inp.d))
+        for t in range(inp.T):
+            for j in range(inp.k):
+                e = inp.ids[t, j]
+                want[t] += float(inp.scores[t, j]) * (w2[e].astype(np.float64) @ aq[t, j])
+        got = orc.forward_tokens_mx(x, inp.ids, inp.scores, w13, w2, act=act)
+        assert np.abs(got - want).max() <= 1e-12 * np.abs(want).max()
+        plain = orc.forward_tokens(x, inp.ids, inp.scores, w13, w2, act=act)
+        assert np.linalg.norm(got - plain) > 1e-3 * np.linalg.norm(plain)
