@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default run: leave out the decode and MXFP8 workloads reported beside prefill")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
@@ -176,6 +178,17 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, copy_bytes: int
     return tab
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def oracle_threads():
     import oracle
     try:
@@ -210,6 +223,8 @@ def cpu_baseline(inp, training: bool, target_s: float):
         "value": tflops,
         "unit": "TFLOP/s",
         "cores": oracle_threads(),
+        "cpu_model": cpu_model(),
+        "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": "%d of %d tokens of the same batch, %s in the fp64 C oracle (token-major, "
                   "OpenMP over tokens), %.1f s; flop counted as %d*k*I*d per token"
@@ -274,12 +289,56 @@ def main():
               "(no collectives, no sharding)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    out = measure(args, args.workload)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(out.pop("_inp"), WORKLOADS[args.workload][1], args.cpu_seconds)
+    else:
+        out.pop("_inp")
+        out["cpu_baseline"] = None
+    default_run = (args.workload == "prefill" and not args.routed and not args.wgrad_accumulate
+                   and not args.recompute_h and args.activation == "swiglu" and not args.copy_probe
+                   and not args.no_extra)
+    if default_run:
+        # the other headline workloads (decode at 1 and 32 tokens: HBM-bound; MXFP8: the
+        # FP8 products), a few steps each, reported beside the prefill line
+        import torch
+        extra = {}
+        for w, steps in (("decode1", 200), ("decode32", 50), ("mxfp8", 10)):
+            torch.cuda.empty_cache()
+            sub = argparse.Namespace(**vars(args))
+            sub.steps, sub.warmup = steps, 3
+            o = measure(sub, w)
+            o.pop("_inp")
+            extra[w] = {key: o[key] for key in ("value", "unit", "ms_per_step", "dtype", "config", "stage_us",
+                                                 "roofline", "decode", "tokens_per_s", "mfma_frac_layer",
+                                                 "gemm_mfma_frac", "steps", "warmup") if key in o}
+        out["other_workloads"] = extra
+    print(json.dumps(out), flush=True)
+
+
+def device_inputs(inp):
+    """The seeded host arrays of one workload as device tensors (BF16 bit patterns kept)."""
+    import numpy as np
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+    out = dict(x=bf16(inp.x), w13=bf16(inp.w13), w2=bf16(inp.w2),
+               ids=torch.from_numpy(inp.ids).to("cuda"), scores=torch.from_numpy(inp.scores).to("cuda"))
+    if inp.dy is not None:
+        out["dy"] = bf16(inp.dy)
+    return out
+
+
+def measure(args, workload):
+    """Time args.steps steps of one workload; returns the JSON fields (and the host
+    inputs under "_inp", for the CPU baseline)."""
     import numpy as np
     import torch
     from mixture_experts_routed_dispatch_amd import inputs, moe
-    from tests.gpu_util import device_inputs
 
-    cfg_name, training = WORKLOADS[args.workload]
+    cfg_name, training = WORKLOADS[workload]
     inp = inputs.generate_config(cfg_name, seed=0, with_dy=training)
     T, d, I, E, k = inp.T, inp.d, inp.I, inp.E, inp.k
     R = T * k
@@ -422,14 +481,14 @@ def main():
         roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": achieved / mfma_peak,
                 "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
-                "traffic": traffic_for(dom, args.workload)}
+                "traffic": traffic_for(dom, workload)}
     else:
         nbytes = min_bytes.get(dom, float("nan"))
         achieved = nbytes / (stage_us[dom] * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "algorithmic_per_launch": nbytes, "avg_launch_us": stage_us[dom],
-                "traffic": traffic_for(dom, args.workload)}
+                "traffic": traffic_for(dom, workload)}
     gemm_us = sum(stage_us.get(s, 0.0) for s in gemm_flop)
     gemm_tflops = (sum(gemm_flop[s] for s in gemm_flop if s in stage_us) / (gemm_us * 1e-6) / 1e12
                    if gemm_us > 0 else None)
@@ -471,18 +530,15 @@ def main():
         "wall_ms_per_step": 1e3 * wall / args.steps,
         "ms_per_step_with_kernel_events": ms_step_profiled,
         "roofline": roof,
+        "_inp": inp,
     }
     if decode:
         out["decode"] = {"active_experts_per_call": n_active_mean,
                          "weight_bytes_per_call": n_active_mean * 3 * I * d * 2.0,
                          "layer_hbm_gbs": layer_bytes / (ms_step * 1e-3) / 1e9,
                          "layer_hbm_frac": layer_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS}
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, training, args.cpu_seconds)
-    else:
-        out["cpu_baseline"] = None
     layer.close()
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

@@ -1,0 +1,123 @@
+// Host sanitizer run of the library's plan logic (tests/test_sanitize.py builds this file
+// with the library's moe_api.cpp under g++ -fsanitize=address,undefined, with the kernel
+// launchers replaced by stubs that fail): plan validation over valid and invalid
+// configurations, workspace layout, the memory report into buffers of every size, the
+// status strings and the host-side refusals of forward / backward, so that an
+// out-of-bounds access, a leak or undefined behaviour in the host code stops the run.
+// No device is touched: none of these calls reaches a HIP runtime function.
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "../../mixture_experts_routed_dispatch_amd/csrc/kernels.h"
+
+namespace moe {
+hipError_t launch_dispatch(const int32_t*, const float*, int, int, int, int32_t*, int32_t*, int32_t*,
+                           int32_t*, float*, int32_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_routed_prep(const int32_t*, int, int64_t, int32_t*, int32_t*, int32_t*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+hipError_t launch_gemm(GemmMode, const GemmArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_gemm_mxfp8(MxMode, const MxGemmArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int, int, int, uint16_t*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+hipError_t launch_score_grad(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, float*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+hipError_t launch_wgrad_rows(const uint16_t*, const uint16_t*, int, const int32_t*, const float*, int64_t, int,
+                             uint16_t*, uint16_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_w13(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_w2(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_decode_w2_one(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_quantize_mxfp8(const uint16_t*, int64_t, int, uint8_t*, uint8_t*, bool, hipStream_t,
+                                 const int32_t*) { return hipErrorInvalidValue; }
+hipError_t launch_route_scales(const uint8_t*, int64_t, const int32_t*, int64_t, int, uint8_t*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
+}  // namespace moe
+
+static int fails = 0;
+#define CHECK(c) do { if (!(c)) { if (fails++ < 10) std::fprintf(stderr, "check failed: %s (line %d)\n", #c, __LINE__); } } while (0)
+
+static moe_config_t cfg(int T, int d, int I, int E, int k) {
+    moe_config_t c;
+    std::memset(&c, 0, sizeof c);
+    c.T = T; c.d = d; c.I = I; c.E = E; c.k = k;
+    return c;
+}
+
+int main() {
+    // valid plans of every kind: their workspace sizes and reports
+    std::vector<moe_config_t> ok;
+    ok.push_back(cfg(8192, 2048, 768, 16, 8));
+    moe_config_t t = cfg(8192, 2048, 768, 128, 8); t.training = 1; ok.push_back(t);
+    t.recompute_h = 1; ok.push_back(t);
+    t.wgrad_accumulate = 1; t.activation = MOE_ACT_GEGLU; ok.push_back(t);
+    ok.push_back(cfg(1, 2048, 768, 128, 8));
+    ok.push_back(cfg(32, 2048, 768, 128, 8));
+    moe_config_t m = cfg(16384, 4096, 2048, 64, 8); m.precision = MOE_MXFP8_E4M3; ok.push_back(m);
+    ok.push_back(cfg(0, 256, 128, 8, 2));
+    ok.push_back(cfg(4096, 256, 64, 256, 32));
+    moe_config_t rc = cfg(300, 128, 256, 8, 2); rc.training = 1; rc.recompute_h = 1; ok.push_back(rc);
+    for (const moe_config_t& c : ok) {
+        moe_plan_t p = nullptr;
+        CHECK(moe_plan(&c, &p) == MOE_OK && p != nullptr);
+        if (!p) continue;
+        CHECK(moe_workspace_bytes(p) > 0 && moe_workspace_bytes(p) % 256 == 0);
+        const size_t n = moe_plan_explain(p, nullptr, 0);
+        CHECK(n > 0);
+        for (size_t len : {size_t(1), size_t(2), size_t(17), n, n + 1, n + 100}) {
+            std::string buf(len + 8, '#');
+            const size_t r = moe_plan_explain(p, &buf[0], len);
+            CHECK(r == n);
+            const size_t w = len - 1 < n ? len - 1 : n;
+            CHECK(buf[w] == '\0' && std::strlen(buf.c_str()) == w && buf[len] == '#');
+        }
+        CHECK(moe_profile(p, 1) == MOE_OK && moe_profile(p, 0) == MOE_OK);
+        float ms[MOE_STAGE_COUNT];
+        int32_t cnt[MOE_STAGE_COUNT];
+        CHECK(moe_profile_read(p, ms, cnt, MOE_STAGE_COUNT) == MOE_OK);
+        // no workspace bound: refused before anything is enqueued
+        moe_weights_t w;
+        std::memset(&w, 0, sizeof w);
+        char dummy[64];
+        w.w13 = dummy; w.w2 = dummy; w.w13_scale = (const uint8_t*)dummy; w.w2_scale = (const uint8_t*)dummy;
+        const moe_status_t fs = moe_forward(p, dummy, (const int32_t*)dummy, (const float*)dummy, &w, dummy, nullptr);
+        CHECK(fs == (c.T == 0 ? MOE_ERR_WORKSPACE : MOE_ERR_WORKSPACE));
+        CHECK(moe_bind_workspace(p, nullptr, 1 << 20) == MOE_ERR_INVALID_ARG);
+        CHECK(moe_bind_workspace(p, dummy + 1, 1 << 20) == MOE_ERR_INVALID_ARG);
+        CHECK(moe_plan_destroy(p) == MOE_OK);
+    }
+    // invalid configurations are refused and allocate nothing
+    struct Bad { moe_config_t c; moe_status_t want; };
+    std::vector<Bad> bad;
+    bad.push_back({cfg(-1, 256, 128, 8, 2), MOE_ERR_INVALID_ARG});
+    bad.push_back({cfg(64, 0, 128, 8, 2), MOE_ERR_INVALID_ARG});
+    bad.push_back({cfg(64, 250, 128, 8, 2), MOE_ERR_UNSUPPORTED});
+    bad.push_back({cfg(64, 256, 100, 8, 2), MOE_ERR_UNSUPPORTED});
+    bad.push_back({cfg(64, 256, 128, 300, 2), MOE_ERR_UNSUPPORTED});
+    bad.push_back({cfg(64, 256, 128, 8, 9), MOE_ERR_UNSUPPORTED});
+    bad.push_back({cfg(64, 256, 128, 64, 33), MOE_ERR_UNSUPPORTED});
+    bad.push_back({cfg(131073, 256, 128, 8, 1), MOE_ERR_UNSUPPORTED});
+    moe_config_t mt = cfg(64, 256, 128, 8, 2); mt.precision = MOE_MXFP8_E4M3; mt.training = 1;
+    bad.push_back({mt, MOE_ERR_UNSUPPORTED});
+    moe_config_t ac = cfg(64, 256, 128, 8, 2); ac.wgrad_accumulate = 1; bad.push_back({ac, MOE_ERR_UNSUPPORTED});
+    moe_config_t ra = cfg(64, 256, 128, 8, 2); ra.activation = 7; bad.push_back({ra, MOE_ERR_INVALID_ARG});
+    moe_config_t pa = cfg(64, 256, 128, 8, 2); pa.path = 9; bad.push_back({pa, MOE_ERR_INVALID_ARG});
+    moe_config_t dp = cfg(64, 256, 128, 8, 8); dp.path = MOE_PATH_DECODE; bad.push_back({dp, MOE_ERR_UNSUPPORTED});
+    for (const Bad& b : bad) {
+        moe_plan_t p = reinterpret_cast<moe_plan_t>(&fails);
+        CHECK(moe_plan(&b.c, &p) == b.want);
+        CHECK(p == nullptr);
+    }
+    CHECK(moe_plan(nullptr, nullptr) == MOE_ERR_INVALID_ARG);
+    CHECK(moe_workspace_bytes(nullptr) == 0 && moe_plan_explain(nullptr, nullptr, 0) == 0);
+    CHECK(moe_plan_destroy(nullptr) == MOE_OK);
+    for (int s = -8; s <= 1; ++s) CHECK(moe_status_string((moe_status_t)s) != nullptr);
+    if (fails) { std::fprintf(stderr, "%d checks failed\n", fails); return 1; }
+    std::printf("host sanitizer run: ok\n");
+    return 0;
+}

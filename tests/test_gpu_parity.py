@@ -4,11 +4,14 @@
   gather, slots and probs on every workload's routing and on adversarial ones;
   the device status word flags invalid routing.
 * Forward (blog post "What it is selling"; nvfp4moe README "MoE layer"):
-  norm-wise relative error <= 2e-2 (BF16) against the fp64 oracle, on small
-  layers that span several tiles with ragged tails, and at the full workload
-  sizes on sampled tokens, with the launch configuration the benchmark times.
-* Backward (DGRAD, WGRAD, router gradient): the same bound on dx, dscores,
-  dW13 and dW2; experts with no row get exactly +0.0.
+  norm-wise relative error <= 2e-2 (BF16) against the fp64 oracle, BF16 results
+  also under the 5e-3 noise floor and every element within 3e-2 (|ref| + rms)
+  (tests/gpu_util.py), on small layers that span several tiles with ragged
+  tails, and at the full workload sizes (every token of the prefill and decode
+  workloads, sampled tokens of the MXFP8 one), with the launch configuration
+  the benchmark times.
+* Backward (DGRAD, WGRAD, router gradient): the same bars on dx, dscores,
+  dW13 and dW2 (also with h recomputed); experts with no row get exactly +0.0.
 * Run-to-run bitwise determinism and HIP-graph replay equal to eager calls.
 """
 import numpy as np
@@ -16,11 +19,10 @@ import pytest
 
 import oracle
 from mixture_experts_routed_dispatch_amd import inputs
-from tests.gpu_util import bf16_dev, dev, device_inputs, maxrel, np_of, rel, say
+from tests.gpu_util import BF16, BF16_WGRAD, MX, MX_QUANT, bf16_dev, check, dev, device_inputs, np_of, rel, say
 
 pytestmark = pytest.mark.gpu
 
-TOL_BF16 = 2e-2
 
 
 @pytest.fixture(scope="module")
@@ -135,9 +137,7 @@ def test_forward_small(torch_cuda, T, d, I, E, k, routing):
     y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
     torch.cuda.synchronize()
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
-    e = rel(np_of(y), ref)
-    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
-    assert e <= TOL_BF16
+    check("y", np_of(y), ref, **BF16)
     layer.close()
 
 
@@ -167,16 +167,9 @@ def test_forward_full_size_sampled(torch_cuda, name, path):
     st, flags = layer.status()
     assert flags == 0
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # bitwise deterministic
-    rng = np.random.default_rng(5)
-    n = min(inp.T, 48)
-    toks = np.sort(rng.choice(inp.T, size=n, replace=False)).astype(np.int32)
-    toks[0] = 0
-    toks[-1] = inp.T - 1
-    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
-    got = np_of(y)[toks]
-    e = rel(got, ref)
-    say("  rel %.3e maxrel %.3e" % (e, maxrel(got, ref)))
-    assert e <= TOL_BF16
+    # every token: the fp64 oracle takes the 8192 prefill tokens in a few seconds
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    check("y (all %d tokens)" % inp.T, np_of(y), ref, **BF16)
     layer.close()
 
 
@@ -235,14 +228,10 @@ def test_forward_ragged_expert_tails(torch_cuda, training):
     toks = np.array(sorted(toks), np.int32)
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
     got = np_of(y)[toks]
-    e_y = rel(got, ref)
-    say("  %d tokens: y rel %.3e maxrel %.3e" % (len(toks), e_y, maxrel(got, ref)))
-    assert e_y <= TOL_BF16
+    check("y (%d tokens)" % len(toks), got, ref, **BF16)
     if training:
         dx_ref, _ = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, toks=toks)
-        e_dx = rel(np_of(dx)[toks], dx_ref)
-        say("  dx rel %.3e" % e_dx)
-        assert e_dx <= TOL_BF16
+        check("dx", np_of(dx)[toks], dx_ref, **BF16)
     layer.close()
 
 
@@ -265,9 +254,7 @@ def test_forward_routed_matches_oracle(torch_cuda, T, d, I, E, k, routing):
     assert layer.status()[1] == 0
     _, o_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, want_o=True)
     got = np_of(out)[slots.reshape(-1)].reshape(T, k, d)
-    e = rel(got, o_ref)
-    say("  rel %.3e maxrel %.3e" % (e, maxrel(got, o_ref)))
-    assert e <= TOL_BF16
+    check("o", got, o_ref, **BF16)
     layer.close()
 
 
@@ -294,9 +281,7 @@ def test_forward_routed_ragged_segments(torch_cuda):
     assert layer.status()[1] == 0
     _, o_ref = oracle.forward_tokens(inp.x, ids, ones, inp.w13, inp.w2, want_o=True)
     got = np_of(out)
-    e = rel(got[:n], o_ref[:, 0])
-    say("  ragged segments: rel %.3e" % e)
-    assert e <= TOL_BF16
+    check("o (ragged segments)", got[:n], o_ref[:, 0], **BF16)
     assert np.all(got[n:] == 3.0)
     layer.close()
 
@@ -327,10 +312,8 @@ def test_forward_routed_mxfp8_ragged_segments(torch_cuda):
     w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
     ref = oracle.forward_tokens(inp.x, ids, ones, w13f, w2f)
     ref_q = oracle.forward_tokens_mx(inp.x, ids, ones, w13f, w2f)
-    e, e_q = rel(got[:n], ref), rel(got[:n], ref_q)
-    say("  mxfp8 ragged segments: rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
-    assert e <= TOL_MX
-    assert e_q <= TOL_MX_QUANT
+    check("o vs fp32 oracle", got[:n], ref, **MX)
+    check("o vs quantizing oracle", got[:n], ref_q, **MX_QUANT)
     assert np.all(got[n:] == 3.0)
     layer.close()
 
@@ -357,9 +340,7 @@ def test_forward_routed_mxfp8_matches_oracle(torch_cuda):
         ids_rows[m_indptr[e]:m_indptr[e + 1], 0] = e
     x_bits = inp.x[gather]
     ref_q = oracle.forward_tokens_mx(x_bits, ids_rows, np.ones((T * k, 1), np.float32), w13f, w2f)
-    e_q = rel(np_of(out), ref_q)
-    say("  mxfp8 routed: rel %.3e (quantizing oracle)" % e_q)
-    assert e_q <= TOL_MX_QUANT
+    check("o vs quantizing oracle", np_of(out), ref_q, **MX_QUANT)
     layer.close()
 
 
@@ -561,9 +542,7 @@ def test_decode_small(torch_cuda, T, d, I, E, k, routing):
     assert flags == 0
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))      # counters reset between calls
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
-    e = rel(np_of(y), ref)
-    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
-    assert e <= TOL_BF16
+    check("y", np_of(y), ref, **BF16)
     layer.close()
 
 
@@ -581,7 +560,7 @@ def test_decode_zero_scores_and_rerouting(torch_cuda):
     y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
     torch.cuda.synchronize()
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
-    assert rel(np_of(y), ref) <= TOL_BF16
+    check("y", np_of(y), ref, **BF16)
     layer.close()
 
 
@@ -710,11 +689,9 @@ def test_backward_small(torch_cuda, T, d, I, E, k, routing):
     dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
     dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
     dw13_ref = dw13_ref.reshape(E, 2 * I, d)
-    errs = dict(y=rel(np_of(y), y_ref), dx=rel(np_of(dx), dx_ref), ds=rel(np_of(ds), ds_ref),
-                dw2=rel(np_of(dw2), dw2_ref), dw13=rel(np_of(dw13), dw13_ref))
-    say("  " + " ".join("%s %.3e" % kv for kv in errs.items()))
-    for kname, v in errs.items():
-        assert v <= TOL_BF16, kname
+    for name, got, ref in (("y", np_of(y), y_ref), ("dx", np_of(dx), dx_ref), ("ds", np_of(ds), ds_ref),
+                           ("dw2", np_of(dw2), dw2_ref), ("dw13", np_of(dw13), dw13_ref)):
+        check(name, got, ref, **(BF16_WGRAD if name.startswith("dw") else BF16))
     counts = np.bincount(inp.ids.ravel(), minlength=E)
     for e in np.nonzero(counts == 0)[0]:
         assert np.all(dw2[e].view(torch.int16).cpu().numpy() == 0)
@@ -750,9 +727,8 @@ def test_backward_split_weight_gradient_tiles(torch_cuda, T, d, I, E, k, hot):
     assert torch.equal(dw2.view(torch.int16), dw2b.view(torch.int16))
     dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
     dw13_ref = dw13_ref.reshape(E, 2 * I, d)
-    e_w2, e_w13 = rel(np_of(dw2), dw2_ref), rel(np_of(dw13), dw13_ref)
-    say("  dw2 %.3e dw13 %.3e" % (e_w2, e_w13))
-    assert max(e_w2, e_w13) <= TOL_BF16
+    check("dw2", np_of(dw2), dw2_ref, **BF16_WGRAD)
+    check("dw13", np_of(dw13), dw13_ref, **BF16_WGRAD)
     layer.close()
 
 
@@ -787,9 +763,8 @@ def test_backward_accumulates_weight_gradients(torch_cuda, T, d, I, E, k, routin
     dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
     dw13_ref = dw13_ref.reshape(E, 2 * I, d) + np_of(dw13_0)
     dw2_ref = dw2_ref + np_of(dw2_0)
-    e13, e2 = rel(np_of(dw13), dw13_ref), rel(np_of(dw2), dw2_ref)
-    say("  dw13 %.3e dw2 %.3e" % (e13, e2))
-    assert max(e13, e2) <= TOL_BF16
+    check("dw13", np_of(dw13), dw13_ref, **BF16_WGRAD)
+    check("dw2", np_of(dw2), dw2_ref, **BF16_WGRAD)
     counts = np.bincount(inp.ids.ravel(), minlength=E)
     for e in np.nonzero(counts == 0)[0]:
         assert torch.equal(dw13[e].view(torch.int16), dw13_0[e].view(torch.int16))
@@ -802,15 +777,15 @@ def test_backward_accumulates_weight_gradients(torch_cuda, T, d, I, E, k, routin
                                                (300, 256, 128, 128, 8, "zipf")])
 def test_backward_recompute_h_matches_saved(torch_cuda, T, d, I, E, k, routing):
     """recompute_h: the forward keeps no h and the backward recomputes it with the same
-    kernel from the same x and W13, so every gradient equals, bit for bit, that of a plan
-    that saved h (which the other backward tests check against the oracle)."""
+    kernel from the same x and W13.  Every gradient is checked against the oracle, and
+    equals, bit for bit, that of a plan that saved h."""
     torch = torch_cuda
     from mixture_experts_routed_dispatch_amd import moe
     say("backward recompute h", T, d, I, E, k, routing)
     inp = inputs.generate(T, d, I, E, k, routing, seed=43, with_dy=True)
     t = device_inputs(inp)
     outs = []
-    for rec in (False, True):
+    for rec in (True, False):
         layer = moe.Layer(T, d, I, E, k, training=True, recompute_h=rec)
         y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
         dx, dw13, dw2, ds = layer.backward(t["dy"], t["x"], t["w13"], t["w2"])
@@ -818,6 +793,12 @@ def test_backward_recompute_h_matches_saved(torch_cuda, T, d, I, E, k, routing):
         assert layer.status()[1] == 0
         outs.append([v.clone() for v in (y, dx, dw13, dw2, ds)])
         layer.close()
+    y_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy)
+    refs = (y_ref, dx_ref, dw13_ref.reshape(E, 2 * I, d), dw2_ref, ds_ref)
+    for name, got, ref in zip(("y", "dx", "dw13", "dw2", "ds"), outs[0], refs):
+        check(name + " (recomputed h)", np_of(got), ref, **(BF16_WGRAD if name.startswith("dw") else BF16))
     for name, a, b in zip(("y", "dx", "dw13", "dw2", "ds"), outs[0], outs[1]):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b), name
@@ -860,19 +841,28 @@ def test_backward_full_size_sampled(torch_cuda):
     for a, b in ((dx, dx2), (dw13, dw13b), (dw2, dw2b), (ds, ds2)):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
+    # 1024 tokens (every expert's first and last routed token among them) for dx and dS,
+    # 64 of the 768 intermediate columns (the first and last of each 256-wide tile among
+    # them) for dW13 and dW2, every expert
     rng = np.random.default_rng(7)
-    toks = np.sort(rng.choice(inp.T, size=32, replace=False)).astype(np.int32)
+    toks = set(rng.choice(inp.T, size=1024, replace=False).tolist())
+    for e in range(inp.E):
+        te = np.nonzero((inp.ids == e).any(axis=1))[0]
+        if len(te):
+            toks.update((int(te[0]), int(te[-1])))
+    toks = np.array(sorted(toks), np.int32)
     dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy,
                                             toks=toks)
-    e_dx, e_ds = rel(np_of(dx)[toks], dx_ref), rel(np_of(ds)[toks], ds_ref)
-    cols = np.sort(rng.choice(inp.I, size=6, replace=False)).astype(np.int32)
+    check("dx (%d tokens)" % len(toks), np_of(dx)[toks], dx_ref, **BF16)
+    check("ds", np_of(ds)[toks], ds_ref, **BF16)
+    cols = set(rng.choice(inp.I, size=58, replace=False).tolist()) | {0, 255, 256, 511, 512, inp.I - 1}
+    cols = np.array(sorted(cols), np.int32)
     dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy,
                                           icols=cols)
     dw2_np = np_of(dw2)[:, :, cols]
     dw13_np = np.stack([np_of(dw13[:, cols, :]), np_of(dw13[:, inp.I + cols, :])], axis=1)
-    e_w2, e_w13 = rel(dw2_np, dw2_ref), rel(dw13_np, dw13_ref)
-    say("  dx %.3e ds %.3e dw2 %.3e dw13 %.3e" % (e_dx, e_ds, e_w2, e_w13))
-    assert max(e_dx, e_ds, e_w2, e_w13) <= TOL_BF16
+    check("dw2 (%d columns)" % len(cols), dw2_np, dw2_ref, **BF16_WGRAD)
+    check("dw13", dw13_np, dw13_ref, **BF16_WGRAD)
     counts = np.bincount(inp.ids.ravel(), minlength=inp.E)
     empty = np.nonzero(counts == 0)[0]
     assert len(empty) >= 8
@@ -973,8 +963,6 @@ def test_prepare_weights_bit_exact(torch_cuda):
 
 # ------------------------------------------------------------------ MXFP8 forward
 
-TOL_MX = 6e-2          # against the FP32 oracle on the prepared weights
-TOL_MX_QUANT = 1e-2    # against the oracle that quantizes x and the SwiGLU output at the same points
 
 MX_SHAPES = [
     # T, d, I, E, k, routing
@@ -1015,10 +1003,8 @@ def test_mxfp8_forward_small(torch_cuda, T, d, I, E, k, routing):
     w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f)
     ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f)
-    e, e_q = rel(y, ref), rel(y, ref_q)
-    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
-    assert e <= TOL_MX
-    assert e_q <= TOL_MX_QUANT
+    check("y vs fp32 oracle", y, ref, **MX)
+    check("y vs quantizing oracle", y, ref_q, **MX_QUANT)
 
 
 def test_mxfp8_forward_full_size_sampled(torch_cuda):
@@ -1030,16 +1016,14 @@ def test_mxfp8_forward_full_size_sampled(torch_cuda):
     del t
     torch.cuda.empty_cache()
     rng = np.random.default_rng(9)
-    toks = np.sort(rng.choice(inp.T, size=24, replace=False)).astype(np.int32)
+    toks = np.sort(rng.choice(inp.T, size=256, replace=False)).astype(np.int32)
     toks[0] = 0
     toks[-1] = inp.T - 1
     w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f, toks=toks)
     ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f, toks=toks)
-    e, e_q = rel(y[toks], ref), rel(y[toks], ref_q)
-    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
-    assert e <= TOL_MX
-    assert e_q <= TOL_MX_QUANT
+    check("y vs fp32 oracle", y[toks], ref, **MX)
+    check("y vs quantizing oracle", y[toks], ref_q, **MX_QUANT)
 
 
 # ------------------------------------------------------------------ GeGLU / ReGLU
@@ -1065,9 +1049,7 @@ def test_forward_gated_activations(torch_cuda, act, name, T, d, I, E, k, routing
     torch.cuda.synchronize()
     assert layer.status()[1] == 0
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, act=act)
-    e = rel(np_of(y), ref)
-    say("  rel %.3e maxrel %.3e" % (e, maxrel(np_of(y), ref)))
-    assert e <= TOL_BF16
+    check("y", np_of(y), ref, **BF16)
     layer.close()
 
 
@@ -1088,11 +1070,9 @@ def test_backward_gated_activations(torch_cuda, act, name, T, d, I, E, k, routin
     y_ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, act=act)
     dx_ref, ds_ref = oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
     dw2_ref, dw13_ref = oracle.wgrad_cols(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, act=act)
-    errs = dict(y=rel(np_of(y), y_ref), dx=rel(np_of(dx), dx_ref), ds=rel(np_of(ds), ds_ref),
-                dw2=rel(np_of(dw2), dw2_ref), dw13=rel(np_of(dw13), dw13_ref.reshape(E, 2 * I, d)))
-    say("  " + " ".join("%s %.3e" % kv for kv in errs.items()))
-    for kname, v in errs.items():
-        assert v <= TOL_BF16, kname
+    for name, got, ref in (("y", np_of(y), y_ref), ("dx", np_of(dx), dx_ref), ("ds", np_of(ds), ds_ref),
+                           ("dw2", np_of(dw2), dw2_ref), ("dw13", np_of(dw13), dw13_ref.reshape(E, 2 * I, d))):
+        check(name, got, ref, **(BF16_WGRAD if name.startswith("dw") else BF16))
     layer.close()
 
 
@@ -1113,8 +1093,6 @@ def test_mxfp8_forward_gated_activations(torch_cuda, act, name):
     w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
     ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13f, w2f, act=act)
     ref_q = oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13f, w2f, act=act)
-    e, e_q = rel(y, ref), rel(y, ref_q)
-    say("  rel %.3e (fp32 oracle)  %.3e (quantizing oracle)" % (e, e_q))
-    assert e <= TOL_MX
-    assert e_q <= TOL_MX_QUANT
+    check("y vs fp32 oracle", y, ref, **MX)
+    check("y vs quantizing oracle", y, ref_q, **MX_QUANT)
     layer.close()
