@@ -52,7 +52,8 @@ typedef enum {
     MOE_ERR_WORKSPACE = -3,    /* no workspace bound, or the bound one is too small */
     MOE_ERR_STATE = -4,        /* e.g. backward without a preceding training forward */
     MOE_ERR_HIP = -5,          /* a HIP runtime call or kernel launch failed */
-    MOE_ERR_ROUTING = -6       /* device-detected invalid routing (moe_get_status) */
+    MOE_ERR_ROUTING = -6,      /* device-detected invalid routing (moe_get_status) */
+    MOE_ERR_TOO_LARGE = -7     /* moe_forward_static: the plan's scratch exceeds MOE_STATIC_SCRATCH_BYTES */
 } moe_status_t;
 
 typedef enum {
@@ -195,6 +196,25 @@ moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const vo
  * the W2 outputs for moe_backward; a later forward overwrites them. */
 moe_status_t moe_forward(moe_plan_t plan, const void* x, const int32_t* ids, const float* scores,
                          const moe_weights_t* w, void* y, void* stream);
+
+/* Forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation, kernels
+ * and result as moe_forward, bit for bit, but the scratch the plan needs lives in a
+ * static array that the library holds on each GPU it runs on, of MOE_STATIC_SCRATCH_BYTES
+ * (32 MiB) per device, kept until the process ends; no workspace needs to be bound.
+ * The caller passes inputs and outputs as for moe_forward.  Inference plans only
+ * (MOE_ERR_UNSUPPORTED for training = 1); a plan whose moe_workspace_bytes exceeds
+ * MOE_STATIC_SCRATCH_BYTES returns MOE_ERR_TOO_LARGE before anything is enqueued.  It
+ * calls no allocating routine (hipMalloc, hipFree or any allocating library call); the
+ * first call on a device looks up that device's copy of the array.  Every call on one
+ * GPU shares that GPU's array, which keeps the last call's contents: calls that overlap
+ * on one GPU (on different streams, or from different plans) race, so serialise them.
+ * The device status word of the call lives in the array too: it is cleared at the start
+ * of each call, and moe_get_status on the plan reads it until the plan's next call.
+ * Leave moe_profile off (its events are created on first use). */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+moe_status_t moe_forward_static(moe_plan_t plan, const void* x, const int32_t* ids, const float* scores,
+                                const moe_weights_t* w, void* y, void* stream);
 
 /* Forward of rows already in expert order (nvfp4moe README, "MoE layer": frameworks
  * that already hold expert-major rows call the layer on them directly).  For each

@@ -129,4 +129,12 @@ hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t
 hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_t* gather, int64_t R,
                                int K, uint8_t* out, hipStream_t s);
 
+// Scratch for moe_forward_static: one array of kStaticScratchBytes per device (the size
+// moe.h states as MOE_STATIC_SCRATCH_BYTES).  static_scratch returns the current device's
+// copy (looked up once per device) and its compute-unit count.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+hipError_t static_scratch(void** ptr, int* num_cu);
+// p[0 .. n) = v, as a kernel (no memset node when the caller captures the stream)
+hipError_t launch_fill_i32(int32_t* p, int n, int32_t v, hipStream_t s);
+
 }  // namespace moe

@@ -43,6 +43,7 @@ struct moe_plan_s {
     int num_cu;
     bool have_saved_forward;
     bool h_aliased;                    // recompute_h: h occupies the dxp / xg / dys region
+    int32_t* status_word;              // device status word of the last call (workspace or static scratch)
     // measurement-only event pairs around kernel stages (moe_profile)
     struct ProfRec { int stage; hipEvent_t a, b; };
     bool prof_on = false;
@@ -170,6 +171,7 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->ws_size = 0;
     p->num_cu = 0;
     p->have_saved_forward = false;
+    p->status_word = nullptr;
     *out = p;
     return MOE_OK;
 }
@@ -264,6 +266,7 @@ moe_status_t moe_bind_workspace(moe_plan_t p, void* dptr, size_t bytes) {
     p->ws_size = bytes;
     p->num_cu = ncu > 0 ? ncu : 256;
     p->have_saved_forward = false;
+    p->status_word = p->at<int32_t>(p->off_status);
     return MOE_OK;
 }
 
@@ -278,6 +281,7 @@ moe_status_t moe_dispatch(moe_plan_t p, const int32_t* ids, const float* scores,
     if (p->R > 0 && (!ids || !scores || !gather || !slots || !probs)) return MOE_ERR_INVALID_ARG;
     if (!p->ws) return MOE_ERR_WORKSPACE;
     const moe_config_t& c = p->cfg;
+    p->status_word = p->at<int32_t>(p->off_status);
     hipError_t e = launch_dispatch(ids, scores, c.T, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr,
                                    gather, slots, probs, p->at<int32_t>(p->off_status),
                                    static_cast<hipStream_t>(stream));
@@ -319,6 +323,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     if (!p->ws) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     p->have_saved_forward = false;
+    p->status_word = p->at<int32_t>(p->off_status);
     if (c.T == 0) {
         p->have_saved_forward = c.training != 0;
         return MOE_OK;
@@ -419,6 +424,29 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     return MOE_OK;
 }
 
+moe_status_t moe_forward_static(moe_plan_t p, const void* x, const int32_t* ids, const float* scores,
+                                const moe_weights_t* w, void* y, void* stream) {
+    if (!p || !w) return MOE_ERR_INVALID_ARG;
+    if (p->cfg.training) return MOE_ERR_UNSUPPORTED;
+    if (p->ws_bytes > kStaticScratchBytes) return MOE_ERR_TOO_LARGE;
+    void* sp = nullptr;
+    int ncu = 0;
+    if (static_scratch(&sp, &ncu) != hipSuccess) return MOE_ERR_HIP;
+    // the forward below runs on the static scratch in place of the bound workspace (the
+    // plan is not reentrant, so swapping its workspace for the call is safe); the status
+    // word is cleared first, by a kernel, since the array keeps the last call's contents
+    struct Swap {
+        moe_plan_s* p; char* ws; size_t size; int ncu;
+        ~Swap() { p->ws = ws; p->ws_size = size; p->num_cu = ncu; }
+    } restore{p, p->ws, p->ws_size, p->num_cu};
+    p->ws = static_cast<char*>(sp);
+    p->ws_size = kStaticScratchBytes;
+    p->num_cu = ncu;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_fill_i32(p->at<int32_t>(p->off_status), 1, 0, s) != hipSuccess) return MOE_ERR_HIP;
+    return moe_forward(p, x, ids, scores, w, y, stream);
+}
+
 moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t* m_indptr,
                                 const moe_weights_t* w, void* out, void* stream) {
     if (!p || !w) return MOE_ERR_INVALID_ARG;
@@ -430,6 +458,7 @@ moe_status_t moe_forward_routed(moe_plan_t p, const void* x_rows, const int32_t*
     if (c.T > 0 && mx && (!w->w13_scale || !w->w2_scale)) return MOE_ERR_INVALID_ARG;
     if (!p->ws) return MOE_ERR_WORKSPACE;
     p->have_saved_forward = false;
+    p->status_word = p->at<int32_t>(p->off_status);
     if (c.T == 0) return MOE_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t* mi = p->at<int32_t>(p->off_m_indptr);
@@ -567,10 +596,10 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
 
 moe_status_t moe_get_status(moe_plan_t p, int32_t* device_flags, int32_t clear, void* stream) {
     if (!p || !device_flags) return MOE_ERR_INVALID_ARG;
-    if (!p->ws) return MOE_ERR_WORKSPACE;
+    if (!p->status_word) return MOE_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int32_t v = 0;
-    int32_t* dflag = p->at<int32_t>(p->off_status);
+    int32_t* dflag = p->status_word;
     if (hipMemcpyAsync(&v, dflag, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return MOE_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
     if (clear && v) {
@@ -612,6 +641,7 @@ const char* moe_status_string(moe_status_t st) {
         case MOE_ERR_STATE: return "invalid call order (no saved training forward)";
         case MOE_ERR_HIP: return "HIP runtime error";
         case MOE_ERR_ROUTING: return "invalid routing detected on the device";
+        case MOE_ERR_TOO_LARGE: return "the plan needs more scratch than the static array holds (MOE_STATIC_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

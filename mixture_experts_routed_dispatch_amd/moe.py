@@ -23,6 +23,8 @@ MOE_ERR_WORKSPACE = -3
 MOE_ERR_STATE = -4
 MOE_ERR_HIP = -5
 MOE_ERR_ROUTING = -6
+MOE_ERR_TOO_LARGE = -7
+MOE_STATIC_SCRATCH_BYTES = 32 << 20
 
 MOE_BF16 = 0
 MOE_MXFP8_E4M3 = 1
@@ -38,7 +40,8 @@ MOE_ACT_SWIGLU, MOE_ACT_GEGLU, MOE_ACT_REGLU = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_destroy",
-           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward", "moe_forward_routed",
+           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward", "moe_forward_static",
+           "moe_forward_routed",
            "moe_backward", "moe_get_status", "moe_status_string", "moe_profile", "moe_plan_explain",
            "moe_profile_read")
 
@@ -95,6 +98,8 @@ def lib():
         L.moe_prepare_weights.restype = ctypes.c_int
         L.moe_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
         L.moe_forward.restype = ctypes.c_int
+        L.moe_forward_static.argtypes = [vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
+        L.moe_forward_static.restype = ctypes.c_int
         L.moe_forward_routed.argtypes = [vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
         L.moe_forward_routed.restype = ctypes.c_int
         L.moe_backward.argtypes = [vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp]
@@ -169,6 +174,10 @@ def weights(w13, w2, w13_scale=0, w2_scale=0) -> MoeWeights:
 
 def moe_forward(plan, x, ids, scores, w: MoeWeights, y, stream=0):
     _ok(lib().moe_forward(plan, x, ids, scores, ctypes.byref(w), y, stream), "moe_forward")
+
+
+def moe_forward_static(plan, x, ids, scores, w: MoeWeights, y, stream=0):
+    _ok(lib().moe_forward_static(plan, x, ids, scores, ctypes.byref(w), y, stream), "moe_forward_static")
 
 
 def moe_forward_routed(plan, x_rows, m_indptr, w: MoeWeights, out, stream=0):

@@ -37,6 +37,8 @@ hipError_t launch_quantize_mxfp8(const uint16_t*, int64_t, int, uint8_t*, uint8_
 hipError_t launch_route_scales(const uint8_t*, int64_t, const int32_t*, int64_t, int, uint8_t*, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t static_scratch(void**, int*) { return hipErrorInvalidValue; }
+hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace moe
 
 static int fails = 0;
@@ -117,6 +119,25 @@ int main() {
     CHECK(moe_workspace_bytes(nullptr) == 0 && moe_plan_explain(nullptr, nullptr, 0) == 0);
     CHECK(moe_plan_destroy(nullptr) == MOE_OK);
     for (int s = -8; s <= 1; ++s) CHECK(moe_status_string((moe_status_t)s) != nullptr);
+    // the static-scratch forward refuses training plans and plans beyond its maximum
+    // before it looks for the array
+    {
+        moe_config_t tc = cfg(64, 256, 128, 8, 2); tc.training = 1;
+        moe_config_t big = cfg(65536, 2048, 768, 16, 2);
+        moe_plan_t p1 = nullptr, p2 = nullptr;
+        CHECK(moe_plan(&tc, &p1) == MOE_OK && moe_plan(&big, &p2) == MOE_OK);
+        moe_weights_t w;
+        std::memset(&w, 0, sizeof w);
+        char dummy[64];
+        CHECK(moe_forward_static(p1, dummy, (const int32_t*)dummy, (const float*)dummy, &w, dummy, nullptr) ==
+              MOE_ERR_UNSUPPORTED);
+        CHECK(moe_workspace_bytes(p2) > MOE_STATIC_SCRATCH_BYTES);
+        CHECK(moe_forward_static(p2, dummy, (const int32_t*)dummy, (const float*)dummy, &w, dummy, nullptr) ==
+              MOE_ERR_TOO_LARGE);
+        CHECK(moe_forward_static(nullptr, dummy, nullptr, nullptr, &w, dummy, nullptr) == MOE_ERR_INVALID_ARG);
+        moe_plan_destroy(p1);
+        moe_plan_destroy(p2);
+    }
     if (fails) { std::fprintf(stderr, "%d checks failed\n", fails); return 1; }
     std::printf("host sanitizer run: ok\n");
     return 0;

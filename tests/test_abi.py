@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_status_strings(L):
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert len(moe.status_string(st)) >= 2 and moe.status_string(st) != "unknown status"
     assert moe.status_string(-99) == "unknown status"
 
