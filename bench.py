@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--wgrad-accumulate", action="store_true",
                     help="train workload: the backward adds the weight gradients into the "
                          "existing dW13 / dW2 (plan option wgrad_accumulate)")
+    ap.add_argument("--mega", action="store_true",
+                    help="decode workloads: the fused one-launch decode (plan option mega: W13, "
+                         "activation and W2 chunked over I, then the combine)")
     ap.add_argument("--recompute-h", action="store_true",
                     help="train workload: the forward keeps no h, the backward recomputes it "
                          "(plan option recompute_h)")
@@ -83,6 +86,7 @@ KERNEL_OF_STAGE = {
     "wgrad_w2": ("grouped_gemm<4,", "wgrad_fixup<4>"), "wgrad_w13": ("grouped_gemm<5,", "wgrad_fixup<5>"),
     "quant_x": ("quantize_kernel", "route_scales_kernel"), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),
     "wgrad_rows": ("wgrad_rows_kernel",), "recompute_h": ("grouped_gemm<0,",),
+    "mega": ("mega_decode", "mega_combine"),
 }
 # the MXFP8 workload's GEMM stages run the block-scaled kernels
 KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0,",), w2=("grouped_gemm_mx<1,",))
@@ -295,7 +299,7 @@ def main():
     else:
         out.pop("_inp")
         out["cpu_baseline"] = None
-    default_run = (args.workload == "prefill" and not args.routed and not args.wgrad_accumulate
+    default_run = (args.workload == "prefill" and not args.routed and not args.wgrad_accumulate and not args.mega
                    and not args.recompute_h and args.activation == "swiglu" and not args.copy_probe
                    and not args.no_extra)
     if default_run:
@@ -347,8 +351,10 @@ def measure(args, workload):
     mx = cfg_name == "mxfp8"
     if (args.wgrad_accumulate or args.recompute_h) and not training:
         raise SystemExit("--wgrad-accumulate, --recompute-h: the train workload only")
+    if args.mega and not decode:
+        raise SystemExit("--mega: the decode workloads only")
     layer = moe.Layer(T, d, I, E, k, training=training,
-                      precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16,
+                      precision=moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16, mega=args.mega,
                       wgrad_accumulate=args.wgrad_accumulate, recompute_h=args.recompute_h,
                       activation=("swiglu", "geglu", "reglu").index(args.activation))
     stream = torch.cuda.current_stream()
@@ -474,7 +480,8 @@ def measure(args, workload):
                  "quant_x": T * d * (2.0 + 1.0 + 1.0 / 32),
                  "decode_w13": n_active_mean * 2 * I * d * 2.0 + 2.0 * T * d + 2.0 * R * I + 4.0 * R,
                  "decode_w2": n_active_mean * d * I * 2.0 + 2.0 * R * I + 2.0 * R * d + 2.0 * T * d
-                 + 8.0 * R}
+                 + 8.0 * R,
+                 "mega": n_active_mean * 3 * I * d * 2.0 + 2.0 * T * d + 2.0 * T * d + 8.0 * R}
     mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     if dom in gemm_flop:
         achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
@@ -517,7 +524,8 @@ def measure(args, workload):
             ("forward+backward" + (", weight gradients accumulated" if args.wgrad_accumulate else "")
              + (", h recomputed in the backward" if args.recompute_h else ""))
             if training else
-            ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed else "forward"),
+            ("forward of pre-dispatched rows (moe_forward_routed: W13 + SwiGLU, W2)" if args.routed
+             else "forward, fused (mega) decode" if args.mega else "forward"),
             "" if args.activation == "swiglu" else ", %s" % {"geglu": "GeGLU", "reglu": "ReGLU"}[args.activation]),
             "T": T, "d": d, "I": I, "E": E, "k": k, "routed_rows": R,
             "flop_per_step": flop},

@@ -94,6 +94,12 @@ typedef struct {
                                   reuses later (blog post, "Caveats": activation-slot
                                   overflow selects recomputation); training plans only */
     int32_t activation;        /* MOE_ACT_*; every path and precision */
+    int32_t mega;              /* 1: the decode path fuses W13 -> activation -> W2 into one
+                                  launch chunked over I, with FP32 partial outputs that a
+                                  light second launch adds up and combines (blog post, "What it
+                                  is selling": Mega fuses both projections into a chunked
+                                  pipeline); decode plans only (inference, BF16, T*k <= 256,
+                                  path AUTO or DECODE) */
 } moe_config_t;
 
 typedef struct {
@@ -264,7 +270,8 @@ const char* moe_status_string(moe_status_t status);
 
 /* Kernel stages of moe_forward / moe_backward.  moe_backward launches SCORE_GRAD,
  * [RECOMPUTE_H,] DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order; the
- * one-token decode runs W2 and the combine as one kernel, recorded as DECODE_W2. */
+ * one-token decode runs W2 and the combine as one kernel, recorded as DECODE_W2; a mega
+ * decode plan runs its one launch as MEGA. */
 #define MOE_STAGE_DISPATCH 0
 #define MOE_STAGE_QUANT_X 1
 #define MOE_STAGE_W13 2
@@ -280,7 +287,8 @@ const char* moe_status_string(moe_status_t status);
 #define MOE_STAGE_DECODE_W2 12
 #define MOE_STAGE_WGRAD_ROWS 13
 #define MOE_STAGE_RECOMPUTE_H 14
-#define MOE_STAGE_COUNT 15
+#define MOE_STAGE_MEGA 15
+#define MOE_STAGE_COUNT 16
 
 /* Per-stage timing with HIP events, for measurement only.  While enabled,
  * moe_forward and moe_backward record a pair of HIP events around each kernel

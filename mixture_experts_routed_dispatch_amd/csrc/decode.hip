@@ -54,16 +54,17 @@ struct DecodeSmem {
 };
 
 // Counts, active experts, the entries sorted by expert, and routing flags, from ids;
-// every workgroup of a launch runs it (block 0 reports the flags).
+// every workgroup of a launch runs it (block 0 reports the flags).  Threads 0 .. 255 do
+// the work; a larger workgroup's other threads only take part in its barriers.
 __device__ void decode_setup(DecodeSmem& sm, const int32_t* __restrict__ ids, int T, int k, int E,
                              int32_t* status, bool report) {
-    static_assert(kThreads == 256, "one thread per expert id and per routed entry");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool worker = tid < 256;
     const int R = T * k;
-    sm.cnt[tid] = 0;
+    if (worker) sm.cnt[tid] = 0;
     __syncthreads();
     int my_e = -1;
-    if (tid < R) {
+    if (worker && tid < R) {
         const int e = ids[tid];
         const bool ok = (unsigned)e < (unsigned)E;
         my_e = ok ? e : -1;
@@ -76,30 +77,37 @@ __device__ void decode_setup(DecodeSmem& sm, const int32_t* __restrict__ ids, in
             if (bad) atomicOr(status, bad);
         }
     }
-    if (tid < R) sm.ids[tid] = my_e;
+    if (worker && tid < R) sm.ids[tid] = my_e;
     __syncthreads();
     // active experts in ascending id (ballot ranks) and the exclusive prefix of the
     // counts over the expert ids (wave scans plus the wave totals)
-    const int c = sm.cnt[tid];
-    const bool active = tid < E && c > 0;
-    const uint64_t b = __ballot(active);
-    int incl = c;
-    for (int off = 1; off < MOE_WAVE; off <<= 1) {
-        const int v = __shfl_up(incl, off, MOE_WAVE);
-        if (lane >= off) incl += v;
+    int c = 0, incl = 0;
+    bool active = false;
+    uint64_t b = 0;
+    if (worker) {
+        c = sm.cnt[tid];
+        active = tid < E && c > 0;
+        b = __ballot(active);
+        incl = c;
+        for (int off = 1; off < MOE_WAVE; off <<= 1) {
+            const int v = __shfl_up(incl, off, MOE_WAVE);
+            if (lane >= off) incl += v;
+        }
+        if (lane == MOE_WAVE - 1) sm.wsum[wave] = incl;
+        if (lane == 0) sm.wact[wave] = __popcll(b);
     }
-    if (lane == MOE_WAVE - 1) sm.wsum[wave] = incl;
-    if (lane == 0) sm.wact[wave] = __popcll(b);
     __syncthreads();
-    int pre = 0, pre_act = 0;
-    for (int w = 0; w < wave; ++w) { pre += sm.wsum[w]; pre_act += sm.wact[w]; }
-    if (active) sm.slot_expert[pre_act + __popcll(b & lanemask_lt())] = tid;
-    sm.pfx[tid] = pre + incl - c;
-    if (tid == kThreads - 1) sm.pfx[256] = pre + incl;
-    if (tid == 0) {
-        int n = 0;
-        for (int w = 0; w < kWaves; ++w) n += sm.wact[w];
-        sm.n_active = n;
+    if (worker) {
+        int pre = 0, pre_act = 0;
+        for (int w = 0; w < wave; ++w) { pre += sm.wsum[w]; pre_act += sm.wact[w]; }
+        if (active) sm.slot_expert[pre_act + __popcll(b & lanemask_lt())] = tid;
+        sm.pfx[tid] = pre + incl - c;
+        if (tid == 255) sm.pfx[256] = pre + incl;
+        if (tid == 0) {
+            int nact = 0;
+            for (int w = 0; w < 4; ++w) nact += sm.wact[w];
+            sm.n_active = nact;
+        }
     }
     __syncthreads();
     // entry q goes after the entries q' < q of its expert
@@ -348,6 +356,223 @@ __global__ __launch_bounds__(kThreads, 1) void decode_w2_one(DecodeArgs g) {
     }
 }
 
+// ---------------------------------------------------------------- "Mega" decode
+// The blog post's Mega mode ("What it is selling": both projections fused into a chunked
+// pipeline) for small batches: one launch streams every active expert's W13 and W2 once,
+// with no round trip of the SwiGLU output through memory, and a second, light launch adds
+// the chunks' partial outputs and combines them.  A work item of the first launch is
+// (active expert e, chunk c of 32 intermediate columns), eight waves per item; for each 16
+// routed rows of e:
+//   * the item's loads are issued at its start: the routed rows of x (copied straight to
+//     LDS), wave w's share of W13 (8 gate and 8 up rows for intermediate columns
+//     c*32 + 8 (w % 4) .., over K half w / 4) and half of its share of W2 (the chunk's 32
+//     columns, 64 contiguous bytes, of every 8th block of 16 W2 rows); the other half of
+//     W2 goes out as soon as the W13 products have freed their registers;
+//   * part 1: g, u for the chunk (the two K halves added through LDS in a fixed order) and
+//     a = silu(g) u rounded to BF16 (where the staged path rounds it) into LDS;
+//   * part 2: the chunk's share of the expert output, o_c[m][n] = sum_{i in chunk}
+//     W2_e[n][i] a[m][i], one MFMA per 16 rows of W2, in FP32, written to
+//     part[entry][c][n].
+// The combine launch then computes
+//   y[t][n] = sum_j s[t][j] * bf16(sum_c part[t*k + j][c][n])   (c in a fixed order, then
+// j ascending from +0.0, FP32, one rounding): the staged path's rounding points, with only
+// the FP32 summation order of o differing.
+constexpr int kMegaChunk = 32;     // intermediate columns per mega item
+constexpr int kMegaThreads = 512;  // eight waves per item
+constexpr int kMegaKC = 64;        // K steps of 32 per load round (2048 elements; two halves)
+constexpr int kMegaNB = 16;        // W2 n-blocks of 16 per wave per load round (d <= 2048: all)
+
+template <int kAct>
+__global__ __launch_bounds__(kMegaThreads, 1) void mega_decode(DecodeArgs g, float* __restrict__ part) {
+    constexpr int IC = kMegaChunk;
+    constexpr int kHalf = kMegaKC / 2;            // K steps per wave per load round
+    __shared__ DecodeSmem sm;
+    __shared__ __attribute__((aligned(16))) uint16_t xs[16][kMegaKC * 32];   // x of 16 routed rows, a K chunk
+    __shared__ __attribute__((aligned(16))) uint16_t as[16][IC];            // a of 16 routed rows, BF16
+    __shared__ f32x4_t gu[4][MOE_WAVE];                                      // K half 1 of each block
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int blk = wave & 3, half = wave >> 2;
+    const int d = g.d, I = g.I, k = g.k, C = I / IC;
+    const int S = d / 32;
+    const bool one = g.T == 1;
+    int items;
+    if (one) {
+        if (blockIdx.x == 0 && tid < kThreads) decode_flags_one_token(g);
+        items = k * C;
+    } else {
+        decode_setup(sm, g.ids, g.T, k, g.E, g.status, blockIdx.x == 0);
+        items = sm.n_active * C;
+    }
+    // consecutive items (neighbouring chunks of one expert, which share the 128-byte lines
+    // of W2) on consecutive workgroups of one XCD
+    const int G = gridDim.x;
+    const int vid = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+    for (int item = vid; item < items; item += G) {
+        const int slot = item / C, c = item - slot * C;
+        int e, M, e0;
+        if (!slot_info(g, sm, one, slot, e, M, e0)) continue;
+        auto entry = [&](int m) { return one ? e0 : sm.ent[e0 + m]; };
+        // W2 loads through a buffer resource over expert e's matrix: lane offset in a VGPR,
+        // the n-block step in an SGPR (64-bit addresses per load would not fit the registers)
+        const uint64_t w2b = (uint64_t)(uintptr_t)(g.w2 + (size_t)e * d * I);
+        const __amdgpu_buffer_rsrc_t w2rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(w2b >> 32)) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)w2b)),
+            (short)0, __builtin_amdgcn_readfirstlane(d * I * 2), 0x00020000);
+        const int w2off = ((16 * wave + n) * I + c * IC + 8 * kq) * 2;   // bytes
+        const int w2step = 8 * 16 * I * 2;                                 // bytes between this wave's n-blocks
+        auto ld_w2 = [&](int q) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(w2rs, w2off, q * w2step, 0);
+            return __builtin_bit_cast(bf16x8_t, v);
+        };
+        const int i0 = c * IC + 8 * blk;
+        const int wr = (n < 8) ? (i0 + n) : (I + i0 + n - 8);
+        const uint16_t* w13r = g.w13 + ((size_t)e * 2 * I + wr) * d + 8 * kq;
+        const int nq_w = ((d / 16) - wave + 7) / 8;   // W2 n-blocks of this wave
+        for (int m0 = 0; m0 < M; m0 += 16) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            bf16x8_t wb[kMegaNB];
+            for (int kc = 0; kc < S; kc += kMegaKC) {
+                // the routed x rows m0 .. min(M, m0 + 16) - 1 of this K chunk go straight to
+                // LDS (1 KiB per wave copy; rows past M stay as they are: they only feed
+                // output rows that are never used), then this wave's W13 loads of the chunk
+                // (K half `half`) and, in the first chunk, its W2 loads
+                const int kw = (S - kc < kMegaKC ? S - kc : kMegaKC) * 32;    // x elements in the chunk
+                const int rows = M - m0 < 16 ? M - m0 : 16;
+                const int pieces = (kw + 511) / 512;                         // 512 elements per copy
+                const int ncopy = rows * pieces;
+                for (int q = wave; q < ncopy; q += kMegaThreads / MOE_WAVE) {
+                    const int r = q / pieces, part512 = q - r * pieces;
+                    const uint32_t dst = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t*)&xs[r][512 * part512];
+                    // lanes past the chunk (a last copy of a row shorter than 512) read the
+                    // chunk's last 8 elements again; those LDS columns are never read
+                    int col = 512 * part512 + 8 * lane;
+                    col = col < kw - 8 ? col : kw - 8;
+                    const uint32_t voff = (uint32_t)(((size_t)(entry(m0 + r) / k) * d + kc * 32 + col) * 2);
+                    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                                 :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(g.x) : "memory");
+                }
+                const int s0 = kc + half * kHalf;
+                bf16x8_t wv[kHalf];
+#pragma unroll
+                for (int s = 0; s < kHalf; ++s)
+                    if (s0 + s < S) wv[s] = ld_bf16x8(w13r + 32 * (s0 + s));
+                if (kc == 0) {
+#pragma unroll
+                    for (int q = 0; q < kMegaNB / 2; ++q)
+                        if (q < nq_w) wb[q] = ld_w2(q);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");           // the x copies (and the rest)
+                __syncthreads();
+#pragma unroll
+                for (int s = 0; s < kHalf; ++s)
+                    if (s0 + s < S) {
+                        const bf16x8_t xa =
+                            *reinterpret_cast<const bf16x8_t*>(&xs[n][32 * (half * kHalf + s) + 8 * kq]);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wv[s], acc, 0, 0, 0);
+                    }
+                __syncthreads();                  // xs is rewritten by the next chunk
+            }
+            // the rest of the first W2 round, now that the W13 registers are free
+#pragma unroll
+            for (int q = kMegaNB / 2; q < kMegaNB; ++q)
+                if (q < nq_w) wb[q] = ld_w2(q);
+            // the two K halves of block blk added in order (half 0 + half 1)
+            if (half == 1) gu[blk][lane] = acc;
+            __syncthreads();
+            if (half == 0) {
+                acc += gu[blk][lane];
+                // the up value of gate column n < 8 sits in lane n + 8 of the same 16-lane group
+                float up[4];
+#pragma unroll
+                for (int z = 0; z < 4; ++z) up[z] = __shfl_down(acc[z], 8, 16);
+                if (n < 8) {
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const int mm = m0 + 4 * kq + z;
+                        as[4 * kq + z][8 * blk + n] =
+                            mm < M ? (uint16_t)f32_to_bf16(act_f<kAct>(acc[z]) * up[z]) : (uint16_t)0;
+                    }
+                }
+            }
+            __syncthreads();
+            // part 2: o_c = W2_e[:, chunk] a for n-blocks wave, wave + 8, ...
+            const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(&as[n][8 * kq]);
+            for (int q0 = 0; q0 < nq_w; q0 += kMegaNB) {
+                if (q0 > 0) {
+#pragma unroll
+                    for (int q = 0; q < kMegaNB; ++q)
+                        if (q0 + q < nq_w) wb[q] = ld_w2(q0 + q);
+                }
+#pragma unroll
+                for (int q = 0; q < kMegaNB; ++q) {
+                    if (q0 + q >= nq_w) break;
+                    const int nb = wave + 8 * (q0 + q);
+                    const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4_t o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, wb[q], zero4, 0, 0, 0);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        const int mm = m0 + 4 * kq + z;
+                        if (mm < M) part[((size_t)entry(mm) * C + c) * d + 16 * nb + n] = o[z];
+                    }
+                }
+            }
+            __syncthreads();                      // as and gu are rewritten by the next row group
+        }
+    }
+}
+
+// The combine of the mega path: units (t, block of 64 features).  Thread (h, j, 8
+// features) sums the chunk partials c = h, h + 4, ... of entry t*k + j in ascending c; the
+// four sums are then added in h order, rounded to BF16 (o), and the k experts added in j
+// order; an entry with an invalid expert id contributes 0.
+__global__ __launch_bounds__(kThreads) void mega_combine(DecodeArgs g, const float* __restrict__ part) {
+    __shared__ float red[4][kMaxTopK][64];
+    const int tid = threadIdx.x;
+    const int d = g.d, k = g.k, C = g.I / kMegaChunk;
+    const int units = g.T * (d / 64);
+    for (int u = blockIdx.x; u < units; u += gridDim.x) {
+        const int t = u / (d / 64), n0 = (u - t * (d / 64)) * 64;
+        for (int p = tid; p < 4 * k * 8; p += kThreads) {
+            const int h = p & 3, f8 = ((p >> 2) & 7) * 8, j = p >> 5;
+            const int q = t * k + j;
+            f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+            if ((unsigned)g.ids[q] < (unsigned)g.E) {
+                const float* src = part + (size_t)q * C * d + n0 + f8;
+                constexpr int kL = 8;             // chunks per thread with loads in flight at once
+                for (int cb = h; cb < C; cb += 4 * kL) {
+                    f32x4_t v[kL][2];
+#pragma unroll
+                    for (int l = 0; l < kL; ++l) {
+                        const int cc = cb + 4 * l;
+                        if (cc < C) {
+                            v[l][0] = *reinterpret_cast<const f32x4_t*>(src + (size_t)cc * d);
+                            v[l][1] = *reinterpret_cast<const f32x4_t*>(src + (size_t)cc * d + 4);
+                        }
+                    }
+#pragma unroll
+                    for (int l = 0; l < kL; ++l)
+                        if (cb + 4 * l < C) { o0 += v[l][0]; o1 += v[l][1]; }
+                }
+            }
+#pragma unroll
+            for (int z = 0; z < 4; ++z) { red[h][j][f8 + z] = o0[z]; red[h][j][f8 + 4 + z] = o1[z]; }
+        }
+        __syncthreads();
+        if (tid < 64) {
+            float y = 0.f;
+            for (int j = 0; j < k; ++j) {
+                const bool valid = (unsigned)g.ids[t * k + j] < (unsigned)g.E;
+                const float o = ((red[0][j][tid] + red[1][j][tid]) + red[2][j][tid]) + red[3][j][tid];
+                y = __builtin_fmaf(g.scores[t * k + j], valid ? bf16_to_f32(f32_to_bf16(o)) : 0.f, y);
+            }
+            g.y[(size_t)t * d + n0 + tid] = (uint16_t)f32_to_bf16(y);
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s) {
@@ -393,6 +618,30 @@ hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
 
 hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s) {
     return launch_decode(decode_w2<false>, decode_w2<true>, g, g.d / 16, g.I / 32, num_cu, s);
+}
+
+int mega_chunk(int, int) { return kMegaChunk; }
+
+hipError_t launch_mega_decode(const DecodeArgs& g, float* part, int num_cu, hipStream_t s) {
+    const int R = g.T * g.k;
+    if (R <= 0) return hipSuccess;
+    if (R > kMaxDecodeRows || g.k > kMaxTopK || g.d % 64 != 0 || g.I % kMegaChunk != 0)
+        return hipErrorInvalidValue;
+    const int slots = R < g.E ? R : g.E;
+    int grid = slots * (g.I / kMegaChunk);
+    const int cap = 2 * num_cu;
+    grid = grid < cap ? grid : cap;
+    if (grid >= 8) grid -= grid % 8;
+    const dim3 gd(grid), bd(kMegaThreads);
+    if (g.act == kActGeGLU) hipLaunchKernelGGL((mega_decode<kActGeGLU>), gd, bd, 0, s, g, part);
+    else if (g.act == kActReGLU) hipLaunchKernelGGL((mega_decode<kActReGLU>), gd, bd, 0, s, g, part);
+    else hipLaunchKernelGGL((mega_decode<kActSwiGLU>), gd, bd, 0, s, g, part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int cgrid = g.T * (g.d / 64);
+    cgrid = cgrid < 4 * num_cu ? cgrid : 4 * num_cu;
+    hipLaunchKernelGGL(mega_combine, dim3(cgrid), dim3(kThreads), 0, s, g, part);
+    return hipGetLastError();
 }
 
 }  // namespace moe

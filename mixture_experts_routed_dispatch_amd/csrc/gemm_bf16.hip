@@ -494,29 +494,48 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 
     f32x16_t acc[4][4];
     // One k step: 16 MFMAs on (pf, qf) in four groups of four (row block a).  Into
-    // each group go the LDS reads of P and Q fragment a of the next k step (from ring
-    // buffer rbuf, k step rks, into npf / nqf) and, after it, copy `dma_first + a` of
-    // the stage being prefetched, so that reads and copies are spread over the MFMAs
-    // instead of queueing up together.  The scheduling fences keep that order (the
-    // copies are inline assembly, which the MFMAs could otherwise drift across).
+    // each group go two LDS fragment reads of the next k step (from ring buffer rbuf, k
+    // step rks, into npf / nqf) and, after them, copy `dma_first + a` of the stage being
+    // prefetched, so that reads and copies are spread over the MFMAs instead of queueing
+    // up together.  The reads go in the order the next step consumes them: its first
+    // group takes P fragment 0 with all four Q fragments, so the Q fragments are read
+    // first (groups 0 and 1) and P fragments 0 .. 3 after them (groups 2 and 3); read in
+    // pairs (P a, Q a) instead, the Q fragment read last was needed by the next step's
+    // fourth MFMA, a few MFMAs after its read was issued.  The scheduling fences keep that
+    // order (the copies are inline assembly, which the MFMAs could otherwise drift across).
+    auto read_item = [&](const char* rbase, int x, int rks, int i, bf16x8_t npf[4], bf16x8_t nqf[4]) {
+        if (i < 4) {
+            if constexpr (kQmn) nqf[i] = read_tr(rbase, trbaseQ, i, rks);
+            else nqf[i] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[i] ^ x));
+        } else {
+            if constexpr (kPmn) npf[i - 4] = read_tr(rbase, trbase, i - 4, rks);
+            else npf[i - 4] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[i - 4] ^ x));
+        }
+    };
     auto mfma_step = [&](const bf16x8_t pf[4], const bf16x8_t qf[4], int rbuf, int rks,
                          bf16x8_t npf[4], bf16x8_t nqf[4], int dma_kt, int dma_buf, int dma_first) {
         const char* rbase = lds + rbuf * BUFB;
         const int x = rks ? 32 : 0;
+        constexpr int kQreads = kQmn ? 2 : 1, kPreads = kPmn ? 2 : 1;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             acc[a][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[0], acc[a][0], 0, 0, 0);
-            if constexpr (kPmn) npf[a] = read_tr(rbase, trbase, a, rks);
-            else npf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragP[a] ^ x));
+            read_item(rbase, x, rks, 2 * a, npf, nqf);
             acc[a][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[1], acc[a][1], 0, 0, 0);
-            if constexpr (kQmn) nqf[a] = read_tr(rbase, trbaseQ, a, rks);
-            else nqf[a] = *reinterpret_cast<const bf16x8_t*>(rbase + (fragQ[a] ^ x));
+            read_item(rbase, x, rks, 2 * a + 1, npf, nqf);
             acc[a][2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[2], acc[a][2], 0, 0, 0);
             acc[a][3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[3], acc[a][3], 0, 0, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, kPmn ? 2 : 1, 0);   // LDS read(s) of P
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, kQmn ? 2 : 1, 0);   // LDS read(s) of Q
+            if (a < 2) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, kQreads, 0);   // LDS read(s) of a Q fragment
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kQreads, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kPreads, 0);   // LDS read(s) of a P fragment
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, kPreads, 0);
+            }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             dma_one(dma_kt, dma_buf, dma_first + a);
             __builtin_amdgcn_sched_barrier(0);

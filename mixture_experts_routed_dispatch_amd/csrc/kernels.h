@@ -116,6 +116,11 @@ hipError_t launch_decode_w2(const DecodeArgs& g, int num_cu, hipStream_t s);
 // of decode_w2 and combine).
 constexpr int kMaxTopK = 32;
 hipError_t launch_decode_w2_one(const DecodeArgs& g, int num_cu, hipStream_t s);
+// "Mega" decode: W13 + activation + W2 chunked over I in one launch (chunks of
+// mega_chunk(T, k) = 32 intermediate columns), FP32 partial expert outputs in part
+// [T*k, I / chunk, d], then a combine launch into y.
+int mega_chunk(int T, int k);
+hipError_t launch_mega_decode(const DecodeArgs& g, float* part, int num_cu, hipStream_t s);
 
 // block_major: scale word (g, row) (bytes of blocks 4 g .. 4 g + 3) at (g * rows + row) * 4
 // (K a multiple of 128); else scales [rows, K/32].

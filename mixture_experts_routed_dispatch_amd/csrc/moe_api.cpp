@@ -23,6 +23,8 @@ namespace {
 constexpr int64_t kMaxRoutedRows = 131072;   // nvfp4moe README, "Limits"
 constexpr int kMaxExperts = 256;             // nvfp4moe README, "Limits"
 constexpr size_t kMaxProfileRecords = 4096;
+// the status region: the sticky device flags (cleared when a workspace is bound)
+constexpr int kStatusWords = 1;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -37,6 +39,7 @@ struct moe_plan_s {
     size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
     size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_xsr, off_aq, off_as;
     size_t off_part, off_split;        // split weight-gradient tiles: partial sums, descriptors
+    size_t off_mega;                   // mega decode: FP32 partial expert outputs [T*k, I / chunk, d]
     size_t ws_bytes;
     char* ws;
     size_t ws_size;
@@ -123,6 +126,8 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     const bool decode_ok = c.training == 0 && c.precision == MOE_BF16 && R > 0 &&
                            R <= kMaxDecodeRows;
     if (c.path == MOE_PATH_DECODE && !decode_ok) return MOE_ERR_UNSUPPORTED;
+    if (c.mega != 0 && c.mega != 1) return MOE_ERR_INVALID_ARG;
+    if (c.mega && (!decode_ok || c.path == MOE_PATH_PREFILL)) return MOE_ERR_UNSUPPORTED;
 
     moe_plan_s* p = new (std::nothrow) moe_plan_s();
     if (!p) return MOE_ERR_INVALID_ARG;
@@ -132,7 +137,7 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->decode = c.path == MOE_PATH_DECODE || (c.path == MOE_PATH_AUTO && decode_ok);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
-    p->off_status = take(sizeof(int32_t));
+    p->off_status = take(sizeof(int32_t) * kStatusWords);   // status word, mega grid-barrier words
     p->off_hist = take(sizeof(int32_t) * (size_t)(p->nchunks > 0 ? p->nchunks : 1) * c.E);
     p->off_m_indptr = take(sizeof(int32_t) * (size_t)(c.E + 1));
     p->off_gather = take(sizeof(int32_t) * (size_t)R);
@@ -166,6 +171,7 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     const bool gemms = !mx && !p->decode;
     p->off_split = take(sizeof(int32_t) * 4 * (kMaxPieces / 2 + 1));
     p->off_part = gemms && c.training ? take(kGemmPartBytes) : 0;
+    p->off_mega = c.mega ? take(sizeof(float) * (size_t)R * (c.I / mega_chunk(c.T, c.k)) * c.d) : 0;
     p->ws_bytes = off;
     p->ws = nullptr;
     p->ws_size = 0;
@@ -192,7 +198,8 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
     };
     add("moe plan: T=%d d=%d I=%d E=%d k=%d, %lld routed rows (T*k), %s, %s, %s path\n", c.T, c.d, c.I, c.E,
         c.k, (long long)R, mx ? "MXFP8 E4M3" : "BF16", c.training ? "training" : "inference",
-        p->decode ? "decode (weight-streaming)" : "grouped-GEMM");
+        p->decode ? (c.mega ? "decode (weight-streaming, mega: one fused launch)" : "decode (weight-streaming)")
+                  : "grouped-GEMM");
     if (c.training)
         add("options: weight gradients %s; h %s\n", c.wgrad_accumulate ? "accumulated" : "overwritten",
             c.recompute_h ? (p->h_aliased ? "recomputed in the backward, in the dX / WGRAD-operand region"
@@ -239,6 +246,9 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
         region("as", (size_t)R * c.I / 32, "scratch", "E8M0 scales of a (block-major)");
     }
     region("split", sizeof(int32_t) * 4 * (kMaxPieces / 2 + 1), "scratch", "split weight-gradient tiles");
+    if (c.mega)
+        region("mega", sizeof(float) * (size_t)R * (c.I / mega_chunk(c.T, c.k)) * c.d, "scratch",
+               "mega decode: FP32 partial expert outputs [T*k, I/chunk, d]");
     if (gemms && c.training)
         region("part", kGemmPartBytes, "backward", "FP32 partial sums of split weight-gradient tiles");
     add("kept from the training forward for the backward: %zu bytes (%.1f MiB)\n", saved, saved / 1048576.0);
@@ -260,7 +270,7 @@ moe_status_t moe_bind_workspace(moe_plan_t p, void* dptr, size_t bytes) {
     if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MOE_ERR_HIP;
-    if (hipMemset(static_cast<char*>(dptr) + p->off_status, 0, sizeof(int32_t)) != hipSuccess)
+    if (hipMemset(static_cast<char*>(dptr) + p->off_status, 0, sizeof(int32_t) * kStatusWords) != hipSuccess)
         return MOE_ERR_HIP;
     p->ws = static_cast<char*>(dptr);
     p->ws_size = bytes;
@@ -340,6 +350,12 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         dg.o = p->at<uint16_t>(p->off_o);
         dg.y = static_cast<uint16_t*>(y);
         dg.status = p->at<int32_t>(p->off_status);
+        if (c.mega) {
+            hipError_t e = staged(p, MOE_STAGE_MEGA, s, [&] {
+                return launch_mega_decode(dg, p->at<float>(p->off_mega), p->num_cu, s);
+            });
+            return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        }
         hipError_t e = staged(p, MOE_STAGE_DECODE_W13, s, [&] { return launch_decode_w13(dg, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
         if (c.T == 1) {
@@ -443,7 +459,7 @@ moe_status_t moe_forward_static(moe_plan_t p, const void* x, const int32_t* ids,
     p->ws_size = kStaticScratchBytes;
     p->num_cu = ncu;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (launch_fill_i32(p->at<int32_t>(p->off_status), 1, 0, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_fill_i32(p->at<int32_t>(p->off_status), kStatusWords, 0, s) != hipSuccess) return MOE_ERR_HIP;
     return moe_forward(p, x, ids, scores, w, y, stream);
 }
 

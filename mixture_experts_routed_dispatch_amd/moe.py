@@ -46,7 +46,8 @@ EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_de
            "moe_profile_read")
 
 STAGES = ("dispatch", "quant_x", "w13", "w2", "combine", "score_grad", "dgrad_w2", "wgrad_w2",
-          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows", "recompute_h")
+          "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows", "recompute_h",
+          "mega")
 
 
 class MoeError(RuntimeError):
@@ -60,7 +61,7 @@ class MoeConfig(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("precision", ctypes.c_int32),
                 ("training", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("wgrad_accumulate", ctypes.c_int32), ("recompute_h", ctypes.c_int32),
-                ("activation", ctypes.c_int32)]
+                ("activation", ctypes.c_int32), ("mega", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -129,8 +130,8 @@ def _ok(status: int, where: str):
 
 
 def moe_plan(T, d, I, E, k, precision=MOE_BF16, training=0, path=MOE_PATH_AUTO,
-             wgrad_accumulate=0, recompute_h=0, activation=MOE_ACT_SWIGLU) -> int:
-    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate, recompute_h, activation)
+             wgrad_accumulate=0, recompute_h=0, activation=MOE_ACT_SWIGLU, mega=0) -> int:
+    cfg = MoeConfig(T, d, I, E, k, precision, training, path, wgrad_accumulate, recompute_h, activation, mega)
     h = ctypes.c_void_p()
     _ok(lib().moe_plan(ctypes.byref(cfg), ctypes.byref(h)), "moe_plan")
     return h.value
@@ -229,12 +230,14 @@ class Layer:
     """One plan plus its torch-allocated workspace; all compute goes through libmoe."""
 
     def __init__(self, T, d, I, E, k, precision=MOE_BF16, training=False, path=MOE_PATH_AUTO,
-                 device="cuda", wgrad_accumulate=False, recompute_h=False, activation=MOE_ACT_SWIGLU):
+                 device="cuda", wgrad_accumulate=False, recompute_h=False, activation=MOE_ACT_SWIGLU,
+                 mega=False):
         import torch
         self.T, self.d, self.I, self.E, self.k = T, d, I, E, k
         self.precision = precision
         self.plan = moe_plan(T, d, I, E, k, precision, int(bool(training)), path,
-                             int(bool(wgrad_accumulate)), int(bool(recompute_h)), int(activation))
+                             int(bool(wgrad_accumulate)), int(bool(recompute_h)), int(activation),
+                             int(bool(mega)))
         nbytes = moe_workspace_bytes(self.plan)
         self.workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         moe_bind_workspace(self.plan, _ptr(self.workspace), self.workspace.numel())

@@ -32,6 +32,8 @@ hipError_t launch_wgrad_rows(const uint16_t*, const uint16_t*, int, const int32_
 hipError_t launch_decode_w13(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_w2(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_decode_w2_one(const DecodeArgs&, int, hipStream_t) { return hipErrorInvalidValue; }
+int mega_chunk(int T, int k) { return T * k <= 64 ? 32 : 64; }
+hipError_t launch_mega_decode(const DecodeArgs&, float*, int, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_quantize_mxfp8(const uint16_t*, int64_t, int, uint8_t*, uint8_t*, bool, hipStream_t,
                                  const int32_t*) { return hipErrorInvalidValue; }
 hipError_t launch_route_scales(const uint8_t*, int64_t, const int32_t*, int64_t, int, uint8_t*, hipStream_t) {
@@ -64,6 +66,8 @@ int main() {
     ok.push_back(cfg(0, 256, 128, 8, 2));
     ok.push_back(cfg(4096, 256, 64, 256, 32));
     moe_config_t rc = cfg(300, 128, 256, 8, 2); rc.training = 1; rc.recompute_h = 1; ok.push_back(rc);
+    moe_config_t mg = cfg(1, 2048, 768, 128, 8); mg.mega = 1; ok.push_back(mg);
+    mg.T = 32; ok.push_back(mg);
     for (const moe_config_t& c : ok) {
         moe_plan_t p = nullptr;
         CHECK(moe_plan(&c, &p) == MOE_OK && p != nullptr);
@@ -110,6 +114,10 @@ int main() {
     moe_config_t ra = cfg(64, 256, 128, 8, 2); ra.activation = 7; bad.push_back({ra, MOE_ERR_INVALID_ARG});
     moe_config_t pa = cfg(64, 256, 128, 8, 2); pa.path = 9; bad.push_back({pa, MOE_ERR_INVALID_ARG});
     moe_config_t dp = cfg(64, 256, 128, 8, 8); dp.path = MOE_PATH_DECODE; bad.push_back({dp, MOE_ERR_UNSUPPORTED});
+    moe_config_t mp = cfg(4096, 256, 128, 8, 2); mp.mega = 1; bad.push_back({mp, MOE_ERR_UNSUPPORTED});
+    moe_config_t mt2 = cfg(8, 256, 128, 8, 2); mt2.mega = 1; mt2.training = 1; bad.push_back({mt2, MOE_ERR_UNSUPPORTED});
+    moe_config_t mf = cfg(8, 256, 128, 8, 2); mf.mega = 1; mf.path = MOE_PATH_PREFILL; bad.push_back({mf, MOE_ERR_UNSUPPORTED});
+    moe_config_t mi = cfg(8, 256, 128, 8, 2); mi.mega = 3; bad.push_back({mi, MOE_ERR_INVALID_ARG});
     for (const Bad& b : bad) {
         moe_plan_t p = reinterpret_cast<moe_plan_t>(&fails);
         CHECK(moe_plan(&b.c, &p) == b.want);

@@ -75,11 +75,17 @@ def test_status_strings(L):
     (dict(T=64, d=256, I=128, E=8, k=2, activation=1), moe.MOE_OK),
     (dict(T=8, d=256, I=128, E=8, k=2, precision=1, activation=2), moe.MOE_OK),
     (dict(T=64, d=256, I=128, E=8, k=2, activation=3), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=1, d=2048, I=768, E=128, k=8, mega=1), moe.MOE_OK),              # fused decode
+    (dict(T=32, d=2048, I=768, E=128, k=8, path=2, mega=1), moe.MOE_OK),
+    (dict(T=64, d=256, I=128, E=8, k=8, mega=1), moe.MOE_ERR_UNSUPPORTED),    # not a decode plan
+    (dict(T=8, d=256, I=128, E=8, k=2, path=1, mega=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d=256, I=128, E=8, k=2, training=1, mega=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d=256, I=128, E=8, k=2, mega=2), moe.MOE_ERR_INVALID_ARG),
 ])
 def test_plan_validation(L, cfg, expect):
     c = moe.MoeConfig(cfg["T"], cfg["d"], cfg["I"], cfg["E"], cfg["k"], cfg.get("precision", 0),
                       cfg.get("training", 0), cfg.get("path", 0), cfg.get("wgrad_accumulate", 0),
-                      cfg.get("recompute_h", 0), cfg.get("activation", 0))
+                      cfg.get("recompute_h", 0), cfg.get("activation", 0), cfg.get("mega", 0))
     h = ctypes.c_void_p()
     st = L.moe_plan(ctypes.byref(c), ctypes.byref(h))
     assert st == expect

@@ -614,6 +614,106 @@ def test_decode_flags_invalid_routing(torch_cuda):
     layer.close()
 
 
+# ------------------------------------------------------------------ mega (fused) decode
+
+@pytest.mark.parametrize("T,d,I,E,k,routing", DECODE_SHAPES)
+def test_mega_decode_small(torch_cuda, T, d, I, E, k, routing):
+    """The fused decode (plan option mega: W13, activation and W2 chunked over I in one
+    launch with FP32 partial outputs, then the combine launch) against the oracle, and
+    bitwise repeatable."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("mega decode small", T, d, I, E, k, routing)
+    inp = inputs.generate(T, d, I, E, k, routing, seed=17)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, path=moe.MOE_PATH_DECODE, mega=True)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    y2 = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    st, flags = layer.status()
+    assert flags == 0
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    check("y (mega)", np_of(y), ref, **BF16)
+    layer.close()
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode32"])
+def test_mega_decode_full_size(torch_cuda, name):
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    say("mega decode full size", name)
+    inp = inputs.generate_config(name, seed=0, with_dy=False)
+    t = device_inputs(inp)
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, mega=True)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    check("y (mega, all %d tokens)" % inp.T, np_of(y), ref, **BF16)
+    layer.close()
+
+
+@pytest.mark.parametrize("act,name", [(1, "geglu"), (2, "reglu")])
+def test_mega_decode_gated_activations(torch_cuda, act, name):
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    T, d, I, E, k = 7, 512, 384, 16, 4
+    say("mega decode", name, T, d, I, E, k)
+    inp = inputs.generate(T, d, I, E, k, "uniform", seed=51)
+    t = device_inputs(inp)
+    layer = moe.Layer(T, d, I, E, k, mega=True, activation=act)
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, act=act)
+    check("y (mega, %s)" % name, np_of(y), ref, **BF16)
+    layer.close()
+
+
+def test_mega_decode_graph_replay_and_flags(torch_cuda):
+    """Captured in a HIP graph, every replay equals the eager result bit for bit; invalid
+    routing is flagged, and the next valid call equals the first."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    inp = inputs.generate(32, 512, 256, 64, 8, seed=23)
+    t = device_inputs(inp)
+    layer = moe.Layer(inp.T, inp.d, inp.I, inp.E, inp.k, mega=True)
+    y_eager = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    y_out = torch.empty_like(y_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"], y=y_out)
+    for rep in range(4):
+        y_out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y_out.view(torch.int16), y_eager.view(torch.int16)), rep
+        layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    bad = inp.ids.copy()
+    bad[3, 2] = bad[3, 0]
+    bad[5, 1] = inp.E + 4
+    layer.forward(t["x"], torch.from_numpy(bad).to(dev()), t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING
+    assert flags & moe.MOE_DEV_ID_DUPLICATE and flags & moe.MOE_DEV_ID_OUT_OF_RANGE
+    y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16))
+    layer.close()
+
+
 @pytest.mark.parametrize("mode", ["bf16", "mxfp8", "bf16-train"])
 def test_forward_flags_invalid_routing(torch_cuda, mode):
     """A grouped-GEMM call (forward, or forward + backward) whose routing holds
