@@ -167,9 +167,10 @@ moe_status_t moe_dispatch(moe_plan_t plan, const int32_t* ids, const float* scor
                           void* stream);
 
 /* OCP MXFP8 conversion of `rows` BF16 rows of length K (a multiple of 32):
- * per block of 32 consecutive elements the E8M0 byte is
- * clamp(floor(log2(max|v|)) - 8 + 127, 0, 254) (0 for an all-zero block) and
- * each element is E4M3(v / 2^(byte - 127)), nearest-even, clamped to +-448.
+ * per block of 32 consecutive elements the scale is the smallest power of two 2^s
+ * with max|v| / 2^s <= 448 (s = ceil(log2(max|v| / 448)): no element saturates), its
+ * E8M0 byte clamp(s + 127, 0, 254) (0 for an all-zero block), and each element is
+ * E4M3(v / 2^s), nearest-even.
  * codes uint8 [rows, K]; scales uint8 [rows, K/32].  Needs no plan.
  * Inputs are meant to be finite.  An infinite or NaN element is encoded as
  * 448 with its sign bit (E4M3's NaN codes are never written), and the scale

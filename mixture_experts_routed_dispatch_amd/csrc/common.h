@@ -105,13 +105,16 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
     return (uint32_t)w;
 }
 
-// E8M0 byte of a block whose largest magnitude is amax (any finite float):
-// floor(log2(amax)) - 8 + 127 read off the exponent field, clamped to [0, 254];
-// zero and FP32 subnormals give 0
+// E8M0 byte of a block whose largest magnitude is amax (any finite float): the smallest
+// power of two X with amax / X <= 448 (E4M3's largest normal), so no element saturates.
+// With amax = m 2^e, m in [1, 2): log2 X = e - 8, or e - 7 when m > 1.75 (the significand
+// field above 0x600000), biased by 127 and clamped to [0, 254]; zero and FP32 subnormals
+// give 0
 __device__ __forceinline__ uint32_t e8m0_scale(float amax) {
-    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFF);   // 0 for zero / subnormal
+    const uint32_t bits = __float_as_uint(amax);
+    const int ef = (int)((bits >> 23) & 0xFF);   // 0 for zero / subnormal
     if (ef == 0) return 0u;
-    int b = ef - 8;                      // (ef - 127) - 8 + 127
+    int b = ef - 8 + ((bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);   // (ef - 127) - 8 [+ 1] + 127
     b = b < 0 ? 0 : (b > 254 ? 254 : b);
     return (uint32_t)b;
 }

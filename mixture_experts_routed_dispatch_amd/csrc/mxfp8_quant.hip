@@ -1,13 +1,13 @@
 // mxfp8_quant.hip -- OCP MXFP8 (E4M3 elements, E8M0 scale per 32) conversion on gfx950.
 //
 // The blog post ("What it is selling") names MXFP8 E4M3 with prepared weights
-// and activations quantized after routing.  The conversion rule is the OCP MX
-// v1.0 one: per block of 32 values along K, the shared exponent is
-// floor(log2(max|v|)) - 8 (8 = largest E4M3 exponent), stored biased by 127
-// and clamped to [0, 254] (0 for an all-zero block); each element is
-// v / 2^(shared) rounded to nearest even on the E4M3 grid and clamped to
-// +-448.  Inputs are BF16, so v / 2^(shared) is exact in FP32 and the
-// codes are a deterministic function of the input bits.
+// and activations quantized after routing.  Per OCP MX v1.0 block of 32 values along
+// K, the shared scale is the smallest power of two 2^s with max|v| / 2^s <= 448
+// (E4M3's largest normal: s = ceil(log2(max|v| / 448))), stored biased by 127 and
+// clamped to [0, 254] (0 for an all-zero block); each element is v / 2^s rounded to
+// nearest even on the E4M3 grid (no element saturates; the clamp to +-448 stays for
+// non-finite input).  Inputs are BF16, so v / 2^s is exact in FP32 and the codes are a
+// deterministic function of the input bits.
 //
 // Scales are stored row-major ([rows, K/32]) or block-major: the four bytes of blocks
 // 4 g .. 4 g + 3 of a row form one word, and word (g, row) sits at (g * rows + row) * 4,

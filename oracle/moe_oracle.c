@@ -22,11 +22,15 @@
  *         path; distinct expert ids per token row; probability weighting and
  *         deterministic combine), "Training" (gather / cu / probs / slots;
  *         router, input and weight gradients), "Limits".
- *   [MX]  The OCP Microscaling Formats (MX) v1.0 specification, section on
- *         converting a vector of scalars to an MX block (shared exponent =
- *         floor(log2(amax)) - emax of the element type; elements rounded to
- *         nearest even and clamped to the largest normal), which the blog
- *         post's "MXFP8 E4M3" mode names.
+ *   [MX]  The OCP Microscaling Formats (MX) v1.0 specification (an MX block is
+ *         32 elements of one element type sharing one E8M0 power-of-two scale;
+ *         elements rounded to nearest even), which the blog post's "MXFP8 E4M3"
+ *         mode names.  The scale taken here is the smallest power of two that
+ *         brings the block maximum within E4M3's largest normal (448):
+ *         2^ceil(log2(amax / 448)), so no element saturates.  (The format
+ *         fixes the encoding, not the choice of scale; the specification's
+ *         reference conversion takes floor(log2(amax)) - 8 instead, which clips
+ *         the elements of a block whose maximum has a significand above 1.75.)
  *
  * Readings where the pages are silent or leave a step open:
  *   - within one expert, routed rows are ordered by ascending token index
@@ -369,17 +373,20 @@ uint8_t orc_e4m3_encode(double v)
     return sign | (uint8_t)(((e + 7) << 3) | (int)m);
 }
 
-/* Shared exponent of one block per the OCP rule: floor(log2(amax)) - 8,
- * stored as an E8M0 byte (biased by 127) clamped to [0, 254]; amax = 0
- * gives 0. */
+/* Shared exponent of one block: the smallest power of two X with amax / X <= 448,
+ * i.e. log2 X = ceil(log2(amax / 448)).  With amax = m * 2^e, m in [1, 2):
+ * amax / 448 = (m / 1.75) * 2^(e - 8), so log2 X = e - 8 when m <= 1.75 and e - 7
+ * when m > 1.75.  Stored as an E8M0 byte (biased by 127) clamped to [0, 254];
+ * amax = 0 gives 0. */
 uint8_t orc_mx_scale_byte(const double* v, int n)
 {
     double amax = 0.0;
     for (int i = 0; i < n; ++i) { double a = fabs(v[i]); if (a > amax) amax = a; }
     if (amax == 0.0) return 0;
     int ex;
-    frexp(amax, &ex);                              /* amax in [2^(ex-1), 2^ex) */
-    int shared = (ex - 1) - 8;
+    double fr = frexp(amax, &ex);                  /* amax = fr * 2^ex, fr in [0.5, 1) */
+    int e = ex - 1;                                /* amax = (2 fr) * 2^e */
+    int shared = e - 8 + (2.0 * fr > 1.75 ? 1 : 0);
     int biased = shared + 127;
     if (biased < 0) biased = 0;
     if (biased > 254) biased = 254;

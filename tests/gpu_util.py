@@ -63,13 +63,16 @@ def say(*a):
 # kernels' BF16 roundings in numpy (a, probs * dy, dh, output) on these test layers
 # gives element errors up to 0.048 of the expert's rms, so there the slice is the
 # expert and elem = 0.12.  MXFP8 against the oracle that quantizes x and the
-# gated-activation output at the same points: a requantized element of `a` can land
-# one E4M3 step (12.5 %) away from the oracle's when the FP32 and fp64 values straddle
-# a rounding boundary, which W2 then spreads over a row; elem = 0.1, maxrel <= 0.1.
+# gated-activation output at the same points: a requantized element of `a` lands one
+# E4M3 step (up to 12.5 % of it) away from the oracle's when the FP32 and fp64 values
+# straddle a rounding boundary; for a large element (5 standard deviations) times a
+# large W2 coefficient (3 / sqrt(I)) that moves one output element by about 0.1 of the
+# output's rms, so elem = 0.25 and maxrel <= 0.1 (a wrong tile or row piece moves
+# elements by about their own magnitude).
 BF16 = dict(tol=2e-2, floor=5e-3, elem=3e-2, maxrel_tol=3e-2)
 BF16_WGRAD = dict(tol=2e-2, floor=5e-3, elem=0.12, maxrel_tol=3e-2, per_slice=True)
 MX = dict(tol=6e-2)
-MX_QUANT = dict(tol=1e-2, elem=0.1, maxrel_tol=0.1)
+MX_QUANT = dict(tol=1e-2, elem=0.25, maxrel_tol=0.1)
 
 
 def check(label, got, ref, tol, floor=None, elem=None, maxrel_tol=None, per_slice=False):

@@ -7,15 +7,17 @@ MXFP8 E4M3 with prepared weights; the OCP MX v1.0 conversion rule).
 * Every code round-trips through decode/encode.
 * Every finite BF16 value, clamped to +-448, encodes exactly as torch's own
   float8_e4m3fn cast (a library routine, round to nearest even).
-* The shared exponent of a block is floor(log2(amax)) - 8 as a biased E8M0
-  byte, clamped to [0, 254]; the dequantized block is within half an E4M3
-  step of the input (or saturates at the top).
+* The shared exponent of a block is the smallest power of two X with
+  amax / X <= 448 (ceil(log2(amax / 448)), i.e. floor(log2(amax)) - 8, plus one
+  when amax's significand exceeds 1.75) as a biased E8M0 byte, clamped to
+  [0, 254]; no element saturates, and the dequantized block is within half an
+  E4M3 step of the input.
 
 The quantization-aware forward (x and the gated-activation output a passed
 through the block-32 quantize->dequantize image) is pinned by:
 * two hand-derived cases (tests/golden/mx_forward_requant.json) in which the
-  re-quantization of a, the quantization of x, the floor scale rule and the
-  block boundaries each change the result;
+  re-quantization of a, the quantization of x, the scale rule (a block maximum
+  with significand above 1.75) and the block boundaries each change the result;
 * reduction to the plain forward: when the re-quantization of a is the identity
   (selector weights put every a on its grid), the quantized forward of x equals
   the plain forward of x's quantize->dequantize image bit for bit;
@@ -67,13 +69,21 @@ def test_all_bf16_values_match_torch_cast(orc):
 
 def test_scale_byte_rule(orc):
     sb = orc.mx_scale_byte
-    assert sb(np.r_[448.0, np.zeros(31)]) == 127            # floor(log2 448) = 8 -> 2^0
-    assert sb(np.r_[1.0, np.zeros(31)]) == 119              # 2^-8
-    assert sb(np.r_[511.9, np.zeros(31)]) == 127
+    assert sb(np.r_[448.0, np.zeros(31)]) == 127            # 448 / 2^0 = 448 fits
+    assert sb(np.r_[449.0, np.zeros(31)]) == 128            # just above: the next power of two
+    assert sb(np.r_[1.0, np.zeros(31)]) == 119              # 2^-8: 1 / 2^-8 = 256
+    assert sb(np.r_[1.75, np.zeros(31)]) == 119             # 1.75 / 2^-8 = 448 exactly
+    assert sb(np.r_[1.75 + 2.0 ** -20, np.zeros(31)]) == 120
+    assert sb(np.r_[511.9, np.zeros(31)]) == 128
     assert sb(np.r_[512.0, np.zeros(31)]) == 128
     assert sb(np.zeros(32)) == 0
     assert sb(np.r_[2.0 ** -130, np.zeros(31)]) == 0        # clamped at the bottom
-    assert sb(np.r_[-3.0, 0.5, np.zeros(30)]) == 120        # amax uses |v|
+    assert sb(np.r_[-3.0, 0.5, np.zeros(31)][:32]) == 120   # amax uses |v|
+    # against the definition: the smallest power of two X with amax / X <= 448
+    rng = np.random.default_rng(3)
+    for amax in np.exp(rng.uniform(-40, 40, 2000)):
+        X = 2.0 ** (sb(np.r_[amax, np.zeros(31)]) - 127)
+        assert amax / X <= 448.0 and amax / (X / 2) > 448.0
 
 
 def test_block_quantize_error_bound(orc):
@@ -85,11 +95,9 @@ def test_block_quantize_error_bound(orc):
     q = v.astype(np.float64) / X                           # value on the element grid
     # half a step of the E4M3 grid at |q| (step 2^(floor(log2|q|)-3), at least 2^-9)
     step = np.exp2(np.maximum(np.floor(np.log2(np.maximum(np.abs(q), 2.0 ** -6))) - 3, -9))
-    err = np.abs(back / X - np.clip(q, -448, 448))
+    assert np.all(np.abs(q) <= 448.0)                        # no element saturates
+    err = np.abs(back / X - q)
     assert np.all(err <= step / 2 + 1e-12)
-    # elements above 448 after scaling saturate to +-448 (the floor rule lets |q| reach 512)
-    sat = np.abs(q) > 448.0
-    assert np.all(np.abs(back[sat] / X[sat]) == 448.0)
     # grid values survive exactly
     on_grid = np.array([orc.e4m3_decode(c) for c in range(0x00, 0x7F)])
     blk = np.r_[on_grid[-32:]].astype(np.float32)           # amax 448 -> scale byte 127
@@ -133,18 +141,27 @@ def test_mx_forward_golden(orc):
 
 
 def _selector_layer(seed, T=6, d=64, I=64, E=3, k=2):
-    """Off-grid x; W1 rows pick one column of x, W3 rows pick the all-ones column 0 times
-    2^-4, except rows 0 and 32 of each expert, which pick column 0 twice (a = 1, the
-    block maximum).  With ReGLU every a is then x_q[c] 2^-4 (or 0, or 1): a 3-bit mantissa
-    within 2^10 of the block's power-of-two maximum, i.e. already on its MX grid."""
+    """Off-grid x whose 32-element blocks each hold a large value (120: scale 2^-1, so
+    values below 2^-7 fall on the coarse subnormal steps of 2^-10) and, in columns 2..9,
+    such tiny values.  W1 rows pick one column of x (never the large ones), W3 rows pick
+    the all-ones column 0 times 2^-4, except rows 0 and 32 of each expert, which pick
+    column 0 twice (a = 1, the block maximum, scale 2^-8).  With ReGLU every a is then
+    x_q[c] 2^-4 (or 0, or 1): on its MX grid (3-bit significands within 2^10 of 1, and
+    the tiny ones k 2^-14 = k 2^-6 steps of the scale), so the re-quantization of a is
+    the identity and only the quantization of x shows."""
     rng = np.random.default_rng(seed)
     x = rng.uniform(-3.9, 3.9, (T, d))
     x[np.abs(x) < 2.0 ** -5] = 0.0
     x[:, 0] = 1.0
+    x[:, 1] = 120.0
+    x[:, 33] = 120.0
+    x[:, 2:10] = rng.uniform(2.0 ** -9, 2.0 ** -7, (T, 8)) * rng.choice([-1.0, 1.0], (T, 8))
     x = x.astype(np.float32)
+    cols_ok = np.array([c for c in range(d) if c not in (0, 1, 33)])
     w13 = np.zeros((E, 2 * I, d), np.float32)
     for e in range(E):
-        cols = rng.integers(1, d, I)
+        cols = rng.choice(cols_ok, I)
+        cols[1:9] = np.arange(2, 10)                       # the tiny columns
         for i in range(I):
             if i % 32 == 0:
                 w13[e, i, 0] = 1.0
@@ -171,13 +188,12 @@ def test_mx_forward_equals_plain_forward_of_quantized_x(orc):
 
 def _dq_torch(v):
     """Quantize->dequantize along the last axis in blocks of 32, written independently
-    of the oracle: scale 2^(floor(log2 amax) - 8) from numpy's frexp, elements through
-    torch's float8_e4m3fn cast after clamping to +-448."""
+    of the oracle: scale 2^ceil(log2(amax / 448)) (numpy's log2 and ceil), elements
+    through torch's float8_e4m3fn cast after clamping to +-448."""
     v = np.asarray(v, np.float64)
     blk = v.reshape(v.shape[:-1] + (v.shape[-1] // 32, 32))
     amax = np.abs(blk).max(-1, keepdims=True)
-    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
-    X = np.where(amax > 0, np.ldexp(1.0, np.clip(ex - 1 - 8, -127, 127)), 1.0)
+    X = np.where(amax > 0, np.exp2(np.clip(np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), -127, 127)), 1.0)
     q = np.clip(blk / X, -448.0, 448.0)
     q8 = torch.from_numpy(q.copy()).to(torch.float8_e4m3fn).to(torch.float64).numpy()
     return (q8 * X).reshape(v.shape)
