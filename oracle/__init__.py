@@ -63,6 +63,7 @@ def _L():
         lib.orc_mx_quantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         lib.orc_mx_dequantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         lib.orc_forward_tokens_mx.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, i32]
+        lib.orc_train_mx.argtypes = [i32] * 5 + [vp] * 6 + [i32] + [vp] * 5
         _lib = lib
     return _lib
 
@@ -233,3 +234,21 @@ def forward_tokens_mx(x, ids, scores, w13, w2, toks=None, act=ACT_SWIGLU):
     _check(_L().orc_forward_tokens_mx(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f),
                                       _p(w2f), n, _p(toks), _p(y), int(act)))
     return y
+
+
+def train_mx(x, ids, scores, w13, w2, dy, act=ACT_SWIGLU):
+    """One MXFP8 training step from BF16 master weights: every expert product takes MX images
+    of both operands along its own reduction dimension, WGRAD operands blocked along each
+    expert's routed rows.  Returns (y, dx, ds, dw13, dw2) in float64."""
+    xf, w13f, w2f, dyf = _f32(x), _f32(w13), _f32(w2), _f32(dy)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    T, d, I, E, k = _shapes(xf, w13f, w2f, ids)
+    y = np.zeros((T, d), np.float64)
+    dx = np.zeros((T, d), np.float64)
+    ds = np.zeros((T, k), np.float64)
+    dw13 = np.zeros((E, 2 * I, d), np.float64)
+    dw2 = np.zeros((E, d, I), np.float64)
+    _check(_L().orc_train_mx(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f), _p(w2f), _p(dyf),
+                             int(act), _p(y), _p(dx), _p(ds), _p(dw13), _p(dw2)))
+    return y, dx, ds, dw13, dw2

@@ -482,3 +482,226 @@ int orc_forward_tokens_mx(int T, int d, int I, int E, int k,
     }
     return failed ? ORC_ERR_ALLOC : ORC_OK;
 }
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 training step (blog post "What it is selling": MXFP8 E4M3 trains as well
+ * as infers, activations quantized after routing; FPROP, DGRAD and WGRAD).
+ *
+ * Every expert product takes both of its operands as MX images, blocked along that
+ * product's own reduction dimension:
+ *   FPROP  h = W13 x       x along d, W13 along d (its rows)
+ *          o = W2 a        a along I, W2 along I (its rows)
+ *   DGRAD  dA = W2^T dO    dO along d, W2 along d (its columns)
+ *          dX = W13^T dh   dh = (dg, du) along 2I, W13 along 2I (its columns)
+ *   WGRAD  dW2  = sum_r dO_r a_r^T     both along the routed rows of the expert
+ *          dW13 = sum_r dh_r x_r^T     (blocks of 32 consecutive rows in dispatch
+ *                                       order; the last block of an expert may be short)
+ * with dO_r = probs[r] * dY[gather[r]].  Readings where the pages are silent:
+ *   - the weights w13 / w2 passed in are the BF16 master weights; each product
+ *     quantizes them along its own reduction dimension;
+ *   - the activations the layer keeps for the backward (h and a) and the gradient dA
+ *     are held in BF16, the precision BF16 mode keeps activations in; they are
+ *     rounded to BF16 (nearest, ties to even) where they are stored, and every later
+ *     quantization starts from the stored value.  dh is used unrounded by DGRAD and
+ *     rounded to BF16 for WGRAD; dO and x enter unrounded.
+ * Outputs (fp64): y [T, d], dx [T, d], ds [T, k] (ds[t][j] = <dY[t], o>),
+ * dw13 [E, 2I, d], dw2 [E, d, I]; an expert with no row gets zero gradients. */
+
+/* nearest BF16 value of v (ties to even); v finite and inside the normal range */
+static double bf16_round(double v)
+{
+    if (v == 0.0) return 0.0;
+    int ex;
+    double m = frexp(v, &ex);                       /* |m| in [0.5, 1) */
+    return ldexp(nearbyint(ldexp(m, 8)), ex - 8);   /* 8 significant bits */
+}
+
+/* MX quantize->dequantize image of n <= 32 values v[0], v[stride], ... in place;
+ * missing elements of a short block count as zeros, which change nothing */
+static void mx_block_image(double* v, int n, size_t stride)
+{
+    double blk[32] = {0};
+    for (int i = 0; i < n; ++i) blk[i] = v[(size_t)i * stride];
+    uint8_t sb = orc_mx_scale_byte(blk, n);
+    double X = ldexp(1.0, (int)sb - 127);
+    for (int i = 0; i < n; ++i) v[(size_t)i * stride] = orc_e4m3_decode(orc_e4m3_encode(blk[i] / X)) * X;
+}
+
+/* images of the `mats` matrices m + e*rows*cols (rows x cols, row-major): along
+ * each row (along_rows != 0), or along each column in blocks of 32 rows */
+static void mx_matrix_image(double* m, int mats, int rows, int cols, int along_rows)
+{
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < mats; ++e) {
+        double* me = m + (size_t)e * rows * cols;
+        if (along_rows) {
+            for (int r = 0; r < rows; ++r)
+                for (int b = 0; b < cols; b += 32) mx_block_image(me + (size_t)r * cols + b, 32, 1);
+        } else {
+            for (int c = 0; c < cols; ++c)
+                for (int b = 0; b < rows; b += 32)
+                    mx_block_image(me + (size_t)b * cols + c, rows - b < 32 ? rows - b : 32, (size_t)cols);
+        }
+    }
+}
+
+int orc_train_mx(int T, int d, int I, int E, int k,
+                 const float* x, const int32_t* ids, const float* scores,
+                 const float* w13, const float* w2, const float* dy, int act,
+                 double* y, double* dx, double* ds, double* dw13, double* dw2)
+{
+    int rc = orc_check_routing(T, E, k, ids);
+    if (rc != ORC_OK) return rc;
+    if (d % 32 || I % 32) return ORC_ERR_RANGE;
+    const size_t R = (size_t)T * k, n13 = (size_t)E * 2 * I * d, n2 = (size_t)E * d * I;
+    int32_t* m_indptr = (int32_t*)malloc(sizeof(int32_t) * ((size_t)E + 1));
+    int32_t* gather = (int32_t*)malloc(sizeof(int32_t) * (R ? R : 1));
+    int32_t* slots = (int32_t*)malloc(sizeof(int32_t) * (R ? R : 1));
+    float* probs = (float*)malloc(sizeof(float) * (R ? R : 1));
+    double* wf13 = (double*)malloc(sizeof(double) * n13);   /* FPROP images */
+    double* wf2 = (double*)malloc(sizeof(double) * n2);
+    double* wb13 = (double*)malloc(sizeof(double) * n13);   /* DGRAD images */
+    double* wb2 = (double*)malloc(sizeof(double) * n2);
+    double* hb = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * I);   /* stored h (BF16) */
+    double* ab = (double*)malloc(sizeof(double) * (R ? R : 1) * I);       /* stored a (BF16) */
+    double* o = (double*)malloc(sizeof(double) * (R ? R : 1) * d);
+    double* dhb = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * I);  /* dh in BF16 */
+    double* dxp = (double*)malloc(sizeof(double) * (R ? R : 1) * d);
+    int failed = !m_indptr || !gather || !slots || !probs || !wf13 || !wf2 || !wb13 || !wb2 || !hb ||
+                 !ab || !o || !dhb || !dxp;
+    if (!failed) rc = orc_dispatch(T, E, k, ids, scores, m_indptr, gather, slots, probs);
+    if (!failed && rc == ORC_OK) {
+        for (size_t z = 0; z < n13; ++z) wf13[z] = wb13[z] = (double)w13[z];
+        for (size_t z = 0; z < n2; ++z) wf2[z] = wb2[z] = (double)w2[z];
+        mx_matrix_image(wf13, E, 2 * I, d, 1);
+        mx_matrix_image(wf2, E, d, I, 1);
+        mx_matrix_image(wb13, E, 2 * I, d, 0);
+        mx_matrix_image(wb2, E, d, I, 0);
+
+        /* FPROP and DGRAD, one routed row at a time */
+#pragma omp parallel for schedule(dynamic, 4)
+        for (size_t r = 0; r < R; ++r) {
+            double* buf = (double*)malloc(sizeof(double) * (2 * (size_t)d + 4 * (size_t)I));
+            if (!buf) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *xq = buf, *dO = xq + d, *a = dO + d, *dA = a + I, *dh = dA + I;
+            int e = 0;
+            while (m_indptr[e + 1] <= (int32_t)r) ++e;
+            const int t = gather[r];
+            const double s = (double)probs[r];
+            const double* f13 = wf13 + (size_t)e * 2 * I * d;
+            const double* f2 = wf2 + (size_t)e * d * I;
+            const double* b13 = wb13 + (size_t)e * 2 * I * d;
+            const double* b2 = wb2 + (size_t)e * d * I;
+            double* h_r = hb + r * 2 * I;
+            for (int c = 0; c < d; ++c) xq[c] = (double)x[(size_t)t * d + c];
+            for (int b = 0; b < d; b += 32) mx_block_image(xq + b, 32, 1);
+            for (int i = 0; i < I; ++i) {
+                double g = 0.0, u = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    g += f13[(size_t)i * d + c] * xq[c];
+                    u += f13[(size_t)(I + i) * d + c] * xq[c];
+                }
+                a[i] = act_f(act, g) * u;
+                h_r[i] = bf16_round(g);
+                h_r[I + i] = bf16_round(u);
+                ab[r * I + i] = bf16_round(a[i]);
+            }
+            for (int b = 0; b < I; b += 32) mx_block_image(a + b, 32, 1);
+            for (int n = 0; n < d; ++n) {
+                double acc = 0.0;
+                for (int i = 0; i < I; ++i) acc += f2[(size_t)n * I + i] * a[i];
+                o[r * d + n] = acc;
+            }
+            /* DGRAD */
+            for (int n = 0; n < d; ++n) dO[n] = s * (double)dy[(size_t)t * d + n];
+            for (int b = 0; b < d; b += 32) mx_block_image(dO + b, 32, 1);
+            for (int i = 0; i < I; ++i) {
+                double acc = 0.0;
+                for (int n = 0; n < d; ++n) acc += b2[(size_t)n * I + i] * dO[n];
+                dA[i] = bf16_round(acc);
+            }
+            for (int i = 0; i < I; ++i) {
+                const double g = h_r[i], u = h_r[I + i];
+                dh[i] = dA[i] * u * act_df(act, g);
+                dh[I + i] = dA[i] * act_f(act, g);
+            }
+            for (int j = 0; j < 2 * I; ++j) dhb[r * 2 * I + j] = bf16_round(dh[j]);
+            for (int b = 0; b < 2 * I; b += 32) mx_block_image(dh + b, 32, 1);
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j < 2 * I; ++j) acc += b13[(size_t)j * d + c] * dh[j];
+                dxp[r * d + c] = acc;
+            }
+            free(buf);
+        }
+    }
+    if (!failed && rc == ORC_OK) {
+        /* combine, router gradient and input gradient per token, j ascending */
+        for (int t = 0; t < T; ++t) {
+            for (int n = 0; n < d; ++n) { y[(size_t)t * d + n] = 0.0; dx[(size_t)t * d + n] = 0.0; }
+            for (int j = 0; j < k; ++j) {
+                const size_t r = (size_t)slots[(size_t)t * k + j];
+                const double s = (double)scores[(size_t)t * k + j];
+                double dot = 0.0;
+                for (int n = 0; n < d; ++n) {
+                    y[(size_t)t * d + n] += s * o[r * d + n];
+                    dx[(size_t)t * d + n] += dxp[r * d + n];
+                    dot += (double)dy[(size_t)t * d + n] * o[r * d + n];
+                }
+                ds[(size_t)t * k + j] = dot;
+            }
+        }
+        /* WGRAD, one expert at a time, operands blocked along its routed rows */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int e = 0; e < E; ++e) {
+            const int r0 = m_indptr[e], rows = m_indptr[e + 1] - r0;
+            double* dw2_e = dw2 + (size_t)e * d * I;
+            double* dw13_e = dw13 + (size_t)e * 2 * I * d;
+            for (size_t z = 0; z < (size_t)d * I; ++z) dw2_e[z] = 0.0;
+            for (size_t z = 0; z < (size_t)2 * I * d; ++z) dw13_e[z] = 0.0;
+            if (rows == 0) continue;
+            double* buf = (double*)malloc(sizeof(double) * (size_t)rows * (2 * (size_t)d + 3 * (size_t)I));
+            if (!buf) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *dOt = buf, *xt = dOt + (size_t)rows * d, *at = xt + (size_t)rows * d,
+                   *dht = at + (size_t)rows * I;
+            for (int q = 0; q < rows; ++q) {
+                const size_t r = (size_t)(r0 + q);
+                const int t = gather[r];
+                for (int n = 0; n < d; ++n) {
+                    dOt[(size_t)q * d + n] = (double)probs[r] * (double)dy[(size_t)t * d + n];
+                    xt[(size_t)q * d + n] = (double)x[(size_t)t * d + n];
+                }
+                for (int i = 0; i < I; ++i) at[(size_t)q * I + i] = ab[r * I + i];
+                for (int j = 0; j < 2 * I; ++j) dht[(size_t)q * 2 * I + j] = dhb[r * 2 * I + j];
+            }
+            mx_matrix_image(dOt, 1, rows, d, 0);
+            mx_matrix_image(xt, 1, rows, d, 0);
+            mx_matrix_image(at, 1, rows, I, 0);
+            mx_matrix_image(dht, 1, rows, 2 * I, 0);
+            for (int q = 0; q < rows; ++q) {
+                for (int n = 0; n < d; ++n) {
+                    const double g = dOt[(size_t)q * d + n];
+                    for (int i = 0; i < I; ++i) dw2_e[(size_t)n * I + i] += g * at[(size_t)q * I + i];
+                }
+                for (int j = 0; j < 2 * I; ++j) {
+                    const double g = dht[(size_t)q * 2 * I + j];
+                    for (int c = 0; c < d; ++c) dw13_e[(size_t)j * d + c] += g * xt[(size_t)q * d + c];
+                }
+            }
+            free(buf);
+        }
+    }
+    free(m_indptr); free(gather); free(slots); free(probs);
+    free(wf13); free(wf2); free(wb13); free(wb2);
+    free(hb); free(ab); free(o); free(dhb); free(dxp);
+    if (rc != ORC_OK) return rc;
+    return failed ? ORC_ERR_ALLOC : ORC_OK;
+}

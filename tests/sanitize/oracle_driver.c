@@ -27,6 +27,9 @@ void orc_mx_dequantize(int64_t rows, int K, const uint8_t* codes, const uint8_t*
 int orc_forward_tokens_mx(int T, int d, int I, int E, int k, const float* x, const int32_t* ids,
                           const float* scores, const float* w13, const float* w2, int ntok,
                           const int32_t* toks, double* y, int act);
+int orc_train_mx(int T, int d, int I, int E, int k, const float* x, const int32_t* ids,
+                 const float* scores, const float* w13, const float* w2, const float* dy, int act,
+                 double* y, double* dx, double* ds, double* dw13, double* dw2);
 
 static uint64_t state = 88172645463325252ull;
 static double uni(void)
@@ -86,10 +89,25 @@ static void run_layer(int T, int d, int I, int E, int k, int act, int empty_from
         float* back = malloc(sizeof(float) * ((size_t)T * d + 1));
         orc_mx_quantize(T, d, x, codes, scales);
         orc_mx_dequantize(T, d, codes, scales, back);
-        /* within half an E4M3 step (1/16 relative) or, at the top of a block whose maximum
-         * saturates at 448 times the scale, within 512/448 - 1 of the value */
-        for (size_t z = 0; z < (size_t)T * d; ++z) CHECK(fabs(back[z] - x[z]) <= 0.143 * fabs(x[z]) + 1e-6);
+        /* within half an E4M3 step: 1/16 of the value for a normal element; x lies in
+         * (-1, 1), so a block scale is at most 2^-8 and a subnormal element is within
+         * 2^-10 of the scale, 2^-18 */
+        for (size_t z = 0; z < (size_t)T * d; ++z) CHECK(fabs(back[z] - x[z]) <= 0.0625 * fabs(x[z]) + 4e-6);
+        /* the MXFP8 training step: every output written, unrouted experts zero */
+        double* ty = calloc((size_t)T * d + 1, sizeof(double));
+        double* tdx = calloc((size_t)T * d + 1, sizeof(double));
+        double* tds = calloc((size_t)T * k + 1, sizeof(double));
+        double* tdw13 = malloc(sizeof(double) * (size_t)E * 2 * I * d);
+        double* tdw2 = malloc(sizeof(double) * (size_t)E * d * I);
+        for (size_t z = 0; z < (size_t)E * d * I; ++z) tdw2[z] = NAN;
+        for (size_t z = 0; z < (size_t)E * 2 * I * d; ++z) tdw13[z] = NAN;
+        CHECK(orc_train_mx(T, d, I, E, k, x, ids, sc, w13, w2, dy, act, ty, tdx, tds, tdw13, tdw2) == 0);
+        for (size_t z = 0; z < (size_t)E * d * I; ++z) CHECK(!isnan(tdw2[z]));
+        for (size_t z = 0; z < (size_t)E * 2 * I * d; ++z) CHECK(!isnan(tdw13[z]));
+        for (int e = span; e < E; ++e)
+            for (size_t z = 0; z < (size_t)d * I; ++z) CHECK(tdw2[(size_t)e * d * I + z] == 0.0);
         free(yq); free(codes); free(scales); free(back);
+        free(ty); free(tdx); free(tds); free(tdw13); free(tdw2);
     }
     /* invalid routing: refused, nothing written past the arrays */
     if (T > 0) {

@@ -23,7 +23,7 @@ through the block-32 quantize->dequantize image) is pinned by:
   the plain forward of x's quantize->dequantize image bit for bit;
 * the a step alone: with x on its grid, y equals W2 applied to the image of the
   plain forward's a under an independent quantizer (torch's float8_e4m3fn cast
-  after the floor rule's power-of-two scaling).
+  after the ceil rule's power-of-two scaling).
 """
 import math
 
