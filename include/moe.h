@@ -84,7 +84,7 @@ typedef struct {
     int32_t E;          /* experts, 1..256 (nvfp4moe README, "Limits") */
     int32_t k;          /* experts per token, 1..min(E, 32) */
     int32_t precision;  /* moe_precision_t */
-    int32_t training;   /* 1: forward saves what moe_backward needs (BF16 only) */
+    int32_t training;   /* 1: forward saves what moe_backward needs */
     int32_t path;       /* MOE_PATH_* */
     int32_t wgrad_accumulate;  /* 1: moe_backward adds the weight gradients into dw13 / dw2
                                   (blog post, "What it is selling": in-place accumulation
@@ -113,17 +113,29 @@ typedef struct {
      * wrong results here; prepare weights with moe_prepare_weights. */
     const uint8_t* w13_scale;
     const uint8_t* w2_scale;
+    /* MXFP8 training backward only (NULL otherwise): the weights prepared along their other
+     * dimension for the input-gradient products (blog post, "What it is selling": MXFP8
+     * trains; each product quantizes along its own reduction dimension), as
+     * moe_prepare_weights_backward writes them:
+     *   w13t  E4M3 codes [E, d, 2I]: W13_e transposed, blocks of 32 along 2I;
+     *         w13t_scale block-major [2I/128, E*d, 4]
+     *   w2t   E4M3 codes [E, I, d]: W2_e transposed, blocks of 32 along d;
+     *         w2t_scale block-major [d/128, E*I, 4] */
+    const uint8_t* w13t;
+    const uint8_t* w13t_scale;
+    const uint8_t* w2t;
+    const uint8_t* w2t_scale;
 } moe_weights_t;
 
 /* Validate cfg against the limits (K = d and I multiples of 64, at most 256
  * experts, at most 131072 routed rows T*k; nvfp4moe README, "Limits"), choose
  * the kernels and lay out the workspace.  Host only: touches no device.
- * MXFP8 plans are forward only and need d % 256 == 0 and I % 128 == 0.
+ * MXFP8 plans need d % 256 == 0 and I % 128 == 0 and run the grouped-GEMM path.
  * Shapes whose activations (T*d*2 bytes), routed intermediates (T*k*2I*2) or
  * per-expert W13 (2I*d*2) reach 2^31 bytes are refused (the kernels address them
- * with 32-bit offsets).  Returns MOE_ERR_UNSUPPORTED for MXFP8 with training = 1
- * and for shapes outside the limits, MOE_ERR_INVALID_ARG for NULL or non-positive
- * sizes.  On success *out owns host memory released by moe_plan_destroy. */
+ * with 32-bit offsets).  Returns MOE_ERR_UNSUPPORTED for shapes outside the limits,
+ * MOE_ERR_INVALID_ARG for NULL or non-positive sizes.  On success *out owns host
+ * memory released by moe_plan_destroy. */
 moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out);
 
 /* Bytes of device workspace the plan needs (the analogue of planning memory
@@ -191,6 +203,18 @@ moe_status_t moe_prepare_weights(moe_plan_t plan, const void* w13_bf16, const vo
                                  uint8_t* w13_q, uint8_t* w13_s, uint8_t* w2_q, uint8_t* w2_s,
                                  void* stream);
 
+/* Prepare BF16 weights for the MXFP8 backward's input-gradient products (blog post,
+ * "What it is selling": MXFP8 trains; each product quantizes its operands along its
+ * own reduction dimension, so DGRAD needs the weights blocked along their other
+ * dimension): w13t_q [E, d, 2I] = W13_e^T quantized in blocks of 32 along 2I,
+ * w13t_s block-major [2I/128, E*d, 4]; w2t_q [E, I, d] = W2_e^T quantized along d,
+ * w2t_s block-major [d/128, E*I, 4] (moe_quantize_mxfp8's rule).  Like
+ * moe_prepare_weights, it is run again after every update of the BF16 weights.  Needs
+ * d and I multiples of 128 (else MOE_ERR_UNSUPPORTED).  Caller-owned outputs. */
+moe_status_t moe_prepare_weights_backward(moe_plan_t plan, const void* w13_bf16, const void* w2_bf16,
+                                          uint8_t* w13t_q, uint8_t* w13t_s, uint8_t* w2t_q, uint8_t* w2t_s,
+                                          void* stream);
+
 /* Forward (FPROP): dispatch, [MXFP8: quantize x], grouped W13 GEMM with the
  * SwiGLU epilogue, [MXFP8: re-quantize the SwiGLU output], grouped W2 GEMM,
  * score-weighted combine in FP32 with j ascending from +0.0 and one rounding
@@ -255,7 +279,15 @@ moe_status_t moe_forward_routed(moe_plan_t plan, const void* x_rows, const int32
  *    experts with no row keep their values)
  *   dscores f32  [T, k]   = dL/dscores[t][j] = <dy[t], expert output of (t, j)>
  * Returns MOE_ERR_STATE if no training forward ran since the workspace was
- * bound.  BF16 plans only. */
+ * bound.  BF16 plans take the BF16 weights in w13 / w2.  MXFP8 plans take the
+ * weights prepared by moe_prepare_weights_backward in w13t / w2t with their scales
+ * (NULL: MOE_ERR_INVALID_ARG), plus, with cfg.recompute_h = 1, the forward's
+ * prepared w13 and w13_scale; every expert product runs on MXFP8 operands quantized
+ * along that product's reduction dimension: dO = scores * dy[token] along d, the
+ * gradient (dg, du) along 2I, and, for the weight gradients, dO, a, (dg, du) and x
+ * along each expert's routed rows (blocks of 32 rows in dispatch order, restarting at
+ * every expert).  The forward's h and a and the gradients dA, (dg, du) are kept in
+ * BF16 between kernels. */
 moe_status_t moe_backward(moe_plan_t plan, const void* dy, const void* x, const moe_weights_t* w,
                           void* dx, void* dw13, void* dw2, float* dscores, void* stream);
 
@@ -270,9 +302,10 @@ moe_status_t moe_get_status(moe_plan_t plan, int32_t* device_flags, int32_t clea
 const char* moe_status_string(moe_status_t status);
 
 /* Kernel stages of moe_forward / moe_backward.  moe_backward launches SCORE_GRAD,
- * [RECOMPUTE_H,] DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order; the
- * one-token decode runs W2 and the combine as one kernel, recorded as DECODE_W2; a mega
- * decode plan runs its one launch as MEGA. */
+ * [RECOMPUTE_H,] DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order
+ * (MXFP8: SCORE_GRAD, [RECOMPUTE_H,] QUANT_DO, DGRAD_W2, ACT_BWD, DGRAD_W13, DX_COMBINE,
+ * QUANT_T, WGRAD_W2, QUANT_T, WGRAD_W13); the one-token decode runs W2 and the combine as
+ * one kernel, recorded as DECODE_W2; a mega decode plan runs its one launch as MEGA. */
 #define MOE_STAGE_DISPATCH 0
 #define MOE_STAGE_QUANT_X 1
 #define MOE_STAGE_W13 2
@@ -289,7 +322,10 @@ const char* moe_status_string(moe_status_t status);
 #define MOE_STAGE_WGRAD_ROWS 13
 #define MOE_STAGE_RECOMPUTE_H 14
 #define MOE_STAGE_MEGA 15
-#define MOE_STAGE_COUNT 16
+#define MOE_STAGE_QUANT_DO 16     /* MXFP8 backward: dO quantized along d */
+#define MOE_STAGE_ACT_BWD 17      /* MXFP8 backward: activation backward, (dg, du) quantized along 2I */
+#define MOE_STAGE_QUANT_T 18      /* MXFP8 backward: weight-gradient operands quantized along rows */
+#define MOE_STAGE_COUNT 19
 
 /* Per-stage timing with HIP events, for measurement only.  While enabled,
  * moe_forward and moe_backward record a pair of HIP events around each kernel

@@ -6,11 +6,20 @@
 // consecutive K elements) with FP32 accumulation, using the block-scaled MFMA
 // v_mfma_scale_f32_32x32x64_f8f6f4:
 //
-//   mode     P (p, k)                  Q (q, k)                K    output
-//   MX_W13   W13_e rows, gate/up pairs xq[gather[r]], xs       d    a = silu(g)*u re-quantized to
-//                                                                   MXFP8 along I: aq [R, I], as [R, I/32]
-//   MX_W2    W2_e rows                 aq[r], as               I    o [R, d] BF16
+//   mode      P (p, k)                  Q (q, k)                K     output
+//   MX_W13    W13_e rows, gate/up pairs xq[gather[r]], xs       d     a = silu(g)*u re-quantized to
+//                                                                     MXFP8 along I: aq [R, I], as [R, I/32]
+//                                                                     (training: also h and a in BF16)
+//   MX_W2     W2_e rows                 aq[r], as               I     o [R, d] BF16
+//   MX_PLAIN  weight-layout rows        routed rows             Kp    BF16 [R, Np]: the input gradients
+//             (W2 or W13 prepared transposed)                         dA = W2^T dO, dXp = W13^T dh
+//   MX_WGRAD  token-layout rows of      token-layout rows of    rows  BF16 [E, Nq, Np]: the weight
+//             a^T or x[gather]^T        dO^T or dh^T            of e  gradients dW2, dW13
 //
+// MX_WGRAD runs K over an expert's routed rows, quantized in blocks of 32 rows and padded
+// to a multiple of 128 (an expert with no row gets 128 zero rows, so its gradient is
+// written as +0); its experts are taken in decreasing order of rows, so that the longest
+// tiles start first.
 // The structure is the BF16 kernel's (workgroup tile 256 x 256, four waves of
 // 128 x 128, a ring of four 32 KiB LDS buffers, direct global-to-LDS copies issued
 // three stages ahead, one continuous stream of stages per workgroup); a stage is
@@ -70,9 +79,10 @@ __device__ __forceinline__ void tile_order(int local, int nQt, int nPt, int& pt,
 
 struct TileCtx {
     int e, mb, rows, pt, qt, nk;
+    int koff, kp;                      // MX_WGRAD: the expert's token-layout offset and padded rows
 };
 
-template <int MODE, int kAct = kActSwiGLU>
+template <int MODE, int kAct = kActSwiGLU, bool kSave = false>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ __attribute__((aligned(1024))) char lsc[NSC * SCB];
@@ -80,6 +90,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ int mptr[257];          // m_indptr, so that the tile walk reads no global memory
     __shared__ int gsrc[2][TQ];        // token ids (MX_W13) of the next two load-cursor tiles
     __shared__ int wtot[NTHR / MOE_WAVE];
+    __shared__ int worder[256], wkp[256], wkoff[256];   // MX_WGRAD: work order, padded rows, offsets
+    constexpr bool kWgrad = MODE == MX_WGRAD;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,30 +106,53 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     };
     const int wp = wave & 1, wq = wave >> 1;
     const int E = g.E;
-    const int K = MODE == MX_W13 ? g.d : g.I;          // K of the product (bytes per row)
+    // K of the product (bytes per row; MX_WGRAD: per expert, in the tile context)
+    const int K = MODE == MX_W13 ? g.d : (MODE == MX_W2 ? g.I : g.Kp);
     const size_t R = (size_t)g.T * g.k;                // routed rows
-    const int nPt = MODE == MX_W13 ? g.I / 128 : g.d / TP;
+    const int nPt = MODE == MX_W13 ? g.I / 128 : (MODE == MX_W2 ? g.d / TP : (g.Np + TP - 1) / TP);
+    const int nQt = kWgrad ? (g.Nq + TQ - 1) / TQ : 0; // MX_WGRAD: q-tiles per expert
 
-    // ---- tile list: tiles of expert e are cum[e] .. cum[e+1]-1
-    {
-        int cnt = 0;
-        if (tid < E) {
-            const int rows = g.m_indptr[tid + 1] - g.m_indptr[tid];
-            cnt = ((rows + TQ - 1) / TQ) * nPt;
-        }
-        int incl = cnt;
+    // exclusive prefix over threads 0 .. E-1 of v into out[1 .. E], out[0] = 0 (ends with a barrier)
+    auto block_scan = [&](int v, int* out) {
+        int incl = v;
         for (int off = 1; off < MOE_WAVE; off <<= 1) {
-            const int v = __shfl_up(incl, off, MOE_WAVE);
-            if (lane >= off) incl += v;
+            const int u = __shfl_up(incl, off, MOE_WAVE);
+            if (lane >= off) incl += u;
         }
         if (lane == MOE_WAVE - 1) wtot[wave] = incl;
-        for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
         __syncthreads();
         int pre = 0;
         for (int w = 0; w < wave; ++w) pre += wtot[w];
-        if (tid < E) cum[tid + 1] = pre + incl;
-        if (tid == 0) cum[0] = 0;
+        if (tid < E) out[tid + 1] = pre + incl;
+        if (tid == 0) out[0] = 0;
         __syncthreads();
+    };
+    // ---- tile list: tiles of expert e (MX_WGRAD: of work position e) are cum[e] .. cum[e+1]-1
+    for (int i = tid; i <= E; i += NTHR) mptr[i] = g.m_indptr[i];
+    __syncthreads();
+    if constexpr (kWgrad) {
+        // padded rows and token-layout offsets in expert order, then the work order:
+        // decreasing padded rows, then expert id
+        const int kp = tid < E ? ((mptr[tid + 1] - mptr[tid] > 0 ? mptr[tid + 1] - mptr[tid] : 1) + kMxWgradPad - 1) /
+                                     kMxWgradPad * kMxWgradPad
+                               : 0;
+        block_scan(kp, cum);
+        if (tid < E) { wkp[tid] = kp; wkoff[tid] = cum[tid]; }
+        __syncthreads();
+        if (tid < E) {
+            int rank = 0;
+            for (int e2 = 0; e2 < E; ++e2) rank += (wkp[e2] > kp || (wkp[e2] == kp && e2 < tid)) ? 1 : 0;
+            worder[rank] = tid;
+        }
+        __syncthreads();
+        block_scan(tid < E ? nQt * nPt : 0, cum);
+    } else {
+        int cnt = 0;
+        if (tid < E) {
+            const int rows = mptr[tid + 1] - mptr[tid];
+            cnt = ((rows + TQ - 1) / TQ) * nPt;
+        }
+        block_scan(cnt, cum);
     }
     const int total = cum[E];
     const int G = gridDim.x;
@@ -135,12 +170,25 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
         }
         lo = __builtin_amdgcn_readfirstlane(lo);
         TileCtx c;
-        c.e = lo;
         const int local = tile - cum[lo];
-        c.mb = mptr[lo];
-        c.rows = mptr[lo + 1] - c.mb;
-        tile_order(local, (c.rows + TQ - 1) / TQ, nPt, c.pt, c.qt);
-        c.nk = K / TKB;                               // even: K is a multiple of 128
+        if constexpr (kWgrad) {
+            c.e = __builtin_amdgcn_readfirstlane(worder[lo]);
+            c.mb = 0;
+            c.rows = g.Nq;                            // q rows of the tile are features
+            c.qt = local / nPt;
+            c.pt = local - c.qt * nPt;
+            c.kp = __builtin_amdgcn_readfirstlane(wkp[c.e]);
+            c.koff = __builtin_amdgcn_readfirstlane(wkoff[c.e]);
+            c.nk = c.kp / TKB;                        // even: kp is a multiple of 128
+        } else {
+            c.e = lo;
+            c.mb = mptr[lo];
+            c.rows = mptr[lo + 1] - c.mb;
+            tile_order(local, (c.rows + TQ - 1) / TQ, nPt, c.pt, c.qt);
+            c.nk = K / TKB;                           // even: K is a multiple of 128
+            c.kp = K;
+            c.koff = 0;
+        }
         return c;
     };
 
@@ -152,9 +200,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
             int ii = c.pt * 128 + (r >> 5) * 16 + (r & 15);
             if (ii >= g.I) ii = g.I - 1;
             return (r & 16) ? g.I + ii : ii;
-        } else {
+        } else if constexpr (MODE == MX_W2) {
             const int pr = c.pt * TP + r;
             return pr < g.d ? pr : g.d - 1;
+        } else {
+            const int pr = c.pt * TP + r;
+            return pr < g.Np ? pr : g.Np - 1;
         }
     };
     // row of the Q operand (token of xq, or routed row of aq) behind Q tile row r, for
@@ -167,7 +218,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     };
     auto q_row = [&](const TileCtx& c, int slot, int r) {
         if constexpr (MODE == MX_W13) return gsrc[slot][r];
-        else return routed_row(c, r);
+        else return routed_row(c, r);                 // MX_WGRAD: the feature row (mb = 0, rows = Nq)
     };
     // Token ids of tile c into gsrc[slot]: wave w copies entries 64 w .. 64 w + 63 (the
     // rows of its own data and scale copies) with one global_load_lds_dword, issued a
@@ -183,11 +234,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                          :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(voff), "s"(g.gather) : "memory");
         }
     };
-    const uint8_t* pdata = MODE == MX_W13 ? g.w13q : g.w2q;
-    const uint8_t* pscale = MODE == MX_W13 ? g.w13s : g.w2s;
-    const uint8_t* qdata = MODE == MX_W13 ? g.xq : g.aq;
-    const uint8_t* qscale = MODE == MX_W13 ? g.xs : g.as;
-    const size_t prows_e = MODE == MX_W13 ? (size_t)2 * g.I : (size_t)g.d;   // P rows per expert
+    const uint8_t* pdata = MODE == MX_W13 ? g.w13q : (MODE == MX_W2 ? g.w2q : g.pq);
+    const uint8_t* pscale = MODE == MX_W13 ? g.w13s : (MODE == MX_W2 ? g.w2s : g.ps);
+    const uint8_t* qdata = MODE == MX_W13 ? g.xq : (MODE == MX_W2 ? g.aq : g.qq);
+    const uint8_t* qscale = MODE == MX_W13 ? g.xs : (MODE == MX_W2 ? g.as : g.qs);
+    // P rows per expert
+    const size_t prows_e = MODE == MX_W13 ? (size_t)2 * g.I : (MODE == MX_W2 ? (size_t)g.d : (size_t)g.Np);
 
     // ------------------------------------------------------------ direct copies
     // Data: wave w copies the 1 KiB blocks 4w .. 4w+3 of each operand of a stage;
@@ -201,20 +253,34 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     uint32_t svoffP = 0, svoffQ = 0;
     const char* pbase_e = nullptr;
     const char* psbase_e = nullptr;
+    const char* qbase_e = reinterpret_cast<const char*>(qdata);     // per expert in MX_WGRAD
+    const char* qsbase_e = reinterpret_cast<const char*>(qscale);
+    // bytes between the scale words of consecutive 128-element K groups
+    size_t pscale_stride = (size_t)E * prows_e * 4, qscale_stride = R * 4;
     auto copy_offsets = [&](const TileCtx& c, int slot) {
         const int fl = fresh_lane();
+        const int Kt = c.kp;                                    // this tile's K (bytes per row)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = (4 * wave + j) * 16 + (fl >> 2);
             const int cl = (fl & 3) ^ swz(r);
-            dvoff[j] = (uint32_t)(p_row(c, r) * K + 16 * cl);
-            dvoff[4 + j] = (uint32_t)(q_row(c, slot, r) * K + 16 * cl);
+            dvoff[j] = (uint32_t)(p_row(c, r) * Kt + 16 * cl);
+            dvoff[4 + j] = (uint32_t)(q_row(c, slot, r) * Kt + 16 * cl);
         }
         const int rs = 64 * wave + fl;
         svoffP = (uint32_t)(p_row(c, rs) * 4);
-        svoffQ = (uint32_t)(routed_row(c, rs) * 4);          // Q scales are in routed order in both modes
-        pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
-        psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * 4);
+        svoffQ = (uint32_t)(routed_row(c, rs) * 4);          // Q scales are in routed (feature) order
+        if constexpr (kWgrad) {
+            pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.koff * g.Np);
+            psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.koff * g.Np / 32);
+            qbase_e = reinterpret_cast<const char*>(qdata + (size_t)c.koff * g.Nq);
+            qsbase_e = reinterpret_cast<const char*>(qscale + (size_t)c.koff * g.Nq / 32);
+            pscale_stride = (size_t)g.Np * 4;
+            qscale_stride = (size_t)g.Nq * 4;
+        } else {
+            pbase_e = reinterpret_cast<const char*>(pdata + (size_t)c.e * prows_e * K);
+            psbase_e = reinterpret_cast<const char*>(pscale + (size_t)c.e * prows_e * 4);
+        }
     };
     auto dma16 = [&](uint32_t lds_addr, uint32_t voff, const char* base) {
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
@@ -228,15 +294,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     auto dma_data = [&](int kt, int buf, int j) {
         const uint32_t dst = lds0 + buf * BUFB + (4 * wave) * 1024;
         if (j < 4) dma16(dst + j * 1024, dvoff[j], pbase_e + kt * TKB);
-        else dma16(dst + OPB + (j - 4) * 1024, dvoff[j], reinterpret_cast<const char*>(qdata) + kt * TKB);
+        else dma16(dst + OPB + (j - 4) * 1024, dvoff[j], qbase_e + kt * TKB);
     };
     // scale words of the stage pair holding stage kt (blocks 2 (kt & ~1) .. +3) into
     // scale slot `slot`
     auto dma_scales = [&](int kt, int slot) {
         const uint32_t dst = lsc0 + slot * SCB + 256 * wave;
         const size_t kp = (size_t)(kt >> 1);                  // stage pair = group of 4 blocks
-        dma4(dst, svoffP, psbase_e + kp * E * prows_e * 4);
-        dma4(dst + 1024, svoffQ, reinterpret_cast<const char*>(qscale) + kp * R * 4);
+        dma4(dst, svoffP, psbase_e + kp * pscale_stride);
+        dma4(dst + 1024, svoffQ, qsbase_e + kp * qscale_stride);
     };
 
     // ------------------------------------------------------------ fragments and scales
@@ -350,16 +416,34 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                                 const float* q = &av[8 * h + 4 * grp];
                                 const uint32_t w = e4m3_pack4(__builtin_ldexpf(q[0], sh), __builtin_ldexpf(q[1], sh),
                                                               __builtin_ldexpf(q[2], sh), __builtin_ldexpf(q[3], sh));
-                                *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i0 + 16 * h + 8 * grp + p_sub) = w;
+                                const int i = i0 + 16 * h + 8 * grp + p_sub;
+                                *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i) = w;
+                                if constexpr (kSave) {
+                                    // the training forward also keeps a and h = (g, u) in BF16
+                                    uint2 av2, hg, hu;
+                                    av2.x = pack_bf16(q[0], q[1]); av2.y = pack_bf16(q[2], q[3]);
+                                    const f32x16_t& t = acc[2 * m + h][b];
+                                    hg.x = pack_bf16(t[4 * grp], t[4 * grp + 1]);
+                                    hg.y = pack_bf16(t[4 * grp + 2], t[4 * grp + 3]);
+                                    hu.x = pack_bf16(t[4 * (grp + 2)], t[4 * (grp + 2) + 1]);
+                                    hu.y = pack_bf16(t[4 * (grp + 2) + 2], t[4 * (grp + 2) + 3]);
+                                    *reinterpret_cast<uint2*>(g.a_out + r * g.I + i) = av2;
+                                    *reinterpret_cast<uint2*>(g.h_out + r * 2 * g.I + i) = hg;
+                                    *reinterpret_cast<uint2*>(g.h_out + r * 2 * g.I + g.I + i) = hu;
+                                }
                             }
                         if (ln < 32) g.as[((size_t)(i0 >> 7) * R + r) * 4 + ((i0 >> 5) & 3)] = (uint8_t)sb;
                     }
                 }
             }
         } else {
-            // o [R, d] in BF16 through LDS (this wave's 8 KiB of the stage buffer just
-            // consumed), stored as whole 256-byte row segments with non-temporal stores
-            // (ordinary ones evict the operands the XCD's workgroups share in L2)
+            // o [R, d] (MX_PLAIN: [R, Np]; MX_WGRAD: expert e's [Nq, Np]) in BF16 through
+            // LDS (this wave's 8 KiB of the stage buffer just consumed), stored as whole
+            // 256-byte row segments with non-temporal stores (ordinary ones evict the
+            // operands the XCD's workgroups share in L2)
+            uint16_t* obase = MODE == MX_W2 ? g.o : g.out;
+            const int ld = MODE == MX_W2 ? g.d : g.Np;
+            if constexpr (kWgrad) obase += (size_t)c.e * g.Nq * g.Np;
             char* stg = lds + buf * BUFB + wave * 8192;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -381,7 +465,22 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                     const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
                     const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
                     const int p = c.pt * TP + wp * 128 + 8 * c16;
-                    if (rr < c.rows && p < g.d) store_nt(g.o + ((size_t)c.mb + rr) * g.d + p, v);
+                    if (rr < c.rows && p < ld) {
+                        uint16_t* dst = obase + ((size_t)c.mb + rr) * ld + p;
+                        if (kWgrad && g.accumulate) {
+                            // in-place accumulation: the BF16 gradient added to the value
+                            // there in FP32, one rounding
+                            const uint4 o = *reinterpret_cast<const uint4*>(dst);
+                            const uint32_t ov[4] = {o.x, o.y, o.z, o.w}, nv[4] = {v.x, v.y, v.z, v.w};
+                            uint32_t sv[4];
+#pragma unroll
+                            for (int z = 0; z < 4; ++z)
+                                sv[z] = pack_bf16(bf16lo(ov[z]) + bf16lo(nv[z]), bf16hi(ov[z]) + bf16hi(nv[z]));
+                            store_nt(dst, make_uint4(sv[0], sv[1], sv[2], sv[3]));
+                        } else {
+                            store_nt(dst, v);
+                        }
+                    }
                 }
                 __builtin_amdgcn_s_waitcnt(0xc07f);
             }
@@ -478,25 +577,34 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     }
 }
 
+template <int MODE, int kAct>
+hipError_t launch_mx_act(const MxGemmArgs& g, dim3 grid, hipStream_t s) {
+    if constexpr (MODE == MX_W13)
+        if (g.h_out) {
+            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, true>), grid, dim3(NTHR), 0, s, g);
+            return hipGetLastError();
+        }
+    hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, false>), grid, dim3(NTHR), 0, s, g);
+    return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t launch_mx_mode(const MxGemmArgs& g, int num_cu, hipStream_t s) {
     const int64_t R = (int64_t)g.T * g.k;
-    const int64_t tiles = (R / TQ + g.E) * (MODE == MX_W13 ? g.I / 128 : g.d / TP);
+    int64_t tiles;
+    if constexpr (MODE == MX_W13) tiles = (R / TQ + g.E) * (g.I / 128);
+    else if constexpr (MODE == MX_W2) tiles = (R / TQ + g.E) * (g.d / TP);
+    else if constexpr (MODE == MX_PLAIN) tiles = (R / TQ + g.E) * ((g.Np + TP - 1) / TP);
+    else tiles = (int64_t)g.E * ((g.Np + TP - 1) / TP) * ((g.Nq + TQ - 1) / TQ);
     int64_t grid = tiles < num_cu ? tiles : num_cu;
     if (grid >= 8) grid -= grid % 8;
     if (grid < 1) grid = 1;
+    const dim3 gd((unsigned)grid);
     if constexpr (MODE == MX_W13) {
-        if (g.act == kActGeGLU) {
-            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kActGeGLU>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
-            return hipGetLastError();
-        }
-        if (g.act == kActReGLU) {
-            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kActReGLU>), dim3((unsigned)grid), dim3(NTHR), 0, s, g);
-            return hipGetLastError();
-        }
+        if (g.act == kActGeGLU) return launch_mx_act<MODE, kActGeGLU>(g, gd, s);
+        if (g.act == kActReGLU) return launch_mx_act<MODE, kActReGLU>(g, gd, s);
     }
-    hipLaunchKernelGGL(grouped_gemm_mx<MODE>, dim3((unsigned)grid), dim3(NTHR), 0, s, g);
-    return hipGetLastError();
+    return launch_mx_act<MODE, kActSwiGLU>(g, gd, s);
 }
 
 }  // namespace
@@ -505,6 +613,8 @@ hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipSt
     switch (mode) {
         case MX_W13: return launch_mx_mode<MX_W13>(g, num_cu, s);
         case MX_W2: return launch_mx_mode<MX_W2>(g, num_cu, s);
+        case MX_PLAIN: return launch_mx_mode<MX_PLAIN>(g, num_cu, s);
+        case MX_WGRAD: return launch_mx_mode<MX_WGRAD>(g, num_cu, s);
     }
     return hipErrorInvalidValue;
 }

@@ -58,7 +58,7 @@ constexpr size_t kGemmPartBytes = (size_t)kMaxPieces * 256 * 256 * sizeof(float)
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
 
 // MXFP8 forward products (OCP E4M3 codes, E8M0 scale per 32 along K).
-enum MxMode { MX_W13 = 0, MX_W2 = 1 };
+enum MxMode { MX_W13 = 0, MX_W2 = 1, MX_PLAIN = 2, MX_WGRAD = 3 };
 
 struct MxGemmArgs {
     int T, d, I, E, k;
@@ -74,9 +74,55 @@ struct MxGemmArgs {
     uint8_t* as;          // block-major words: (g, r) at (g * R + r) * 4
     uint16_t* o;          // [R, d]      BF16 expert outputs (MX_W2 output)
     int act;              // gated activation of the W13 epilogue
+    // MX_W13 of a training forward: BF16 copies kept for the backward (NULL otherwise)
+    uint16_t* h_out;      // [R, 2I]     (g, u)
+    uint16_t* a_out;      // [R, I]      a before its re-quantization
+    // MX_PLAIN (the input-gradient products): D[r][n] = sum_k P_e[n][k] Q[r][k]
+    //   P: weight layout, codes [E][Np][Kp], block-major scales [Kp/128][E*Np][4]
+    //   Q: routed rows, codes [R][Kp], block-major scales [Kp/128][R][4]
+    //   out: BF16 [R][Np]
+    // MX_WGRAD (the weight gradients): D_e[q][p] = sum_r Q_e[q][r] P_e[p][r] over the
+    // routed rows of expert e, the operands in the token layout: expert e's rows padded to
+    // kp_e = roundup(max(rows_e, 1), 128) and prefixed koff_e = sum of kp over the experts
+    // before it; codes [N][kp_e] at koff_e * N, scales block-major [kp_e/128][N][4] at
+    // byte koff_e * N / 32 (N = Np for P, Nq for Q); out: BF16 [E][Nq][Np], overwritten
+    int Kp, Np, Nq;
+    const uint8_t* pq;
+    const uint8_t* ps;
+    const uint8_t* qq;
+    const uint8_t* qs;
+    uint16_t* out;
+    int accumulate;       // MX_WGRAD: out = bf16(out + bf16(D)) instead of bf16(D)
 };
 
 hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipStream_t s);
+
+// Token-layout padding of MX_WGRAD operands: kp_e = roundup(max(rows_e, 1), 128); the
+// sum over experts is at most R + 128 E.
+constexpr int kMxWgradPad = 128;
+
+// MXFP8 quantization for the backward (OCP MX blocks of 32, the same scale rule as
+// launch_quantize_mxfp8):
+// rows r < R of probs[r] * dy[gather[r]] along d: codes [R][d], block-major scales
+// [d/128][R][4] (gather entries outside [0, T) read row 0)
+hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, const int32_t* gather, const float* probs,
+                                 int64_t R, int d, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// SwiGLU (GeGLU, ReGLU) backward of MXFP8 training: dg = dA u f'(g), du = dA f(g) from dA
+// [R][I] and h = (g, u) [R][2I] (BF16); dh = (dg, du) in BF16 [R][2I] and quantized along
+// 2I: codes [R][2I], block-major scales [2I/128][R][4]
+hipError_t launch_mx_act_backward(const uint16_t* dA, const uint16_t* h, int64_t R, int I, int act,
+                                  uint16_t* dh, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Transposing quantization.  Weight layout (weights != 0): `segs` matrices src + e*K*N of
+// K rows x N columns (BF16) become codes [e][N][K] (the transpose, quantized along K) with
+// block-major scales [K/128][segs*N][4]; K a multiple of 128.  Token layout (weights == 0):
+// segment e is the routed rows m_indptr[e] .. m_indptr[e+1] and becomes codes [N][kp_e]
+// at koff_e * N (rows past the segment as zeros) with scales [kp_e/128][N][4] at byte
+// koff_e * N / 32 (kp_e, koff_e as for MX_WGRAD); routed row r is src row r, or with
+// gather the token row gather[r] of src [T, N] (entries outside [0, T) read row 0), times
+// probs[r] when probs is given.  segs <= 256.
+hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N, const int32_t* m_indptr,
+                                     const int32_t* gather, const float* probs, int T, bool weights,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 // y[t] = sum_j w[t][j] * src[slots[t][j]] (w = NULL means weight 1; slots = NULL means
 // row t*k + j), FP32, j ascending.

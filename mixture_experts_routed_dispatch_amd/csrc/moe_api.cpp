@@ -38,6 +38,11 @@ struct moe_plan_s {
     // workspace offsets (bytes)
     size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
     size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_xsr, off_aq, off_as;
+    // MXFP8 backward: dO and (dg, du) quantized along d and 2I (codes, block-major scales), and
+    // the weight-gradient operands in the token layout (P and Q codes and scales)
+    size_t off_doq, off_dos, off_dhq, off_dhs, off_tp, off_tps, off_tq, off_tqs;
+    size_t tp_feat, tq_feat;           // features of the largest P / Q token-layout operand
+    int64_t ntok;                      // token-layout rows: T*k + 128 E
     size_t off_part, off_split;        // split weight-gradient tiles: partial sums, descriptors
     size_t off_mega;                   // mega decode: FP32 partial expert outputs [T*k, I / chunk, d]
     size_t ws_bytes;
@@ -93,6 +98,115 @@ hipError_t staged(moe_plan_s* p, int stage, hipStream_t s, F&& fn) {
 }
 }  // namespace
 
+namespace {
+// MXFP8 backward (see moe_backward in moe.h): every expert product on MXFP8 operands
+// quantized along its own reduction dimension
+moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe_weights_t* w, void* dx,
+                         void* dw13, void* dw2, float* dscores, hipStream_t s) {
+    const moe_config_t& c = p->cfg;
+    const int64_t R = p->R;
+    int32_t* m_indptr = p->at<int32_t>(p->off_m_indptr);
+    const int32_t* gather = p->at<int32_t>(p->off_gather);
+    const int32_t* slots = p->at<int32_t>(p->off_slots);
+    const float* probs = p->at<float>(p->off_probs);
+    uint16_t* a = p->at<uint16_t>(p->off_a);
+    uint16_t* h = p->at<uint16_t>(p->off_h);
+    uint16_t* dh = p->at<uint16_t>(p->off_dh);
+    uint16_t* dxp = p->at<uint16_t>(p->off_dxp);        // dA, then dxp
+    uint8_t* tp = p->at<uint8_t>(p->off_tp);
+    uint8_t* tps = p->at<uint8_t>(p->off_tps);
+    uint8_t* tq = p->at<uint8_t>(p->off_tq);
+    uint8_t* tqs = p->at<uint8_t>(p->off_tqs);
+    const uint16_t* dy16 = static_cast<const uint16_t*>(dy);
+    const uint16_t* x16 = static_cast<const uint16_t*>(x);
+    MxGemmArgs mg{};
+    mg.T = c.T; mg.d = c.d; mg.I = c.I; mg.E = c.E; mg.k = c.k;
+    mg.act = c.activation;
+    mg.m_indptr = m_indptr; mg.gather = gather;
+    mg.accumulate = c.wgrad_accumulate;
+    hipError_t e;
+    if (c.T == 0) {
+        // no routed rows: every expert is empty and its weight gradient +0 (or kept)
+        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr, nullptr,
+                                 nullptr, nullptr, p->at<int32_t>(p->off_status), s)) != hipSuccess)
+            return MOE_ERR_HIP;
+    } else {
+        e = staged(p, MOE_STAGE_SCORE_GRAD, s, [&] {
+            return launch_score_grad(dy16, p->at<uint16_t>(p->off_o), slots, c.T, c.k, c.d, dscores, s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        if (c.recompute_h) {
+            // h and a again from the forward's quantized x (still in the workspace) and
+            // W13: the same kernel and inputs, so the same values
+            MxGemmArgs gr = mg;
+            gr.xq = p->at<uint8_t>(p->off_xq); gr.xs = p->at<uint8_t>(p->off_xsr);
+            gr.w13q = static_cast<const uint8_t*>(w->w13); gr.w13s = w->w13_scale;
+            gr.aq = p->at<uint8_t>(p->off_aq); gr.as = p->at<uint8_t>(p->off_as);
+            gr.h_out = h; gr.a_out = a;
+            e = staged(p, MOE_STAGE_RECOMPUTE_H, s, [&] { return launch_gemm_mxfp8(MX_W13, gr, p->num_cu, s); });
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
+        uint8_t* doq = p->at<uint8_t>(p->off_doq);
+        uint8_t* dos = p->at<uint8_t>(p->off_dos);
+        uint8_t* dhq = p->at<uint8_t>(p->off_dhq);
+        uint8_t* dhs = p->at<uint8_t>(p->off_dhs);
+        e = staged(p, MOE_STAGE_QUANT_DO, s, [&] {
+            return launch_mx_scaled_rows(dy16, c.T, gather, probs, R, c.d, doq, dos, s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        // dA [R, I] = dO W2_e: P = W2_e^T [I, d] blocked along d
+        MxGemmArgs g1 = mg;
+        g1.Kp = c.d; g1.Np = c.I;
+        g1.pq = w->w2t; g1.ps = w->w2t_scale; g1.qq = doq; g1.qs = dos;
+        g1.out = dxp;
+        e = staged(p, MOE_STAGE_DGRAD_W2, s, [&] { return launch_gemm_mxfp8(MX_PLAIN, g1, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_ACT_BWD, s, [&] {
+            return launch_mx_act_backward(dxp, h, R, c.I, c.activation, dh, dhq, dhs, s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        // dxp [R, d] = (dg, du) W13_e: P = W13_e^T [d, 2I] blocked along 2I
+        MxGemmArgs g2 = mg;
+        g2.Kp = 2 * c.I; g2.Np = c.d;
+        g2.pq = w->w13t; g2.ps = w->w13t_scale; g2.qq = dhq; g2.qs = dhs;
+        g2.out = dxp;
+        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_PLAIN, g2, p->num_cu, s); });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        e = staged(p, MOE_STAGE_DX_COMBINE, s, [&] {
+            return launch_combine(dxp, slots, nullptr, c.T, c.k, c.d, static_cast<uint16_t*>(dx), s);
+        });
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    // weight gradients: operands in the token layout (blocks of 32 routed rows of one expert)
+    const int32_t* gth = c.T > 0 ? gather : nullptr;
+    const float* prb = c.T > 0 ? probs : nullptr;
+    e = staged(p, MOE_STAGE_QUANT_T, s, [&] {
+        hipError_t qe = launch_mx_transpose_quant(a, c.E, 0, c.I, m_indptr, nullptr, nullptr, 0, false, tp, tps, s);
+        if (qe != hipSuccess) return qe;
+        return launch_mx_transpose_quant(dy16, c.E, 0, c.d, m_indptr, gth, prb, c.T, false, tq, tqs, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MxGemmArgs g3 = mg;                 // dW2_e [d, I] = sum_r dO_r a_r^T
+    g3.Np = c.I; g3.Nq = c.d;
+    g3.pq = tp; g3.ps = tps; g3.qq = tq; g3.qs = tqs;
+    g3.out = static_cast<uint16_t*>(dw2);
+    e = staged(p, MOE_STAGE_WGRAD_W2, s, [&] { return launch_gemm_mxfp8(MX_WGRAD, g3, p->num_cu, s); });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = staged(p, MOE_STAGE_QUANT_T, s, [&] {
+        hipError_t qe = launch_mx_transpose_quant(x16, c.E, 0, c.d, m_indptr, gth, nullptr, c.T, false, tp, tps, s);
+        if (qe != hipSuccess) return qe;
+        return launch_mx_transpose_quant(dh, c.E, 0, 2 * c.I, m_indptr, nullptr, nullptr, 0, false, tq, tqs, s);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    MxGemmArgs g4 = mg;                 // dW13_e [2I, d] = sum_r dh_r x_r^T
+    g4.Np = c.d; g4.Nq = 2 * c.I;
+    g4.pq = tp; g4.ps = tps; g4.qq = tq; g4.qs = tqs;
+    g4.out = static_cast<uint16_t*>(dw13);
+    e = staged(p, MOE_STAGE_WGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_WGRAD, g4, p->num_cu, s); });
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+}  // namespace
+
 extern "C" {
 
 moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
@@ -113,9 +227,12 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (c.E > kMaxExperts || c.k > c.E || c.k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)c.T * c.k;
     if (R > kMaxRoutedRows) return MOE_ERR_UNSUPPORTED;
-    // MXFP8 runs forward only (the blog post's MXFP8 training path is not built here);
-    // its kernels take K in stages of 64 codes and P tiles of 256 rows
-    if (c.precision == MOE_MXFP8_E4M3 && (c.training || c.d % 256 != 0 || c.I % 128 != 0))
+    // MXFP8 kernels take K in stages of 64 codes and P tiles of 256 rows
+    if (c.precision == MOE_MXFP8_E4M3 && (c.d % 256 != 0 || c.I % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+    // MXFP8 weight gradients address a token-layout operand (features x padded rows) with
+    // 32-bit offsets
+    if (c.precision == MOE_MXFP8_E4M3 && c.training &&
+        (int64_t)(c.d > 2 * c.I ? c.d : 2 * c.I) * (R + (int64_t)kMxWgradPad * c.E) >= (1LL << 32))
         return MOE_ERR_UNSUPPORTED;
     // 32-bit byte offsets inside x, the routed intermediates and one expert's weights
     if ((int64_t)c.T * c.d * 2 >= (1LL << 31) || R * 2 * c.I * 2 >= (1LL << 31) ||
@@ -144,16 +261,19 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_slots = take(sizeof(int32_t) * (size_t)R);
     p->off_probs = take(sizeof(float) * (size_t)R);
     const bool mx = c.precision == MOE_MXFP8_E4M3;
-    p->off_a = mx ? 0 : take(2 * (size_t)R * c.I);
+    const bool mxt = mx && c.training;
+    // a in BF16: the BF16 path's W2 operand; MXFP8 training keeps it for the weight gradient
+    p->off_a = (!mx || c.training) ? take(2 * (size_t)R * c.I) : 0;
     p->off_o = take(2 * (size_t)R * c.d);
     const size_t h_bytes = 2 * (size_t)R * 2 * c.I;
     p->off_h = (c.training && !c.recompute_h) ? take(h_bytes) : 0;
     p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
-    p->off_dxp = c.training ? take(2 * (size_t)R * c.d) : 0;
-    p->off_xg = c.training ? take(2 * (size_t)R * c.d) : 0;
-    p->off_dys = c.training ? take(2 * (size_t)R * c.d) : 0;
+    // MXFP8: dA [R, I] first, then dxp [R, d]
+    p->off_dxp = c.training ? take(2 * (size_t)R * (mx && c.I > c.d ? c.I : c.d)) : 0;
+    p->off_xg = (c.training && !mx) ? take(2 * (size_t)R * c.d) : 0;
+    p->off_dys = (c.training && !mx) ? take(2 * (size_t)R * c.d) : 0;
     p->h_aliased = false;
-    if (c.training && c.recompute_h) {
+    if (c.training && c.recompute_h && !mx) {
         // the recomputed h lives from the start of the backward to DGRAD W2; dxp, xg and
         // dys (consecutive) are first written after that, so h takes their place
         if (h_bytes <= p->off_dys + 2 * (size_t)R * c.d - p->off_dxp) {
@@ -168,6 +288,27 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_xsr = mx ? take((size_t)R * c.d / 32) : 0;
     p->off_aq = mx ? take((size_t)R * c.I) : 0;
     p->off_as = mx ? take((size_t)R * c.I / 32) : 0;
+    p->ntok = R + (int64_t)kMxWgradPad * c.E;
+    p->tp_feat = (size_t)(c.I > c.d ? c.I : c.d);              // P: a^T (I), then x^T (d)
+    p->tq_feat = (size_t)(c.d > 2 * c.I ? c.d : 2 * c.I);      // Q: dO^T (d), then dh^T (2I)
+    p->off_doq = mxt ? take((size_t)R * c.d) : 0;
+    p->off_dos = mxt ? take((size_t)R * c.d / 32) : 0;
+    p->off_dhq = mxt ? take((size_t)R * 2 * c.I) : 0;
+    p->off_dhs = mxt ? take((size_t)R * 2 * c.I / 32) : 0;
+    p->off_tp = mxt ? take(p->tp_feat * p->ntok) : 0;
+    p->off_tps = mxt ? take(p->tp_feat * p->ntok / 32) : 0;
+    p->off_tq = mxt ? take(p->tq_feat * p->ntok) : 0;
+    p->off_tqs = mxt ? take(p->tq_feat * p->ntok / 32) : 0;
+    if (mxt && c.recompute_h) {
+        // the recomputed h is read last by the activation backward; the token-layout
+        // operands are first written after the input gradients, so h takes their place
+        if (h_bytes <= p->off_tqs + p->tq_feat * p->ntok / 32 - p->off_tp) {
+            p->off_h = p->off_tp;
+            p->h_aliased = true;
+        } else {
+            p->off_h = take(h_bytes);
+        }
+    }
     const bool gemms = !mx && !p->decode;
     p->off_split = take(sizeof(int32_t) * 4 * (kMaxPieces / 2 + 1));
     p->off_part = gemms && c.training ? take(kGemmPartBytes) : 0;
@@ -223,20 +364,38 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
     saved_region("gather", sizeof(int32_t) * (size_t)R, "token of each routed row [R]");
     saved_region("slots", sizeof(int32_t) * (size_t)R, "routed row of each (t, j) [T, k]");
     saved_region("probs", sizeof(float) * (size_t)R, "score of each routed row [R]");
-    if (!mx) saved_region("a", 2 * (size_t)R * c.I, "SwiGLU output [R, I] BF16");
+    if (!mx || c.training)
+        saved_region("a", 2 * (size_t)R * c.I, mx ? "SwiGLU output [R, I] BF16 (weight-gradient operand)"
+                                                  : "SwiGLU output [R, I] BF16");
     saved_region("o", 2 * (size_t)R * c.d, "expert outputs [R, d] BF16");
     if (c.training) {
         const size_t hb = 2 * (size_t)R * 2 * c.I;
         if (c.recompute_h)
-            region("h", p->h_aliased ? 0 : hb, "backward", "W13 pre-activations (g, u) [R, 2I] BF16, recomputed");
+            region("h", p->h_aliased ? 0 : hb, "backward",
+                   "W13 pre-activations (g, u) [R, 2I] BF16, recomputed");
         else
             saved_region("h", hb, "W13 pre-activations (g, u) [R, 2I] BF16");
         region("dh", 2 * (size_t)R * 2 * c.I, "backward", "gradient w.r.t. (g, u) [R, 2I] BF16");
-        region("dxp", 2 * (size_t)R * c.d, "backward",
-               p->h_aliased ? "per-row input gradients [R, d] BF16 (first h, recomputed, with xg and dys)"
-                            : "per-row input gradients [R, d] BF16");
-        region("xg", 2 * (size_t)R * c.d, "backward", "x[gather] [R, d] BF16 (weight-gradient operand)");
-        region("dys", 2 * (size_t)R * c.d, "backward", "probs * dy[gather] [R, d] BF16 (weight-gradient operand)");
+        if (mx) {
+            region("dxp", 2 * (size_t)R * (c.I > c.d ? c.I : c.d), "backward",
+                   "dA [R, I] BF16, then the per-row input gradients [R, d] BF16");
+            region("dOq", (size_t)R * c.d + (size_t)R * c.d / 32, "backward",
+                   "probs * dy[gather] quantized along d: codes [R, d], scales [d/128, R, 4]");
+            region("dhq", (size_t)R * 2 * c.I + (size_t)R * 2 * c.I / 32, "backward",
+                   "(dg, du) quantized along 2I: codes [R, 2I], scales [2I/128, R, 4]");
+            region("tokP", (p->tp_feat * p->ntok) * 33 / 32, "backward",
+                   p->h_aliased ? "a^T, then x[gather]^T, quantized along routed rows (first h, recomputed)"
+                                : "a^T, then x[gather]^T, quantized along routed rows (token layout)");
+            region("tokQ", (p->tq_feat * p->ntok) * 33 / 32, "backward",
+                   "dO^T, then (dg, du)^T, quantized along routed rows (token layout)");
+        } else {
+            region("dxp", 2 * (size_t)R * c.d, "backward",
+                   p->h_aliased ? "per-row input gradients [R, d] BF16 (first h, recomputed, with xg and dys)"
+                                : "per-row input gradients [R, d] BF16");
+            region("xg", 2 * (size_t)R * c.d, "backward", "x[gather] [R, d] BF16 (weight-gradient operand)");
+            region("dys", 2 * (size_t)R * c.d, "backward",
+                   "probs * dy[gather] [R, d] BF16 (weight-gradient operand)");
+        }
     }
     if (mx) {
         region("xq", (size_t)c.T * c.d, "scratch", "E4M3 codes of x [T, d]");
@@ -323,6 +482,22 @@ moe_status_t moe_prepare_weights(moe_plan_t p, const void* w13, const void* w2, 
     return MOE_OK;
 }
 
+moe_status_t moe_prepare_weights_backward(moe_plan_t p, const void* w13, const void* w2, uint8_t* w13t_q,
+                                          uint8_t* w13t_s, uint8_t* w2t_q, uint8_t* w2t_s, void* stream) {
+    if (!p || !w13 || !w2 || !w13t_q || !w13t_s || !w2t_q || !w2t_s) return MOE_ERR_INVALID_ARG;
+    const moe_config_t& c = p->cfg;
+    if (c.d % 128 != 0 || c.I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // W13_e [2I, d] -> codes [d, 2I] blocked along 2I; W2_e [d, I] -> codes [I, d] blocked along d
+    if (launch_mx_transpose_quant(static_cast<const uint16_t*>(w13), c.E, 2 * c.I, c.d, nullptr, nullptr, nullptr,
+                                  0, true, w13t_q, w13t_s, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (launch_mx_transpose_quant(static_cast<const uint16_t*>(w2), c.E, c.d, c.I, nullptr, nullptr, nullptr, 0,
+                                  true, w2t_q, w2t_s, s) != hipSuccess)
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const float* scores,
                          const moe_weights_t* w, void* y, void* stream) {
     if (!p || !w) return MOE_ERR_INVALID_ARG;
@@ -402,6 +577,11 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
         mg.w2q = static_cast<const uint8_t*>(w->w2); mg.w2s = w->w2_scale;
         mg.aq = p->at<uint8_t>(p->off_aq); mg.as = p->at<uint8_t>(p->off_as);
         mg.o = p->at<uint16_t>(p->off_o);
+        if (c.training && !c.recompute_h) {
+            // kept for the backward: h for the activation backward, a for dW2
+            mg.h_out = p->at<uint16_t>(p->off_h);
+            mg.a_out = p->at<uint16_t>(p->off_a);
+        }
         e = staged(p, MOE_STAGE_W13, s, [&] { return launch_gemm_mxfp8(MX_W13, mg, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
         e = staged(p, MOE_STAGE_W2, s, [&] { return launch_gemm_mxfp8(MX_W2, mg, p->num_cu, s); });
@@ -410,7 +590,9 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
             return launch_combine(p->at<uint16_t>(p->off_o), slots, scores, c.T, c.k, c.d,
                                   static_cast<uint16_t*>(y), s);
         });
-        return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+        if (e != hipSuccess) return MOE_ERR_HIP;
+        p->have_saved_forward = c.training != 0;
+        return MOE_OK;
     }
     GemmArgs g{};
     g.T = c.T; g.d = c.d; g.I = c.I; g.E = c.E; g.k = c.k;
@@ -531,12 +713,17 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
                           void* dx, void* dw13, void* dw2, float* dscores, void* stream) {
     if (!p || !w) return MOE_ERR_INVALID_ARG;
     const moe_config_t& c = p->cfg;
-    if (!c.training || c.precision != MOE_BF16) return MOE_ERR_STATE;
-    if (!dw13 || !dw2 || !w->w13 || !w->w2) return MOE_ERR_INVALID_ARG;
+    if (!c.training) return MOE_ERR_STATE;
+    const bool mx = c.precision == MOE_MXFP8_E4M3;
+    if (!dw13 || !dw2) return MOE_ERR_INVALID_ARG;
+    if (!mx && (!w->w13 || !w->w2)) return MOE_ERR_INVALID_ARG;
+    if (mx && (!w->w13t || !w->w13t_scale || !w->w2t || !w->w2t_scale)) return MOE_ERR_INVALID_ARG;
+    if (mx && c.recompute_h && c.T > 0 && (!w->w13 || !w->w13_scale)) return MOE_ERR_INVALID_ARG;
     if (c.T > 0 && (!dy || !x || !dx || !dscores)) return MOE_ERR_INVALID_ARG;
     if (!p->ws) return MOE_ERR_WORKSPACE;
     if (!p->have_saved_forward) return MOE_ERR_STATE;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (mx) return mx_backward(p, dy, x, w, dx, dw13, dw2, dscores, s);
     hipError_t e;
     const int32_t* slots = p->at<int32_t>(p->off_slots);
     if (c.T > 0) {

@@ -101,6 +101,192 @@ __global__ void __launch_bounds__(kThreads) route_scales_kernel(const uint32_t* 
     }
 }
 
+// One MX block of 32 FP32 values: E8M0 scale byte and 32 E4M3 codes (8 words).
+__device__ __forceinline__ uint32_t quant_block32(const float* v, uint32_t out[8]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+    const uint32_t sb = e8m0_scale(amax);
+    const int sh = 127 - (int)sb;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        out[i] = e4m3_pack4(__builtin_ldexpf(v[4 * i], sh), __builtin_ldexpf(v[4 * i + 1], sh),
+                            __builtin_ldexpf(v[4 * i + 2], sh), __builtin_ldexpf(v[4 * i + 3], sh));
+    return sb;
+}
+
+__device__ __forceinline__ void store_codes32(uint8_t* dst, const uint32_t w[8]) {
+    uint4* d = reinterpret_cast<uint4*>(dst);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Byte of block kb of routed row r in the block-major layout [K/128][R][4].
+__device__ __forceinline__ int64_t bm_index(int64_t R, int64_t r, int kb) {
+    return ((int64_t)(kb >> 2) * R + r) * 4 + (kb & 3);
+}
+
+// dO of the MXFP8 backward: rows probs[r] * dy[gather[r]] (FP32) quantized along d; one
+// thread per (row, block of 32)
+__global__ __launch_bounds__(kThreads) void mx_scaled_rows_kernel(const uint16_t* __restrict__ dy, int T,
+                                                                  const int32_t* __restrict__ gather,
+                                                                  const float* __restrict__ probs, int64_t R, int d,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales) {
+    const int kb_row = d / 32;
+    const int64_t nb = R * kb_row;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nb; b += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = b / kb_row;
+        const int kb = (int)(b - r * kb_row);
+        uint32_t tok = (uint32_t)gather[r];
+        if (tok >= (uint32_t)T) tok = 0;
+        const float pr = probs[r];
+        const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)tok * d + 32 * kb);
+        float v[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 q = src[c];
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                v[8 * c + 2 * z] = pr * bf16lo(w[z]);
+                v[8 * c + 2 * z + 1] = pr * bf16hi(w[z]);
+            }
+        }
+        uint32_t out[8];
+        const uint32_t sb = quant_block32(v, out);
+        store_codes32(codes + r * d + 32 * kb, out);
+        scales[bm_index(R, r, kb)] = (uint8_t)sb;
+    }
+}
+
+// The gated activation's backward of the MXFP8 backward: one thread per (row, block of 32
+// intermediate columns): dg = dA u f'(g) and du = dA f(g) from BF16 dA and h; dh in BF16
+// and both blocks quantized along 2I
+template <int kAct>
+__global__ __launch_bounds__(kThreads) void mx_act_backward_kernel(const uint16_t* __restrict__ dA,
+                                                                   const uint16_t* __restrict__ h, int64_t R, int I,
+                                                                   uint16_t* __restrict__ dh,
+                                                                   uint8_t* __restrict__ codes,
+                                                                   uint8_t* __restrict__ scales) {
+    const int kb_row = I / 32;
+    const int64_t nb = R * kb_row;
+    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nb; b += (int64_t)gridDim.x * kThreads) {
+        const int64_t r = b / kb_row;
+        const int kb = (int)(b - r * kb_row);
+        const int i0 = 32 * kb;
+        float dg[32], du[32];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint4 a4 = reinterpret_cast<const uint4*>(dA + r * I + i0)[c];
+            const uint4 g4 = reinterpret_cast<const uint4*>(h + r * 2 * I + i0)[c];
+            const uint4 u4 = reinterpret_cast<const uint4*>(h + r * 2 * I + I + i0)[c];
+            const uint32_t aw[4] = {a4.x, a4.y, a4.z, a4.w};
+            const uint32_t gw[4] = {g4.x, g4.y, g4.z, g4.w};
+            const uint32_t uw[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    const float a = hh ? bf16hi(aw[z]) : bf16lo(aw[z]);
+                    const float gv = hh ? bf16hi(gw[z]) : bf16lo(gw[z]);
+                    const float uv = hh ? bf16hi(uw[z]) : bf16lo(uw[z]);
+                    float f, df;
+                    act_f_df<kAct>(gv, f, df);
+                    dg[8 * c + 2 * z + hh] = a * uv * df;
+                    du[8 * c + 2 * z + hh] = a * f;
+                }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint4 og, ou;
+            og.x = pack_bf16(dg[8 * c], dg[8 * c + 1]); og.y = pack_bf16(dg[8 * c + 2], dg[8 * c + 3]);
+            og.z = pack_bf16(dg[8 * c + 4], dg[8 * c + 5]); og.w = pack_bf16(dg[8 * c + 6], dg[8 * c + 7]);
+            ou.x = pack_bf16(du[8 * c], du[8 * c + 1]); ou.y = pack_bf16(du[8 * c + 2], du[8 * c + 3]);
+            ou.z = pack_bf16(du[8 * c + 4], du[8 * c + 5]); ou.w = pack_bf16(du[8 * c + 6], du[8 * c + 7]);
+            reinterpret_cast<uint4*>(dh + r * 2 * I + i0)[c] = og;
+            reinterpret_cast<uint4*>(dh + r * 2 * I + I + i0)[c] = ou;
+        }
+        uint32_t out[8];
+        uint32_t sb = quant_block32(dg, out);
+        store_codes32(codes + r * 2 * I + i0, out);
+        scales[bm_index(R, r, kb)] = (uint8_t)sb;
+        sb = quant_block32(du, out);
+        store_codes32(codes + r * 2 * I + I + i0, out);
+        scales[bm_index(R, r, kb_row + kb)] = (uint8_t)sb;
+    }
+}
+
+// Transposing quantization (see launch_mx_transpose_quant): one thread per (column n,
+// block of 32 rows k0 .. k0 + 31) of segment blockIdx.z; the 32 values of a column come
+// from 32 rows (consecutive threads read consecutive columns), and the thread writes the
+// 32 codes of the column's block contiguously plus its scale byte.
+__global__ __launch_bounds__(kThreads) void mx_transpose_quant_kernel(const uint16_t* __restrict__ src, int segs,
+                                                                      int K, int N,
+                                                                      const int32_t* __restrict__ m_indptr,
+                                                                      const int32_t* __restrict__ gather,
+                                                                      const float* __restrict__ probs, int T,
+                                                                      bool weights, uint8_t* __restrict__ codes,
+                                                                      uint8_t* __restrict__ scales) {
+    __shared__ int koff_s[257];
+    const int e = blockIdx.z;
+    int rows, kp, r0;
+    int64_t koff;
+    if (weights) {
+        rows = K; kp = K; r0 = 0; koff = (int64_t)e * K;
+    } else {
+        // padded rows of every segment and their prefix (segments <= 256)
+        if (threadIdx.x == 0) {
+            int acc = 0;
+            for (int s2 = 0; s2 < segs; ++s2) {
+                koff_s[s2] = acc;
+                const int rs = m_indptr[s2 + 1] - m_indptr[s2];
+                acc += ((rs > 0 ? rs : 1) + kMxWgradPad - 1) / kMxWgradPad * kMxWgradPad;
+            }
+            koff_s[segs] = acc;
+        }
+        __syncthreads();
+        r0 = m_indptr[e];
+        rows = m_indptr[e + 1] - r0;
+        koff = koff_s[e];
+        kp = koff_s[e + 1] - koff_s[e];
+    }
+    const int n = blockIdx.y * kThreads + threadIdx.x;
+    if (n >= N) return;
+    const uint16_t* col = weights ? src + (int64_t)e * K * N + n : src + n;
+    for (int kb = blockIdx.x; kb < kp / 32; kb += gridDim.x) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int k = 32 * kb + j;
+            float val = 0.0f;
+            if (weights) {
+                val = bf16_to_f32(col[(int64_t)k * N]);
+            } else if (k < rows) {
+                // routed row r0 + k: a row of src itself, or (gather) the token row it
+                // came from, times (probs) its score
+                int64_t row = r0 + k;
+                if (gather) {
+                    uint32_t t = (uint32_t)gather[row];
+                    row = t < (uint32_t)T ? t : 0;
+                }
+                val = bf16_to_f32(col[row * N]);
+                if (probs) val *= probs[r0 + k];
+            }
+            v[j] = val;
+        }
+        uint32_t out[8];
+        const uint32_t sb = quant_block32(v, out);
+        if (weights) {
+            store_codes32(codes + ((int64_t)e * N + n) * K + 32 * kb, out);
+            scales[((int64_t)(kb >> 2) * segs * N + (int64_t)e * N + n) * 4 + (kb & 3)] = (uint8_t)sb;
+        } else {
+            store_codes32(codes + koff * N + (int64_t)n * kp + 32 * kb, out);
+            scales[koff * N / 32 + ((int64_t)(kb >> 2) * N + n) * 4 + (kb & 3)] = (uint8_t)sb;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_route_scales(const uint8_t* scales, int64_t rows, const int32_t* gather, int64_t R,
@@ -127,6 +313,45 @@ hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t
     if (grid > 65536) grid = 65536;
     hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, v, nblocks, K / 32,
                        rows, rows_dev, block_major, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, const int32_t* gather, const float* probs,
+                                 int64_t R, int d, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    if (d % 128 != 0) return hipErrorInvalidValue;
+    const int64_t nb = R * (d / 32);
+    if (nb == 0) return hipSuccess;
+    int64_t grid = (nb + kThreads - 1) / kThreads;
+    if (grid > 65536) grid = 65536;
+    hipLaunchKernelGGL(mx_scaled_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, dy, T, gather, probs, R, d,
+                       codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_act_backward(const uint16_t* dA, const uint16_t* h, int64_t R, int I, int act,
+                                  uint16_t* dh, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    if (I % 64 != 0) return hipErrorInvalidValue;
+    const int64_t nb = R * (I / 32);
+    if (nb == 0) return hipSuccess;
+    int64_t grid = (nb + kThreads - 1) / kThreads;
+    if (grid > 65536) grid = 65536;
+    const dim3 gd((unsigned)grid), bd(kThreads);
+    if (act == kActGeGLU) hipLaunchKernelGGL(mx_act_backward_kernel<kActGeGLU>, gd, bd, 0, s, dA, h, R, I, dh, codes, scales);
+    else if (act == kActReGLU) hipLaunchKernelGGL(mx_act_backward_kernel<kActReGLU>, gd, bd, 0, s, dA, h, R, I, dh, codes, scales);
+    else hipLaunchKernelGGL(mx_act_backward_kernel<kActSwiGLU>, gd, bd, 0, s, dA, h, R, I, dh, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N, const int32_t* m_indptr,
+                                     const int32_t* gather, const float* probs, int T, bool weights,
+                                     uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    if (segs <= 0 || segs > 256 || N <= 0) return hipErrorInvalidValue;
+    if (weights && (K <= 0 || K % 128 != 0)) return hipErrorInvalidValue;
+    if (!weights && (!m_indptr || (gather && T <= 0))) return hipErrorInvalidValue;
+    const dim3 gd(weights ? (unsigned)(K / 32 < 64 ? K / 32 : 64) : 64u, (unsigned)((N + kThreads - 1) / kThreads),
+                  (unsigned)segs);
+    hipLaunchKernelGGL(mx_transpose_quant_kernel, gd, dim3(kThreads), 0, s, src, segs, K, N, m_indptr, gather, probs,
+                       T, weights, codes, scales);
     return hipGetLastError();
 }
 

@@ -40,14 +40,15 @@ MOE_ACT_SWIGLU, MOE_ACT_GEGLU, MOE_ACT_REGLU = 0, 1, 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_plan", "moe_workspace_bytes", "moe_bind_workspace", "moe_plan_destroy",
-           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_forward", "moe_forward_static",
+           "moe_dispatch", "moe_quantize_mxfp8", "moe_prepare_weights", "moe_prepare_weights_backward",
+           "moe_forward", "moe_forward_static",
            "moe_forward_routed",
            "moe_backward", "moe_get_status", "moe_status_string", "moe_profile", "moe_plan_explain",
            "moe_profile_read")
 
 STAGES = ("dispatch", "quant_x", "w13", "w2", "combine", "score_grad", "dgrad_w2", "wgrad_w2",
           "dgrad_w13", "wgrad_w13", "dx_combine", "decode_w13", "decode_w2", "wgrad_rows", "recompute_h",
-          "mega")
+          "mega", "quant_do", "act_bwd", "quant_t")
 
 
 class MoeError(RuntimeError):
@@ -66,7 +67,9 @@ class MoeConfig(ctypes.Structure):
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("w13", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p)]
+                ("w13_scale", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p),
+                ("w13t", ctypes.c_void_p), ("w13t_scale", ctypes.c_void_p),
+                ("w2t", ctypes.c_void_p), ("w2t_scale", ctypes.c_void_p)]
 
 
 _lib = None
@@ -96,6 +99,8 @@ def lib():
         L.moe_quantize_mxfp8.argtypes = [vp, i64, i32, vp, vp, vp]
         L.moe_quantize_mxfp8.restype = ctypes.c_int
         L.moe_prepare_weights.argtypes = [vp] * 8
+        L.moe_prepare_weights_backward.argtypes = [vp] * 8
+        L.moe_prepare_weights_backward.restype = ctypes.c_int
         L.moe_prepare_weights.restype = ctypes.c_int
         L.moe_forward.argtypes = [vp, vp, vp, vp, ctypes.POINTER(MoeWeights), vp, vp]
         L.moe_forward.restype = ctypes.c_int
@@ -169,8 +174,14 @@ def moe_prepare_weights(plan, w13, w2, w13_q, w13_s, w2_q, w2_s, stream=0):
         "moe_prepare_weights")
 
 
-def weights(w13, w2, w13_scale=0, w2_scale=0) -> MoeWeights:
-    return MoeWeights(w13, w2, w13_scale or None, w2_scale or None)
+def moe_prepare_weights_backward(plan, w13, w2, w13t_q, w13t_s, w2t_q, w2t_s, stream=0):
+    _ok(lib().moe_prepare_weights_backward(plan, w13, w2, w13t_q, w13t_s, w2t_q, w2t_s, stream),
+        "moe_prepare_weights_backward")
+
+
+def weights(w13, w2, w13_scale=0, w2_scale=0, w13t=0, w13t_scale=0, w2t=0, w2t_scale=0) -> MoeWeights:
+    return MoeWeights(w13, w2, w13_scale or None, w2_scale or None, w13t or None, w13t_scale or None,
+                      w2t or None, w2t_scale or None)
 
 
 def moe_forward(plan, x, ids, scores, w: MoeWeights, y, stream=0):
@@ -288,7 +299,11 @@ class Layer:
         moe_forward_routed(self.plan, _ptr(x_rows), _ptr(m_indptr), w, _ptr(out), _stream(stream))
         return out
 
-    def backward(self, dy, x, w13, w2, dx=None, dw13=None, dw2=None, dscores=None, stream=None):
+    def backward(self, dy, x, w13, w2, dx=None, dw13=None, dw2=None, dscores=None, stream=None,
+                 w13_scale=None, w13t=None, w13t_scale=None, w2t=None, w2t_scale=None):
+        """BF16 plans take the BF16 weights; MXFP8 plans the tensors of
+        prepare_weights_backward (w13t, w13t_scale, w2t, w2t_scale) and, with
+        recompute_h, the forward's prepared w13 and w13_scale (w2 unused)."""
         import torch
         dev = dy.device
         if dx is None:
@@ -299,8 +314,10 @@ class Layer:
             dw2 = torch.empty((self.E, self.d, self.I), dtype=torch.bfloat16, device=dev)
         if dscores is None:
             dscores = torch.empty((self.T, self.k), dtype=torch.float32, device=dev)
-        moe_backward(self.plan, _ptr(dy), _ptr(x), weights(_ptr(w13), _ptr(w2)), _ptr(dx),
-                     _ptr(dw13), _ptr(dw2), _ptr(dscores), _stream(stream))
+        w = weights(_ptr(w13), _ptr(w2), _ptr(w13_scale), 0, _ptr(w13t), _ptr(w13t_scale), _ptr(w2t),
+                    _ptr(w2t_scale))
+        moe_backward(self.plan, _ptr(dy), _ptr(x), w, _ptr(dx), _ptr(dw13), _ptr(dw2), _ptr(dscores),
+                     _stream(stream))
         return dx, dw13, dw2, dscores
 
     def prepare_weights(self, w13, w2, stream=None):
@@ -315,6 +332,20 @@ class Layer:
         moe_prepare_weights(self.plan, _ptr(w13), _ptr(w2), _ptr(w13_q), _ptr(w13_s), _ptr(w2_q),
                             _ptr(w2_s), _stream(stream))
         return w13_q, w13_s, w2_q, w2_s
+
+    def prepare_weights_backward(self, w13, w2, stream=None):
+        """(w13t, w13t_scale, w2t, w2t_scale) for the MXFP8 backward: W13_e^T [d, 2I] and
+        W2_e^T [I, d] quantized along their last dimension, scales block-major."""
+        import torch
+        dev = w13.device
+        E, I, d = self.E, self.I, self.d
+        w13t = torch.empty((E, d, 2 * I), dtype=torch.uint8, device=dev)
+        w13t_s = torch.empty((2 * I // 128, E * d, 4), dtype=torch.uint8, device=dev)
+        w2t = torch.empty((E, I, d), dtype=torch.uint8, device=dev)
+        w2t_s = torch.empty((d // 128, E * I, 4), dtype=torch.uint8, device=dev)
+        moe_prepare_weights_backward(self.plan, _ptr(w13), _ptr(w2), _ptr(w13t), _ptr(w13t_s), _ptr(w2t),
+                                     _ptr(w2t_s), _stream(stream))
+        return w13t, w13t_s, w2t, w2t_s
 
     def status(self, clear=True, stream=None):
         return moe_get_status(self.plan, clear, _stream(stream))

@@ -39,6 +39,12 @@ hipError_t launch_quantize_mxfp8(const uint16_t*, int64_t, int, uint8_t*, uint8_
 hipError_t launch_route_scales(const uint8_t*, int64_t, const int32_t*, int64_t, int, uint8_t*, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t launch_mx_scaled_rows(const uint16_t*, int, const int32_t*, const float*, int64_t, int, uint8_t*,
+                                 uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mx_act_backward(const uint16_t*, const uint16_t*, int64_t, int, int, uint16_t*, uint8_t*,
+                                  uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mx_transpose_quant(const uint16_t*, int, int, int, const int32_t*, const int32_t*, const float*,
+                                     int, bool, uint8_t*, uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t static_scratch(void**, int*) { return hipErrorInvalidValue; }
 hipError_t launch_fill_i32(int32_t*, int, int32_t, hipStream_t) { return hipErrorInvalidValue; }
 }  // namespace moe
@@ -63,6 +69,10 @@ int main() {
     ok.push_back(cfg(1, 2048, 768, 128, 8));
     ok.push_back(cfg(32, 2048, 768, 128, 8));
     moe_config_t m = cfg(16384, 4096, 2048, 64, 8); m.precision = MOE_MXFP8_E4M3; ok.push_back(m);
+    m.training = 1; ok.push_back(m);                   // MXFP8 training, h saved
+    m.recompute_h = 1; ok.push_back(m);                // h recomputed into the token-layout region
+    moe_config_t m2 = cfg(300, 256, 1024, 8, 2); m2.precision = MOE_MXFP8_E4M3; m2.training = 1;
+    m2.recompute_h = 1; m2.wgrad_accumulate = 1; ok.push_back(m2);   // h larger than that region
     ok.push_back(cfg(0, 256, 128, 8, 2));
     ok.push_back(cfg(4096, 256, 64, 256, 32));
     moe_config_t rc = cfg(300, 128, 256, 8, 2); rc.training = 1; rc.recompute_h = 1; ok.push_back(rc);
@@ -108,8 +118,10 @@ int main() {
     bad.push_back({cfg(64, 256, 128, 8, 9), MOE_ERR_UNSUPPORTED});
     bad.push_back({cfg(64, 256, 128, 64, 33), MOE_ERR_UNSUPPORTED});
     bad.push_back({cfg(131073, 256, 128, 8, 1), MOE_ERR_UNSUPPORTED});
-    moe_config_t mt = cfg(64, 256, 128, 8, 2); mt.precision = MOE_MXFP8_E4M3; mt.training = 1;
-    bad.push_back({mt, MOE_ERR_UNSUPPORTED});
+    moe_config_t mt = cfg(64, 128, 128, 8, 2); mt.precision = MOE_MXFP8_E4M3; mt.training = 1;
+    bad.push_back({mt, MOE_ERR_UNSUPPORTED});           // MXFP8 needs d % 256 == 0
+    moe_config_t md = cfg(8, 256, 128, 8, 2); md.precision = MOE_MXFP8_E4M3; md.path = MOE_PATH_DECODE;
+    bad.push_back({md, MOE_ERR_UNSUPPORTED});
     moe_config_t ac = cfg(64, 256, 128, 8, 2); ac.wgrad_accumulate = 1; bad.push_back({ac, MOE_ERR_UNSUPPORTED});
     moe_config_t ra = cfg(64, 256, 128, 8, 2); ra.activation = 7; bad.push_back({ra, MOE_ERR_INVALID_ARG});
     moe_config_t pa = cfg(64, 256, 128, 8, 2); pa.path = 9; bad.push_back({pa, MOE_ERR_INVALID_ARG});
@@ -143,6 +155,27 @@ int main() {
         CHECK(moe_forward_static(p2, dummy, (const int32_t*)dummy, (const float*)dummy, &w, dummy, nullptr) ==
               MOE_ERR_TOO_LARGE);
         CHECK(moe_forward_static(nullptr, dummy, nullptr, nullptr, &w, dummy, nullptr) == MOE_ERR_INVALID_ARG);
+        moe_plan_destroy(p1);
+        moe_plan_destroy(p2);
+    }
+    // the MXFP8 backward and its weight preparation refuse missing operands on the host
+    {
+        moe_config_t tc = cfg(64, 256, 128, 8, 2); tc.precision = MOE_MXFP8_E4M3; tc.training = 1;
+        moe_config_t odd = cfg(64, 192, 128, 8, 2);
+        moe_plan_t p1 = nullptr, p2 = nullptr;
+        CHECK(moe_plan(&tc, &p1) == MOE_OK && moe_plan(&odd, &p2) == MOE_OK);
+        moe_weights_t w;
+        std::memset(&w, 0, sizeof w);
+        char dummy[64];
+        uint8_t* u = reinterpret_cast<uint8_t*>(dummy);
+        CHECK(moe_backward(p1, dummy, dummy, &w, dummy, dummy, dummy, (float*)dummy, nullptr) == MOE_ERR_INVALID_ARG);
+        w.w13t = u; w.w13t_scale = u; w.w2t = u;
+        CHECK(moe_backward(p1, dummy, dummy, &w, dummy, dummy, dummy, (float*)dummy, nullptr) == MOE_ERR_INVALID_ARG);
+        w.w2t_scale = u;
+        CHECK(moe_backward(p1, dummy, dummy, &w, dummy, dummy, dummy, (float*)dummy, nullptr) == MOE_ERR_WORKSPACE);
+        CHECK(moe_prepare_weights_backward(p1, dummy, nullptr, u, u, u, u, nullptr) == MOE_ERR_INVALID_ARG);
+        CHECK(moe_prepare_weights_backward(p2, dummy, dummy, u, u, u, u, nullptr) == MOE_ERR_UNSUPPORTED);
+        CHECK(moe_prepare_weights_backward(p1, dummy, dummy, u, u, u, u, nullptr) == MOE_ERR_HIP);   // stub launcher
         moe_plan_destroy(p1);
         moe_plan_destroy(p2);
     }

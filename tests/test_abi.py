@@ -56,7 +56,9 @@ def test_status_strings(L):
     (dict(T=8, d=256, I=128, E=8, k=2, precision=7), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, training=2), moe.MOE_ERR_INVALID_ARG),
     (dict(T=8, d=256, I=128, E=8, k=2, path=9), moe.MOE_ERR_INVALID_ARG),
-    (dict(T=8, d=256, I=128, E=8, k=2, precision=1, training=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=8, d=256, I=128, E=8, k=2, precision=1, training=1), moe.MOE_OK),   # MXFP8 training
+    (dict(T=16384, d=4096, I=2048, E=64, k=8, precision=1, training=1, recompute_h=1), moe.MOE_OK),
+    (dict(T=8, d=256, I=128, E=8, k=2, precision=1, path=2), moe.MOE_ERR_UNSUPPORTED),  # no MXFP8 decode
     (dict(T=8, d=256, I=128, E=8, k=2, precision=1), moe.MOE_OK),            # MXFP8 forward
     (dict(T=16384, d=4096, I=2048, E=64, k=8, precision=1), moe.MOE_OK),     # the MXFP8 workload
     (dict(T=8, d=192, I=128, E=8, k=2, precision=1), moe.MOE_ERR_UNSUPPORTED),  # d % 256
@@ -184,6 +186,36 @@ def test_plan_explain_mxfp8_regions(L):
         assert sum(sizes.values()) <= moe.moe_workspace_bytes(plan)
     finally:
         moe.moe_plan_destroy(plan)
+
+
+def test_plan_explain_mxfp8_training(L):
+    """An MXFP8 training plan keeps a in BF16 for dW2 and holds the backward's quantized
+    operands: dO along d (codes + scales, R d 33/32 bytes), (dg, du) along 2I, and the
+    token-layout weight-gradient operands over T*k + 128 E rows (P: max(I, d) features,
+    Q: max(d, 2I)); recomputing h puts it in the token-layout region, R * 2I * 2 bytes less."""
+    T, d, I, E, k = 16384, 4096, 2048, 64, 8
+    keep = moe.moe_plan(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3, training=1)
+    rec = moe.moe_plan(T, d, I, E, k, precision=moe.MOE_MXFP8_E4M3, training=1, recompute_h=1)
+    try:
+        R, ntok = T * k, T * k + 128 * E
+
+        def sizes(plan):
+            out = {}
+            for line in moe.moe_plan_explain(plan).splitlines():
+                f = line.split()
+                if line.startswith("  ") and len(f) >= 3 and f[1].isdigit():
+                    out[f[0]] = int(f[1])
+            return out
+        sk, sr = sizes(keep), sizes(rec)
+        assert sk["a"] == 2 * R * I and sk["h"] == 2 * R * 2 * I
+        assert sk["dOq"] == R * d * 33 // 32 and sk["dhq"] == R * 2 * I * 33 // 32
+        assert sk["tokP"] == max(I, d) * ntok * 33 // 32 and sk["tokQ"] == max(d, 2 * I) * ntok * 33 // 32
+        assert "h" not in sr and "xg" not in sk and "dys" not in sk
+        assert moe.moe_workspace_bytes(keep) - moe.moe_workspace_bytes(rec) == 2 * R * 2 * I
+        assert "first h, recomputed" in moe.moe_plan_explain(rec)
+    finally:
+        moe.moe_plan_destroy(keep)
+        moe.moe_plan_destroy(rec)
 
 
 def test_plan_explain_and_recompute_workspace(L):
