@@ -6,7 +6,7 @@ A step is one call of the layer's hot path on one batch of seeded synthetic
 input already resident in HBM: for the forward workloads dispatch, W13 grouped
 GEMM with the SwiGLU epilogue, W2 grouped GEMM and the score-weighted combine;
 for "train" also the whole backward (router gradient, DGRAD, WGRAD, dX
-combine).  Timing uses HIP events on the stream the library launches on;
+combine); "train-mxfp8" is the same step on MXFP8 operands.  Timing uses HIP events on the stream the library launches on;
 per-kernel durations come from the library's own event pairs around each
 stage during the same timed region.  Prints one JSON line.
 """
@@ -29,13 +29,14 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense FP8 MFMA, published
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, published
 
 WORKLOADS = {
-    # name: (config in inputs.CONFIGS, training)
-    "prefill": ("prefill", False),
-    "tiny": ("tiny", False),
-    "train": ("train", True),
-    "decode1": ("decode1", False),
-    "decode32": ("decode32", False),
-    "mxfp8": ("mxfp8", False),
+    # name: (config in inputs.CONFIGS, training, MXFP8)
+    "prefill": ("prefill", False, False),
+    "tiny": ("tiny", False, False),
+    "train": ("train", True, False),
+    "train-mxfp8": ("train", True, True),
+    "decode1": ("decode1", False, False),
+    "decode32": ("decode32", False, False),
+    "mxfp8": ("mxfp8", False, True),
 }
 
 
@@ -88,8 +89,12 @@ KERNEL_OF_STAGE = {
     "wgrad_rows": ("wgrad_rows_kernel",), "recompute_h": ("grouped_gemm<0,",),
     "mega": ("mega_decode", "mega_combine"),
 }
-# the MXFP8 workload's GEMM stages run the block-scaled kernels
-KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0,",), w2=("grouped_gemm_mx<1,",))
+# the MXFP8 workloads' GEMM stages run the block-scaled kernels
+KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0,",), w2=("grouped_gemm_mx<1,",),
+                          recompute_h=("grouped_gemm_mx<0,",), dgrad_w2=("grouped_gemm_mx<2,",),
+                          dgrad_w13=("grouped_gemm_mx<2,",), wgrad_w2=("grouped_gemm_mx<3,",),
+                          wgrad_w13=("grouped_gemm_mx<3,",), quant_do=("mx_scaled_rows_kernel",),
+                          act_bwd=("mx_act_backward_kernel",), quant_t=("mx_transpose_quant_kernel",))
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -106,7 +111,7 @@ def source_hash():
 
 
 def kernel_of_stage(workload: str):
-    return KERNEL_OF_STAGE_MX if workload == "mxfp8" else KERNEL_OF_STAGE
+    return KERNEL_OF_STAGE_MX if WORKLOADS[workload][2] else KERNEL_OF_STAGE
 
 
 def _load_traffic():
@@ -201,28 +206,45 @@ def oracle_threads():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(inp, training: bool, target_s: float):
-    """The oracle as it stands, on a bounded token sample of the same batch."""
+def cpu_baseline(inp, training: bool, target_s: float, mx: bool = False):
+    """The oracle as it stands, on a bounded token sample of the same batch.  MXFP8: the
+    forward with x and a quantized (forward_tokens_mx, on the prepared weights'
+    dequantized values, prepared once outside the timing); training: the oracle's MXFP8
+    training step (train_mx) on the first n tokens, which also builds its weight images
+    in every call."""
     import numpy as np
     import oracle
     oracle.build(force=False)
     T, d, I, k = inp.T, inp.d, inp.I, inp.k
     flop_per_token = 6.0 * k * I * d * (3.0 if training else 1.0)
+    if mx and not training:
+        w13, w2 = (oracle.mx_dequantize(*oracle.mx_quantize(w)) for w in (inp.w13, inp.w2))
+    else:
+        w13, w2 = inp.w13, inp.w2
     n = min(T, 4)
     rng = np.random.default_rng(123)
     spent = 0.0
     while True:
         toks = np.sort(rng.choice(T, size=n, replace=False)).astype(np.int32)
         t0 = time.perf_counter()
-        oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, toks=toks)
-        if training:
-            oracle.backward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy, toks=toks)
+        if mx and training:
+            oracle.train_mx(inp.x[:n], inp.ids[:n], inp.scores[:n], w13, w2, inp.dy[:n])
+        elif mx:
+            oracle.forward_tokens_mx(inp.x, inp.ids, inp.scores, w13, w2, toks=toks)
+        else:
+            oracle.forward_tokens(inp.x, inp.ids, inp.scores, w13, w2, toks=toks)
+            if training:
+                oracle.backward_tokens(inp.x, inp.ids, inp.scores, w13, w2, inp.dy, toks=toks)
         dt = time.perf_counter() - t0
         spent += dt
         if dt >= target_s * 0.5 or n >= T or spent > 3 * target_s:
             break
         n = min(T, max(n + 1, int(n * min(8.0, target_s / max(dt, 1e-3)))))
     tflops = flop_per_token * n / dt / 1e12
+    what = ("the MXFP8 training step (train_mx) on the first %d of %d tokens, weight images included"
+            % (n, T) if mx and training else
+            "%d of %d tokens of the same batch, %s" % (n, T, "forward + backward" if training else
+                                                     ("MXFP8 forward" if mx else "forward")))
     return {
         "value": tflops,
         "unit": "TFLOP/s",
@@ -230,10 +252,8 @@ def cpu_baseline(inp, training: bool, target_s: float):
         "cpu_model": cpu_model(),
         "host_logical_cpus": os.cpu_count(),
         "kind": "oracle",
-        "sample": "%d of %d tokens of the same batch, %s in the fp64 C oracle (token-major, "
-                  "OpenMP over tokens), %.1f s; flop counted as %d*k*I*d per token"
-                  % (n, T, "forward + backward" if training else "forward", dt,
-                     18 if training else 6),
+        "sample": "%s in the fp64 C oracle (OpenMP over tokens / rows / experts), %.1f s; flop "
+                  "counted as %d*k*I*d per token" % (what, dt, 18 if training else 6),
         "tokens_per_s": n / dt,
     }
 
@@ -295,7 +315,8 @@ def main():
 
     out = measure(args, args.workload)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(out.pop("_inp"), WORKLOADS[args.workload][1], args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(out.pop("_inp"), WORKLOADS[args.workload][1], args.cpu_seconds,
+                                           mx=WORKLOADS[args.workload][2])
     else:
         out.pop("_inp")
         out["cpu_baseline"] = None
@@ -342,13 +363,12 @@ def measure(args, workload):
     import torch
     from mixture_experts_routed_dispatch_amd import inputs, moe
 
-    cfg_name, training = WORKLOADS[workload]
+    cfg_name, training, mx = WORKLOADS[workload]
     inp = inputs.generate_config(cfg_name, seed=0, with_dy=training)
     T, d, I, E, k = inp.T, inp.d, inp.I, inp.E, inp.k
     R = T * k
     t = device_inputs(inp)
     decode = cfg_name.startswith("decode")
-    mx = cfg_name == "mxfp8"
     if (args.wgrad_accumulate or args.recompute_h) and not training:
         raise SystemExit("--wgrad-accumulate, --recompute-h: the train workload only")
     if args.mega and not decode:
@@ -373,9 +393,22 @@ def measure(args, workload):
     ids_list = [t["ids"]]
     w_list = [(t["w13"], t["w2"])]
     w_scales = [(None, None)]
+    bwd_w = None
+    prep_us = None
     if mx:
-        # weights prepared to MXFP8 once, outside the timed region
+        # weights prepared to MXFP8 once, outside the timed region (timed on their own)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
+        if training:
+            bwd_w = layer.prepare_weights_backward(t["w13"], t["w2"])
+        torch.cuda.synchronize()
+        e0.record()
+        layer.prepare_weights(t["w13"], t["w2"])
+        if training:
+            layer.prepare_weights_backward(t["w13"], t["w2"])
+        e1.record()
+        torch.cuda.synchronize()
+        prep_us = 1e3 * e0.elapsed_time(e1)
         w_list, w_scales = [(w13q, w2q)], [(w13s, w2s)]
         del t["w13"], t["w2"]
     if cfg_name == "decode1":
@@ -390,8 +423,9 @@ def measure(args, workload):
     n_active_mean = float(np.mean(n_active))
     if len(w_scales) < len(w_list):
         w_scales = w_scales + [(None, None)] * (len(w_list) - len(w_scales))
+    bw = [v.data_ptr() for v in bwd_w] if bwd_w is not None else [0, 0, 0, 0]
     wlist = [moe.weights(a.data_ptr(), b.data_ptr(), sa.data_ptr() if sa is not None else 0,
-                         sb.data_ptr() if sb is not None else 0)
+                         sb.data_ptr() if sb is not None else 0, *bw)
              for (a, b), (sa, sb) in zip(w_list, w_scales)]
     state = {"i": 0}
 
@@ -481,7 +515,13 @@ def measure(args, workload):
                  "decode_w13": n_active_mean * 2 * I * d * 2.0 + 2.0 * T * d + 2.0 * R * I + 4.0 * R,
                  "decode_w2": n_active_mean * d * I * 2.0 + 2.0 * R * I + 2.0 * R * d + 2.0 * T * d
                  + 8.0 * R,
-                 "mega": n_active_mean * 3 * I * d * 2.0 + 2.0 * T * d + 2.0 * T * d + 8.0 * R}
+                 "mega": n_active_mean * 3 * I * d * 2.0 + 2.0 * T * d + 2.0 * T * d + 8.0 * R,
+                 "quant_do": 2.0 * R * d + R * d * 33.0 / 32 + 8.0 * R,
+                 "act_bwd": 2.0 * R * I + 4.0 * R * 2 * I + R * 2 * I * 33.0 / 32}
+    ntok = R + 128.0 * E
+    # each of the two token-layout stages: both operands read once, written padded with scales
+    min_bytes["quant_t"] = 0.5 * (2.0 * R * (I + d) + (I + d) * ntok * 33.0 / 32
+                                  + 2.0 * R * (d + 2 * I) + (d + 2 * I) * ntok * 33.0 / 32)
     mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     if dom in gemm_flop:
         achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
@@ -513,6 +553,7 @@ def measure(args, workload):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "mxfp8-e4m3" if mx else "bf16",
+        "weight_prepare_us": prep_us,
         "data": "synthetic: seeded numpy draws, x ~ N(0,1), W ~ N(0,1/fan_in) in BF16, "
                 + ("Zipf(1.2) top-k routing with 8 forced-empty experts, dY ~ N(0,1)"
                    if cfg_name == "train" else "uniform distinct top-k routing")

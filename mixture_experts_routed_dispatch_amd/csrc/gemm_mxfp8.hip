@@ -310,14 +310,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     // 32x32x64 fp8 MFMA takes, in lane half g = lane >> 5, bytes 16g..16g+15 of both MX
     // blocks of the stage: block 0 in registers 0-3, block 1 in registers 4-7 (chunks g
     // and 2 + g of the 64-byte row); the scale of (row, block h) sits in lane half h
+    // (recomputed after every epilogue from the lane id read afresh, so that they are not
+    // held across it: the epilogue of the training forward, which also stores h and a,
+    // runs short of registers)
     int fragP[4][2], fragQ[4][2];
+    auto frag_offsets = [&]() {
+        const int fl = fresh_lane();
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            fragP[b][h] = lofs(wp * 128 + b * 32 + (lane & 31), (lane >> 5) + 2 * h);
-            fragQ[b][h] = OPB + lofs(wq * 128 + b * 32 + (lane & 31), (lane >> 5) + 2 * h);
-        }
+            for (int h = 0; h < 2; ++h) {
+                fragP[b][h] = lofs(wp * 128 + b * 32 + (fl & 31), (fl >> 5) + 2 * h);
+                fragQ[b][h] = OPB + lofs(wq * 128 + b * 32 + (fl & 31), (fl >> 5) + 2 * h);
+            }
+    };
+    frag_offsets();
     auto read_frag = [&](const char* base, int off0, int off1) {
         const uint4 x = *reinterpret_cast<const uint4*>(base + off0);
         const uint4 y = *reinterpret_cast<const uint4*>(base + off1);
@@ -403,6 +410,21 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                                 const float v = act_f<kAct>(gv) * uv;
                                 av[8 * h + 4 * grp + z] = v;
                                 amax = __builtin_fmaxf(amax, __builtin_fabsf(v));
+                                if constexpr (kSave) {
+                                    // the training forward keeps h = (g, u) in BF16, staged
+                                    // through this wave's 8 KiB of the stage buffer just
+                                    // consumed: row q_in (256 bytes) holds its 64 gate values
+                                    // (16-byte chunks 0..7) and 64 up values (chunks 8..15)
+                                    if (z & 1) {
+                                        const float gp = acc[2 * m + h][b][4 * grp + z - 1];
+                                        const float up = acc[2 * m + h][b][4 * (grp + 2) + z - 1];
+                                        const int cg = 2 * (2 * m + h) + grp;
+                                        char* srow = lds + buf * BUFB + wave * 8192 + q_in * 256 + (p_sub << 1) +
+                                                     ((z >> 1) << 2);
+                                        *reinterpret_cast<uint32_t*>(srow + ((cg ^ (q_in & 15)) << 4)) = pack_bf16(gp, gv);
+                                        *reinterpret_cast<uint32_t*>(srow + (((8 + cg) ^ (q_in & 15)) << 4)) = pack_bf16(up, uv);
+                                    }
+                                }
                             }
                     amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
                     const uint32_t sb = e8m0_scale(amax);
@@ -419,21 +441,31 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
                                 const int i = i0 + 16 * h + 8 * grp + p_sub;
                                 *reinterpret_cast<uint32_t*>(g.aq + r * g.I + i) = w;
                                 if constexpr (kSave) {
-                                    // the training forward also keeps a and h = (g, u) in BF16
-                                    uint2 av2, hg, hu;
+                                    // and a before its re-quantization, in BF16
+                                    uint2 av2;
                                     av2.x = pack_bf16(q[0], q[1]); av2.y = pack_bf16(q[2], q[3]);
-                                    const f32x16_t& t = acc[2 * m + h][b];
-                                    hg.x = pack_bf16(t[4 * grp], t[4 * grp + 1]);
-                                    hg.y = pack_bf16(t[4 * grp + 2], t[4 * grp + 3]);
-                                    hu.x = pack_bf16(t[4 * (grp + 2)], t[4 * (grp + 2) + 1]);
-                                    hu.y = pack_bf16(t[4 * (grp + 2) + 2], t[4 * (grp + 2) + 3]);
                                     *reinterpret_cast<uint2*>(g.a_out + r * g.I + i) = av2;
-                                    *reinterpret_cast<uint2*>(g.h_out + r * 2 * g.I + i) = hg;
-                                    *reinterpret_cast<uint2*>(g.h_out + r * 2 * g.I + g.I + i) = hu;
                                 }
                             }
                         if (ln < 32) g.as[((size_t)(i0 >> 7) * R + r) * 4 + ((i0 >> 5) & 3)] = (uint8_t)sb;
                     }
+                }
+                if constexpr (kSave) {
+                    // the staged h rows go out as two 128-byte segments each (g, then u)
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
+                    const char* stg = lds + buf * BUFB + wave * 8192;
+                    const int ibase = c.pt * 128 + wp * 64;
+#pragma unroll
+                    for (int it = 0; it < 8; ++it) {
+                        const int row = 4 * it + (ln >> 4);
+                        const int c16 = ln & 15;
+                        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 256 + ((c16 ^ (row & 15)) << 4));
+                        const int rr2 = c.qt * TQ + wq * 128 + b * 32 + row;
+                        const int i = ibase + 8 * (c16 & 7);
+                        if (rr2 < c.rows && i < g.I)
+                            *reinterpret_cast<uint4*>(g.h_out + ((size_t)c.mb + rr2) * 2 * g.I + (c16 >> 3) * g.I + i) = v;
+                    }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);
                 }
             }
         } else {
@@ -574,6 +606,16 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
         if (c_tile >= total) break;
         __syncthreads();               // the staging slots are copied into again from the next stage
         cc = coords(c_tile);
+        frag_offsets();
+        // the next tile's first stage again, from its ring buffer and scale slot (neither
+        // is written before that stage runs), so that its fragments are not held in
+        // registers across the epilogue
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            pa[b] = read_frag(lds + (gs & 3) * BUFB, fragP[b][0], fragP[b][1]);
+            qa[b] = read_frag(lds + (gs & 3) * BUFB, fragQ[b][0], fragQ[b][1]);
+        }
+        read_scales((gs >> 1) % NSC, spa, sqa);
     }
 }
 

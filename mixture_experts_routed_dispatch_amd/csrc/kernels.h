@@ -119,7 +119,8 @@ hipError_t launch_mx_act_backward(const uint16_t* dA, const uint16_t* h, int64_t
 // at koff_e * N (rows past the segment as zeros) with scales [kp_e/128][N][4] at byte
 // koff_e * N / 32 (kp_e, koff_e as for MX_WGRAD); routed row r is src row r, or with
 // gather the token row gather[r] of src [T, N] (entries outside [0, T) read row 0), times
-// probs[r] when probs is given.  segs <= 256.
+// probs[r] when probs is given; K is then the number of routed rows (sizes the grid).
+// segs <= 256, N a multiple of 64.
 hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N, const int32_t* m_indptr,
                                      const int32_t* gather, const float* probs, int T, bool weights,
                                      uint8_t* codes, uint8_t* scales, hipStream_t s);

@@ -181,9 +181,9 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
     const int32_t* gth = c.T > 0 ? gather : nullptr;
     const float* prb = c.T > 0 ? probs : nullptr;
     e = staged(p, MOE_STAGE_QUANT_T, s, [&] {
-        hipError_t qe = launch_mx_transpose_quant(a, c.E, 0, c.I, m_indptr, nullptr, nullptr, 0, false, tp, tps, s);
+        hipError_t qe = launch_mx_transpose_quant(a, c.E, (int)R, c.I, m_indptr, nullptr, nullptr, 0, false, tp, tps, s);
         if (qe != hipSuccess) return qe;
-        return launch_mx_transpose_quant(dy16, c.E, 0, c.d, m_indptr, gth, prb, c.T, false, tq, tqs, s);
+        return launch_mx_transpose_quant(dy16, c.E, (int)R, c.d, m_indptr, gth, prb, c.T, false, tq, tqs, s);
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
     MxGemmArgs g3 = mg;                 // dW2_e [d, I] = sum_r dO_r a_r^T
@@ -193,9 +193,9 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
     e = staged(p, MOE_STAGE_WGRAD_W2, s, [&] { return launch_gemm_mxfp8(MX_WGRAD, g3, p->num_cu, s); });
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = staged(p, MOE_STAGE_QUANT_T, s, [&] {
-        hipError_t qe = launch_mx_transpose_quant(x16, c.E, 0, c.d, m_indptr, gth, nullptr, c.T, false, tp, tps, s);
+        hipError_t qe = launch_mx_transpose_quant(x16, c.E, (int)R, c.d, m_indptr, gth, nullptr, c.T, false, tp, tps, s);
         if (qe != hipSuccess) return qe;
-        return launch_mx_transpose_quant(dh, c.E, 0, 2 * c.I, m_indptr, nullptr, nullptr, 0, false, tq, tqs, s);
+        return launch_mx_transpose_quant(dh, c.E, (int)R, 2 * c.I, m_indptr, nullptr, nullptr, 0, false, tq, tqs, s);
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
     MxGemmArgs g4 = mg;                 // dW13_e [2I, d] = sum_r dh_r x_r^T

@@ -217,10 +217,18 @@ __global__ __launch_bounds__(kThreads) void mx_act_backward_kernel(const uint16_
     }
 }
 
-// Transposing quantization (see launch_mx_transpose_quant): one thread per (column n,
-// block of 32 rows k0 .. k0 + 31) of segment blockIdx.z; the 32 values of a column come
-// from 32 rows (consecutive threads read consecutive columns), and the thread writes the
-// 32 codes of the column's block contiguously plus its scale byte.
+// Transposing quantization (see launch_mx_transpose_quant), one workgroup per tile of
+// 128 source rows (one group of four MX blocks along the rows) x 64 columns:
+//   1. two threads per row copy the row's 64 columns (128 contiguous bytes) into LDS as
+//      FP32, [row][65] (scaled by probs, zero past the segment's rows);
+//   2. thread (column f = t / 4, block b = t % 4) quantizes rows 32 b .. 32 b + 31 of
+//      column f and writes their 32 codes, so that the four threads of a column write
+//      its 128 contiguous code bytes and its scale word together.
+// Token layout: the tiles of all segments are numbered in segment order (segment e has
+// kp_e / 128 of them), gridDim.x covers the largest possible total, and workgroups past
+// the actual one exit.  Weight layout: blockIdx.z is the matrix, blockIdx.x its tile.
+constexpr int kTqRows = 128, kTqCols = 64, kTqLd = kTqCols + 1;
+
 __global__ __launch_bounds__(kThreads) void mx_transpose_quant_kernel(const uint16_t* __restrict__ src, int segs,
                                                                       int K, int N,
                                                                       const int32_t* __restrict__ m_indptr,
@@ -228,61 +236,117 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_quant_kernel(const uint
                                                                       const float* __restrict__ probs, int T,
                                                                       bool weights, uint8_t* __restrict__ codes,
                                                                       uint8_t* __restrict__ scales) {
-    __shared__ int koff_s[257];
-    const int e = blockIdx.z;
-    int rows, kp, r0;
+    __shared__ float tile[kTqRows * kTqLd];
+    __shared__ int wsum[kThreads / 64];
+    __shared__ int info[4];            // segment, tile within it, first routed row, rows
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.y * kTqCols;
+    int e, kt, r0, rows, kp;
     int64_t koff;
     if (weights) {
-        rows = K; kp = K; r0 = 0; koff = (int64_t)e * K;
+        e = blockIdx.z;
+        kt = blockIdx.x;
+        r0 = 0;
+        rows = K;
+        kp = K;
+        koff = (int64_t)e * K;
     } else {
-        // padded rows of every segment and their prefix (segments <= 256)
-        if (threadIdx.x == 0) {
-            int acc = 0;
-            for (int s2 = 0; s2 < segs; ++s2) {
-                koff_s[s2] = acc;
-                const int rs = m_indptr[s2 + 1] - m_indptr[s2];
-                acc += ((rs > 0 ? rs : 1) + kMxWgradPad - 1) / kMxWgradPad * kMxWgradPad;
-            }
-            koff_s[segs] = acc;
+        // tiles per segment and their prefix, then the segment holding tile blockIdx.x
+        int nt = 0, rs = 0, mb = 0;
+        if (tid < segs) {
+            mb = m_indptr[tid];
+            rs = m_indptr[tid + 1] - mb;
+            nt = ((rs > 0 ? rs : 1) + kMxWgradPad - 1) / kMxWgradPad;
         }
+        int incl = nt;
+        const int lane = tid & 63, wave = tid >> 6;
+        for (int off = 1; off < 64; off <<= 1) {
+            const int v = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += v;
+        }
+        if (lane == 63) wsum[wave] = incl;
+        if (tid == 0) info[0] = -1;
         __syncthreads();
-        r0 = m_indptr[e];
-        rows = m_indptr[e + 1] - r0;
-        koff = koff_s[e];
-        kp = koff_s[e + 1] - koff_s[e];
+        int pre = 0;
+        for (int w = 0; w < wave; ++w) pre += wsum[w];
+        const int first = pre + incl - nt;
+        const int j = blockIdx.x;
+        if (tid < segs && j >= first && j < first + nt) {
+            info[0] = tid;
+            info[1] = j - first;
+            info[2] = mb;
+            info[3] = rs;
+        }
+        // koff of the segment = 128 * (tiles before it): kept by the owning thread
+        __syncthreads();
+        e = info[0];
+        if (e < 0) return;                         // past the last tile
+        kt = info[1];
+        r0 = info[2];
+        rows = info[3];
+        __syncthreads();
+        if (tid == e) info[0] = first;
+        __syncthreads();
+        koff = (int64_t)info[0] * kMxWgradPad;
+        kp = 0;                                     // not needed below (codes stride is kp)
+        {
+            const int rr = rows > 0 ? rows : 1;
+            kp = (rr + kMxWgradPad - 1) / kMxWgradPad * kMxWgradPad;
+        }
     }
-    const int n = blockIdx.y * kThreads + threadIdx.x;
-    if (n >= N) return;
-    const uint16_t* col = weights ? src + (int64_t)e * K * N + n : src + n;
-    for (int kb = blockIdx.x; kb < kp / 32; kb += gridDim.x) {
+    // 1. rows kt * 128 .. + 127 of the segment, columns n0 .. n0 + 63
+    {
+        const int row = tid >> 1, half = tid & 1;
+        const int k = kt * kTqRows + row;
+        float v[32];
+        if (k < rows) {
+            int64_t srow;
+            float sc = 1.0f;
+            if (weights) {
+                srow = (int64_t)e * K + k;
+            } else {
+                srow = r0 + k;
+                if (probs) sc = probs[srow];
+                if (gather) {
+                    const uint32_t t = (uint32_t)gather[srow];
+                    srow = t < (uint32_t)T ? t : 0;
+                }
+            }
+            const uint4* p = reinterpret_cast<const uint4*>(src + srow * N + n0 + 32 * half);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint4 q = p[c];
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                    v[8 * c + 2 * z] = sc * bf16lo(w[z]);
+                    v[8 * c + 2 * z + 1] = sc * bf16hi(w[z]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) tile[row * kTqLd + 32 * half + i] = v[i];
+    }
+    __syncthreads();
+    // 2. column f, rows 32 b .. 32 b + 31 of the tile
+    {
+        const int f = tid >> 2, b = tid & 3;
         float v[32];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const int k = 32 * kb + j;
-            float val = 0.0f;
-            if (weights) {
-                val = bf16_to_f32(col[(int64_t)k * N]);
-            } else if (k < rows) {
-                // routed row r0 + k: a row of src itself, or (gather) the token row it
-                // came from, times (probs) its score
-                int64_t row = r0 + k;
-                if (gather) {
-                    uint32_t t = (uint32_t)gather[row];
-                    row = t < (uint32_t)T ? t : 0;
-                }
-                val = bf16_to_f32(col[row * N]);
-                if (probs) val *= probs[r0 + k];
-            }
-            v[j] = val;
-        }
+        for (int j = 0; j < 32; ++j) v[j] = tile[(32 * b + j) * kTqLd + f];
         uint32_t out[8];
         const uint32_t sb = quant_block32(v, out);
+        const int n = n0 + f;
+        const int kb = kt * 4 + b;                  // MX block along the rows
         if (weights) {
             store_codes32(codes + ((int64_t)e * N + n) * K + 32 * kb, out);
-            scales[((int64_t)(kb >> 2) * segs * N + (int64_t)e * N + n) * 4 + (kb & 3)] = (uint8_t)sb;
+            scales[((int64_t)kt * segs * N + (int64_t)e * N + n) * 4 + b] = (uint8_t)sb;
         } else {
             store_codes32(codes + koff * N + (int64_t)n * kp + 32 * kb, out);
-            scales[koff * N / 32 + ((int64_t)(kb >> 2) * N + n) * 4 + (kb & 3)] = (uint8_t)sb;
+            scales[koff * N / 32 + ((int64_t)kt * N + n) * 4 + b] = (uint8_t)sb;
         }
     }
 }
@@ -345,11 +409,14 @@ hipError_t launch_mx_act_backward(const uint16_t* dA, const uint16_t* h, int64_t
 hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N, const int32_t* m_indptr,
                                      const int32_t* gather, const float* probs, int T, bool weights,
                                      uint8_t* codes, uint8_t* scales, hipStream_t s) {
-    if (segs <= 0 || segs > 256 || N <= 0) return hipErrorInvalidValue;
-    if (weights && (K <= 0 || K % 128 != 0)) return hipErrorInvalidValue;
-    if (!weights && (!m_indptr || (gather && T <= 0))) return hipErrorInvalidValue;
-    const dim3 gd(weights ? (unsigned)(K / 32 < 64 ? K / 32 : 64) : 64u, (unsigned)((N + kThreads - 1) / kThreads),
-                  (unsigned)segs);
+    if (segs <= 0 || segs > kThreads || N <= 0 || N % kTqCols != 0) return hipErrorInvalidValue;
+    if (weights && (K <= 0 || K % kTqRows != 0)) return hipErrorInvalidValue;
+    if (!weights && (!m_indptr || K < 0 || (gather && T <= 0))) return hipErrorInvalidValue;
+    // token layout: K is the number of routed rows; the tiles number at most
+    // K / 128 + segs (each segment rounds up to a multiple of 128, at least 128)
+    const int64_t tiles = weights ? K / kTqRows : (int64_t)K / kTqRows + segs;
+    if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const dim3 gd((unsigned)tiles, (unsigned)(N / kTqCols), weights ? (unsigned)segs : 1u);
     hipLaunchKernelGGL(mx_transpose_quant_kernel, gd, dim3(kThreads), 0, s, src, segs, K, N, m_indptr, gather, probs,
                        T, weights, codes, scales);
     return hipGetLastError();
