@@ -63,7 +63,7 @@ def _L():
         lib.orc_mx_quantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         lib.orc_mx_dequantize.argtypes = [ctypes.c_int64, i32, vp, vp, vp]
         lib.orc_forward_tokens_mx.argtypes = [i32] * 5 + [vp] * 5 + [i32, vp, vp, i32]
-        lib.orc_train_mx.argtypes = [i32] * 5 + [vp] * 6 + [i32] + [vp] * 5
+        lib.orc_train_mx.argtypes = [i32] * 5 + [vp] * 6 + [i32] + [i32] + [vp] * 4 + [i32] + [vp] * 3
         _lib = lib
     return _lib
 
@@ -236,19 +236,28 @@ def forward_tokens_mx(x, ids, scores, w13, w2, toks=None, act=ACT_SWIGLU):
     return y
 
 
-def train_mx(x, ids, scores, w13, w2, dy, act=ACT_SWIGLU):
+def train_mx(x, ids, scores, w13, w2, dy, act=ACT_SWIGLU, toks=None, icols=None):
     """One MXFP8 training step from BF16 master weights: every expert product takes MX images
     of both operands along its own reduction dimension, WGRAD operands blocked along each
-    expert's routed rows.  Returns (y, dx, ds, dw13, dw2) in float64."""
+    expert's routed rows.  Returns (y, dx, ds, dw13, dw2) in float64 for the tokens `toks`
+    (default all) and the intermediate indices `icols` (default all: dw13 [E, 2I, d],
+    dw2 [E, d, I]; else dw13 [E, 2, ni, d] gate and up rows of icols, dw2 [E, d, ni])."""
     xf, w13f, w2f, dyf = _f32(x), _f32(w13), _f32(w2), _f32(dy)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     scores = np.ascontiguousarray(scores, dtype=np.float32)
     T, d, I, E, k = _shapes(xf, w13f, w2f, ids)
-    y = np.zeros((T, d), np.float64)
-    dx = np.zeros((T, d), np.float64)
-    ds = np.zeros((T, k), np.float64)
-    dw13 = np.zeros((E, 2 * I, d), np.float64)
-    dw2 = np.zeros((E, d, I), np.float64)
+    full_cols = icols is None
+    toks = np.arange(T, dtype=np.int32) if toks is None else np.ascontiguousarray(toks, np.int32)
+    icols = np.arange(I, dtype=np.int32) if full_cols else np.ascontiguousarray(icols, np.int32)
+    n, ni = len(toks), len(icols)
+    y = np.zeros((n, d), np.float64)
+    dx = np.zeros((n, d), np.float64)
+    ds = np.zeros((n, k), np.float64)
+    dw13 = np.zeros((E, 2, ni, d), np.float64)
+    dw2 = np.zeros((E, d, ni), np.float64)
     _check(_L().orc_train_mx(T, d, I, E, k, _p(xf), _p(ids), _p(scores), _p(w13f), _p(w2f), _p(dyf),
-                             int(act), _p(y), _p(dx), _p(ds), _p(dw13), _p(dw2)))
+                             int(act), n, _p(toks), _p(y), _p(dx), _p(ds), ni, _p(icols), _p(dw13),
+                             _p(dw2)))
+    if full_cols:
+        dw13 = dw13.reshape(E, 2 * I, d)
     return y, dx, ds, dw13, dw2

@@ -504,8 +504,13 @@ int orc_forward_tokens_mx(int T, int d, int I, int E, int k,
  *     rounded to BF16 (nearest, ties to even) where they are stored, and every later
  *     quantization starts from the stored value.  dh is used unrounded by DGRAD and
  *     rounded to BF16 for WGRAD; dO and x enter unrounded.
- * Outputs (fp64): y [T, d], dx [T, d], ds [T, k] (ds[t][j] = <dY[t], o>),
- * dw13 [E, 2I, d], dw2 [E, d, I]; an expert with no row gets zero gradients. */
+ * Outputs (fp64), for the tokens toks[0 .. ntok) and the intermediate indices
+ * icols[0 .. ni) (pass every index for the whole step):
+ *   y, dx [ntok, d]; ds [ntok, k] (ds[t][j] = <dY[t], o>);
+ *   dw13 [E, 2, ni, d]: gate rows icols, then up rows I + icols;  dw2 [E, d, ni].
+ * An expert with no row gets zero gradients.  The weight gradients of a column need
+ * that column of a and dh on every routed row; those are computed column by column,
+ * apart from the token rows, which run whole. */
 
 /* nearest BF16 value of v (ties to even); v finite and inside the normal range */
 static double bf16_round(double v)
@@ -545,133 +550,187 @@ static void mx_matrix_image(double* m, int mats, int rows, int cols, int along_r
     }
 }
 
+/* the same for float matrices (the weights): each image value is an E4M3 code times
+ * a power of two, exact in float32 */
+static void mx_matrix_image_f(float* m, int mats, int rows, int cols, int along_rows)
+{
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < mats; ++e) {
+        float* me = m + (size_t)e * rows * cols;
+        double blk[32];
+        if (along_rows) {
+            for (int r = 0; r < rows; ++r)
+                for (int b = 0; b < cols; b += 32) {
+                    for (int i = 0; i < 32; ++i) blk[i] = (double)me[(size_t)r * cols + b + i];
+                    mx_block_image(blk, 32, 1);
+                    for (int i = 0; i < 32; ++i) me[(size_t)r * cols + b + i] = (float)blk[i];
+                }
+        } else {
+            for (int c = 0; c < cols; ++c)
+                for (int b = 0; b < rows; b += 32) {
+                    const int n = rows - b < 32 ? rows - b : 32;
+                    for (int i = 0; i < n; ++i) blk[i] = (double)me[(size_t)(b + i) * cols + c];
+                    mx_block_image(blk, n, 1);
+                    for (int i = 0; i < n; ++i) me[(size_t)(b + i) * cols + c] = (float)blk[i];
+                }
+        }
+    }
+}
+
 int orc_train_mx(int T, int d, int I, int E, int k,
                  const float* x, const int32_t* ids, const float* scores,
                  const float* w13, const float* w2, const float* dy, int act,
-                 double* y, double* dx, double* ds, double* dw13, double* dw2)
+                 int ntok, const int32_t* toks, double* y, double* dx, double* ds,
+                 int ni, const int32_t* icols, double* dw13, double* dw2)
 {
     int rc = orc_check_routing(T, E, k, ids);
     if (rc != ORC_OK) return rc;
     if (d % 32 || I % 32) return ORC_ERR_RANGE;
+    for (int q = 0; q < ntok; ++q) if (toks[q] < 0 || toks[q] >= T) return ORC_ERR_RANGE;
+    for (int q = 0; q < ni; ++q) if (icols[q] < 0 || icols[q] >= I) return ORC_ERR_RANGE;
     const size_t R = (size_t)T * k, n13 = (size_t)E * 2 * I * d, n2 = (size_t)E * d * I;
+    const size_t R1 = R ? R : 1;
     int32_t* m_indptr = (int32_t*)malloc(sizeof(int32_t) * ((size_t)E + 1));
-    int32_t* gather = (int32_t*)malloc(sizeof(int32_t) * (R ? R : 1));
-    int32_t* slots = (int32_t*)malloc(sizeof(int32_t) * (R ? R : 1));
-    float* probs = (float*)malloc(sizeof(float) * (R ? R : 1));
-    double* wf13 = (double*)malloc(sizeof(double) * n13);   /* FPROP images */
-    double* wf2 = (double*)malloc(sizeof(double) * n2);
-    double* wb13 = (double*)malloc(sizeof(double) * n13);   /* DGRAD images */
-    double* wb2 = (double*)malloc(sizeof(double) * n2);
-    double* hb = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * I);   /* stored h (BF16) */
-    double* ab = (double*)malloc(sizeof(double) * (R ? R : 1) * I);       /* stored a (BF16) */
-    double* o = (double*)malloc(sizeof(double) * (R ? R : 1) * d);
-    double* dhb = (double*)malloc(sizeof(double) * (R ? R : 1) * 2 * I);  /* dh in BF16 */
-    double* dxp = (double*)malloc(sizeof(double) * (R ? R : 1) * d);
-    int failed = !m_indptr || !gather || !slots || !probs || !wf13 || !wf2 || !wb13 || !wb2 || !hb ||
-                 !ab || !o || !dhb || !dxp;
+    int32_t* gather = (int32_t*)malloc(sizeof(int32_t) * R1);
+    int32_t* slots = (int32_t*)malloc(sizeof(int32_t) * R1);
+    float* probs = (float*)malloc(sizeof(float) * R1);
+    float* wf13 = (float*)malloc(sizeof(float) * n13);   /* FPROP images */
+    float* wf2 = (float*)malloc(sizeof(float) * n2);
+    float* wb13 = (float*)malloc(sizeof(float) * n13);   /* DGRAD images */
+    float* wb2 = (float*)malloc(sizeof(float) * n2);
+    double* ab = (double*)malloc(sizeof(double) * R1 * (ni ? ni : 1));        /* stored a (BF16), columns icols */
+    double* dhb = (double*)malloc(sizeof(double) * R1 * 2 * (ni ? ni : 1));   /* dh in BF16: dg, du of icols */
+    int failed = !m_indptr || !gather || !slots || !probs || !wf13 || !wf2 || !wb13 || !wb2 || !ab || !dhb;
     if (!failed) rc = orc_dispatch(T, E, k, ids, scores, m_indptr, gather, slots, probs);
     if (!failed && rc == ORC_OK) {
-        for (size_t z = 0; z < n13; ++z) wf13[z] = wb13[z] = (double)w13[z];
-        for (size_t z = 0; z < n2; ++z) wf2[z] = wb2[z] = (double)w2[z];
-        mx_matrix_image(wf13, E, 2 * I, d, 1);
-        mx_matrix_image(wf2, E, d, I, 1);
-        mx_matrix_image(wb13, E, 2 * I, d, 0);
-        mx_matrix_image(wb2, E, d, I, 0);
+        memcpy(wf13, w13, sizeof(float) * n13);
+        memcpy(wb13, w13, sizeof(float) * n13);
+        memcpy(wf2, w2, sizeof(float) * n2);
+        memcpy(wb2, w2, sizeof(float) * n2);
+        mx_matrix_image_f(wf13, E, 2 * I, d, 1);
+        mx_matrix_image_f(wf2, E, d, I, 1);
+        mx_matrix_image_f(wb13, E, 2 * I, d, 0);
+        mx_matrix_image_f(wb2, E, d, I, 0);
 
-        /* FPROP and DGRAD, one routed row at a time */
-#pragma omp parallel for schedule(dynamic, 4)
-        for (size_t r = 0; r < R; ++r) {
-            double* buf = (double*)malloc(sizeof(double) * (2 * (size_t)d + 4 * (size_t)I));
+        /* the token rows, whole: FPROP, DGRAD, combine and router gradient */
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int q = 0; q < ntok; ++q) {
+            double* buf = (double*)malloc(sizeof(double) * (4 * (size_t)d + 6 * (size_t)I));
             if (!buf) {
 #pragma omp atomic write
                 failed = 1;
                 continue;
             }
-            double *xq = buf, *dO = xq + d, *a = dO + d, *dA = a + I, *dh = dA + I;
+            double *xq = buf, *dO = xq + d, *o = dO + d, *dxp = o + d, *gb = dxp + d, *ub = gb + I,
+                   *a = ub + I, *dA = a + I, *dh = dA + I;
+            const int t = toks[q];
+            double* y_t = y + (size_t)q * d;
+            double* dx_t = dx + (size_t)q * d;
+            for (int n = 0; n < d; ++n) { y_t[n] = 0.0; dx_t[n] = 0.0; }
+            for (int c = 0; c < d; ++c) xq[c] = (double)x[(size_t)t * d + c];
+            for (int b = 0; b < d; b += 32) mx_block_image(xq + b, 32, 1);
+            for (int j = 0; j < k; ++j) {
+                const int e = ids[(size_t)t * k + j];
+                const double s = (double)scores[(size_t)t * k + j];
+                const float* f13 = wf13 + (size_t)e * 2 * I * d;
+                const float* f2 = wf2 + (size_t)e * d * I;
+                const float* b13 = wb13 + (size_t)e * 2 * I * d;
+                const float* b2 = wb2 + (size_t)e * d * I;
+                for (int i = 0; i < I; ++i) {
+                    double g = 0.0, u = 0.0;
+                    for (int c = 0; c < d; ++c) {
+                        g += (double)f13[(size_t)i * d + c] * xq[c];
+                        u += (double)f13[(size_t)(I + i) * d + c] * xq[c];
+                    }
+                    a[i] = act_f(act, g) * u;
+                    gb[i] = bf16_round(g);
+                    ub[i] = bf16_round(u);
+                }
+                for (int b = 0; b < I; b += 32) mx_block_image(a + b, 32, 1);
+                double dot = 0.0;
+                for (int n = 0; n < d; ++n) {
+                    double acc = 0.0;
+                    for (int i = 0; i < I; ++i) acc += (double)f2[(size_t)n * I + i] * a[i];
+                    o[n] = acc;
+                    y_t[n] += s * acc;
+                    dot += (double)dy[(size_t)t * d + n] * acc;
+                }
+                ds[(size_t)q * k + j] = dot;
+                /* DGRAD */
+                for (int n = 0; n < d; ++n) dO[n] = s * (double)dy[(size_t)t * d + n];
+                for (int b = 0; b < d; b += 32) mx_block_image(dO + b, 32, 1);
+                for (int i = 0; i < I; ++i) {
+                    double acc = 0.0;
+                    for (int n = 0; n < d; ++n) acc += (double)b2[(size_t)n * I + i] * dO[n];
+                    dA[i] = bf16_round(acc);
+                }
+                for (int i = 0; i < I; ++i) {
+                    dh[i] = dA[i] * ub[i] * act_df(act, gb[i]);
+                    dh[I + i] = dA[i] * act_f(act, gb[i]);
+                }
+                for (int b = 0; b < 2 * I; b += 32) mx_block_image(dh + b, 32, 1);
+                for (int c = 0; c < d; ++c) {
+                    double acc = 0.0;
+                    for (int jj = 0; jj < 2 * I; ++jj) acc += (double)b13[(size_t)jj * d + c] * dh[jj];
+                    dx_t[c] += acc;
+                }
+            }
+            free(buf);
+        }
+
+        /* columns icols of a and dh on every routed row, for the weight gradients */
+#pragma omp parallel for schedule(dynamic, 16)
+        for (size_t r = 0; r < R; ++r) {
+            double* buf = (double*)malloc(sizeof(double) * 2 * (size_t)d);
+            if (!buf) {
+#pragma omp atomic write
+                failed = 1;
+                continue;
+            }
+            double *xq = buf, *dO = xq + d;
             int e = 0;
             while (m_indptr[e + 1] <= (int32_t)r) ++e;
             const int t = gather[r];
             const double s = (double)probs[r];
-            const double* f13 = wf13 + (size_t)e * 2 * I * d;
-            const double* f2 = wf2 + (size_t)e * d * I;
-            const double* b13 = wb13 + (size_t)e * 2 * I * d;
-            const double* b2 = wb2 + (size_t)e * d * I;
-            double* h_r = hb + r * 2 * I;
+            const float* f13 = wf13 + (size_t)e * 2 * I * d;
+            const float* b2 = wb2 + (size_t)e * d * I;
             for (int c = 0; c < d; ++c) xq[c] = (double)x[(size_t)t * d + c];
             for (int b = 0; b < d; b += 32) mx_block_image(xq + b, 32, 1);
-            for (int i = 0; i < I; ++i) {
-                double g = 0.0, u = 0.0;
-                for (int c = 0; c < d; ++c) {
-                    g += f13[(size_t)i * d + c] * xq[c];
-                    u += f13[(size_t)(I + i) * d + c] * xq[c];
-                }
-                a[i] = act_f(act, g) * u;
-                h_r[i] = bf16_round(g);
-                h_r[I + i] = bf16_round(u);
-                ab[r * I + i] = bf16_round(a[i]);
-            }
-            for (int b = 0; b < I; b += 32) mx_block_image(a + b, 32, 1);
-            for (int n = 0; n < d; ++n) {
-                double acc = 0.0;
-                for (int i = 0; i < I; ++i) acc += f2[(size_t)n * I + i] * a[i];
-                o[r * d + n] = acc;
-            }
-            /* DGRAD */
             for (int n = 0; n < d; ++n) dO[n] = s * (double)dy[(size_t)t * d + n];
             for (int b = 0; b < d; b += 32) mx_block_image(dO + b, 32, 1);
-            for (int i = 0; i < I; ++i) {
-                double acc = 0.0;
-                for (int n = 0; n < d; ++n) acc += b2[(size_t)n * I + i] * dO[n];
-                dA[i] = bf16_round(acc);
-            }
-            for (int i = 0; i < I; ++i) {
-                const double g = h_r[i], u = h_r[I + i];
-                dh[i] = dA[i] * u * act_df(act, g);
-                dh[I + i] = dA[i] * act_f(act, g);
-            }
-            for (int j = 0; j < 2 * I; ++j) dhb[r * 2 * I + j] = bf16_round(dh[j]);
-            for (int b = 0; b < 2 * I; b += 32) mx_block_image(dh + b, 32, 1);
-            for (int c = 0; c < d; ++c) {
-                double acc = 0.0;
-                for (int j = 0; j < 2 * I; ++j) acc += b13[(size_t)j * d + c] * dh[j];
-                dxp[r * d + c] = acc;
+            for (int q = 0; q < ni; ++q) {
+                const int i = icols[q];
+                double g = 0.0, u = 0.0, acc = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    g += (double)f13[(size_t)i * d + c] * xq[c];
+                    u += (double)f13[(size_t)(I + i) * d + c] * xq[c];
+                }
+                for (int n = 0; n < d; ++n) acc += (double)b2[(size_t)n * I + i] * dO[n];
+                const double gq = bf16_round(g), uq = bf16_round(u), dA = bf16_round(acc);
+                ab[r * ni + q] = bf16_round(act_f(act, g) * u);
+                dhb[(r * 2 + 0) * ni + q] = bf16_round(dA * uq * act_df(act, gq));
+                dhb[(r * 2 + 1) * ni + q] = bf16_round(dA * act_f(act, gq));
             }
             free(buf);
         }
-    }
-    if (!failed && rc == ORC_OK) {
-        /* combine, router gradient and input gradient per token, j ascending */
-        for (int t = 0; t < T; ++t) {
-            for (int n = 0; n < d; ++n) { y[(size_t)t * d + n] = 0.0; dx[(size_t)t * d + n] = 0.0; }
-            for (int j = 0; j < k; ++j) {
-                const size_t r = (size_t)slots[(size_t)t * k + j];
-                const double s = (double)scores[(size_t)t * k + j];
-                double dot = 0.0;
-                for (int n = 0; n < d; ++n) {
-                    y[(size_t)t * d + n] += s * o[r * d + n];
-                    dx[(size_t)t * d + n] += dxp[r * d + n];
-                    dot += (double)dy[(size_t)t * d + n] * o[r * d + n];
-                }
-                ds[(size_t)t * k + j] = dot;
-            }
-        }
+
         /* WGRAD, one expert at a time, operands blocked along its routed rows */
 #pragma omp parallel for schedule(dynamic, 1)
         for (int e = 0; e < E; ++e) {
             const int r0 = m_indptr[e], rows = m_indptr[e + 1] - r0;
-            double* dw2_e = dw2 + (size_t)e * d * I;
-            double* dw13_e = dw13 + (size_t)e * 2 * I * d;
-            for (size_t z = 0; z < (size_t)d * I; ++z) dw2_e[z] = 0.0;
-            for (size_t z = 0; z < (size_t)2 * I * d; ++z) dw13_e[z] = 0.0;
+            double* dw2_e = dw2 + (size_t)e * d * ni;
+            double* dw13_e = dw13 + (size_t)e * 2 * ni * d;
+            for (size_t z = 0; z < (size_t)d * ni; ++z) dw2_e[z] = 0.0;
+            for (size_t z = 0; z < (size_t)2 * ni * d; ++z) dw13_e[z] = 0.0;
             if (rows == 0) continue;
-            double* buf = (double*)malloc(sizeof(double) * (size_t)rows * (2 * (size_t)d + 3 * (size_t)I));
+            double* buf = (double*)malloc(sizeof(double) * (size_t)rows * (2 * (size_t)d + 3 * (size_t)ni));
             if (!buf) {
 #pragma omp atomic write
                 failed = 1;
                 continue;
             }
             double *dOt = buf, *xt = dOt + (size_t)rows * d, *at = xt + (size_t)rows * d,
-                   *dht = at + (size_t)rows * I;
+                   *dht = at + (size_t)rows * ni;
             for (int q = 0; q < rows; ++q) {
                 const size_t r = (size_t)(r0 + q);
                 const int t = gather[r];
@@ -679,21 +738,23 @@ int orc_train_mx(int T, int d, int I, int E, int k,
                     dOt[(size_t)q * d + n] = (double)probs[r] * (double)dy[(size_t)t * d + n];
                     xt[(size_t)q * d + n] = (double)x[(size_t)t * d + n];
                 }
-                for (int i = 0; i < I; ++i) at[(size_t)q * I + i] = ab[r * I + i];
-                for (int j = 0; j < 2 * I; ++j) dht[(size_t)q * 2 * I + j] = dhb[r * 2 * I + j];
+                for (int c = 0; c < ni; ++c) at[(size_t)q * ni + c] = ab[r * ni + c];
+                for (int c = 0; c < 2 * ni; ++c) dht[(size_t)q * 2 * ni + c] = dhb[r * 2 * ni + c];
             }
             mx_matrix_image(dOt, 1, rows, d, 0);
             mx_matrix_image(xt, 1, rows, d, 0);
-            mx_matrix_image(at, 1, rows, I, 0);
-            mx_matrix_image(dht, 1, rows, 2 * I, 0);
+            if (ni > 0) {
+                mx_matrix_image(at, 1, rows, ni, 0);
+                mx_matrix_image(dht, 1, rows, 2 * ni, 0);
+            }
             for (int q = 0; q < rows; ++q) {
                 for (int n = 0; n < d; ++n) {
-                    const double g = dOt[(size_t)q * d + n];
-                    for (int i = 0; i < I; ++i) dw2_e[(size_t)n * I + i] += g * at[(size_t)q * I + i];
+                    const double gv = dOt[(size_t)q * d + n];
+                    for (int c = 0; c < ni; ++c) dw2_e[(size_t)n * ni + c] += gv * at[(size_t)q * ni + c];
                 }
-                for (int j = 0; j < 2 * I; ++j) {
-                    const double g = dht[(size_t)q * 2 * I + j];
-                    for (int c = 0; c < d; ++c) dw13_e[(size_t)j * d + c] += g * xt[(size_t)q * d + c];
+                for (int jj = 0; jj < 2 * ni; ++jj) {
+                    const double gv = dht[(size_t)q * 2 * ni + jj];
+                    for (int c = 0; c < d; ++c) dw13_e[(size_t)jj * d + c] += gv * xt[(size_t)q * d + c];
                 }
             }
             free(buf);
@@ -701,7 +762,7 @@ int orc_train_mx(int T, int d, int I, int E, int k,
     }
     free(m_indptr); free(gather); free(slots); free(probs);
     free(wf13); free(wf2); free(wb13); free(wb2);
-    free(hb); free(ab); free(o); free(dhb); free(dxp);
+    free(ab); free(dhb);
     if (rc != ORC_OK) return rc;
     return failed ? ORC_ERR_ALLOC : ORC_OK;
 }

@@ -29,7 +29,8 @@ int orc_forward_tokens_mx(int T, int d, int I, int E, int k, const float* x, con
                           const int32_t* toks, double* y, int act);
 int orc_train_mx(int T, int d, int I, int E, int k, const float* x, const int32_t* ids,
                  const float* scores, const float* w13, const float* w2, const float* dy, int act,
-                 double* y, double* dx, double* ds, double* dw13, double* dw2);
+                 int ntok, const int32_t* toks, double* y, double* dx, double* ds,
+                 int ni, const int32_t* icols, double* dw13, double* dw2);
 
 static uint64_t state = 88172645463325252ull;
 static double uni(void)
@@ -101,7 +102,21 @@ static void run_layer(int T, int d, int I, int E, int k, int act, int empty_from
         double* tdw2 = malloc(sizeof(double) * (size_t)E * d * I);
         for (size_t z = 0; z < (size_t)E * d * I; ++z) tdw2[z] = NAN;
         for (size_t z = 0; z < (size_t)E * 2 * I * d; ++z) tdw13[z] = NAN;
-        CHECK(orc_train_mx(T, d, I, E, k, x, ids, sc, w13, w2, dy, act, ty, tdx, tds, tdw13, tdw2) == 0);
+        int32_t* all_i = malloc(sizeof(int32_t) * I);
+        for (int i = 0; i < I; ++i) all_i[i] = i;
+        CHECK(orc_train_mx(T, d, I, E, k, x, ids, sc, w13, w2, dy, act, T, toks, ty, tdx, tds, I, all_i,
+                           tdw13, tdw2) == 0);
+        /* a subset of tokens and columns writes only its own outputs */
+        if (T > 1 && I > 2) {
+            int32_t sub_t[1] = {T - 1}, sub_i[2] = {I - 1, 0};
+            double* sy = calloc((size_t)d * 2, sizeof(double));
+            double* sdw13 = calloc((size_t)E * 2 * 2 * d + 1, sizeof(double));
+            double* sdw2 = calloc((size_t)E * d * 2 + 1, sizeof(double));
+            CHECK(orc_train_mx(T, d, I, E, k, x, ids, sc, w13, w2, dy, act, 1, sub_t, sy, sy + d, tds, 2, sub_i,
+                               sdw13, sdw2) == 0);
+            free(sy); free(sdw13); free(sdw2);
+        }
+        free(all_i);
         for (size_t z = 0; z < (size_t)E * d * I; ++z) CHECK(!isnan(tdw2[z]));
         for (size_t z = 0; z < (size_t)E * 2 * I * d; ++z) CHECK(!isnan(tdw13[z]));
         for (int e = span; e < E; ++e)

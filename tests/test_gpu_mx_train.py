@@ -248,3 +248,46 @@ def test_mxfp8_training_graph_replay_matches_eager(torch_cuda):
         torch.cuda.synchronize()
     assert layer.status()[1] == 0
     layer.close()
+
+
+def test_mxfp8_training_full_size_sampled(torch_cuda):
+    """The training workload's shape (T=8192 d=2048 I=768 E=128 k=8, Zipf routing with
+    empty experts) on MXFP8 operands, in the launch configuration the benchmark times:
+    256 sampled tokens (the first and last included) of y, dx and dscores, and 16
+    sampled intermediate columns (0 and I-1 included) of dW13 (gate and up rows) and
+    dW2 for every expert, against the oracle's MXFP8 step on the same samples and the
+    FP32 oracle of the prepared-weight layer."""
+    torch = torch_cuda
+    say("mxfp8 training full size: T=8192 d=2048 I=768 E=128 k=8 zipf")
+    inp = inputs.generate_config("train", seed=0, with_dy=True)
+    t = device_inputs(inp)
+    layer = _layer(inp)
+    got = [np_of(v) for v in _step(layer, t, _prepared(layer, t))]
+    torch.cuda.synchronize()
+    assert layer.status()[1] == 0
+    layer.close()
+    del t
+    torch.cuda.empty_cache()
+    y, dx, dw13, dw2, ds = got
+    rng = np.random.default_rng(3)
+    toks = np.sort(rng.choice(inp.T, 256, replace=False)).astype(np.int32)
+    toks[0], toks[-1] = 0, inp.T - 1
+    icols = np.sort(rng.choice(inp.I, 16, replace=False)).astype(np.int32)
+    icols[0], icols[-1] = 0, inp.I - 1
+    I = inp.I
+    gdw13 = np.stack([dw13[:, icols], dw13[:, I + icols]], 1)
+    gdw2 = dw2[:, :, icols]
+    qy, qdx, qds, qdw13, qdw2 = oracle.train_mx(inp.x, inp.ids, inp.scores, inp.w13, inp.w2, inp.dy,
+                                                toks=toks, icols=icols)
+    for name, g, r in (("y", y[toks], qy), ("dx", dx[toks], qdx), ("ds", ds[toks], qds)):
+        check(name + " vs quantizing oracle", g, r, **MX_QUANT)
+    for name, g, r in (("dw13", gdw13, qdw13), ("dw2", gdw2, qdw2)):
+        check(name + " vs quantizing oracle", g, r, **MX_QUANT_WGRAD)
+    w13f, w2f = _prepared_f32(inp.w13), _prepared_f32(inp.w2)
+    x32, dy32 = oracle._f32(inp.x), oracle._f32(inp.dy)
+    py = oracle.forward_tokens(x32, inp.ids, inp.scores, w13f, w2f, toks=toks)
+    pdx, pds = oracle.backward_tokens(x32, inp.ids, inp.scores, w13f, w2f, dy32, toks=toks)
+    pdw2, pdw13 = oracle.wgrad_cols(x32, inp.ids, inp.scores, w13f, w2f, dy32, icols=icols)
+    for name, g, r in (("y", y[toks], py), ("dx", dx[toks], pdx), ("ds", ds[toks], pds),
+                       ("dw13", gdw13, pdw13.reshape(gdw13.shape)), ("dw2", gdw2, pdw2)):
+        check(name + " vs fp32 oracle", g, r, **MX)

@@ -200,3 +200,20 @@ def test_mx_train_matches_independent_construction(orc, act):
     # the quantization is visible: the plain step differs
     pdx, _ = orc.backward_tokens(x, inp.ids, inp.scores, w13, w2, dy, act=act)
     assert np.linalg.norm(got[1] - pdx) > 1e-3 * np.linalg.norm(pdx)
+
+
+def test_mx_train_subsets_equal_full_step(orc):
+    """Token and column subsets give the full step's values: the token rows of dx, ds and
+    y, and the weight-gradient columns (gate and up rows of dW13, columns of dW2)."""
+    from mixture_experts_routed_dispatch_amd import inputs
+    inp = inputs.generate(T=70, d=64, I=96, E=4, k=2, seed=29, with_dy=True)
+    x, w13, w2, dy = (orc._f32(a) for a in (inp.x, inp.w13, inp.w2, inp.dy))
+    full = orc.train_mx(x, inp.ids, inp.scores, w13, w2, dy)
+    toks = np.array([69, 0, 33], np.int32)
+    icols = np.array([95, 0, 40, 41], np.int32)
+    y, dx, ds, dw13, dw2 = orc.train_mx(x, inp.ids, inp.scores, w13, w2, dy, toks=toks, icols=icols)
+    assert np.array_equal(y, full[0][toks]) and np.array_equal(dx, full[1][toks])
+    assert np.array_equal(ds, full[2][toks])
+    I = 96
+    assert np.array_equal(dw13[:, 0], full[3][:, icols]) and np.array_equal(dw13[:, 1], full[3][:, I + icols])
+    assert np.array_equal(dw2, full[4][:, :, icols])
