@@ -875,6 +875,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
         __syncthreads();               // the staging slots are copied into again from the next stage
         cc = coords(c_item);
         frag_offsets();
+        // the next stage's first fragments again, from its ring buffer (not written before
+        // that stage runs), so that they are not held in registers across the epilogue
+        read_frags(gs & 3, 0, fa, fc);
     }
 }
 
