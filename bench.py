@@ -80,7 +80,7 @@ def parse():
 KERNEL_OF_STAGE = {
     # stage name (library event pairs) -> substrings of the symbols (as rocprofv3 reports
     # them) of every kernel the stage launches
-    "dispatch": ("dispatch_count", "dispatch_place"),
+    "dispatch": ("dispatch_kernel",),
     "w13": ("grouped_gemm<0,", "fwd_fixup<0,"), "w2": ("grouped_gemm<1,", "fwd_fixup<1,"),
     "combine": ("combine_kernel",), "score_grad": ("score_grad_kernel",),
     "dgrad_w2": ("grouped_gemm<2,",), "dgrad_w13": ("grouped_gemm<3,",),

@@ -627,6 +627,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 __builtin_amdgcn_sched_barrier(0);
+                // saved h: one row pointer per block (the wave's 64 columns are all inside
+                // I or all past it, I being a multiple of 64), constant offsets per store
+                const int hr = c.qt * TQ + wq * 128 + b * 32 + q_in;
+                const bool hlive = kSaveH && hr < c.rows && c.pt * 128 + wp * 64 < g.I;
+                uint16_t* hrow = kSaveH ? g.out_h + ((size_t)c.mb + (hlive ? hr : 0)) * 2 * g.I + c.pt * 128 + wp * 64 + p_sub
+                                        : nullptr;
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -644,15 +650,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                         v.y = pack_bf16(av[2], av[3]);
                         *reinterpret_cast<uint2*>(stg + q_in * 128 + ((c8 ^ (q_in & 7)) << 4) + (p_sub << 1)) = v;
                         if constexpr (kSaveH) {
-                            const int rr = c.qt * TQ + wq * 128 + b * 32 + q_in;
-                            const int i = c.pt * 128 + wp * 64 + a * 16 + 8 * grp + p_sub;
-                            if (rr < c.rows && i < g.I) {
-                                const size_t r = (size_t)c.mb + rr;
+                            if (hlive) {
                                 uint2 hg, hu;
                                 hg.x = pack_bf16(gv[0], gv[1]); hg.y = pack_bf16(gv[2], gv[3]);
                                 hu.x = pack_bf16(uv[0], uv[1]); hu.y = pack_bf16(uv[2], uv[3]);
-                                *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + i) = hg;
-                                *reinterpret_cast<uint2*>(g.out_h + r * 2 * g.I + g.I + i) = hu;
+                                *reinterpret_cast<uint2*>(hrow + a * 16 + 8 * grp) = hg;
+                                *reinterpret_cast<uint2*>(hrow + g.I + a * 16 + 8 * grp) = hu;
                             }
                         }
                     }

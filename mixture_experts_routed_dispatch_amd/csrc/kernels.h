@@ -16,10 +16,10 @@ constexpr int kDispatchChunk = 2048;
 
 inline int dispatch_chunks(int64_t R) { return (int)((R + kDispatchChunk - 1) / kDispatchChunk); }
 
-// dispatch: hist is int32 [nchunks, E] scratch; status is the sticky flag word.
+// dispatch (one launch, no scratch); status is the sticky flag word.  E <= 256.
 hipError_t launch_dispatch(const int32_t* ids, const float* scores, int T, int k, int E,
-                           int32_t* hist, int32_t* m_indptr, int32_t* gather, int32_t* slots,
-                           float* probs, int32_t* status, hipStream_t s);
+                           int32_t* m_indptr, int32_t* gather, int32_t* slots, float* probs,
+                           int32_t* status, hipStream_t s);
 
 // Pre-dispatched rows: validates a caller's m_indptr [E+1] into m_out (all zeros and
 // kDevBadIndptr when it does not rise from 0 or passes R) and writes gather[r] = r, r < R.

@@ -33,10 +33,9 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 struct moe_plan_s {
     moe_config_t cfg;
     int64_t R;
-    int nchunks;
     bool decode;
     // workspace offsets (bytes)
-    size_t off_status, off_hist, off_m_indptr, off_gather, off_slots, off_probs;
+    size_t off_status, off_m_indptr, off_gather, off_slots, off_probs;
     size_t off_a, off_o, off_h, off_dh, off_dxp, off_xg, off_dys, off_xq, off_xs, off_xsr, off_aq, off_as;
     // MXFP8 backward: dO and (dg, du) quantized along d and 2I (codes, block-major scales), and
     // the weight-gradient operands in the token layout (P and Q codes and scales)
@@ -127,7 +126,7 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
     hipError_t e;
     if (c.T == 0) {
         // no routed rows: every expert is empty and its weight gradient +0 (or kept)
-        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr, nullptr,
+        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E, m_indptr, nullptr,
                                  nullptr, nullptr, p->at<int32_t>(p->off_status), s)) != hipSuccess)
             return MOE_ERR_HIP;
     } else {
@@ -250,12 +249,10 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (!p) return MOE_ERR_INVALID_ARG;
     p->cfg = c;
     p->R = R;
-    p->nchunks = dispatch_chunks(R);
     p->decode = c.path == MOE_PATH_DECODE || (c.path == MOE_PATH_AUTO && decode_ok);
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = align256(off + bytes); return o; };
-    p->off_status = take(sizeof(int32_t) * kStatusWords);   // status word, mega grid-barrier words
-    p->off_hist = take(sizeof(int32_t) * (size_t)(p->nchunks > 0 ? p->nchunks : 1) * c.E);
+    p->off_status = take(sizeof(int32_t) * kStatusWords);   // the sticky status word
     p->off_m_indptr = take(sizeof(int32_t) * (size_t)(c.E + 1));
     p->off_gather = take(sizeof(int32_t) * (size_t)R);
     p->off_slots = take(sizeof(int32_t) * (size_t)R);
@@ -358,8 +355,6 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
         if (c.training) saved += bytes;
     };
     region("status", sizeof(int32_t), "flags", "sticky device routing flags (moe_get_status)");
-    region("hist", sizeof(int32_t) * (size_t)(p->nchunks > 0 ? p->nchunks : 1) * c.E, "scratch",
-           "dispatch: per-chunk expert counts");
     saved_region("m_indptr", sizeof(int32_t) * (size_t)(c.E + 1), "expert row offsets [E+1]");
     saved_region("gather", sizeof(int32_t) * (size_t)R, "token of each routed row [R]");
     saved_region("slots", sizeof(int32_t) * (size_t)R, "routed row of each (t, j) [T, k]");
@@ -451,7 +446,7 @@ moe_status_t moe_dispatch(moe_plan_t p, const int32_t* ids, const float* scores,
     if (!p->ws) return MOE_ERR_WORKSPACE;
     const moe_config_t& c = p->cfg;
     p->status_word = p->at<int32_t>(p->off_status);
-    hipError_t e = launch_dispatch(ids, scores, c.T, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr,
+    hipError_t e = launch_dispatch(ids, scores, c.T, c.k, c.E, m_indptr,
                                    gather, slots, probs, p->at<int32_t>(p->off_status),
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
@@ -549,7 +544,7 @@ moe_status_t moe_forward(moe_plan_t p, const void* x, const int32_t* ids, const 
     int32_t* slots = p->at<int32_t>(p->off_slots);
     float* probs = p->at<float>(p->off_probs);
     hipError_t e = staged(p, MOE_STAGE_DISPATCH, s, [&] {
-        return launch_dispatch(ids, scores, c.T, c.k, c.E, p->at<int32_t>(p->off_hist), m_indptr,
+        return launch_dispatch(ids, scores, c.T, c.k, c.E, m_indptr,
                                gather, slots, probs, p->at<int32_t>(p->off_status), s);
     });
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -755,7 +750,7 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     if (c.T == 0) {
         // no routed rows: every expert gradient is +0 (the weight-gradient kernels write them)
         g.m_indptr = p->at<int32_t>(p->off_m_indptr);
-        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E, p->at<int32_t>(p->off_hist),
+        if ((e = launch_dispatch(nullptr, nullptr, 0, c.k, c.E,
                                  p->at<int32_t>(p->off_m_indptr), nullptr, nullptr, nullptr,
                                  p->at<int32_t>(p->off_status), s)) != hipSuccess)
             return MOE_ERR_HIP;

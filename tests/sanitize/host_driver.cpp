@@ -14,8 +14,8 @@
 #include "../../mixture_experts_routed_dispatch_amd/csrc/kernels.h"
 
 namespace moe {
-hipError_t launch_dispatch(const int32_t*, const float*, int, int, int, int32_t*, int32_t*, int32_t*,
-                           int32_t*, float*, int32_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_dispatch(const int32_t*, const float*, int, int, int, int32_t*, int32_t*, int32_t*, float*,
+                           int32_t*, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_routed_prep(const int32_t*, int, int64_t, int32_t*, int32_t*, int32_t*, hipStream_t) {
     return hipErrorInvalidValue;
 }
