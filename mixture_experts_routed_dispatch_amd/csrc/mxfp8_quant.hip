@@ -217,13 +217,15 @@ __global__ __launch_bounds__(kThreads) void mx_act_backward_kernel(const uint16_
     }
 }
 
-// Transposing quantization (see launch_mx_transpose_quant), one workgroup per tile of
-// 128 source rows (one group of four MX blocks along the rows) x 64 columns:
+// Transposing quantization (see launch_mx_transpose_quant).  A workgroup takes 128 source
+// rows (one group of four MX blocks along the rows) and walks every gridDim.y-th tile of
+// 64 columns, the next tile's loads in flight while the current one is converted:
 //   1. two threads per row copy the row's 64 columns (128 contiguous bytes) into LDS as
 //      FP32, [row][65] (scaled by probs, zero past the segment's rows);
 //   2. thread (column f = t / 4, block b = t % 4) quantizes rows 32 b .. 32 b + 31 of
 //      column f and writes their 32 codes, so that the four threads of a column write
 //      its 128 contiguous code bytes and its scale word together.
+// The row tile's segment, source rows and scores are looked up once per workgroup.
 // Token layout: the tiles of all segments are numbered in segment order (segment e has
 // kp_e / 128 of them), gridDim.x covers the largest possible total, and workgroups past
 // the actual one exit.  Weight layout: blockIdx.z is the matrix, blockIdx.x its tile.
@@ -240,7 +242,6 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_quant_kernel(const uint
     __shared__ int wsum[kThreads / 64];
     __shared__ int info[4];            // segment, tile within it, first routed row, rows
     const int tid = threadIdx.x;
-    const int n0 = blockIdx.y * kTqCols;
     int e, kt, r0, rows, kp;
     int64_t koff;
     if (weights) {
@@ -288,66 +289,71 @@ __global__ __launch_bounds__(kThreads) void mx_transpose_quant_kernel(const uint
         if (tid == e) info[0] = first;
         __syncthreads();
         koff = (int64_t)info[0] * kMxWgradPad;
-        kp = 0;                                     // not needed below (codes stride is kp)
-        {
-            const int rr = rows > 0 ? rows : 1;
-            kp = (rr + kMxWgradPad - 1) / kMxWgradPad * kMxWgradPad;
-        }
+        kp = ((rows > 0 ? rows : 1) + kMxWgradPad - 1) / kMxWgradPad * kMxWgradPad;   // row stride of the codes
     }
-    // 1. rows kt * 128 .. + 127 of the segment, columns n0 .. n0 + 63
-    {
-        const int row = tid >> 1, half = tid & 1;
-        const int k = kt * kTqRows + row;
-        float v[32];
-        if (k < rows) {
-            int64_t srow;
-            float sc = 1.0f;
-            if (weights) {
-                srow = (int64_t)e * K + k;
-            } else {
-                srow = r0 + k;
-                if (probs) sc = probs[srow];
-                if (gather) {
-                    const uint32_t t = (uint32_t)gather[srow];
-                    srow = t < (uint32_t)T ? t : 0;
-                }
-            }
-            const uint4* p = reinterpret_cast<const uint4*>(src + srow * N + n0 + 32 * half);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 q = p[c];
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                    v[8 * c + 2 * z] = sc * bf16lo(w[z]);
-                    v[8 * c + 2 * z + 1] = sc * bf16hi(w[z]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) v[i] = 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < 32; ++i) tile[row * kTqLd + 32 * half + i] = v[i];
-    }
-    __syncthreads();
-    // 2. column f, rows 32 b .. 32 b + 31 of the tile
-    {
-        const int f = tid >> 2, b = tid & 3;
-        float v[32];
-#pragma unroll
-        for (int j = 0; j < 32; ++j) v[j] = tile[(32 * b + j) * kTqLd + f];
-        uint32_t out[8];
-        const uint32_t sb = quant_block32(v, out);
-        const int n = n0 + f;
-        const int kb = kt * 4 + b;                  // MX block along the rows
+    // the thread's source row (two threads per row, 32 columns each), loaded once
+    const int row = tid >> 1, half = tid & 1;
+    const int kr = kt * kTqRows + row;
+    const bool live = kr < rows;
+    int64_t srow = 0;
+    float sc = 1.0f;
+    if (live) {
         if (weights) {
-            store_codes32(codes + ((int64_t)e * N + n) * K + 32 * kb, out);
-            scales[((int64_t)kt * segs * N + (int64_t)e * N + n) * 4 + b] = (uint8_t)sb;
+            srow = (int64_t)e * K + kr;
         } else {
-            store_codes32(codes + koff * N + (int64_t)n * kp + 32 * kb, out);
-            scales[koff * N / 32 + ((int64_t)kt * N + n) * 4 + b] = (uint8_t)sb;
+            srow = r0 + kr;
+            if (probs) sc = probs[srow];
+            if (gather) {
+                const uint32_t t = (uint32_t)gather[srow];
+                srow = t < (uint32_t)T ? t : 0;
+            }
         }
+    }
+    const uint16_t* rowp = src + srow * N + 32 * half;
+    auto load = [&](int ft, uint4 q[4]) {
+        const uint4* p = reinterpret_cast<const uint4*>(rowp + (int64_t)ft * kTqCols);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[c] = live ? p[c] : make_uint4(0, 0, 0, 0);
+    };
+    const int nft = N / kTqCols;
+    uint4 cur[4];
+    load(blockIdx.y, cur);
+    for (int ft = blockIdx.y; ft < nft; ft += gridDim.y) {
+        // the next column tile's loads go out before this one is converted
+        uint4 nxt[4];
+        if (ft + (int)gridDim.y < nft) load(ft + gridDim.y, nxt);
+        __syncthreads();                            // the previous tile's readers are done
+        // 1. the row's 32 columns into LDS as FP32 (times probs; zero past the rows)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t w[4] = {cur[c].x, cur[c].y, cur[c].z, cur[c].w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                tile[row * kTqLd + 32 * half + 8 * c + 2 * z] = sc * bf16lo(w[z]);
+                tile[row * kTqLd + 32 * half + 8 * c + 2 * z + 1] = sc * bf16hi(w[z]);
+            }
+        }
+        __syncthreads();
+        // 2. column f, rows 32 b .. 32 b + 31 of the tile
+        {
+            const int f = tid >> 2, b = tid & 3;
+            float v[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) v[j] = tile[(32 * b + j) * kTqLd + f];
+            uint32_t out[8];
+            const uint32_t sb = quant_block32(v, out);
+            const int n = ft * kTqCols + f;
+            const int kb = kt * 4 + b;                  // MX block along the rows
+            if (weights) {
+                store_codes32(codes + ((int64_t)e * N + n) * K + 32 * kb, out);
+                scales[((int64_t)kt * segs * N + (int64_t)e * N + n) * 4 + b] = (uint8_t)sb;
+            } else {
+                store_codes32(codes + koff * N + (int64_t)n * kp + 32 * kb, out);
+                scales[koff * N / 32 + ((int64_t)kt * N + n) * 4 + b] = (uint8_t)sb;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cur[c] = nxt[c];
     }
 }
 
@@ -416,7 +422,9 @@ hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N
     // K / 128 + segs (each segment rounds up to a multiple of 128, at least 128)
     const int64_t tiles = weights ? K / kTqRows : (int64_t)K / kTqRows + segs;
     if (tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-    const dim3 gd((unsigned)tiles, (unsigned)(N / kTqCols), weights ? (unsigned)segs : 1u);
+    // column tiles of 64 split over up to 4 workgroups per row tile, each walking its share
+    const int ngrp = N / kTqCols < 4 ? N / kTqCols : 4;
+    const dim3 gd((unsigned)tiles, (unsigned)ngrp, weights ? (unsigned)segs : 1u);
     hipLaunchKernelGGL(mx_transpose_quant_kernel, gd, dim3(kThreads), 0, s, src, segs, K, N, m_indptr, gather, probs,
                        T, weights, codes, scales);
     return hipGetLastError();
