@@ -91,9 +91,10 @@ KERNEL_OF_STAGE = {
 }
 # the MXFP8 workloads' GEMM stages run the block-scaled kernels
 KERNEL_OF_STAGE_MX = dict(KERNEL_OF_STAGE, w13=("grouped_gemm_mx<0,",), w2=("grouped_gemm_mx<1,",),
-                          recompute_h=("grouped_gemm_mx<0,",), dgrad_w2=("grouped_gemm_mx<2,",),
-                          dgrad_w13=("grouped_gemm_mx<2,",), wgrad_w2=("grouped_gemm_mx<3,",),
-                          wgrad_w13=("grouped_gemm_mx<3,",), quant_do=("mx_scaled_rows_kernel",),
+                          recompute_h=("grouped_gemm_mx<0,",), dgrad_w2=("grouped_gemm_mx<2, 0, false, 0>",),
+                          dgrad_w13=("grouped_gemm_mx<2, 0, false, 1>",),
+                          wgrad_w2=("grouped_gemm_mx<3, 0, false, 0>",),
+                          wgrad_w13=("grouped_gemm_mx<3, 0, false, 1>",), quant_do=("mx_scaled_rows_kernel",),
                           act_bwd=("mx_act_backward_kernel",), quant_t=("mx_transpose_quant_kernel",))
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -325,10 +326,11 @@ def main():
                    and not args.no_extra)
     if default_run:
         # the other headline workloads (decode at 1 and 32 tokens: HBM-bound; MXFP8: the
-        # FP8 products), a few steps each, reported beside the prefill line
+        # FP8 products; training in BF16 and MXFP8), a few steps each, reported beside the
+        # prefill line
         import torch
         extra = {}
-        for w, steps in (("decode1", 200), ("decode32", 50), ("mxfp8", 10)):
+        for w, steps in (("decode1", 200), ("decode32", 50), ("mxfp8", 10), ("train", 10), ("train-mxfp8", 10)):
             torch.cuda.empty_cache()
             sub = argparse.Namespace(**vars(args))
             sub.steps, sub.warmup = steps, 3
@@ -336,7 +338,7 @@ def main():
             o.pop("_inp")
             extra[w] = {key: o[key] for key in ("value", "unit", "ms_per_step", "dtype", "config", "stage_us",
                                                  "roofline", "decode", "tokens_per_s", "mfma_frac_layer",
-                                                 "gemm_mfma_frac", "steps", "warmup") if key in o}
+                                                 "gemm_mfma_frac", "steps", "warmup", "weight_prepare_us") if key in o}
         out["other_workloads"] = extra
     print(json.dumps(out), flush=True)
 

@@ -82,7 +82,9 @@ struct TileCtx {
     int koff, kp;                      // MX_WGRAD: the expert's token-layout offset and padded rows
 };
 
-template <int MODE, int kAct = kActSwiGLU, bool kSave = false>
+// kProd only names the instance (1: the W13-side product of MX_PLAIN / MX_WGRAD), so that
+// per-kernel traces and counters tell the two backward products of a mode apart.
+template <int MODE, int kAct = kActSwiGLU, bool kSave = false, int kProd = 0>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
     __shared__ __attribute__((aligned(1024))) char lsc[NSC * SCB];
@@ -619,18 +621,18 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     }
 }
 
-template <int MODE, int kAct>
+template <int MODE, int kAct, int kProd>
 hipError_t launch_mx_act(const MxGemmArgs& g, dim3 grid, hipStream_t s) {
     if constexpr (MODE == MX_W13)
         if (g.h_out) {
-            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, true>), grid, dim3(NTHR), 0, s, g);
+            hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, true, kProd>), grid, dim3(NTHR), 0, s, g);
             return hipGetLastError();
         }
-    hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, false>), grid, dim3(NTHR), 0, s, g);
+    hipLaunchKernelGGL((grouped_gemm_mx<MODE, kAct, false, kProd>), grid, dim3(NTHR), 0, s, g);
     return hipGetLastError();
 }
 
-template <int MODE>
+template <int MODE, int kProd = 0>
 hipError_t launch_mx_mode(const MxGemmArgs& g, int num_cu, hipStream_t s) {
     const int64_t R = (int64_t)g.T * g.k;
     int64_t tiles;
@@ -643,10 +645,10 @@ hipError_t launch_mx_mode(const MxGemmArgs& g, int num_cu, hipStream_t s) {
     if (grid < 1) grid = 1;
     const dim3 gd((unsigned)grid);
     if constexpr (MODE == MX_W13) {
-        if (g.act == kActGeGLU) return launch_mx_act<MODE, kActGeGLU>(g, gd, s);
-        if (g.act == kActReGLU) return launch_mx_act<MODE, kActReGLU>(g, gd, s);
+        if (g.act == kActGeGLU) return launch_mx_act<MODE, kActGeGLU, kProd>(g, gd, s);
+        if (g.act == kActReGLU) return launch_mx_act<MODE, kActReGLU, kProd>(g, gd, s);
     }
-    return launch_mx_act<MODE, kActSwiGLU>(g, gd, s);
+    return launch_mx_act<MODE, kActSwiGLU, kProd>(g, gd, s);
 }
 
 }  // namespace
@@ -657,6 +659,8 @@ hipError_t launch_gemm_mxfp8(MxMode mode, const MxGemmArgs& g, int num_cu, hipSt
         case MX_W2: return launch_mx_mode<MX_W2>(g, num_cu, s);
         case MX_PLAIN: return launch_mx_mode<MX_PLAIN>(g, num_cu, s);
         case MX_WGRAD: return launch_mx_mode<MX_WGRAD>(g, num_cu, s);
+        case MX_PLAIN_W13: return launch_mx_mode<MX_PLAIN, 1>(g, num_cu, s);
+        case MX_WGRAD_W13: return launch_mx_mode<MX_WGRAD, 1>(g, num_cu, s);
     }
     return hipErrorInvalidValue;
 }

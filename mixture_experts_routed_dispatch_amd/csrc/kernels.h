@@ -58,7 +58,9 @@ constexpr size_t kGemmPartBytes = (size_t)kMaxPieces * 256 * 256 * sizeof(float)
 hipError_t launch_gemm(GemmMode mode, const GemmArgs& g, int num_cu, hipStream_t s);
 
 // MXFP8 forward products (OCP E4M3 codes, E8M0 scale per 32 along K).
-enum MxMode { MX_W13 = 0, MX_W2 = 1, MX_PLAIN = 2, MX_WGRAD = 3 };
+// MX_PLAIN_W13 / MX_WGRAD_W13: MX_PLAIN / MX_WGRAD as a kernel instance of their own (the
+// W13-side backward products), so that traces tell them from the W2 side.
+enum MxMode { MX_W13 = 0, MX_W2 = 1, MX_PLAIN = 2, MX_WGRAD = 3, MX_PLAIN_W13 = 4, MX_WGRAD_W13 = 5 };
 
 struct MxGemmArgs {
     int T, d, I, E, k;

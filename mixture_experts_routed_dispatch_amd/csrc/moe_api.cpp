@@ -169,7 +169,7 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
         g2.Kp = 2 * c.I; g2.Np = c.d;
         g2.pq = w->w13t; g2.ps = w->w13t_scale; g2.qq = dhq; g2.qs = dhs;
         g2.out = dxp;
-        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_PLAIN, g2, p->num_cu, s); });
+        e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_PLAIN_W13, g2, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
         e = staged(p, MOE_STAGE_DX_COMBINE, s, [&] {
             return launch_combine(dxp, slots, nullptr, c.T, c.k, c.d, static_cast<uint16_t*>(dx), s);
@@ -201,7 +201,7 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
     g4.Np = c.d; g4.Nq = 2 * c.I;
     g4.pq = tp; g4.ps = tps; g4.qq = tq; g4.qs = tqs;
     g4.out = static_cast<uint16_t*>(dw13);
-    e = staged(p, MOE_STAGE_WGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_WGRAD, g4, p->num_cu, s); });
+    e = staged(p, MOE_STAGE_WGRAD_W13, s, [&] { return launch_gemm_mxfp8(MX_WGRAD_W13, g4, p->num_cu, s); });
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 }  // namespace
