@@ -714,7 +714,7 @@ def test_mega_decode_graph_replay_and_flags(torch_cuda):
     layer.close()
 
 
-@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "bf16-train"])
+@pytest.mark.parametrize("mode", ["bf16", "mxfp8", "bf16-train", "mxfp8-train"])
 def test_forward_flags_invalid_routing(torch_cuda, mode):
     """A grouped-GEMM call (forward, or forward + backward) whose routing holds
     out-of-range ids flags them and stays in bounds: the dispatch leaves the routed rows
@@ -723,7 +723,7 @@ def test_forward_flags_invalid_routing(torch_cuda, mode):
     layer bit for bit."""
     torch = torch_cuda
     from mixture_experts_routed_dispatch_amd import moe
-    mx, train = mode == "mxfp8", mode == "bf16-train"
+    mx, train = mode.startswith("mxfp8"), mode.endswith("-train")
     inp = inputs.generate(300, 256, 128, 8, 2, "uniform", seed=23, with_dy=train)
     t = device_inputs(inp)
     prec = moe.MOE_MXFP8_E4M3 if mx else moe.MOE_BF16
@@ -731,7 +731,12 @@ def test_forward_flags_invalid_routing(torch_cuda, mode):
     def run(layer, ids):
         if mx:
             w13q, w13s, w2q, w2s = layer.prepare_weights(t["w13"], t["w2"])
-            return [layer.forward(t["x"], ids, t["scores"], w13q, w2q, w13s, w2s)]
+            y = layer.forward(t["x"], ids, t["scores"], w13q, w2q, w13s, w2s)
+            if not train:
+                return [y]
+            w13t, w13ts, w2t, w2ts = layer.prepare_weights_backward(t["w13"], t["w2"])
+            return [y] + list(layer.backward(t["dy"], t["x"], w13q, w2q, w13t=w13t, w13t_scale=w13ts,
+                                             w2t=w2t, w2t_scale=w2ts))
         y = layer.forward(t["x"], ids, t["scores"], t["w13"], t["w2"])
         if not train:
             return [y]
