@@ -29,9 +29,9 @@
 // ascending id, and each expert's entries in ascending (t, j) order).
 //
 // Both products use v_mfma_f32_16x16x32_bf16 with 16 weight rows as the 16 columns
-// and up to 16 routed rows as the 16 rows; lane l loads 16 contiguous bytes of weight
-// row (l & 15) at K offset 32 s + 8 (l >> 4), so one load of a wave covers 64
-// contiguous bytes of 16 rows; kBatch loads are issued before the MFMAs that use them.
+// and up to 16 routed rows as the 16 rows.  The weights stream with nontemporal loads
+// that each cover whole 128-byte lines of 8 rows (mma_line_pairs), kBatch K steps of 32
+// per wave in flight before the MFMAs that use them.
 #include "common.h"
 #include "kernels.h"
 
@@ -135,44 +135,102 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
     return *reinterpret_cast<const bf16x8_t*>(p);
 }
 
-// acc(16 rows x 16 cols) = A * B over K steps 0 .. S - 1 (32 each): B column (l & 15)
-// from wrow (already offset by 8 (l >> 4) elements), A row (l & 15) from arow at the
-// same offset, or zeros when the row is absent.
-template <int B = kBatch>
-__device__ __forceinline__ f32x4_t mma_row_block(const uint16_t* wrow, const uint16_t* arow,
-                                                 bool arow_valid, int S) {
+// acc(16 rows x 16 cols) = A * B over K pairs 0 .. P - 1 (64 elements = 128 bytes of a
+// row each).  The weights stream as whole 128-byte lines with nontemporal loads: per pair
+// a wave issues two loads, X covering B columns 0..7 and Y columns 8..15, in which lane l
+// fetches bytes 16 (l >> 3) of the pair of column row (l & 7) (X) and 8 + (l & 7) (Y); xo
+// and yo are those rows' byte offsets from the bases xb and yb at the wave's first K
+// element (wave-uniform bases and 32-bit lane offsets keep the addresses in few registers).  (Eight rows x 128 bytes per load
+// streams about 15 % faster from HBM than 16 rows x 64 bytes, which is the MFMA's own
+// operand layout.)  The 16x16x32 MFMA wants, in 16-lane group q, column (l & 15) at one
+// 8-element chunk common to the group; X and Y hold chunk 2q in lanes 16q .. 16q + 7 and
+// chunk 2q + 1 in lanes 16q + 8 .. 16q + 15, so a rotate by 8 inside each 16-lane row (DPP
+// row_ror:8) and a select give the two operands: chunk 2q for the first MFMA and 2q + 1
+// for the second.  A row (l & 15) is read at the same chunks through the buffer resource ars at
+// byte offset ao (the routed row at the wave's first K element); a lane whose row is
+// absent passes kNoRow, past the resource's end, and reads zeros without a memory access.
+// (A conditional load with zeros on the other side compiles to a divergent branch whose
+// zero writes wait for every load in flight: one round trip per K pair.)  B pairs are loaded before
+// the MFMAs that use them.
+__device__ __forceinline__ bf16x8_t rotate8_select(bf16x8_t keep, bf16x8_t rot, bool take_rot) {
+    const int4 kv = *reinterpret_cast<const int4*>(&keep);
+    const int4 rv = *reinterpret_cast<const int4*>(&rot);
+    // the rotation runs in every lane (a DPP read of a lane outside the exec mask gives 0)
+    const int4 r = {__builtin_amdgcn_update_dpp(0, rv.x, 0x128, 0xF, 0xF, true),
+                    __builtin_amdgcn_update_dpp(0, rv.y, 0x128, 0xF, 0xF, true),
+                    __builtin_amdgcn_update_dpp(0, rv.z, 0x128, 0xF, 0xF, true),
+                    __builtin_amdgcn_update_dpp(0, rv.w, 0x128, 0xF, 0xF, true)};
+    int4 o;
+    o.x = take_rot ? r.x : kv.x;
+    o.y = take_rot ? r.y : kv.y;
+    o.z = take_rot ? r.z : kv.z;
+    o.w = take_rot ? r.w : kv.w;
+    return *reinterpret_cast<const bf16x8_t*>(&o);
+}
+
+// Raw buffer resource over `bytes` bytes at base (a uniform kernel argument).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kNoRow = 0x80000000u;   // beyond every resource: reads zeros
+
+template <int B = kBatch / 2>
+__device__ __forceinline__ f32x4_t mma_line_pairs(const char* xb, uint32_t xo, const char* yb, uint32_t yo,
+                                                  __amdgpu_buffer_rsrc_t ars, uint32_t ao, int P) {
+    const int lane = threadIdx.x & 63;
+    const bool hi = (lane & 8) != 0;                   // lanes 8..15 of each 16-lane row
+    xo += 16 * (lane >> 3);
+    yo += 16 * (lane >> 3);
+    ao += 32 * (lane >> 4);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const bf16x8_t zero = {};
-    for (int base = 0; base < S; base += B) {
-        bf16x8_t wb[B], xa[B];
+    for (int base = 0; base < P; base += B) {
+        bf16x8_t xw[B], yw[B], a0[B], a1[B];
 #pragma unroll
         for (int j = 0; j < B; ++j) {
-            const int s = base + j;
-            if (s < S) {
-                wb[j] = ld_bf16x8(wrow + 32 * s);
-                xa[j] = arow_valid ? ld_bf16x8(arow + 32 * s) : zero;
+            const uint32_t kb = 128u * (uint32_t)(base + j);
+            if (base + j < P) {
+                xw[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(xb + (xo + kb)));
+                yw[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(yb + (yo + kb)));
+                a0[j] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(ars, ao + kb, 0, 0));
+                a1[j] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(ars, ao + kb + 16, 0, 0));
             }
         }
 #pragma unroll
         for (int j = 0; j < B; ++j)
-            if (base + j < S) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[j], wb[j], acc, 0, 0, 0);
+            if (base + j < P) {
+                // lanes 0..7 of a row: X's own chunk 2q, or X rotated (chunk 2q + 1);
+                // lanes 8..15: Y rotated (chunk 2q), or Y's own chunk 2q + 1
+                const bf16x8_t b0 = rotate8_select(xw[j], yw[j], hi);
+                const bf16x8_t b1 = rotate8_select(yw[j], xw[j], !hi);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[j], b0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[j], b1, acc, 0, 0, 0);
+            }
     }
     return acc;
 }
 
+// One token: the k expert ids into sm.slot_expert (the slots are the entries), so that
+// an item reads its expert from LDS and not from global memory, whose wait would also
+// wait for the previous item's stores.
+__device__ __forceinline__ void one_token_slots(DecodeSmem& sm, const DecodeArgs& g) {
+    if ((int)threadIdx.x < g.k) sm.slot_expert[threadIdx.x] = g.ids[threadIdx.x];
+    __syncthreads();
+}
+
 // The expert, routed-row count and first entry of active slot `slot`; false when the
-// slot's expert id is invalid (one-token path: the slot is the entry itself).
+// slot's expert id is invalid (one-token path: the slot is the entry itself).  The values
+// are uniform over the wave (the workgroup, with a K split), and kept in scalar registers.
 __device__ __forceinline__ bool slot_info(const DecodeArgs& g, const DecodeSmem& sm, bool one, int slot,
                                           int& e, int& M, int& e0) {
     if (one) {
-        e = g.ids[slot];
+        e = __builtin_amdgcn_readfirstlane(sm.slot_expert[slot]);
         M = 1;
         e0 = slot;
         return (unsigned)e < (unsigned)g.E;
     }
-    e = sm.slot_expert[slot];
-    e0 = sm.pfx[e];
-    M = sm.pfx[e + 1] - e0;
+    e = __builtin_amdgcn_readfirstlane(sm.slot_expert[slot]);
+    e0 = __builtin_amdgcn_readfirstlane(sm.pfx[e]);
+    M = __builtin_amdgcn_readfirstlane(sm.pfx[e + 1]) - e0;
     return true;
 }
 
@@ -183,23 +241,25 @@ __device__ __forceinline__ bool slot_info(const DecodeArgs& g, const DecodeSmem&
 template <bool kSplit, class F>
 __device__ __forceinline__ void for_items(int items, int nblk, F f) {
     const int nw = kSplit ? (int)gridDim.x : (int)gridDim.x * kWaves;
-    const int first = kSplit ? (int)blockIdx.x : (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+    const int first = kSplit ? (int)blockIdx.x
+                             : (int)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    items = __builtin_amdgcn_readfirstlane(items);
     for (int item = first; item < items; item += nw) {
         const int slot = item / nblk;
         f(slot, item - slot * nblk);
     }
 }
 
-// K split: wave w takes steps [S w / 4, S (w + 1) / 4) of the S steps of 32.
+// K split: wave w takes pairs [P w / 4, P (w + 1) / 4) of the P pairs of 64 elements.
 template <bool kSplit>
-__device__ __forceinline__ void wave_steps(int S, int& s0, int& s1) {
+__device__ __forceinline__ void wave_pairs(int P, int& p0, int& p1) {
     if (kSplit) {
         const int w = threadIdx.x >> 6;
-        s0 = S * w / kWaves;
-        s1 = S * (w + 1) / kWaves;
+        p0 = P * w / kWaves;
+        p1 = P * (w + 1) / kWaves;
     } else {
-        s0 = 0;
-        s1 = S;
+        p0 = 0;
+        p1 = P;
     }
 }
 
@@ -234,27 +294,29 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
     int items;
     if (one) {
         if (blockIdx.x == 0) decode_flags_one_token(g);
+        one_token_slots(sm, g);
         items = k * nIB;
     } else {
         decode_setup(sm, g.ids, g.T, k, g.E, g.status, blockIdx.x == 0);
         items = sm.n_active * nIB;
     }
-    int s0, s1;
-    wave_steps<kSplit>(d / 32, s0, s1);
+    int p0, p1;
+    wave_pairs<kSplit>(d / 64, p0, p1);
     for_items<kSplit>(items, nIB, [&](int slot, int ib) {
         int e, M, e0;
         if (!slot_info(g, sm, one, slot, e, M, e0)) return;
         auto entry = [&](int m) { return one ? e0 : sm.ent[e0 + m]; };
         const int i0 = ib * 8;
-        // columns 0..7: gate rows i0..i0+7; columns 8..15: up rows I+i0..I+i0+7
-        const int wrow = (n < 8) ? (i0 + n) : (I + i0 + n - 8);
-        const uint16_t* wp = g.w13 + ((size_t)e * 2 * I + wrow) * d + 8 * kq;
+        // columns 0..7: gate rows i0..i0+7 (X); columns 8..15: up rows I+i0..I+i0+7 (Y)
+        const char* wb = reinterpret_cast<const char*>(g.w13 + ((size_t)e * 2 * I + i0) * d);
+        const uint32_t xo = (uint32_t)((lane & 7) * d + 64 * p0) * 2u;
+        const uint32_t yo = xo + (uint32_t)I * (uint32_t)d * 2u;
         for (int m0 = 0; m0 < M; m0 += 16) {
             const int m = m0 + n;
             const bool mv = m < M;
-            const int tok = mv ? entry(m) / k : 0;
+            const uint32_t xoff = mv ? (uint32_t)((entry(m) / k) * d + 64 * p0) * 2u : kNoRow;
             const f32x4_t acc = reduce_waves<kSplit>(
-                mma_row_block(wp + 32 * s0, g.x + (size_t)tok * d + 8 * kq + 32 * s0, mv, s1 - s0), red, par);
+                mma_line_pairs(wb, xo, wb, yo, rows_rsrc(g.x, (uint32_t)g.T * d * 2u), xoff, p1 - p0), red, par);
             // lane l holds rows 4 kq + z of column n; the up value of gate column c < 8
             // sits in lane l + 8 of the same 16-lane group
             float up[4];
@@ -285,24 +347,28 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
     const bool one = g.T == 1;
     int items;
     if (one) {
+        one_token_slots(sm, g);
         items = k * nNB;
     } else {
         decode_setup(sm, g.ids, g.T, k, g.E, g.status, false);
         items = sm.n_active * nNB;
     }
-    int s0, s1;
-    wave_steps<kSplit>(I / 32, s0, s1);
+    int p0, p1;
+    wave_pairs<kSplit>(I / 64, p0, p1);
     for_items<kSplit>(items, nNB, [&](int slot, int nb) {
         int e, M, e0;
         if (!slot_info(g, sm, one, slot, e, M, e0)) return;
         auto entry = [&](int m) { return one ? e0 : sm.ent[e0 + m]; };
         const int n0 = nb * 16;
-        const uint16_t* wp = g.w2 + ((size_t)e * d + n0 + n) * I + 8 * kq;
+        const char* wb = reinterpret_cast<const char*>(g.w2 + ((size_t)e * d + n0) * I);
+        const uint32_t xo = (uint32_t)((lane & 7) * I + 64 * p0) * 2u;                   // columns 0..7
+        const uint32_t yo = xo + (uint32_t)I * 16u;                                        // columns 8..15
         for (int m0 = 0; m0 < M; m0 += 16) {
             const int m = m0 + n;
             const bool mv = m < M;
-            const uint16_t* ap = g.a + (size_t)(mv ? entry(m) : 0) * I + 8 * kq;
-            const f32x4_t acc = reduce_waves<kSplit>(mma_row_block(wp + 32 * s0, ap + 32 * s0, mv, s1 - s0), red, par);
+            const uint32_t ao = mv ? (uint32_t)(entry(m) * I + 64 * p0) * 2u : kNoRow;
+            const f32x4_t acc = reduce_waves<kSplit>(
+                mma_line_pairs(wb, xo, wb, yo, rows_rsrc(g.a, (uint32_t)(g.T * k) * I * 2u), ao, p1 - p0), red, par);
             if (lead) {
 #pragma unroll
                 for (int z = 0; z < 4; ++z) {
@@ -321,8 +387,8 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
 // of W2 of expert 2p, columns 8..15 the same rows of expert 2p + 1, A row 0 is a_2p and
 // row 1 is a_2p+1, so D[0][c] and D[1][8 + c] are the two experts' outputs.  Wave w takes
 // the pairs w, w + 4, ...; an invalid expert id contributes 0.  One workgroup per CU (d / 8
-// of them), each wave loading 24 K steps at once: at K = I = 768 its whole pair in one
-// round trip.
+// of them), each wave loading 12 K pairs (768 elements) at once: at K = I = 768 its whole
+// pair of experts in one round trip.
 __global__ __launch_bounds__(kThreads, 1) void decode_w2_one(DecodeArgs g) {
     __shared__ float ov[kMaxTopK][8];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -333,13 +399,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_w2_one(DecodeArgs g) {
     for (int nb = blockIdx.x; nb < d / 8; nb += gridDim.x) {
         const int n0 = nb * 8;
         for (int p = wave; p < npair; p += kWaves) {
-            const int jc = 2 * p + (n >> 3);               // expert slot of B column n
-            const int ec = valid(jc) ? g.ids[jc] : 0;
-            const uint16_t* wp = g.w2 + ((size_t)ec * d + n0 + (n & 7)) * I + 8 * kq;
+            // B columns 0..7 (X): expert slot 2p; columns 8..15 (Y): slot 2p + 1
+            const int ex = valid(2 * p) ? g.ids[2 * p] : 0;
+            const int ey = valid(2 * p + 1) ? g.ids[2 * p + 1] : 0;
+            const char* xb = reinterpret_cast<const char*>(g.w2 + ((size_t)ex * d + n0) * I);
+            const char* yb = reinterpret_cast<const char*>(g.w2 + ((size_t)ey * d + n0) * I);
+            const uint32_t wo = (uint32_t)((lane & 7) * I) * 2u;
             const int jr = 2 * p + n;                       // expert slot of A row n (rows 0, 1)
             const bool rv = n < 2 && valid(jr);
-            const uint16_t* ap = g.a + (size_t)(rv ? jr : 0) * I + 8 * kq;
-            const f32x4_t acc = mma_row_block<24>(wp, ap, rv, I / 32);
+            const uint32_t ao = rv ? (uint32_t)(jr * I) * 2u : kNoRow;
+            const f32x4_t acc = mma_line_pairs<12>(xb, wo, yb, wo, rows_rsrc(g.a, (uint32_t)k * I * 2u), ao, I / 64);
             // lanes with kq = 0 hold rows 0..3 of column n
             if (kq == 0) {
                 if (n < 8 && 2 * p < k) ov[2 * p][n] = valid(2 * p) ? acc[0] : 0.f;
@@ -399,6 +468,7 @@ __global__ __launch_bounds__(kMegaThreads, 1) void mega_decode(DecodeArgs g, flo
     int items;
     if (one) {
         if (blockIdx.x == 0 && tid < kThreads) decode_flags_one_token(g);
+        one_token_slots(sm, g);
         items = k * C;
     } else {
         decode_setup(sm, g.ids, g.T, k, g.E, g.status, blockIdx.x == 0);
