@@ -687,80 +687,93 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             // LDS (16-byte chunk c of row q at slot c ^ (q & 15)) so that each lane then owns
             // 8 consecutive columns of one row: h is read and dh written in 16-byte row
             // pieces (8-byte pieces of 32 rows per instruction cost about 40k cycles per
-            // tile each way).  The h loads of a half block are issued before its staging.
+            // tile each way).  The h loads (and probs) of the next half block are issued
+            // before the current one is staged, computed and stored, so that the eight
+            // half blocks do not wait for eight memory round trips in turn.
+            auto load_h = [&](int hb, uint4 hg[4], uint4 hu[4], float sc[4]) {
+                const int b = hb >> 1, ah = hb & 1;
+                const int i0 = c.pt * TP + wp * 128 + 64 * ah + 8 * (ln & 7);
+                const int ic = i0 < g.I ? i0 : g.I - 8;
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+                for (int it = 0; it < 4; ++it) {
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + 8 * it + (ln >> 3);
+                    const size_t r = (size_t)c.mb + (rr < c.rows ? rr : c.rows - 1);
+                    hg[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + ic);
+                    hu[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + g.I + ic);
+                    sc[it] = g.probs[r];
+                }
+            };
+            auto half_block = [&](int hb, const uint4 hg[4], const uint4 hu[4], const float sc[4]) {
+                const int b = hb >> 1, ah = hb & 1;
+                const int i0 = c.pt * TP + wp * 128 + 64 * ah + 8 * (ln & 7);   // this lane's 8 columns
 #pragma unroll
-                for (int ah = 0; ah < 2; ++ah) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    const int i0 = c.pt * TP + wp * 128 + 64 * ah + 8 * (ln & 7);   // this lane's 8 columns
-                    const int ic = i0 < g.I ? i0 : g.I - 8;
-                    uint4 hg[4], hu[4];
-                    float sc[4];
+                for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int rr = c.qt * TQ + wq * 128 + b * 32 + 8 * it + (ln >> 3);
-                        const size_t r = (size_t)c.mb + (rr < c.rows ? rr : c.rows - 1);
-                        hg[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + ic);
-                        hu[it] = *reinterpret_cast<const uint4*>(g.h + r * 2 * g.I + g.I + ic);
-                        sc[it] = g.probs[r];
+                    for (int grp = 0; grp < 4; ++grp) {
+                        const int c16 = (32 * a2 + 8 * grp + p_sub) >> 2;
+                        const int a = 2 * ah + a2;
+                        f32x4_t v = {acc[a][b][4 * grp], acc[a][b][4 * grp + 1], acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]};
+                        *reinterpret_cast<f32x4_t*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4)) = v;
                     }
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own LDS writes are done
+                f32x4_t sv[8];
 #pragma unroll
-                    for (int a2 = 0; a2 < 2; ++a2)
+                for (int it = 0; it < 4; ++it) {
+                    const int row = 8 * it + (ln >> 3), c8 = ln & 7;
+                    sv[2 * it] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8) ^ (row & 15)) << 4));
+                    sv[2 * it + 1] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4));
+                }
+                lds_values_ready(sv);
 #pragma unroll
-                        for (int grp = 0; grp < 4; ++grp) {
-                            const int c16 = (32 * a2 + 8 * grp + p_sub) >> 2;
-                            const int a = 2 * ah + a2;
-                            f32x4_t v = {acc[a][b][4 * grp], acc[a][b][4 * grp + 1], acc[a][b][4 * grp + 2], acc[a][b][4 * grp + 3]};
-                            *reinterpret_cast<f32x4_t*>(stg + q_in * 256 + ((c16 ^ (q_in & 15)) << 4)) = v;
-                        }
-                    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the wave's own LDS writes are done
-                    f32x4_t sv[8];
+                for (int it = 0; it < 4; ++it) {
+                    const int row = 8 * it + (ln >> 3);
+                    const f32x4_t v0 = sv[2 * it], v1 = sv[2 * it + 1];
+                    const float av[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    const uint32_t gw[4] = {hg[it].x, hg[it].y, hg[it].z, hg[it].w};
+                    const uint32_t uw[4] = {hu[it].x, hu[it].y, hu[it].z, hu[it].w};
+                    uint32_t og[4], ou[4];
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int row = 8 * it + (ln >> 3), c8 = ln & 7;
-                        sv[2 * it] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8) ^ (row & 15)) << 4));
-                        sv[2 * it + 1] = *reinterpret_cast<const f32x4_t*>(stg + row * 256 + (((2 * c8 + 1) ^ (row & 15)) << 4));
-                    }
-                    lds_values_ready(sv);
+                    for (int z = 0; z < 4; ++z) {
+                        float dg2[2], du2[2];
 #pragma unroll
-                    for (int it = 0; it < 4; ++it) {
-                        const int row = 8 * it + (ln >> 3);
-                        const f32x4_t v0 = sv[2 * it], v1 = sv[2 * it + 1];
-                        const float av[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                        const uint32_t gw[4] = {hg[it].x, hg[it].y, hg[it].z, hg[it].w};
-                        const uint32_t uw[4] = {hu[it].x, hu[it].y, hu[it].z, hu[it].w};
-                        uint32_t og[4], ou[4];
-#pragma unroll
-                        for (int z = 0; z < 4; ++z) {
-                            float dg2[2], du2[2];
-#pragma unroll
-                            for (int h2 = 0; h2 < 2; ++h2) {
-                                const float gv = h2 ? bf16hi(gw[z]) : bf16lo(gw[z]);
-                                const float uv = h2 ? bf16hi(uw[z]) : bf16lo(uw[z]);
-                                const float dA = sc[it] * av[2 * z + h2];
-                                if constexpr (kAct == kActSwiGLU) {
-                                    const float sg = sigmoid_f(gv);
-                                    dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
-                                    du2[h2] = dA * gv * sg;
-                                } else {
-                                    float f, df;
-                                    act_f_df<kAct>(gv, f, df);
-                                    dg2[h2] = dA * uv * df;
-                                    du2[h2] = dA * f;
-                                }
+                        for (int h2 = 0; h2 < 2; ++h2) {
+                            const float gv = h2 ? bf16hi(gw[z]) : bf16lo(gw[z]);
+                            const float uv = h2 ? bf16hi(uw[z]) : bf16lo(uw[z]);
+                            const float dA = sc[it] * av[2 * z + h2];
+                            if constexpr (kAct == kActSwiGLU) {
+                                const float sg = sigmoid_f(gv);
+                                dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
+                                du2[h2] = dA * gv * sg;
+                            } else {
+                                float f, df;
+                                act_f_df<kAct>(gv, f, df);
+                                dg2[h2] = dA * uv * df;
+                                du2[h2] = dA * f;
                             }
-                            og[z] = pack_bf16(dg2[0], dg2[1]);
-                            ou[z] = pack_bf16(du2[0], du2[1]);
                         }
-                        const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
-                        if (rr < c.rows && i0 < g.I) {
-                            const size_t r = (size_t)c.mb + rr;
-                            *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + i0) = make_uint4(og[0], og[1], og[2], og[3]);
-                            *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + g.I + i0) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
-                        }
+                        og[z] = pack_bf16(dg2[0], dg2[1]);
+                        ou[z] = pack_bf16(du2[0], du2[1]);
+                    }
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + row;
+                    if (rr < c.rows && i0 < g.I) {
+                        const size_t r = (size_t)c.mb + rr;
+                        *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + i0) = make_uint4(og[0], og[1], og[2], og[3]);
+                        *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + g.I + i0) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
                     }
                 }
+            };
+            uint4 hg0[4], hu0[4], hg1[4], hu1[4];
+            float sc0[4], sc1[4];
+            load_h(0, hg0, hu0, sc0);
+#pragma unroll
+            for (int hb = 0; hb < 8; hb += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_h(hb + 1, hg1, hu1, sc1);
+                half_block(hb, hg0, hu0, sc0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (hb + 2 < 8) load_h(hb + 2, hg0, hu0, sc0);
+                half_block(hb + 1, hg1, hu1, sc1);
+            }
         } else {
             // weight gradients: out[e][q][p], q < Qsz rows, p < Psz columns
             const int Psz = (MODE == WGRAD_W2) ? g.I : g.d;
