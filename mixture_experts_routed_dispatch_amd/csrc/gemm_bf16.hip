@@ -438,6 +438,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
     // wait until at most one stage (8 copies) of this wave's copies is outstanding
     auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
+    constexpr bool kEarlyWait = MODE == FWD_W13 || MODE == DGRAD_W2;   // see the stage stream
     // ------------------------------------------------------------ fragments
     // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
     // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
@@ -765,6 +766,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             uint4 hg0[4], hu0[4], hg1[4], hu1[4];
             float sc0[4], sc1[4];
             load_h(0, hg0, hu0, sc0);
+            // every copy issued before these 12 loads has landed (kEarlyWait)
+            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 #pragma unroll
             for (int hb = 0; hb < 8; hb += 2) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -882,9 +885,16 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
             advance_load();
-            wait_dma();                // this wave's copies of stage gs + 2 have landed
+            // this wave's copies of stage gs + 2 have landed.  FWD_W13 and DGRAD_W2: in the
+            // first stage of a tile they already had, since they were issued before the
+            // previous tile's epilogue, which waits for every copy before its first store
+            // (DGRAD_W2 after issuing its first h loads); a wait here would count the
+            // epilogue's stores too and hold the stage until they are written (DGRAD_W2
+            // 313 -> 274 us at the training shape; the other modes gain nothing).
+            if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
             __syncthreads();
         }
+        if constexpr (MODE == FWD_W13) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (!kRagged || cc.np == 1) epilogue(cc, (gs - 1) & 3);
         else store_piece(cc);
         if (++c_item >= n_items) break;
