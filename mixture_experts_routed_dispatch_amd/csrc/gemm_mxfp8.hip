@@ -94,6 +94,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
     __shared__ int wtot[NTHR / MOE_WAVE];
     __shared__ int worder[256], wkp[256], wkoff[256];   // MX_WGRAD: work order, padded rows, offsets
     constexpr bool kWgrad = MODE == MX_WGRAD;
+    // W13 and the weight gradients: the next tile's first stage skips its wait (below)
+    constexpr bool kEarlyWait = MODE == MX_W13 || MODE == MX_WGRAD;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -589,7 +591,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
             // (odd: no scales)
             stage(std::integral_constant<int, 0>(), pa, qa, spa, sqa, (gs + 1) & 3, pb, qb, l_kt, (gs + 3) & 3);
             advance_load();
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            // stage gs + 2 has landed; in a tile's first stage it already had (kEarlyWait)
+            if (!kEarlyWait || kt != 0 || c_tile == vid) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
             __syncthreads();
             // odd stage gs + 1: fragments (pb, qb), scale byte 2; copies of stage gs + 4
             // after the scale words of the pair it starts; the next pair's scale words
@@ -603,6 +606,10 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm_mx(MxGemmArgs g) {
 #pragma unroll
             for (int b = 0; b < 4; ++b) { spa[b] = spb[b]; sqa[b] = sqb[b]; }
         }
+        // kEarlyWait: every copy issued so far lands before the epilogue's first store, so
+        // that the next tile's first stage need not wait: its wait would count the
+        // epilogue's stores and hold the stage until they are written
+        if constexpr (kEarlyWait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         epilogue(cc, (gs - 1) & 3);
         c_tile += G;
         if (c_tile >= total) break;
