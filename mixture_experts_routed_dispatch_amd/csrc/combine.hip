@@ -128,45 +128,51 @@ __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __
 }
 
 // Row-major operands of the weight-gradient products: xg[r] = x[gather[r]] and
-// dys[r] = bf16(probs[r] * dy[gather[r]]) for routed rows r.  One workgroup per row
-// (grid-strided), one 16-byte chunk of each per thread.  Entries of gather past the
-// routed count (left unwritten by the dispatch for invalid expert ids) are read clamped
-// to token 0; the products read only the rows of their experts.
+// dys[r] = bf16(probs[r] * dy[gather[r]]) for routed rows r.  Token-major: one
+// workgroup per token t (grid-strided) reads x[t] and dy[t] once, one 16-byte chunk
+// of each per thread, and writes them to the token's routed rows r = slots[t][j].  A
+// row is written only when gather[r] == t: an entry with an invalid expert id has slot
+// 0, and passes that test only if row 0 is the same token's, where it writes what row
+// 0's own entry writes.  Rows past the routed count stay unwritten; the products read
+// only the rows of their experts.  (Row-major in r, the k reads of each token lay far
+// apart in time and missed in L2: 537 MB fetched for 67 MB of x and dy.)
 __global__ __launch_bounds__(kThreads) void wgrad_rows_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ dy,
+                                                              const int32_t* __restrict__ slots,
                                                               const int32_t* __restrict__ gather,
                                                               const float* __restrict__ probs,
-                                                              int64_t R, int d, uint32_t T,
+                                                              int T, int k, int d,
                                                               uint16_t* __restrict__ xg,
                                                               uint16_t* __restrict__ dys) {
-    for (int64_t r = blockIdx.x; r < R; r += gridDim.x) {
-        uint32_t tu = (uint32_t)gather[r];
-        if (tu >= T) tu = 0;
-        const size_t t = tu;
-        const float sc = probs[r];
+    for (int t = blockIdx.x; t < T; t += gridDim.x) {
         for (int n = threadIdx.x * 8; n < d; n += kThreads * 8) {
-            const uint4 xv = *reinterpret_cast<const uint4*>(x + t * d + n);
-            const uint4 gv = *reinterpret_cast<const uint4*>(dy + t * d + n);
+            const uint4 xv = *reinterpret_cast<const uint4*>(x + (size_t)t * d + n);
+            const uint4 gv = *reinterpret_cast<const uint4*>(dy + (size_t)t * d + n);
             const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-            uint32_t ow[4];
+            for (int j = 0; j < k; ++j) {
+                const int r = slots[(size_t)t * k + j];
+                if (gather[r] != t) continue;
+                const float sc = probs[r];
+                uint32_t ow[4];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) ow[z] = pack_bf16(sc * bf16lo(gw[z]), sc * bf16hi(gw[z]));
-            *reinterpret_cast<uint4*>(xg + (size_t)r * d + n) = xv;
-            *reinterpret_cast<uint4*>(dys + (size_t)r * d + n) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+                for (int z = 0; z < 4; ++z) ow[z] = pack_bf16(sc * bf16lo(gw[z]), sc * bf16hi(gw[z]));
+                *reinterpret_cast<uint4*>(xg + (size_t)r * d + n) = xv;
+                *reinterpret_cast<uint4*>(dys + (size_t)r * d + n) = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+            }
         }
     }
 }
 
 }  // namespace
 
-hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, int T, const int32_t* gather,
-                             const float* probs, int64_t R, int d, uint16_t* xg, uint16_t* dys,
+hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, int T, int k, const int32_t* slots,
+                             const int32_t* gather, const float* probs, int d, uint16_t* xg, uint16_t* dys,
                              hipStream_t s) {
-    if (R == 0) return hipSuccess;
-    if (T <= 0) return hipErrorInvalidValue;
-    const int64_t grid = R < 65536 ? R : 65536;
-    hipLaunchKernelGGL(wgrad_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, dy, gather,
-                       probs, R, d, (uint32_t)T, xg, dys);
+    if (T == 0 || k == 0) return hipSuccess;
+    if (T < 0 || k < 0 || d % 8 != 0) return hipErrorInvalidValue;
+    const int grid = T < 65536 ? T : 65536;
+    hipLaunchKernelGGL(wgrad_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, x, dy, slots, gather,
+                       probs, T, k, d, xg, dys);
     return hipGetLastError();
 }
 

@@ -136,10 +136,10 @@ hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_
                              int k, int d, float* ds, hipStream_t s);
 
 // Operands of the weight gradients: xg[r] = x[gather[r]], dys[r] = bf16(probs[r] *
-// dy[gather[r]]), both [R, d]; x and dy have T rows, gather entries outside [0, T)
-// read row 0.
-hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, int T, const int32_t* gather,
-                             const float* probs, int64_t R, int d, uint16_t* xg, uint16_t* dys,
+// dy[gather[r]]), both [R, d], for the routed rows r = slots[t][j] of valid entries
+// (gather[r] == t); other rows are left as they are.
+hipError_t launch_wgrad_rows(const uint16_t* x, const uint16_t* dy, int T, int k, const int32_t* slots,
+                             const int32_t* gather, const float* probs, int d, uint16_t* xg, uint16_t* dys,
                              hipStream_t s);
 
 // Small-batch (decode) path: T*k <= kMaxDecodeRows routed entries, E <= 256.

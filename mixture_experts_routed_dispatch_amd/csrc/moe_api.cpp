@@ -778,7 +778,7 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
         e = staged(p, MOE_STAGE_WGRAD_ROWS, s, [&] {
-            return launch_wgrad_rows(g.x, g.dy, c.T, g.gather, g.probs, p->R, c.d, p->at<uint16_t>(p->off_xg),
+            return launch_wgrad_rows(g.x, g.dy, c.T, c.k, slots, g.gather, g.probs, c.d, p->at<uint16_t>(p->off_xg),
                                      p->at<uint16_t>(p->off_dys), s);
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
