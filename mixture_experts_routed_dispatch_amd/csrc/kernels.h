@@ -105,10 +105,12 @@ constexpr int kMxWgradPad = 128;
 
 // MXFP8 quantization for the backward (OCP MX blocks of 32, the same scale rule as
 // launch_quantize_mxfp8):
-// rows r < R of probs[r] * dy[gather[r]] along d: codes [R][d], block-major scales
-// [d/128][R][4] (gather entries outside [0, T) read row 0)
-hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, const int32_t* gather, const float* probs,
-                                 int64_t R, int d, uint8_t* codes, uint8_t* scales, hipStream_t s);
+// the routed rows r = slots[t][j] (valid entries: gather[r] == t) of probs[r] *
+// dy[gather[r]] along d: codes [R][d], block-major scales [d/128][R][4]; other rows are
+// left as they are
+hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, int k, const int32_t* slots, const int32_t* gather,
+                                 const float* probs, int64_t R, int d, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s);
 // SwiGLU (GeGLU, ReGLU) backward of MXFP8 training: dg = dA u f'(g), du = dA f(g) from dA
 // [R][I] and h = (g, u) [R][2I] (BF16); dh = (dg, du) in BF16 [R][2I] and quantized along
 // 2I: codes [R][2I], block-major scales [2I/128][R][4]

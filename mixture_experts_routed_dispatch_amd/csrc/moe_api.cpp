@@ -150,7 +150,7 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
         uint8_t* dhq = p->at<uint8_t>(p->off_dhq);
         uint8_t* dhs = p->at<uint8_t>(p->off_dhs);
         e = staged(p, MOE_STAGE_QUANT_DO, s, [&] {
-            return launch_mx_scaled_rows(dy16, c.T, gather, probs, R, c.d, doq, dos, s);
+            return launch_mx_scaled_rows(dy16, c.T, c.k, slots, gather, probs, R, c.d, doq, dos, s);
         });
         if (e != hipSuccess) return MOE_ERR_HIP;
         // dA [R, I] = dO W2_e: P = W2_e^T [I, d] blocked along d

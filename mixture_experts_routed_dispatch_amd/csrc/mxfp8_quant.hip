@@ -126,37 +126,47 @@ __device__ __forceinline__ int64_t bm_index(int64_t R, int64_t r, int kb) {
     return ((int64_t)(kb >> 2) * R + r) * 4 + (kb & 3);
 }
 
-// dO of the MXFP8 backward: rows probs[r] * dy[gather[r]] (FP32) quantized along d; one
-// thread per (row, block of 32)
-__global__ __launch_bounds__(kThreads) void mx_scaled_rows_kernel(const uint16_t* __restrict__ dy, int T,
+// dO of the MXFP8 backward: rows r of probs[r] * dy[gather[r]] (FP32) quantized along d.
+// Token-major: one wave per token t (grid-strided), lane = block of 32 along d, reads dy[t]
+// once and quantizes it for each of the token's routed rows r = slots[t][j] with
+// gather[r] == t (an entry with an invalid expert id has slot 0 and passes only if row 0
+// is the same token's, where it writes what row 0's own entry writes).  Rows past the
+// routed count stay unwritten; the products read only the rows of their experts.
+// (Row-major, the k reads of each token lay far apart in time and missed in L2.)
+__global__ __launch_bounds__(kThreads) void mx_scaled_rows_kernel(const uint16_t* __restrict__ dy, int T, int k,
+                                                                  const int32_t* __restrict__ slots,
                                                                   const int32_t* __restrict__ gather,
                                                                   const float* __restrict__ probs, int64_t R, int d,
                                                                   uint8_t* __restrict__ codes,
                                                                   uint8_t* __restrict__ scales) {
     const int kb_row = d / 32;
-    const int64_t nb = R * kb_row;
-    for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nb; b += (int64_t)gridDim.x * kThreads) {
-        const int64_t r = b / kb_row;
-        const int kb = (int)(b - r * kb_row);
-        uint32_t tok = (uint32_t)gather[r];
-        if (tok >= (uint32_t)T) tok = 0;
-        const float pr = probs[r];
-        const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)tok * d + 32 * kb);
-        float v[32];
+    const int lane = threadIdx.x % MOE_WAVE;
+    const int nw = gridDim.x * (kThreads / MOE_WAVE);
+    for (int t = blockIdx.x * (kThreads / MOE_WAVE) + (int)(threadIdx.x / MOE_WAVE); t < T; t += nw) {
+        for (int kb = lane; kb < kb_row; kb += MOE_WAVE) {
+            const uint4* src = reinterpret_cast<const uint4*>(dy + (int64_t)t * d + 32 * kb);
+            uint32_t w[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint4 q = src[c];
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            for (int c = 0; c < 4; ++c) {
+                const uint4 q = src[c];
+                w[4 * c] = q.x; w[4 * c + 1] = q.y; w[4 * c + 2] = q.z; w[4 * c + 3] = q.w;
+            }
+            for (int j = 0; j < k; ++j) {
+                const int64_t r = slots[(int64_t)t * k + j];
+                if (gather[r] != t) continue;
+                const float pr = probs[r];
+                float v[32];
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-                v[8 * c + 2 * z] = pr * bf16lo(w[z]);
-                v[8 * c + 2 * z + 1] = pr * bf16hi(w[z]);
+                for (int z = 0; z < 16; ++z) {
+                    v[2 * z] = pr * bf16lo(w[z]);
+                    v[2 * z + 1] = pr * bf16hi(w[z]);
+                }
+                uint32_t out[8];
+                const uint32_t sb = quant_block32(v, out);
+                store_codes32(codes + r * d + 32 * kb, out);
+                scales[bm_index(R, r, kb)] = (uint8_t)sb;
             }
         }
-        uint32_t out[8];
-        const uint32_t sb = quant_block32(v, out);
-        store_codes32(codes + r * d + 32 * kb, out);
-        scales[bm_index(R, r, kb)] = (uint8_t)sb;
     }
 }
 
@@ -386,15 +396,16 @@ hipError_t launch_quantize_mxfp8(const uint16_t* v, int64_t rows, int K, uint8_t
     return hipGetLastError();
 }
 
-hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, const int32_t* gather, const float* probs,
-                                 int64_t R, int d, uint8_t* codes, uint8_t* scales, hipStream_t s) {
-    if (d % 128 != 0) return hipErrorInvalidValue;
-    const int64_t nb = R * (d / 32);
-    if (nb == 0) return hipSuccess;
-    int64_t grid = (nb + kThreads - 1) / kThreads;
+hipError_t launch_mx_scaled_rows(const uint16_t* dy, int T, int k, const int32_t* slots, const int32_t* gather,
+                                 const float* probs, int64_t R, int d, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t s) {
+    if (d % 128 != 0 || T < 0 || k < 0) return hipErrorInvalidValue;
+    if (T == 0 || k == 0 || R == 0) return hipSuccess;
+    constexpr int kWavesPerBlock = kThreads / MOE_WAVE;
+    int64_t grid = ((int64_t)T + kWavesPerBlock - 1) / kWavesPerBlock;
     if (grid > 65536) grid = 65536;
-    hipLaunchKernelGGL(mx_scaled_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, dy, T, gather, probs, R, d,
-                       codes, scales);
+    hipLaunchKernelGGL(mx_scaled_rows_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, dy, T, k, slots, gather,
+                       probs, R, d, codes, scales);
     return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ hipError_t launch_quantize_mxfp8(const uint16_t*, int64_t, int, uint8_t*, uint8_
 hipError_t launch_route_scales(const uint8_t*, int64_t, const int32_t*, int64_t, int, uint8_t*, hipStream_t) {
     return hipErrorInvalidValue;
 }
-hipError_t launch_mx_scaled_rows(const uint16_t*, int, const int32_t*, const float*, int64_t, int, uint8_t*,
-                                 uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_mx_scaled_rows(const uint16_t*, int, int, const int32_t*, const int32_t*, const float*, int64_t,
+                                 int, uint8_t*, uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mx_act_backward(const uint16_t*, const uint16_t*, int64_t, int, int, uint16_t*, uint8_t*,
                                   uint8_t*, hipStream_t) { return hipErrorInvalidValue; }
 hipError_t launch_mx_transpose_quant(const uint16_t*, int, int, int, const int32_t*, const int32_t*, const float*,
