@@ -766,8 +766,6 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             uint4 hg0[4], hu0[4], hg1[4], hu1[4];
             float sc0[4], sc1[4];
             load_h(0, hg0, hu0, sc0);
-            // every copy issued before these 12 loads has landed (kEarlyWait)
-            asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
 #pragma unroll
             for (int hb = 0; hb < 8; hb += 2) {
                 __builtin_amdgcn_sched_barrier(0);
@@ -887,14 +885,14 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             advance_load();
             // this wave's copies of stage gs + 2 have landed.  FWD_W13 and DGRAD_W2: in the
             // first stage of a tile they already had, since they were issued before the
-            // previous tile's epilogue, which waits for every copy before its first store
-            // (DGRAD_W2 after issuing its first h loads); a wait here would count the
-            // epilogue's stores too and hold the stage until they are written (DGRAD_W2
-            // 313 -> 274 us at the training shape; the other modes gain nothing).
+            // previous tile's epilogue, which waits for every copy before it starts; a wait
+            // here would count the epilogue's stores too and hold the stage until they are
+            // written (DGRAD_W2 313 -> 274 us at the training shape; the other modes gain
+            // nothing).
             if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
             __syncthreads();
         }
-        if constexpr (MODE == FWD_W13) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (kEarlyWait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (!kRagged || cc.np == 1) epilogue(cc, (gs - 1) & 3);
         else store_piece(cc);
         if (++c_item >= n_items) break;
