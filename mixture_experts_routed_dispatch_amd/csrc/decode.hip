@@ -24,9 +24,10 @@
 // empty); the second for short K (W2 at 32 tokens, K = I = 768).
 //
 // With one token the experts are the k ids themselves (distinct by the layer's
-// precondition), and the W2 products and the combine are one launch (decode_w2_one).  With more tokens every workgroup first sorts the routed entries by
-// expert in LDS (counts, their prefix over the expert ids, the active experts in
-// ascending id, and each expert's entries in ascending (t, j) order).
+// precondition), and the W2 products and the combine are one launch (decode_w2_one).
+// With more tokens every workgroup first sorts the routed entries by expert in LDS
+// (counts, their prefix over the expert ids, the active experts in ascending id, and
+// each expert's entries in ascending (t, j) order).
 //
 // Both products use v_mfma_f32_16x16x32_bf16 with 16 weight rows as the 16 columns
 // and up to 16 routed rows as the 16 rows.  The weights stream with nontemporal loads
@@ -136,22 +137,23 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
 }
 
 // acc(16 rows x 16 cols) = A * B over K pairs 0 .. P - 1 (64 elements = 128 bytes of a
-// row each).  The weights stream as whole 128-byte lines with nontemporal loads: per pair
-// a wave issues two loads, X covering B columns 0..7 and Y columns 8..15, in which lane l
-// fetches bytes 16 (l >> 3) of the pair of column row (l & 7) (X) and 8 + (l & 7) (Y); xo
-// and yo are those rows' byte offsets from the bases xb and yb at the wave's first K
-// element (wave-uniform bases and 32-bit lane offsets keep the addresses in few registers).  (Eight rows x 128 bytes per load
-// streams about 15 % faster from HBM than 16 rows x 64 bytes, which is the MFMA's own
-// operand layout.)  The 16x16x32 MFMA wants, in 16-lane group q, column (l & 15) at one
-// 8-element chunk common to the group; X and Y hold chunk 2q in lanes 16q .. 16q + 7 and
-// chunk 2q + 1 in lanes 16q + 8 .. 16q + 15, so a rotate by 8 inside each 16-lane row (DPP
-// row_ror:8) and a select give the two operands: chunk 2q for the first MFMA and 2q + 1
-// for the second.  A row (l & 15) is read at the same chunks through the buffer resource ars at
-// byte offset ao (the routed row at the wave's first K element); a lane whose row is
-// absent passes kNoRow, past the resource's end, and reads zeros without a memory access.
-// (A conditional load with zeros on the other side compiles to a divergent branch whose
-// zero writes wait for every load in flight: one round trip per K pair.)  B pairs are loaded before
-// the MFMAs that use them.
+// row each).  The weights stream as whole 128-byte lines with nontemporal loads: per
+// pair a wave issues two loads, X covering B columns 0..7 and Y columns 8..15, in which
+// lane l fetches bytes 16 (l >> 3) of the pair of column row (l & 7) (X) and 8 + (l & 7)
+// (Y); xo and yo are those rows' byte offsets from the bases xb and yb at the wave's
+// first K element (wave-uniform bases and 32-bit lane offsets keep the addresses in few
+// registers).  (Eight rows x 128 bytes per load streams about 15 % faster from HBM than
+// 16 rows x 64 bytes, which is the MFMA's own operand layout.)  The 16x16x32 MFMA wants,
+// in 16-lane group q, column (l & 15) at one 8-element chunk common to the group; X and
+// Y hold chunk 2q in lanes 16q .. 16q + 7 and chunk 2q + 1 in lanes 16q + 8 .. 16q + 15,
+// so a rotate by 8 inside each 16-lane row (DPP row_ror:8) and a select give the two
+// operands: chunk 2q for the first MFMA and 2q + 1 for the second.  A row (l & 15) is
+// read at the same chunks through the buffer resource ars at byte offset ao (the routed
+// row at the wave's first K element); a lane whose row is absent passes kNoRow, past the
+// resource's end, and reads zeros without a memory access.  (A conditional load with
+// zeros on the other side compiles to a divergent branch whose zero writes wait for
+// every load in flight: one round trip per K pair.)  B pairs are loaded before the MFMAs
+// that use them.
 __device__ __forceinline__ bf16x8_t rotate8_select(bf16x8_t keep, bf16x8_t rot, bool take_rot) {
     const int4 kv = *reinterpret_cast<const int4*>(&keep);
     const int4 rv = *reinterpret_cast<const int4*>(&rot);
