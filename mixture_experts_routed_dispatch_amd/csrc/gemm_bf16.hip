@@ -438,7 +438,8 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     };
     // wait until at most one stage (8 copies) of this wave's copies is outstanding
     auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
-    constexpr bool kEarlyWait = MODE == FWD_W13 || MODE == DGRAD_W2;   // see the stage stream
+    constexpr bool kEarlyWait = MODE == FWD_W13 || MODE == DGRAD_W2 || MODE == WGRAD_W2 ||
+                                MODE == WGRAD_W13;                     // see the stage stream
     // ------------------------------------------------------------ fragments
     // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
     // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
@@ -883,12 +884,12 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             __builtin_amdgcn_sched_barrier(0);
             mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
             advance_load();
-            // this wave's copies of stage gs + 2 have landed.  FWD_W13 and DGRAD_W2: in the
+            // this wave's copies of stage gs + 2 have landed.  kEarlyWait modes: in the
             // first stage of a tile they already had, since they were issued before the
             // previous tile's epilogue, which waits for every copy before it starts; a wait
             // here would count the epilogue's stores too and hold the stage until they are
-            // written (DGRAD_W2 313 -> 274 us at the training shape; the other modes gain
-            // nothing).
+            // written (DGRAD_W2 313 -> 274 us at the training shape, the weight gradients
+            // 1-4 us; FWD_W2 and DGRAD_W13 gain nothing).
             if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
             __syncthreads();
         }
