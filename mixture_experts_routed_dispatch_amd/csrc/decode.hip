@@ -336,6 +336,167 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w13(DecodeArgs g) {
     });
 }
 
+// W13 with more items than resident workgroups (many tokens): the K split of decode_w13,
+// with the next unit's weights in flight while the current unit's products, wave
+// reduction and stores run, so that the reduction's barrier does not leave the memory
+// pipe empty.  A unit is (item, group of 16 routed rows).  The unit's x rows sit in LDS
+// (copied straight from memory, zeros past the expert's rows), so that a wave's
+// registers hold only weights, two units' worth; workgroup b takes a contiguous range of
+// items, mostly blocks of one expert, whose x rows are copied once.  A wave's share of K
+// is at most kPipePairs pairs and d at most kPipeMaxD; the launcher checks.
+constexpr int kPipePairs = kBatch / 2;
+constexpr int kPipeMaxD = 2048;
+constexpr int kPipeRowBytes = 2 * kPipeMaxD + 16;     // padded: 16 rows' fragment reads hit every bank once
+
+struct PipeUnit {
+    int it, m0, e, M, e0;
+    bool valid;
+};
+
+template <int kAct>
+__global__ __launch_bounds__(kThreads, 2) void decode_w13_pipe(DecodeArgs g) {
+    __shared__ DecodeSmem sm;
+    __shared__ f32x4_t red[2][kWaves][MOE_WAVE];
+    __shared__ __attribute__((aligned(16))) char xs[16 * kPipeRowBytes];
+    int par = 0;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool lead = wave == 0;                           // the wave that stores
+    const bool hi = (lane & 8) != 0;
+    const int n = lane & 15, kq = lane >> 4;
+    const int d = g.d, I = g.I, k = g.k;
+    const int nIB = I / 8;
+    const bool one = g.T == 1;
+    int items;
+    if (one) {
+        if (blockIdx.x == 0) decode_flags_one_token(g);
+        one_token_slots(sm, g);
+        items = k * nIB;
+    } else {
+        decode_setup(sm, g.ids, g.T, k, g.E, g.status, blockIdx.x == 0);
+        items = sm.n_active * nIB;
+    }
+    items = __builtin_amdgcn_readfirstlane(items);
+    const int G = gridDim.x, b = blockIdx.x;
+    const int q = items / G, r = items - q * G;
+    const int it_begin = b * q + (b < r ? b : r);
+    const int it_end = it_begin + q + (b < r ? 1 : 0);
+    int p0, p1;
+    wave_pairs<true>(d / 64, p0, p1);
+    const int P = p1 - p0;
+
+    // the first valid unit at or after item it (row group 0)
+    auto unit_at = [&](int it) {
+        PipeUnit u;
+        u.valid = false;
+        u.m0 = 0;
+        for (; it < it_end; ++it) {
+            int e, M, e0;
+            if (slot_info(g, sm, one, it / nIB, e, M, e0)) {
+                u.it = it; u.e = e; u.M = M; u.e0 = e0; u.valid = true;
+                return u;
+            }
+        }
+        u.it = it_end; u.e = 0; u.M = 0; u.e0 = 0;
+        return u;
+    };
+    auto next_unit = [&](const PipeUnit& u) {
+        if (u.m0 + 16 < u.M) {
+            PipeUnit v = u;
+            v.m0 += 16;
+            return v;
+        }
+        return unit_at(u.it + 1);
+    };
+    auto entry = [&](const PipeUnit& u, int m) { return one ? u.e0 : sm.ent[u.e0 + m]; };
+    auto same_rows = [&](const PipeUnit& u, const PipeUnit& v) { return u.it / nIB == v.it / nIB && u.m0 == v.m0; };
+
+    // x rows m0 .. m0 + 15 of unit u into xs (row i at i * kPipeRowBytes), 1 KiB per copy:
+    // copy c of the 16 * (2d / 1024) is row c / (2d / 1024), piece c % (2d / 1024); wave w
+    // issues copies w, w + 4, ...; rows past the expert's read zeros (offset past the end)
+    const __amdgpu_buffer_rsrc_t xrs = rows_rsrc(g.x, (uint32_t)g.T * d * 2u);
+    const uint32_t xs0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)xs;
+    auto fill_x = [&](const PipeUnit& u) {
+        const int pieces = (2 * d) / 1024;
+        for (int c = wave; c < 16 * pieces; c += kWaves) {
+            const int row = c / pieces, piece = c - row * pieces;
+            const int m = u.m0 + row;
+            const uint32_t src = m < u.M ? (uint32_t)(entry(u, m) / k) * (uint32_t)d * 2u + 1024u * piece + 16u * lane
+                                         : kNoRow;
+            const uint32_t dst = xs0 + (uint32_t)(row * kPipeRowBytes + 1024 * piece);
+            asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :: "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src), "s"(xrs) : "memory");
+        }
+    };
+    const uint32_t xo = (uint32_t)((lane & 7) * d + 64 * p0) * 2u + 16u * (uint32_t)(lane >> 3);
+    const uint32_t yo = xo + (uint32_t)I * (uint32_t)d * 2u;
+    // weights of unit u: columns 0..7 gate rows i0..i0+7 (X), 8..15 up rows (Y)
+    auto load_w = [&](const PipeUnit& u, bf16x8_t xw[kPipePairs], bf16x8_t yw[kPipePairs]) {
+        const int i0 = (u.it - (u.it / nIB) * nIB) * 8;
+        const char* wb = reinterpret_cast<const char*>(g.w13 + ((size_t)u.e * 2 * I + i0) * d);
+#pragma unroll
+        for (int j = 0; j < kPipePairs; ++j)
+            if (j < P) {
+                xw[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(wb + (xo + 128u * j)));
+                yw[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(wb + (yo + 128u * j)));
+            }
+    };
+    // A row (lane & 15) of the pair chunks from xs
+    const char* xrow = xs + n * kPipeRowBytes + 128 * p0 + 32 * kq;
+    // products, wave reduction and the stores of a for unit u
+    auto finish = [&](const PipeUnit& u, const bf16x8_t xw[kPipePairs], const bf16x8_t yw[kPipePairs]) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kPipePairs; ++j)
+            if (j < P) {
+                const bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(xrow + 128 * j);
+                const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(xrow + 128 * j + 16);
+                const bf16x8_t b0 = rotate8_select(xw[j], yw[j], hi);
+                const bf16x8_t b1 = rotate8_select(yw[j], xw[j], !hi);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
+            }
+        acc = reduce_waves<true>(acc, red, par);           // ends with a barrier: xs is free again
+        float up[4];
+#pragma unroll
+        for (int z = 0; z < 4; ++z) up[z] = __shfl_down(acc[z], 8, 16);
+        if (lead && n < 8) {
+            const int i0 = (u.it - (u.it / nIB) * nIB) * 8;
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const int mm = u.m0 + 4 * kq + z;
+                if (mm < u.M) g.a[(size_t)entry(u, mm) * I + i0 + n] = (uint16_t)f32_to_bf16(act_f<kAct>(acc[z]) * up[z]);
+            }
+        }
+    };
+    // the x rows of unit v: copied, waited for (with every load before them) and published
+    auto refill = [&](const PipeUnit& v) {
+        fill_x(v);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    bf16x8_t wx0[kPipePairs], wy0[kPipePairs], wx1[kPipePairs], wy1[kPipePairs];
+    PipeUnit u = unit_at(it_begin);
+    if (!u.valid) return;
+    load_w(u, wx0, wy0);
+    refill(u);
+    while (true) {
+        // unit u in buffer 0; the next unit's weights into buffer 1
+        PipeUnit v = next_unit(u);
+        if (v.valid) load_w(v, wx1, wy1);
+        finish(u, wx0, wy0);
+        if (!v.valid) break;
+        if (!same_rows(u, v)) refill(v);
+        // unit v in buffer 1; the next unit's weights into buffer 0
+        u = next_unit(v);
+        if (u.valid) load_w(u, wx0, wy0);
+        finish(v, wx1, wy1);
+        if (!u.valid) break;
+        if (!same_rows(v, u)) refill(u);
+    }
+}
+
 template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
     __shared__ DecodeSmem sm;
@@ -681,6 +842,18 @@ hipError_t launch_decode(K1 wave_kernel, K2 split_kernel, const DecodeArgs& g, i
 }
 
 hipError_t launch_decode_w13(const DecodeArgs& g, int num_cu, hipStream_t s) {
+    // many items per workgroup (many tokens) and a wave's K share within kPipePairs pairs:
+    // the pipelined kernel, two workgroups per CU
+    const int R = g.T * g.k;
+    const int slots = R < g.E ? R : g.E;
+    const int items = slots * (g.I / 8);
+    if (R > 0 && g.d <= kPipeMaxD && g.d <= 64 * kWaves * kPipePairs && g.d % 512 == 0 && items >= 8 * num_cu) {
+        const int grid = 2 * num_cu;
+        if (g.act == kActGeGLU) hipLaunchKernelGGL(decode_w13_pipe<kActGeGLU>, dim3(grid), dim3(kThreads), 0, s, g);
+        else if (g.act == kActReGLU) hipLaunchKernelGGL(decode_w13_pipe<kActReGLU>, dim3(grid), dim3(kThreads), 0, s, g);
+        else hipLaunchKernelGGL(decode_w13_pipe<kActSwiGLU>, dim3(grid), dim3(kThreads), 0, s, g);
+        return hipGetLastError();
+    }
     if (g.act == kActGeGLU)
         return launch_decode(decode_w13<false, kActGeGLU>, decode_w13<true, kActGeGLU>, g, g.I / 8, g.d / 32, num_cu, s);
     if (g.act == kActReGLU)

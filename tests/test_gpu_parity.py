@@ -525,6 +525,8 @@ DECODE_SHAPES = [
     (30, 256, 128, 128, 8, "zipf"),        # skewed, some experts with many rows, most empty
     (256, 128, 64, 200, 1, "uniform"),     # T*k at the decode limit
     (32, 1024, 512, 64, 8, "uniform"),     # enough items for one wave per item (no K split)
+    (64, 256, 2048, 8, 4, "uniform"),      # W13 items >= 8 per CU (pipelined W13), 32 rows per expert
+    (48, 512, 2048, 16, 4, "zipf"),        # the same, skewed: row groups of 16 past the first
 ]
 
 
