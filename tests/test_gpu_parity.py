@@ -527,6 +527,7 @@ DECODE_SHAPES = [
     (32, 1024, 512, 64, 8, "uniform"),     # enough items for one wave per item (no K split)
     (64, 256, 2048, 8, 4, "uniform"),      # W13 items >= 8 per CU (pipelined W13), 32 rows per expert
     (48, 512, 2048, 16, 4, "zipf"),        # the same, skewed: row groups of 16 past the first
+    (64, 2048, 256, 24, 4, "zipf"),        # one wave per W2 item, skewed: row groups past 16
 ]
 
 
