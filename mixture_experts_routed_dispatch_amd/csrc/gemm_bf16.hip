@@ -44,6 +44,8 @@
 // work items go to workgroups of one XCD so that the operand slices they share stay
 // in its L2.  The weight gradients order and cut their tiles for balance (see the
 // work list below) and add split tiles up in wgrad_fixup.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -440,6 +442,9 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     auto wait_dma = [&]() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
     constexpr bool kEarlyWait = MODE == FWD_W13 || MODE == DGRAD_W2 || MODE == WGRAD_W2 ||
                                 MODE == WGRAD_W13;                     // see the stage stream
+    // Q is the routed rows (tiles end at an expert's last row), and the registers allow
+    // the partial-tile copies of the stage loop (W13 holds 512 per lane already)
+    constexpr bool kRowsQ = MODE == FWD_W2 || MODE == DGRAD_W2 || MODE == DGRAD_W13;
     // ------------------------------------------------------------ fragments
     // fragment b of P (Q): rows wp*128 + 32 b + (lane & 31) (wq*128 + ...), k chunk (lane >> 5)
     // for k step 0 of a stage; k step 1 is chunk + 2, i.e. the byte offset ^ 32.
@@ -539,6 +544,26 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                 __builtin_amdgcn_sched_group_barrier(0x100, kPreads, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            dma_one(dma_kt, dma_buf, dma_first + a);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // A k step of a wave whose tile rows end inside its 128 Q rows (a ragged tail of an
+    // expert): the MFMAs of Q blocks b < L only (the others would feed rows that are never
+    // stored), with the same fragment reads and copies as mfma_step.
+    auto mfma_step_part = [&](auto live_tag, const bf16x8_t pf[4], const bf16x8_t qf[4], int rbuf, int rks,
+                              bf16x8_t npf[4], bf16x8_t nqf[4], int dma_kt, int dma_buf, int dma_first) {
+        constexpr int L = decltype(live_tag)::value;
+        const char* rbase = lds + rbuf * BUFB;
+        const int x = rks ? 32 : 0;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int b = 0; b < L; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[a], qf[b], acc[a][b], 0, 0, 0);
+            read_item(rbase, x, rks, 2 * a, npf, nqf);
+            read_item(rbase, x, rks, 2 * a + 1, npf, nqf);
             dma_one(dma_kt, dma_buf, dma_first + a);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -874,24 +899,51 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
             for (int b = 0; b < 4; ++b)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-        for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
-            // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd) and
-            // issuing the first half of the copies of stage gs + 3
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(fa, fc, gs & 3, 1, fb, fd, lc.k0 + l_kt, (gs + 3) & 3, 0);
-            // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments and
-            // issuing the rest of the copies of stage gs + 3
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
-            advance_load();
-            // this wave's copies of stage gs + 2 have landed.  kEarlyWait modes: in the
-            // first stage of a tile they already had, since they were issued before the
-            // previous tile's epilogue, which waits for every copy before it starts; a wait
-            // here would count the epilogue's stores too and hold the stage until they are
-            // written (DGRAD_W2 313 -> 274 us at the training shape, the weight gradients
-            // 1-4 us; FWD_W2 and DGRAD_W13 gain nothing).
-            if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
-            __syncthreads();
+        if constexpr (kRowsQ) {
+            // the stages of the tile; L < 4: this wave's live Q blocks (rows past the
+            // expert's end are never stored, so their MFMAs are skipped)
+            auto stages = [&](auto live_tag) {
+                constexpr int L = decltype(live_tag)::value;
+                for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
+                    // k step 0: MFMAs on (fa, fc) while reading step 1's fragments (fb, fd) and
+                    // issuing the first half of the copies of stage gs + 3
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (L == 4) mfma_step(fa, fc, gs & 3, 1, fb, fd, lc.k0 + l_kt, (gs + 3) & 3, 0);
+                    else mfma_step_part(live_tag, fa, fc, gs & 3, 1, fb, fd, lc.k0 + l_kt, (gs + 3) & 3, 0);
+                    // k step 1: MFMAs on (fb, fd) while reading stage gs + 1's first fragments and
+                    // issuing the rest of the copies of stage gs + 3
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (L == 4) mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
+                    else mfma_step_part(live_tag, fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
+                    advance_load();
+                    // this wave's copies of stage gs + 2 have landed.  kEarlyWait modes: in the
+                    // first stage of a tile they already had, since they were issued before the
+                    // previous tile's epilogue, which waits for every copy before it starts; a
+                    // wait here would count the epilogue's stores too and hold the stage until
+                    // they are written (DGRAD_W2 313 -> 274 us at the training shape, the weight
+                    // gradients 1-4 us; FWD_W2 and DGRAD_W13 gain nothing).
+                    if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
+                    __syncthreads();
+                }
+            };
+            const int left = cc.rows - cc.qt * TQ - wq * 128;          // this wave's rows in the tile
+            const int live = left <= 0 ? 0 : (left >= 128 ? 4 : (left + 31) / 32);
+            if (live == 4) stages(std::integral_constant<int, 4>{});
+            else if (live == 3) stages(std::integral_constant<int, 3>{});
+            else if (live == 2) stages(std::integral_constant<int, 2>{});
+            else if (live == 1) stages(std::integral_constant<int, 1>{});
+            else stages(std::integral_constant<int, 0>{});
+        } else {
+            // the same loop written out (as a lambda call it costs the W13 kernels spills)
+            for (int kt = 0; kt < cc.nk; ++kt, ++gs) {
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_step(fa, fc, gs & 3, 1, fb, fd, lc.k0 + l_kt, (gs + 3) & 3, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_step(fb, fd, (gs + 1) & 3, 0, fa, fc, lc.k0 + l_kt, (gs + 3) & 3, 4);
+                advance_load();
+                if (!kEarlyWait || kt != 0 || c_item == 0) wait_dma();
+                __syncthreads();
+            }
         }
         if constexpr (kEarlyWait) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (!kRagged || cc.np == 1) epilogue(cc, (gs - 1) & 3);
