@@ -528,6 +528,10 @@ DECODE_SHAPES = [
     (64, 256, 2048, 8, 4, "uniform"),      # W13 items >= 8 per CU (pipelined W13), 32 rows per expert
     (48, 512, 2048, 16, 4, "zipf"),        # the same, skewed: row groups of 16 past the first
     (64, 2048, 256, 24, 4, "zipf"),        # one wave per W2 item, skewed: row groups past 16
+    (1, 512, 256, 16, 4, "uniform"),       # one token: W13 split four ways over K, then W2 + combine
+    (1, 1024, 640, 64, 6, "uniform"),      # one token, k = 6: three expert pairs in the W2 launch
+    (1, 512, 192, 32, 5, "uniform"),       # one token, odd k: the last expert pair half empty
+    (1, 4096, 512, 16, 4, "uniform"),      # one token, d = 4096: 512 blocks of 8 outputs in the W2 launch
 ]
 
 
@@ -567,9 +571,12 @@ def test_decode_zero_scores_and_rerouting(torch_cuda):
     layer.close()
 
 
-def test_decode_graph_replay_matches_eager(torch_cuda):
+@pytest.mark.parametrize("T", [4, 1])
+def test_decode_graph_replay_matches_eager(torch_cuda, T):
+    """Replays of a captured decode call (T = 4: three launches with the combine; T = 1:
+    W13, then W2 with the combine) equal the eager result."""
     torch = torch_cuda
-    inp = inputs.generate(4, 512, 256, 16, 4, seed=23)
+    inp = inputs.generate(T, 512, 256, 16, 4, seed=23)
     t = device_inputs(inp)
     layer = make_layer(inp, path=2)
     y_eager = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
@@ -614,6 +621,34 @@ def test_decode_flags_invalid_routing(torch_cuda):
     layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
     st, flags = layer.status()
     assert st == moe.MOE_OK and flags == 0
+    layer.close()
+
+
+def test_decode_one_token_flags_and_recovery(torch_cuda):
+    """One token with invalid routing (a repeated id, an id past E): each flag is raised
+    alone, and the next valid calls match the oracle."""
+    torch = torch_cuda
+    from mixture_experts_routed_dispatch_amd import moe
+    inp = inputs.generate(1, 512, 256, 16, 4, seed=37)
+    t = device_inputs(inp)
+    layer = make_layer(inp, path=2)
+    ref = oracle.forward_tokens(inp.x, inp.ids, inp.scores, inp.w13, inp.w2)
+    bad = inp.ids.copy()
+    bad[0, 2] = bad[0, 1]
+    layer.forward(t["x"], torch.from_numpy(bad).to(dev()), t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags == moe.MOE_DEV_ID_DUPLICATE
+    bad = inp.ids.copy()
+    bad[0, 3] = inp.E + 5
+    layer.forward(t["x"], torch.from_numpy(bad).to(dev()), t["scores"], t["w13"], t["w2"])
+    st, flags = layer.status(clear=True)
+    assert st == moe.MOE_ERR_ROUTING and flags == moe.MOE_DEV_ID_OUT_OF_RANGE
+    for _ in range(3):
+        y = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
+        torch.cuda.synchronize()
+        st, flags = layer.status()
+        assert st == moe.MOE_OK and flags == 0
+        check("y", np_of(y), ref, **BF16)
     layer.close()
 
 
