@@ -571,12 +571,13 @@ def test_decode_zero_scores_and_rerouting(torch_cuda):
     layer.close()
 
 
-@pytest.mark.parametrize("T", [4, 1])
-def test_decode_graph_replay_matches_eager(torch_cuda, T):
-    """Replays of a captured decode call (T = 4: three launches with the combine; T = 1:
-    W13, then W2 with the combine) equal the eager result."""
+@pytest.mark.parametrize("T,d,I,E,k", [(4, 512, 256, 16, 4), (1, 512, 256, 16, 4), (32, 1024, 512, 64, 8)])
+def test_decode_graph_replay_matches_eager(torch_cuda, T, d, I, E, k):
+    """Replays of a captured decode call equal the eager result: T = 4 (W2 split over K
+    per item) and T = 32 (one wave per W2 item), three launches with the combine; T = 1,
+    W13, then W2 with the combine."""
     torch = torch_cuda
-    inp = inputs.generate(T, 512, 256, 16, 4, seed=23)
+    inp = inputs.generate(T, d, I, E, k, seed=23)
     t = device_inputs(inp)
     layer = make_layer(inp, path=2)
     y_eager = layer.forward(t["x"], t["ids"], t["scores"], t["w13"], t["w2"])
