@@ -305,7 +305,8 @@ const char* moe_status_string(moe_status_t status);
  * [RECOMPUTE_H,] DGRAD_W2, DGRAD_W13, DX_COMBINE, WGRAD_ROWS, WGRAD_W2, WGRAD_W13 in that order
  * (MXFP8: SCORE_GRAD, [RECOMPUTE_H,] QUANT_DO, DGRAD_W2, ACT_BWD, DGRAD_W13, DX_COMBINE,
  * QUANT_T, WGRAD_W2, QUANT_T, WGRAD_W13); the one-token decode runs W2 and the combine as
- * one kernel, recorded as DECODE_W2; a mega decode plan runs its one launch as MEGA. */
+ * one kernel, recorded as DECODE_W2; a mega decode plan records its two launches (the
+ * chunked products, then the sum of the chunks with the combine) as one stage, MEGA. */
 #define MOE_STAGE_DISPATCH 0
 #define MOE_STAGE_QUANT_X 1
 #define MOE_STAGE_W13 2
