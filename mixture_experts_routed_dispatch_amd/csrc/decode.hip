@@ -469,31 +469,43 @@ __global__ __launch_bounds__(kThreads, 2) void decode_w13_pipe(DecodeArgs g) {
             }
         }
     };
-    // the x rows of unit v: copied, waited for (with every load before them) and published
-    auto refill = [&](const PipeUnit& v) {
-        fill_x(v);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the x rows of a unit copied and published; with `after`, the next unit's weights
+    // (2 P loads) were issued after the copies, and the wait leaves them in flight
+    auto wait_x = [&](bool after) {
+        if (after && P == kPipePairs) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
+    static_assert(2 * kPipePairs == 16, "the wait above is written as vmcnt(16)");
 
+    // Two weight buffers; the unit in buffer 0 and the next one's weights in flight into
+    // buffer 1, then the roles swap.  When a unit's x rows differ from the previous
+    // unit's, they are copied into xs once the previous unit's products are done (its
+    // reduction ends with a barrier), the following unit's weights go out behind them,
+    // and the wait covers the copies (and the older loads) only.
     bf16x8_t wx0[kPipePairs], wy0[kPipePairs], wx1[kPipePairs], wy1[kPipePairs];
     PipeUnit u = unit_at(it_begin);
     if (!u.valid) return;
     load_w(u, wx0, wy0);
-    refill(u);
+    fill_x(u);
+    PipeUnit v = next_unit(u);
+    if (v.valid) load_w(v, wx1, wy1);
+    wait_x(v.valid);
     while (true) {
-        // unit u in buffer 0; the next unit's weights into buffer 1
-        PipeUnit v = next_unit(u);
-        if (v.valid) load_w(v, wx1, wy1);
-        finish(u, wx0, wy0);
+        finish(u, wx0, wy0);                       // unit u (buffer 0); v's weights in buffer 1
         if (!v.valid) break;
-        if (!same_rows(u, v)) refill(v);
-        // unit v in buffer 1; the next unit's weights into buffer 0
+        const bool fresh_v = !same_rows(u, v);
+        if (fresh_v) fill_x(v);
         u = next_unit(v);
         if (u.valid) load_w(u, wx0, wy0);
-        finish(v, wx1, wy1);
+        if (fresh_v) wait_x(u.valid);
+        finish(v, wx1, wy1);                       // unit v (buffer 1); u's weights in buffer 0
         if (!u.valid) break;
-        if (!same_rows(v, u)) refill(u);
+        const bool fresh_u = !same_rows(v, u);
+        if (fresh_u) fill_x(u);
+        v = next_unit(u);
+        if (v.valid) load_w(v, wx1, wy1);
+        if (fresh_u) wait_x(v.valid);
     }
 }
 
