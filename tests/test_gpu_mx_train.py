@@ -96,6 +96,7 @@ MXT_SHAPES = [
     (200, 256, 128, 64, 8, "zipf"),        # skew and empty experts
     (130, 256, 128, 1, 1, "uniform"),      # dense layer: 130 rows, two token-layout groups
     (1024, 1024, 512, 8, 4, "uniform"),    # several tiles in every product
+    (320, 256, 128, 256, 32, "zipf"),      # E = 256, k = 32, skewed (empty and one-row experts)
 ]
 
 

@@ -124,6 +124,7 @@ SMALL_SHAPES = [
     (300, 256, 128, 128, 8, "zipf"),       # skew, 8+ empty experts, many 1-row experts
     (130, 128, 64, 1, 1, "uniform"),       # dense layer (E = 1, k = 1)
     (1, 256, 128, 16, 4, "uniform"),       # one token
+    (320, 256, 128, 256, 32, "zipf"),      # the expert and top-k limits (E = 256, k = 32), skewed
 ]
 
 
@@ -816,6 +817,7 @@ BWD_SHAPES = [
     (257, 320, 192, 5, 2, "uniform"),
     (300, 256, 128, 128, 8, "zipf"),
     (130, 128, 64, 1, 1, "uniform"),
+    (320, 256, 128, 256, 32, "zipf"),       # E = 256, k = 32, skewed (empty and one-row experts)
 ]
 
 
@@ -1116,6 +1118,7 @@ MX_SHAPES = [
     (200, 256, 128, 64, 8, "zipf"),        # skew and empty experts
     (130, 256, 128, 1, 1, "uniform"),      # dense layer
     (100, 2304, 128, 4, 2, "uniform"),     # 18 scale words per row: a partial second group chunk
+    (320, 256, 128, 256, 32, "zipf"),      # the expert and top-k limits (E = 256, k = 32), skewed
 ]
 
 
