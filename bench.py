@@ -82,7 +82,7 @@ KERNEL_OF_STAGE = {
     # them) of every kernel the stage launches
     "dispatch": ("dispatch_kernel",),
     "w13": ("grouped_gemm<0,", "fwd_fixup<0,"), "w2": ("grouped_gemm<1,", "fwd_fixup<1,"),
-    "combine": ("combine_kernel",), "score_grad": ("score_grad_kernel",),
+    "combine": ("combine_kernel",), "score_grad": ("score_grad_kernel", "score_grad_sum_kernel"),
     "dgrad_w2": ("grouped_gemm<2,",), "dgrad_w13": ("grouped_gemm<3,",),
     "wgrad_w2": ("grouped_gemm<4,", "wgrad_fixup<4>"), "wgrad_w13": ("grouped_gemm<5,", "wgrad_fixup<5>"),
     "quant_x": ("quantize_kernel", "route_scales_kernel"), "decode_w13": ("decode_w13",), "decode_w2": ("decode_w2",),

@@ -127,6 +127,22 @@ __global__ __launch_bounds__(kThreads) void score_grad_kernel(const uint16_t* __
     }
 }
 
+// The router gradient from the partials the W2 data-gradient product leaves: <dy[t], o>
+// with o = W2 a equals sum_i (dy[t] W2)[i] a[i], which that product's epilogue has at
+// hand (its accumulators before the probs scaling, and a from the saved h), in pieces of
+// 64 columns.  Entry q (= t k + j) adds its row's pieces in slot order, from +0.0, so
+// the result does not depend on the launch.
+__global__ __launch_bounds__(kThreads) void score_grad_sum_kernel(const float* __restrict__ part,
+                                                                  const int32_t* __restrict__ slots,
+                                                                  int R, int nslots, float* __restrict__ ds) {
+    const int q = blockIdx.x * kThreads + threadIdx.x;
+    if (q >= R) return;
+    const float* p = part + (size_t)slots[q] * nslots;
+    float s = 0.0f;
+    for (int i = 0; i < nslots; ++i) s += p[i];
+    ds[q] = s;
+}
+
 // Row-major operands of the weight-gradient products: xg[r] = x[gather[r]] and
 // dys[r] = bf16(probs[r] * dy[gather[r]]) for routed rows r.  Token-major: one
 // workgroup per token t (grid-strided) reads x[t] and dy[t] once, one 16-byte chunk
@@ -181,6 +197,14 @@ hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float
     if (T == 0) return hipSuccess;
     const dim3 grid((d / 8 + kThreads - 1) / kThreads, T);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, src, slots, w, T, k, d, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_score_grad_sum(const float* part, const int32_t* slots, int R, int nslots, float* ds,
+                                 hipStream_t s) {
+    if (R == 0) return hipSuccess;
+    hipLaunchKernelGGL(score_grad_sum_kernel, dim3((R + kThreads - 1) / kThreads), dim3(kThreads), 0, s,
+                       part, slots, R, nslots, ds);
     return hipGetLastError();
 }
 

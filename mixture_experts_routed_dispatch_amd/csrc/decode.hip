@@ -566,34 +566,47 @@ __global__ __launch_bounds__(kThreads, 3) void decode_w2(DecodeArgs g) {
 // pair of experts in one round trip.
 __global__ __launch_bounds__(kThreads, 1) void decode_w2_one(DecodeArgs g) {
     __shared__ float ov[kMaxTopK][8];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float sc[kMaxTopK];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, kq = lane >> 4;
     const int d = g.d, I = g.I, k = g.k;
     const int npair = (k + 1) / 2;
-    auto valid = [&](int j) { return j < k && (unsigned)g.ids[j] < (unsigned)g.E; };
+    // the scores, loaded before the weights so that the combine does not wait for them
+    // once the products are done (they reach LDS with the products, below)
+    const float score = tid < k ? g.scores[tid] : 0.f;
+    // expert id of slot j, or -1 (j >= k or an invalid id); uniform, read before the
+    // weight loads that depend on it
+    auto expert = [&](int j) {
+        const int e = j < k ? __builtin_amdgcn_readfirstlane(g.ids[j]) : -1;
+        return (unsigned)e < (unsigned)g.E ? e : -1;
+    };
     for (int nb = blockIdx.x; nb < d / 8; nb += gridDim.x) {
         const int n0 = nb * 8;
         for (int p = wave; p < npair; p += kWaves) {
             // B columns 0..7 (X): expert slot 2p; columns 8..15 (Y): slot 2p + 1
-            const int ex = valid(2 * p) ? g.ids[2 * p] : 0;
-            const int ey = valid(2 * p + 1) ? g.ids[2 * p + 1] : 0;
+            const int e_x = expert(2 * p), e_y = expert(2 * p + 1);
+            const bool vx = e_x >= 0, vy = e_y >= 0;
+            const int ex = vx ? e_x : 0;
+            const int ey = vy ? e_y : 0;
             const char* xb = reinterpret_cast<const char*>(g.w2 + ((size_t)ex * d + n0) * I);
             const char* yb = reinterpret_cast<const char*>(g.w2 + ((size_t)ey * d + n0) * I);
             const uint32_t wo = (uint32_t)((lane & 7) * I) * 2u;
             const int jr = 2 * p + n;                       // expert slot of A row n (rows 0, 1)
-            const bool rv = n < 2 && valid(jr);
+            const bool rv = (n == 0 && vx) || (n == 1 && vy);
             const uint32_t ao = rv ? (uint32_t)(jr * I) * 2u : kNoRow;
             const f32x4_t acc = mma_line_pairs<12>(xb, wo, yb, wo, rows_rsrc(g.a, (uint32_t)k * I * 2u), ao, I / 64);
             // lanes with kq = 0 hold rows 0..3 of column n
             if (kq == 0) {
-                if (n < 8 && 2 * p < k) ov[2 * p][n] = valid(2 * p) ? acc[0] : 0.f;
-                if (n >= 8 && 2 * p + 1 < k) ov[2 * p + 1][n - 8] = valid(2 * p + 1) ? acc[1] : 0.f;
+                if (n < 8 && 2 * p < k) ov[2 * p][n] = vx ? acc[0] : 0.f;
+                if (n >= 8 && 2 * p + 1 < k) ov[2 * p + 1][n - 8] = vy ? acc[1] : 0.f;
             }
         }
+        if (tid < k) sc[tid] = score;
         __syncthreads();
         if (tid < 8) {
             float y = 0.f;
-            for (int j = 0; j < k; ++j) y = __builtin_fmaf(g.scores[j], bf16_to_f32(f32_to_bf16(ov[j][tid])), y);
+            for (int j = 0; j < k; ++j) y = __builtin_fmaf(sc[j], bf16_to_f32(f32_to_bf16(ov[j][tid])), y);
             g.y[n0 + tid] = (uint16_t)f32_to_bf16(y);
         }
         __syncthreads();

@@ -127,6 +127,21 @@ struct TileCtx {
 // are copied out to scratch by the register allocator.
 // kAct (FWD_W13 and DGRAD_W2): the gated activation, a template parameter so that the
 // SwiGLU kernels stay as they are.
+// v summed over each group of 8 consecutive lanes, the total in all 8: lane pairs
+// (xor 1), then quads (xor 2), then the two quads (row_half_mirror pairs lane i with
+// 7 - i, which holds the other quad's sum), all through DPP.  Every lane of a group
+// ends with the same bits.  All 64 lanes must be active.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float sum_lanes8(float v) {
+    v += dpp_f32<0xB1>(v);      // quad_perm [1, 0, 3, 2]
+    v += dpp_f32<0x4E>(v);      // quad_perm [2, 3, 0, 1]
+    v += dpp_f32<0x141>(v);     // row_half_mirror
+    return v;
+}
+
 template <int MODE, bool kSaveH = false, int kAct = kActSwiGLU>
 __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
     __shared__ __attribute__((aligned(1024))) char lds[NBUF * BUFB];
@@ -730,8 +745,15 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                     sc[it] = g.probs[r];
                 }
             };
+            // With g.ds_part, each half block also leaves the router gradient's piece of its
+            // rows: the sum over its 64 columns of acc (dy W2, before the probs scaling)
+            // times a = f(g) u from the saved h (columns past I add nothing), once the
+            // row's dh is stored; the eight lanes of a row add their pieces (a fixed tree)
+            // and the first stores it in slot 4 pt + 2 wp + ah.  (One piece over both half
+            // blocks of a row block, held across the next one's loads, spills.)
             auto half_block = [&](int hb, const uint4 hg[4], const uint4 hu[4], const float sc[4]) {
                 const int b = hb >> 1, ah = hb & 1;
+                float dsum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                 const int i0 = c.pt * TP + wp * 128 + 64 * ah + 8 * (ln & 7);   // this lane's 8 columns
 #pragma unroll
                 for (int a2 = 0; a2 < 2; ++a2)
@@ -759,6 +781,7 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                     const uint32_t gw[4] = {hg[it].x, hg[it].y, hg[it].z, hg[it].w};
                     const uint32_t uw[4] = {hu[it].x, hu[it].y, hu[it].z, hu[it].w};
                     uint32_t og[4], ou[4];
+                    float fv[8];                          // f(g) of the lane's 8 columns
 #pragma unroll
                     for (int z = 0; z < 4; ++z) {
                         float dg2[2], du2[2];
@@ -771,11 +794,13 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                                 const float sg = sigmoid_f(gv);
                                 dg2[h2] = dA * uv * sg * (1.0f + gv * (1.0f - sg));
                                 du2[h2] = dA * gv * sg;
+                                fv[2 * z + h2] = gv * sg;
                             } else {
                                 float f, df;
                                 act_f_df<kAct>(gv, f, df);
                                 dg2[h2] = dA * uv * df;
                                 du2[h2] = dA * f;
+                                fv[2 * z + h2] = f;
                             }
                         }
                         og[z] = pack_bf16(dg2[0], dg2[1]);
@@ -787,6 +812,20 @@ __global__ __launch_bounds__(NTHR, 1) void grouped_gemm(GemmArgs g) {
                         *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + i0) = make_uint4(og[0], og[1], og[2], og[3]);
                         *reinterpret_cast<uint4*>(g.out + r * 2 * g.I + g.I + i0) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
                     }
+                    float dl = 0.0f;
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+                        dl = __builtin_fmaf(av[2 * z], fv[2 * z] * bf16lo(uw[z]), dl);
+                        dl = __builtin_fmaf(av[2 * z + 1], fv[2 * z + 1] * bf16hi(uw[z]), dl);
+                    }
+                    dsum[it] += i0 < g.I ? dl : 0.0f;
+                }
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const float v = sum_lanes8(dsum[it]);
+                    const int rr = c.qt * TQ + wq * 128 + b * 32 + 8 * it + (ln >> 3);
+                    if (g.ds_part != nullptr && (ln & 7) == 0 && rr < c.rows)
+                        g.ds_part[((size_t)c.mb + rr) * g.ds_slots + 4 * c.pt + 2 * wp + ah] = v;
                 }
             };
             uint4 hg0[4], hu0[4], hg1[4], hu1[4];

@@ -49,6 +49,11 @@ struct GemmArgs {
     int32_t* nsplit;      // number of split tiles of the last weight-gradient launch
     int accumulate;       // weight gradients: add into out instead of overwriting
     int act;              // gated activation (kActSwiGLU / kActGeGLU / kActReGLU)
+    // DGRAD_W2, when set: [R, ds_slots] FP32 partial router gradients, slot 4 pt + 2 wp + ah
+    // of row r = sum over the 64 columns i of column tile pt, quarter 2 wp + ah, of
+    // (dy W2)[r][i] a[r][i]
+    float* ds_part;
+    int ds_slots;
 };
 
 // Pieces of split weight-gradient tiles in one launch (sizes their FP32 partial sums).
@@ -134,6 +139,9 @@ hipError_t launch_mx_transpose_quant(const uint16_t* src, int segs, int K, int N
 hipError_t launch_combine(const uint16_t* src, const int32_t* slots, const float* w, int T, int k,
                           int d, uint16_t* y, hipStream_t s);
 // ds[t][j] = <dy[t], o[slots[t][j]]> in FP32.
+// dS[q] = sum of the nslots partials of q's routed row slots[q], in slot order.
+hipError_t launch_score_grad_sum(const float* part, const int32_t* slots, int R, int nslots, float* ds,
+                                 hipStream_t s);
 hipError_t launch_score_grad(const uint16_t* dy, const uint16_t* o, const int32_t* slots, int T,
                              int k, int d, float* ds, hipStream_t s);
 

@@ -721,7 +721,13 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     if (mx) return mx_backward(p, dy, x, w, dx, dw13, dw2, dscores, s);
     hipError_t e;
     const int32_t* slots = p->at<int32_t>(p->off_slots);
-    if (c.T > 0) {
+    // The router gradient: partial dot products from the W2 data-gradient product's
+    // epilogue (one per routed row and 64 columns of I), held in the split-tile buffer,
+    // which the weight gradients use only afterwards, and summed right after that
+    // product; else (more partials than the buffer holds) from o and dy.
+    const int ds_slots = 4 * ((c.I + 255) / 256);
+    const bool fused_ds = (size_t)p->R * ds_slots * sizeof(float) <= kGemmPartBytes;
+    if (c.T > 0 && !fused_ds) {
         e = staged(p, MOE_STAGE_SCORE_GRAD, s, [&] {
             return launch_score_grad(static_cast<const uint16_t*>(dy), p->at<uint16_t>(p->off_o),
                                      slots, c.T, c.k, c.d, dscores, s);
@@ -767,8 +773,17 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
         // input gradients first, each consumer right after its producer, so that dh and
         // dxp are still in the memory-side cache when they are read back
         g.out = p->at<uint16_t>(p->off_dh);
+        g.ds_part = fused_ds ? g.part : nullptr;
+        g.ds_slots = ds_slots;
         e = staged(p, MOE_STAGE_DGRAD_W2, s, [&] { return launch_gemm(DGRAD_W2, g, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;
+        g.ds_part = nullptr;
+        if (fused_ds) {
+            e = staged(p, MOE_STAGE_SCORE_GRAD, s, [&] {
+                return launch_score_grad_sum(g.part, slots, (int)p->R, ds_slots, dscores, s);
+            });
+            if (e != hipSuccess) return MOE_ERR_HIP;
+        }
         g.out = p->at<uint16_t>(p->off_dxp);
         e = staged(p, MOE_STAGE_DGRAD_W13, s, [&] { return launch_gemm(DGRAD_W13, g, p->num_cu, s); });
         if (e != hipSuccess) return MOE_ERR_HIP;

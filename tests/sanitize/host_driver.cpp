@@ -24,6 +24,9 @@ hipError_t launch_gemm_mxfp8(MxMode, const MxGemmArgs&, int, hipStream_t) { retu
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int, int, int, uint16_t*, hipStream_t) {
     return hipErrorInvalidValue;
 }
+hipError_t launch_score_grad_sum(const float*, const int32_t*, int, int, float*, hipStream_t) {
+    return hipErrorInvalidValue;
+}
 hipError_t launch_score_grad(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, float*, hipStream_t) {
     return hipErrorInvalidValue;
 }
