@@ -50,6 +50,7 @@ struct moe_plan_s {
     int num_cu;
     bool have_saved_forward;
     bool h_aliased;                    // recompute_h: h occupies the dxp / xg / dys region
+    bool dh_aliased;                   // BF16 training: dh occupies o's region (see below)
     int32_t* status_word;              // device status word of the last call (workspace or static scratch)
     // measurement-only event pairs around kernel stages (moe_profile)
     struct ProfRec { int stage; hipEvent_t a, b; };
@@ -208,6 +209,14 @@ moe_status_t mx_backward(moe_plan_s* p, const void* dy, const void* x, const moe
 
 extern "C" {
 
+// The BF16 backward's router gradient comes from partial sums of the W2 data-gradient
+// product (one FP32 per routed row and 64 columns of I, router_grad_slots per row), held
+// in the split-tile buffer, when they fit there; else from o and dy.
+static int router_grad_slots(int I) { return 4 * ((I + 255) / 256); }
+static bool fused_router_grad(int64_t R, int I) {
+    return (size_t)R * router_grad_slots(I) * sizeof(float) <= kGemmPartBytes;
+}
+
 moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     if (!cfg || !out) return MOE_ERR_INVALID_ARG;
     *out = nullptr;
@@ -264,7 +273,10 @@ moe_status_t moe_plan(const moe_config_t* cfg, moe_plan_t* out) {
     p->off_o = take(2 * (size_t)R * c.d);
     const size_t h_bytes = 2 * (size_t)R * 2 * c.I;
     p->off_h = (c.training && !c.recompute_h) ? take(h_bytes) : 0;
-    p->off_dh = c.training ? take(2 * (size_t)R * 2 * c.I) : 0;
+    // BF16 training takes the router gradient from the W2 data-gradient partials, so the
+    // backward never reads o: dh, first written by that product, takes o's place when it fits
+    p->dh_aliased = c.training && !mx && fused_router_grad(R, c.I) && 2 * (size_t)c.I <= (size_t)c.d;
+    p->off_dh = !c.training ? 0 : p->dh_aliased ? p->off_o : take(2 * (size_t)R * 2 * c.I);
     // MXFP8: dA [R, I] first, then dxp [R, d]
     p->off_dxp = c.training ? take(2 * (size_t)R * (mx && c.I > c.d ? c.I : c.d)) : 0;
     p->off_xg = (c.training && !mx) ? take(2 * (size_t)R * c.d) : 0;
@@ -362,7 +374,10 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
     if (!mx || c.training)
         saved_region("a", 2 * (size_t)R * c.I, mx ? "SwiGLU output [R, I] BF16 (weight-gradient operand)"
                                                   : "SwiGLU output [R, I] BF16");
-    saved_region("o", 2 * (size_t)R * c.d, "expert outputs [R, d] BF16");
+    if (p->dh_aliased)
+        region("o", 2 * (size_t)R * c.d, "fwd/bwd", "expert outputs [R, d] BF16; in the backward dh (g, u gradient [R, 2I])");
+    else
+        saved_region("o", 2 * (size_t)R * c.d, "expert outputs [R, d] BF16");
     if (c.training) {
         const size_t hb = 2 * (size_t)R * 2 * c.I;
         if (c.recompute_h)
@@ -370,7 +385,7 @@ size_t moe_plan_explain(moe_plan_t p, char* buf, size_t len) {
                    "W13 pre-activations (g, u) [R, 2I] BF16, recomputed");
         else
             saved_region("h", hb, "W13 pre-activations (g, u) [R, 2I] BF16");
-        region("dh", 2 * (size_t)R * 2 * c.I, "backward", "gradient w.r.t. (g, u) [R, 2I] BF16");
+        region("dh", p->dh_aliased ? 0 : 2 * (size_t)R * 2 * c.I, "backward", "gradient w.r.t. (g, u) [R, 2I] BF16");
         if (mx) {
             region("dxp", 2 * (size_t)R * (c.I > c.d ? c.I : c.d), "backward",
                    "dA [R, I] BF16, then the per-row input gradients [R, d] BF16");
@@ -725,8 +740,8 @@ moe_status_t moe_backward(moe_plan_t p, const void* dy, const void* x, const moe
     // epilogue (one per routed row and 64 columns of I), held in the split-tile buffer,
     // which the weight gradients use only afterwards, and summed right after that
     // product; else (more partials than the buffer holds) from o and dy.
-    const int ds_slots = 4 * ((c.I + 255) / 256);
-    const bool fused_ds = (size_t)p->R * ds_slots * sizeof(float) <= kGemmPartBytes;
+    const int ds_slots = router_grad_slots(c.I);
+    const bool fused_ds = fused_router_grad(p->R, c.I);
     if (c.T > 0 && !fused_ds) {
         e = staged(p, MOE_STAGE_SCORE_GRAD, s, [&] {
             return launch_score_grad(static_cast<const uint16_t*>(dy), p->at<uint16_t>(p->off_o),
