@@ -525,12 +525,32 @@ def measure(args, workload):
     min_bytes["quant_t"] = 0.5 * (2.0 * R * (I + d) + (I + d) * ntok * 33.0 / 32
                                   + 2.0 * R * (d + 2 * I) + (d + 2 * I) * ntok * 33.0 / 32)
     mfma_peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    # The weight gradients write an output the size of the expert weights (E*2I*d BF16 for
+    # W13), which can outweigh their products: algorithmic bytes = the gradient written
+    # once (and read once when accumulated) + both operands read once (BF16, or E4M3 codes
+    # with one E8M0 scale per 32).
+    eb = (1.0 + 1.0 / 32) if mx else 2.0
+    acc_rw = 2.0 if args.wgrad_accumulate else 1.0
+    gemm_bytes = {"wgrad_w2": acc_rw * 2.0 * E * d * I + eb * R * (d + I),
+                  "wgrad_w13": acc_rw * 2.0 * E * 2 * I * d + eb * R * (2 * I + d)}
     if dom in gemm_flop:
         achieved = gemm_flop[dom] / (stage_us[dom] * 1e-6) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": achieved / mfma_peak,
-                "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
-                "traffic": traffic_for(dom, workload)}
+        nb = gemm_bytes.get(dom)
+        t_mfma = gemm_flop[dom] / (mfma_peak * 1e12)
+        if nb is not None and nb / (PEAK_HBM_GBS * 1e9) > t_mfma:
+            # bytes bind: the HBM roofline, with the MFMA fraction beside it
+            bach = nb / (stage_us[dom] * 1e-6) / 1e9
+            roof = {"bound": "hbm", "kernel": dom, "achieved": bach, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": bach / PEAK_HBM_GBS,
+                    "algorithmic_per_launch": nb, "avg_launch_us": stage_us[dom],
+                    "traffic": traffic_for(dom, workload),
+                    "mfma": {"achieved": achieved, "peak": mfma_peak, "unit": "TFLOP/s",
+                             "frac": achieved / mfma_peak}}
+        else:
+            roof = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": mfma_peak,
+                    "unit": "TFLOP/s", "frac": achieved / mfma_peak,
+                    "algorithmic_per_launch": gemm_flop[dom], "avg_launch_us": stage_us[dom],
+                    "traffic": traffic_for(dom, workload)}
     else:
         nbytes = min_bytes.get(dom, float("nan"))
         achieved = nbytes / (stage_us[dom] * 1e-6) / 1e9
